@@ -1,0 +1,295 @@
+"""CPU oracle for the MoE expert-parallel layout / dispatch / combine core.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``, never by the library.  The
+arithmetic lives in ``oracle.c`` (plain C, one definition per function, each
+citing the passage of the pages it writes out); this module only builds that
+file with gcc and marshals numpy arrays into it.  It imports nothing from the
+HIP library and the library imports nothing from here.
+
+Pages cited (titles as published):
+  [Ch4]  "Chapter 4  V1: layout, dispatch and combine", sections 4.1-4.5
+  [NvLL] "DeepEP Normal vs Low-Latency dual-mode analysis"
+  [Phil] "Normal vs Low-Latency: two communication philosophies in DeepEP V1 / V2 / DeepGEMM"
+
+Pins (CPU tests, ``tests/test_oracle_*.py``): an independent pure-Python brute
+force on tiny inputs, invariants fixed by the pages (per-expert counts sum to
+the valid top-k entries; identity dispatch + combine divided by the number of
+receiving ranks returns the input; the expected-ranks closed form of [NvLL]
+V2 SM-count model), exhaustive nearest-value search for the E4M3 and bf16
+encoders, and library casts (numpy fp32 division, torch float8/bf16 casts).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+X_BF16, X_FP8, X_BF16_CAST_FP8 = 0, 1, 2
+FP8_GROUP = 128
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` with gcc into ``liboracle.so`` (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fno-fast-math", "-ffp-contract=off",
+                               "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB)
+        _declare(_lib)
+    return _lib
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+
+
+def _declare(lib):
+    lib.oracle_layout.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+    lib.oracle_layout.restype = _I
+    lib.oracle_dispatch.argtypes = [_I] * 8 + [_I, _P, _P, _I, _P, _P, _P, _P, _I64] + [_P] * 11
+    lib.oracle_dispatch.restype = _I
+    lib.oracle_cached_dispatch.argtypes = [_I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I64, _P, _P]
+    lib.oracle_cached_dispatch.restype = _I
+    lib.oracle_combine.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _P, _P, _P, _P]
+    lib.oracle_combine.restype = _I
+    lib.oracle_fp8_quantize.argtypes = [_I64, _I, _P, _I, _P, _P, _P]
+    lib.oracle_fp8_quantize.restype = _I
+    lib.oracle_ll_msg_bytes.argtypes = [_I, _I]
+    lib.oracle_ll_msg_bytes.restype = _I64
+    lib.oracle_ll_dispatch.argtypes = [_I] * 8 + [_P, _P, _I, _I, _I] + [_P] * 9
+    lib.oracle_ll_dispatch.restype = _I
+    lib.oracle_e4m3_encode_n.argtypes = [_I64, _P, _P]
+    lib.oracle_e4m3_decode_n.argtypes = [_I64, _P, _P]
+    lib.oracle_bf16_round_n.argtypes = [_I64, _P, _P]
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous numpy arrays"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments" % what)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------- scalars
+def e4m3_encode(a: np.ndarray) -> np.ndarray:
+    a = _c(a, np.float32).reshape(-1)
+    out = np.empty(a.shape, np.uint8)
+    _load().oracle_e4m3_encode_n(a.size, _ptr(a), _ptr(out))
+    return out
+
+
+def e4m3_decode(c: np.ndarray) -> np.ndarray:
+    c = _c(c, np.uint8).reshape(-1)
+    out = np.empty(c.shape, np.float32)
+    _load().oracle_e4m3_decode_n(c.size, _ptr(c), _ptr(out))
+    return out
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    a = _c(a, np.float32).reshape(-1)
+    out = np.empty(a.shape, np.uint16)
+    _load().oracle_bf16_round_n(a.size, _ptr(a), _ptr(out))
+    return out
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    return (_c(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def fp8_quantize(x_bf16: np.ndarray, round_scale: bool):
+    """x_bf16: uint16 [rows][H] -> (codes u8 [rows][H], scale_inv f32 [rows][H/128], ue8m0 u8 or None)."""
+    x = _c(x_bf16, np.uint16)
+    rows, H = x.shape
+    codes = np.empty((rows, H), np.uint8)
+    sci = np.empty((rows, H // FP8_GROUP), np.float32)
+    ue = np.empty((rows, H // FP8_GROUP), np.uint8) if round_scale else None
+    _check(_load().oracle_fp8_quantize(rows, H, _ptr(x), int(round_scale), _ptr(codes), _ptr(sci), _ptr(ue)),
+           "fp8_quantize")
+    return codes, sci, ue
+
+
+# --------------------------------------------------------------------------- O1
+def layout(topk_idx: np.ndarray, S: int, E: int, R: int) -> dict:
+    """topk_idx int64 [S*T][K] -> per-rank / per-RDMA-rank / per-expert counts and is_token_in_rank."""
+    idx = _c(topk_idx, np.int64)
+    N, K = idx.shape
+    assert S > 0 and N % S == 0
+    T = N // S
+    ntpr = np.empty((S, R), np.int32)
+    ntp_rdma = np.empty((S, R // 8), np.int32) if R > 8 else None
+    ntpe = np.empty((S, E), np.int32)
+    in_rank = np.empty((N, R), np.uint8)
+    _check(_load().oracle_layout(S, T, K, E, R, _ptr(idx), _ptr(ntpr), _ptr(ntp_rdma), _ptr(ntpe), _ptr(in_rank)),
+           "layout")
+    return dict(num_tokens_per_rank=ntpr, num_tokens_per_rdma_rank=ntp_rdma, num_tokens_per_expert=ntpe,
+                is_token_in_rank=in_rank)
+
+
+# --------------------------------------------------------------------------- O2 + O3
+def dispatch(x: np.ndarray, topk_idx, topk_weights, is_token_in_rank: np.ndarray, num_tokens_per_expert,
+             S: int, E: int, R: int, C: int, expert_alignment: int = 1, x_kind: int = X_BF16,
+             x_scales=None, round_scale: bool = False, capacity: int | None = None) -> dict:
+    """Normal-mode dispatch.  x: uint16 bf16 bits [N][H] (kinds 0, 2) or uint8 codes [N][H] (kind 1)."""
+    in_rank = _c(is_token_in_rank, np.uint8)
+    N, R_ = in_rank.shape
+    assert R_ == R and N % S == 0
+    T = N // S
+    H = x.shape[1]
+    x = _c(x, np.uint8 if x_kind == X_FP8 else np.uint16)
+    K = topk_idx.shape[1] if topk_idx is not None else 0
+    idx = _c(topk_idx, np.int64) if topk_idx is not None else None
+    w = _c(topk_weights, np.float32) if topk_weights is not None else None
+    ntpe = _c(num_tokens_per_expert, np.int32) if num_tokens_per_expert is not None else None
+    xs = _c(x_scales, np.float32) if x_scales is not None else None
+    total = int(in_rank.astype(np.int64).sum())
+    cap = total if capacity is None else int(capacity)
+    G = H // FP8_GROUP
+    L = E // R
+    if x_kind == X_BF16:
+        recv_x = np.zeros((cap, H), np.uint16)
+        recv_sc = None
+    else:
+        recv_x = np.zeros((cap, H), np.uint8)
+        recv_sc = np.zeros((cap, G), np.float32)
+    recv_src = np.full((cap,), -1, np.int32)
+    recv_idx = np.full((cap, K), -1, np.int64) if idx is not None else None
+    recv_w = np.zeros((cap, K), np.float32) if (idx is not None and w is not None) else None
+    nrte = np.zeros((R, L), np.int32) if ntpe is not None else None
+    rpm = np.empty((S, R), np.int32)
+    cpm = np.empty((S, R, C), np.int32)
+    rcpm = np.empty((R, S, C), np.int32)
+    off = np.empty((R + 1,), np.int32)
+    send_head = np.empty((N, R), np.int32)
+    _check(_load().oracle_dispatch(S, T, H, K, E, R, C, expert_alignment, x_kind, _ptr(x), _ptr(xs),
+                                   int(round_scale), _ptr(idx), _ptr(w), _ptr(in_rank), _ptr(ntpe), cap,
+                                   _ptr(recv_x), _ptr(recv_sc), _ptr(recv_src), _ptr(recv_idx), _ptr(recv_w),
+                                   _ptr(nrte), _ptr(rpm), _ptr(cpm), _ptr(rcpm), _ptr(off), _ptr(send_head)),
+           "dispatch")
+    return dict(recv_x=recv_x, recv_x_scales=recv_sc, recv_src_idx=recv_src, recv_topk_idx=recv_idx,
+                recv_topk_weights=recv_w, num_recv_tokens_per_expert=nrte, rank_prefix_matrix=rpm,
+                channel_prefix_matrix=cpm, recv_channel_prefix_matrix=rcpm, recv_rank_offset=off,
+                send_head=send_head, num_recv=int(off[R]))
+
+
+# --------------------------------------------------------------------------- O5
+def cached_dispatch(x: np.ndarray, send_head: np.ndarray, recv_rank_offset: np.ndarray, S: int, capacity: int,
+                    x_kind: int = X_BF16, x_scales=None, round_scale: bool = False) -> dict:
+    sh = _c(send_head, np.int32)
+    off = _c(recv_rank_offset, np.int32)
+    N, R = sh.shape
+    T = N // S
+    H = x.shape[1]
+    x = _c(x, np.uint8 if x_kind == X_FP8 else np.uint16)
+    xs = _c(x_scales, np.float32) if x_scales is not None else None
+    G = H // FP8_GROUP
+    if x_kind == X_BF16:
+        recv_x = np.zeros((capacity, H), np.uint16)
+        recv_sc = None
+    else:
+        recv_x = np.zeros((capacity, H), np.uint8)
+        recv_sc = np.zeros((capacity, G), np.float32)
+    _check(_load().oracle_cached_dispatch(S, T, H, R, x_kind, _ptr(x), _ptr(xs), int(round_scale), _ptr(sh),
+                                          _ptr(off), capacity, _ptr(recv_x), _ptr(recv_sc)), "cached_dispatch")
+    return dict(recv_x=recv_x, recv_x_scales=recv_sc)
+
+
+# --------------------------------------------------------------------------- O4
+def combine(y: np.ndarray, recv_topk_weights, send_head: np.ndarray, recv_rank_offset: np.ndarray, S: int,
+            K: int = 0, want_f64: bool = False, want_f32: bool = False) -> dict:
+    """y: uint16 bf16 bits [capacity][H] in the receive layout."""
+    y = _c(y, np.uint16)
+    cap, H = y.shape
+    sh = _c(send_head, np.int32)
+    off = _c(recv_rank_offset, np.int32)
+    N, R = sh.shape
+    T = N // S
+    w = _c(recv_topk_weights, np.float32) if recv_topk_weights is not None else None
+    if w is not None:
+        K = w.shape[1]
+    out = np.empty((N, H), np.uint16)
+    out_w = np.empty((N, K), np.float32) if w is not None else None
+    out32 = np.empty((N, H), np.float32) if want_f32 else None
+    out64 = np.empty((N, H), np.float64) if want_f64 else None
+    _check(_load().oracle_combine(S, T, H, K, R, _ptr(y), _ptr(w), _ptr(sh), _ptr(off), cap, _ptr(out), _ptr(out_w),
+                                  _ptr(out32), _ptr(out64)), "combine")
+    return dict(combined_x=out, combined_topk_weights=out_w, combined_f32=out32, combined_f64=out64)
+
+
+# --------------------------------------------------------------------------- O7 + O8
+def ll_msg_bytes(H: int, use_fp8: bool) -> int:
+    return int(_load().oracle_ll_msg_bytes(H, int(use_fp8)))
+
+
+def ll_dispatch(x: np.ndarray, topk_idx: np.ndarray, S: int, M: int, E: int, R: int, dest_rank: int,
+                use_fp8: bool, round_scale: bool = False, use_ue8m0: bool = False,
+                cumulative_stats: np.ndarray | None = None) -> dict:
+    """Low-latency dispatch seen from rank ``dest_rank``.  x: uint16 bf16 bits [S*T][H]."""
+    x = _c(x, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    N, H = x.shape
+    K = idx.shape[1]
+    T = N // S
+    L = E // R
+    G = H // FP8_GROUP
+    mb = ll_msg_bytes(H, use_fp8)
+    msg = np.zeros((L, S, M, mb), np.uint8)
+    cnt = np.zeros((L, S), np.int32)
+    if use_fp8:
+        prx = np.zeros((L, S * M, H), np.uint8)
+        prs = np.zeros((L, S * M, G), np.float32)
+        pue = np.zeros((L, S * M, G), np.uint8) if use_ue8m0 else None
+    else:
+        prx = np.zeros((L, S * M, H), np.uint16)
+        prs = None
+        pue = None
+    src = np.full((L, S * M), -1, np.int32)
+    lr = np.zeros((L, S), np.int64)
+    pc = np.zeros((L,), np.int32)
+    cs = _c(cumulative_stats, np.int32).copy() if cumulative_stats is not None else None
+    _check(_load().oracle_ll_dispatch(S, T, M, H, K, E, R, dest_rank, _ptr(x), _ptr(idx), int(use_fp8),
+                                      int(round_scale), int(use_ue8m0), _ptr(msg), _ptr(cnt), _ptr(prx), _ptr(prs),
+                                      _ptr(pue), _ptr(src), _ptr(lr), _ptr(pc), _ptr(cs)), "ll_dispatch")
+    return dict(msg_buf=msg, msg_count=cnt, packed_recv_x=prx, packed_recv_x_scales=prs,
+                packed_recv_x_scales_ue8m0=pue, packed_recv_src_info=src, packed_recv_layout_range=lr,
+                packed_recv_count=pc, cumulative_local_expert_recv_stats=cs)
+
+
+def calc_diff(x: np.ndarray, y: np.ndarray) -> float:
+    """1 - 2*sum(x*y) / sum(x^2 + y^2) in float64: 0 iff x == y ([Ch4] 4.4 uses a
+    difference measure of this name with a 5e-6 bar; the pages do not define it,
+    this is our reading)."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    den = float((x * x + y * y).sum())
+    if den == 0.0:
+        return 0.0
+    return 1.0 - 2.0 * float((x * y).sum()) / den

@@ -1,0 +1,320 @@
+"""Pins for the oracle's layout (O1), notify/dispatch (O2, O3), cached dispatch
+(O5) and combine (O4).
+
+Each oracle result is checked against (a) the independent pure-Python brute
+force on small shapes, edge cases included, (b) invariants fixed by the pages
+on full-size inputs, and (c) a hand-worked example.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+from combine_get_dispatch_histogram_amd import workloads as wl
+
+
+def _rand_topk(rng, N, E, K, mask_p=0.0, dup_p=0.0):
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(N)]) if N else np.zeros((0, K), np.int64)
+    idx = idx.astype(np.int64)
+    if N and dup_p > 0 and K > 1:
+        d = rng.random(N) < dup_p
+        idx[d, 1] = idx[d, 0]                          # a duplicated expert in one token's top-k
+    if N and mask_p > 0:
+        idx[rng.random((N, K)) < mask_p] = -1
+    return idx
+
+
+SMALL = [
+    # S, T, E, R, K, C
+    (1, 1, 4, 1, 1, 1),
+    (1, 7, 8, 2, 2, 3),
+    (2, 5, 8, 4, 2, 24),      # more channels than tokens: empty channels
+    (4, 32, 16, 4, 4, 24),    # the tiny workload's shape
+    (3, 9, 12, 3, 3, 4),      # R not a power of two
+    (2, 6, 32, 16, 4, 5),     # R > 8: two RDMA groups
+    (1, 13, 128, 64, 8, 7),   # R = 64
+    (2, 0, 8, 2, 2, 3),       # no tokens at all
+]
+
+
+@pytest.mark.parametrize("shape", SMALL)
+@pytest.mark.parametrize("mask_p,dup_p", [(0.0, 0.0), (0.3, 0.0), (0.2, 0.3), (1.0, 0.0)])
+def test_layout_matches_brute(orc, shape, mask_p, dup_p):
+    S, T, E, R, K, C = shape
+    rng = np.random.default_rng(hash((shape, mask_p, dup_p)) % 2 ** 32)
+    idx = _rand_topk(rng, S * T, E, K, mask_p, dup_p)
+    got = orc.layout(idx, S, E, R)
+    want = brute.layout(idx, S, E, R)
+    assert got["num_tokens_per_rank"].tolist() == want["num_tokens_per_rank"]
+    assert got["num_tokens_per_expert"].tolist() == want["num_tokens_per_expert"]
+    assert got["is_token_in_rank"].tolist() == (want["is_token_in_rank"] or np.zeros((0, R), int).tolist())
+    if R > 8:
+        assert got["num_tokens_per_rdma_rank"].tolist() == want["num_tokens_per_rdma_rank"]
+    else:
+        assert got["num_tokens_per_rdma_rank"] is None
+
+
+def test_layout_out_of_range_experts_ignored(orc):
+    idx = np.array([[0, 7, 8, -3], [100, -1, 3, 3]], np.int64)    # E = 8: 8 and 100 are outside
+    got = orc.layout(idx, 1, 8, 2)
+    assert got["num_tokens_per_expert"].tolist() == [[1, 0, 0, 2, 0, 0, 0, 1]]
+    assert got["is_token_in_rank"].tolist() == [[1, 1], [1, 0]]
+    assert got["num_tokens_per_rank"].tolist() == [[2, 1]]
+
+
+def test_layout_rejects_bad_shapes(orc):
+    idx = np.zeros((4, 2), np.int64)
+    with pytest.raises(ValueError):
+        orc.layout(idx, 1, 10, 4)      # E % R != 0
+    with pytest.raises(ValueError):
+        orc.layout(idx, 1, 120, 12)    # R > 8 but not a multiple of 8
+
+
+def test_layout_hand_example(orc):
+    """Hand-worked: 2 sources x 2 tokens, E = 8 experts on R = 4 ranks (2 each), K = 3.
+    s0 t0 -> experts {0, 1, 5}: ranks {0, 2};  s0 t1 -> {7, -1, 6}: rank {3}
+    s1 t0 -> {2, 3, 4}: ranks {1, 2};          s1 t1 -> {-1, -1, -1}: none."""
+    idx = np.array([[0, 1, 5], [7, -1, 6], [2, 3, 4], [-1, -1, -1]], np.int64)
+    got = orc.layout(idx, 2, 8, 4)
+    assert got["is_token_in_rank"].tolist() == [[1, 0, 1, 0], [0, 0, 0, 1], [0, 1, 1, 0], [0, 0, 0, 0]]
+    assert got["num_tokens_per_rank"].tolist() == [[1, 0, 1, 1], [0, 1, 1, 0]]
+    assert got["num_tokens_per_expert"].tolist() == [[1, 1, 0, 0, 0, 1, 1, 1], [0, 0, 1, 1, 1, 0, 0, 0]]
+    # dispatch with C = 2 channels of 1 token: rank 2 receives (s0,t0) then (s1,t0)
+    x = np.arange(4 * 8, dtype=np.uint16).reshape(4, 8)
+    d = orc.dispatch(x, idx, np.full((4, 3), 0.25, np.float32), got["is_token_in_rank"],
+                     got["num_tokens_per_expert"], S=2, E=8, R=4, C=2)
+    assert d["recv_rank_offset"].tolist() == [0, 1, 2, 4, 5]
+    assert d["recv_src_idx"].tolist() == [0, 0, 0, 0, 1]
+    assert d["recv_x"][:, 0].tolist() == [0, 16, 0, 16, 8]
+    assert d["send_head"].tolist() == [[0, -1, 0, -1], [-1, -1, -1, 0], [-1, 0, 1, -1], [-1, -1, -1, -1]]
+    assert d["rank_prefix_matrix"].tolist() == [[1, 0, 1, 1], [1, 1, 2, 1]]
+    assert d["channel_prefix_matrix"][0].tolist() == [[1, 1], [0, 0], [1, 1], [0, 1]]
+    assert d["recv_channel_prefix_matrix"][2].tolist() == [[1, 1], [2, 2]]
+    # rank 2's rows hold local expert ids (expert - 2*2) or -1, weights or 0
+    assert d["recv_topk_idx"][2:4].tolist() == [[-1, -1, 1], [-1, -1, 0]]
+    assert d["recv_topk_weights"][2:4].tolist() == [[0, 0, 0.25], [0, 0, 0.25]]
+    assert d["num_recv_tokens_per_expert"].tolist() == [[1, 1], [1, 1], [1, 1], [1, 1]]
+
+
+@pytest.mark.parametrize("shape", SMALL)
+@pytest.mark.parametrize("mask_p,dup_p", [(0.0, 0.0), (0.25, 0.25)])
+def test_dispatch_matches_brute(orc, shape, mask_p, dup_p):
+    S, T, E, R, K, C = shape
+    H = 16
+    rng = np.random.default_rng(hash((shape, mask_p, dup_p, "d")) % 2 ** 32)
+    idx = _rand_topk(rng, S * T, E, K, mask_p, dup_p)
+    w = rng.random((S * T, K)).astype(np.float32)
+    x = rng.integers(0, 65535, (S * T, H), dtype=np.uint16)
+    lay = orc.layout(idx, S, E, R)
+    align = 4
+    d = orc.dispatch(x, idx, w, lay["is_token_in_rank"], lay["num_tokens_per_expert"], S=S, E=E, R=R, C=C,
+                     expert_alignment=align)
+    received, cpm, rpm, rcpm = brute.dispatch_plan(lay["is_token_in_rank"], S, C)
+    assert np.array_equal(d["channel_prefix_matrix"], cpm)
+    assert np.array_equal(d["rank_prefix_matrix"], rpm)
+    assert np.array_equal(d["recv_channel_prefix_matrix"], rcpm)
+    T_ = T
+    L = E // R
+    row = 0
+    for r in range(R):
+        assert d["recv_rank_offset"][r] == row
+        for j, (s, t) in enumerate(received[r]):
+            g = row + j
+            assert d["recv_src_idx"][g] == t
+            assert np.array_equal(d["recv_x"][g], x[s * T_ + t])
+            assert d["send_head"][s * T_ + t, r] == j
+            for k in range(K):
+                e = idx[s * T_ + t, k]
+                mine = 0 <= e < E and e // L == r
+                assert d["recv_topk_idx"][g, k] == (e - r * L if mine else -1)
+                assert d["recv_topk_weights"][g, k] == (w[s * T_ + t, k] if mine else 0.0)
+        row += len(received[r])
+    assert d["recv_rank_offset"][R] == row
+    for (n, r) in itertools.product(range(S * T), range(R)):
+        if not lay["is_token_in_rank"][n, r]:
+            assert d["send_head"][n, r] == -1
+    counts = np.zeros((R, L), np.int64)
+    for e in idx[(idx >= 0) & (idx < E)].tolist():
+        counts[e // L, e % L] += 1
+    assert np.array_equal(d["num_recv_tokens_per_expert"], -(-counts // align) * align)
+
+
+def test_dispatch_capacity_bound(orc):
+    """Rows past the capacity are not written; the true total is still reported."""
+    rng = np.random.default_rng(7)
+    S, T, E, R, K = 2, 10, 8, 4, 3
+    idx = _rand_topk(rng, S * T, E, K)
+    lay = orc.layout(idx, S, E, R)
+    x = rng.integers(0, 65535, (S * T, 8), dtype=np.uint16)
+    full = orc.dispatch(x, idx, None, lay["is_token_in_rank"], None, S=S, E=E, R=R, C=3)
+    cap = full["num_recv"] // 2
+    part = orc.dispatch(x, idx, None, lay["is_token_in_rank"], None, S=S, E=E, R=R, C=3, capacity=cap)
+    assert part["recv_rank_offset"][R] == full["num_recv"]
+    assert np.array_equal(part["recv_x"], full["recv_x"][:cap])
+    assert np.array_equal(part["send_head"], full["send_head"])
+
+
+def _normal_case(orc, w, seed=0):
+    inp = wl.normal_inputs(w, seed)
+    idx = inp["topk_idx"].numpy()
+    lay = orc.layout(idx, w.S, w.E, w.R)
+    return inp, idx, lay
+
+
+def test_layout_invariants_full_size(orc):
+    w = wl.NORMAL
+    inp, idx, lay = _normal_case(orc, w)
+    ntpe, ntpr, itr = lay["num_tokens_per_expert"], lay["num_tokens_per_rank"], lay["is_token_in_rank"]
+    # per-expert counts sum to the number of valid (non-negative) top-k entries, per source
+    assert np.array_equal(ntpe.sum(axis=1), (idx >= 0).reshape(w.S, w.T * w.K).sum(axis=1))
+    assert np.array_equal(ntpr, itr.reshape(w.S, w.T, w.R).sum(axis=1))
+    # the receive volume matches the expected-ranks closed form of the V2 SM-count model
+    rho = itr.sum(axis=1).mean()
+    expect = brute.expected_groups_hit(w.E, w.K, w.R)
+    sd = itr.sum(axis=1).std() / math.sqrt(w.N)
+    assert abs(rho - expect) < 5 * sd, (rho, expect)
+    assert abs(expect - 5.2947) < 1e-4
+
+
+def test_layout_rdma_invariants_large(orc):
+    w = wl.LARGE
+    g = torch.Generator().manual_seed(0)
+    idx = wl.topk_uniform(w.N, w.E, w.K, g).numpy()
+    lay = orc.layout(idx, w.S, w.E, w.R)
+    ntpr, rdma, itr = lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"], lay["is_token_in_rank"]
+    grp = ntpr.reshape(w.S, w.R // 8, 8)
+    assert np.all(grp.max(axis=2) <= rdma) and np.all(rdma <= np.minimum(w.T, grp.sum(axis=2)))
+    hit = itr.reshape(w.N, w.R // 8, 8).any(axis=2)
+    assert np.array_equal(rdma, hit.reshape(w.S, w.T, -1).sum(axis=1))
+    assert abs(hit.sum(axis=1).mean() - brute.expected_groups_hit(w.E, w.K, w.R // 8)) < 0.02
+    assert abs(itr.sum(axis=1).mean() - brute.expected_groups_hit(w.E, w.K, w.R)) < 0.02
+
+
+@pytest.mark.parametrize("wname", ["tiny", "normal"])
+def test_dispatch_combine_identity_roundtrip(orc, wname):
+    """Combining an identity-expert dispatch and dividing by the number of ranks
+    that received each token returns the input (Ch.4 section 4.4 test contract,
+    calc_diff < 5e-6); the reduced weights return topk_weights exactly."""
+    w = wl.WORKLOADS[wname]
+    inp, idx, lay = _normal_case(orc, w)
+    x = wl.bf16_bits(inp["x"])
+    wts = inp["topk_weights"].numpy()
+    d = orc.dispatch(x, idx, wts, lay["is_token_in_rank"], lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R,
+                     C=w.C)
+    # self-verifying placement: every row equals the row it names
+    off = d["recv_rank_offset"]
+    rpm = d["rank_prefix_matrix"]
+    for r in range(w.R):
+        rows = np.arange(off[r], off[r + 1])
+        j = rows - off[r]
+        src = np.searchsorted(rpm[:, r], j, side="right")
+        n = src * w.T + d["recv_src_idx"][rows]
+        assert np.array_equal(d["recv_x"][rows], x[n])
+        assert np.array_equal(d["send_head"][n, r], j)
+        assert np.all(np.diff(n) > 0)                      # sorted by (source, token)
+    c = orc.combine(d["recv_x"], d["recv_topk_weights"], d["send_head"], off, S=w.S, want_f64=True)
+    cnt = lay["is_token_in_rank"].sum(axis=1).astype(np.float64)
+    xf = orc.bf16_to_f32(x).reshape(x.shape).astype(np.float64)
+    got = orc.bf16_to_f32(c["combined_x"]).reshape(x.shape).astype(np.float64)
+    ok = cnt > 0
+    assert orc.calc_diff(got[ok] / cnt[ok, None], xf[ok]) < 5e-6
+    assert np.all(got[~ok] == 0)
+    # the fp64 sum of c identical rows is exactly c*x
+    assert np.array_equal(c["combined_f64"][ok], xf[ok] * cnt[ok, None])
+    valid = idx >= 0
+    assert np.array_equal(c["combined_topk_weights"][valid & ok[:, None]], wts[valid & ok[:, None]])
+    assert np.all(c["combined_topk_weights"][~valid] == 0)
+
+
+def test_combine_matches_brute_random(orc):
+    rng = np.random.default_rng(11)
+    S, T, E, R, K, C, H = 3, 7, 12, 6, 3, 2, 24
+    idx = _rand_topk(rng, S * T, E, K, 0.2)
+    lay = orc.layout(idx, S, E, R)
+    x = np.zeros((S * T, H), np.uint16)
+    d = orc.dispatch(x, idx, rng.random((S * T, K)).astype(np.float32), lay["is_token_in_rank"], None, S=S, E=E,
+                     R=R, C=C)
+    yf = (rng.standard_normal((d["num_recv"], H)) * rng.choice([1e-3, 1, 1e3], (d["num_recv"], 1))).astype(
+        np.float32)
+    yf[0, :3] = -0.0
+    y = brute.bf16_round_lib(yf).reshape(yf.shape)
+    c = orc.combine(y, d["recv_topk_weights"], d["send_head"], d["recv_rank_offset"], S=S, want_f64=True)
+    for n in range(S * T):
+        rows = [d["recv_rank_offset"][r] + d["send_head"][n, r] for r in range(R) if d["send_head"][n, r] >= 0]
+        for h in range(H):
+            acc = brute.combine_token([brute.bf16_value(int(y[g, h])) for g in rows])
+            want = 0 if acc is None else int(brute.bf16_round_lib(np.array([acc], np.float32))[0])
+            assert c["combined_x"][n, h] == want, (n, h)
+        for k in range(K):
+            acc = brute.combine_token([d["recv_topk_weights"][g, k] for g in rows])
+            assert c["combined_topk_weights"][n, k] == (0.0 if acc is None else acc)
+
+
+def test_combine_accuracy_vs_fp64(orc):
+    """Random expert outputs: the fp32 sum is within the textbook summation
+    bound (n-1) 2^-24 sum|y| of the exact sum, the bf16 output is the fp32 sum
+    rounded once (relative 2^-8), so the max relative error against the fp32
+    reference is < 1e-2."""
+    w = wl.NORMAL
+    inp, idx, lay = _normal_case(orc, w)
+    x = np.zeros((w.N, 8), np.uint16)
+    d = orc.dispatch(x, idx, None, lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R, C=w.C)
+    H = 256
+    y = wl.bf16_bits(wl.expert_outputs(d["num_recv"], H, seed=1))
+    c = orc.combine(y, None, d["send_head"], d["recv_rank_offset"], S=w.S, want_f64=True, want_f32=True)
+    absum = orc.combine(y & np.uint16(0x7FFF), None, d["send_head"], d["recv_rank_offset"], S=w.S,
+                        want_f64=True)["combined_f64"]
+    n = lay["is_token_in_rank"].sum(axis=1).astype(np.float64)[:, None]
+    f32 = c["combined_f32"].astype(np.float64)
+    exact = c["combined_f64"]
+    assert np.all(np.abs(f32 - exact) <= np.maximum(n - 1, 0) * 2.0 ** -24 * absum)
+    got = orc.bf16_to_f32(c["combined_x"]).reshape(w.N, H).astype(np.float64)
+    assert np.all(np.abs(got - f32) <= 2.0 ** -8 * np.abs(f32))
+    rel = np.abs(got - f32) / np.maximum(np.abs(f32), 1e-6)
+    assert rel.max() < 1e-2
+
+
+def test_cached_dispatch_equals_fresh(orc):
+    w = wl.TINY
+    inp, idx, lay = _normal_case(orc, w)
+    x = wl.bf16_bits(inp["x"])
+    d = orc.dispatch(x, idx, inp["topk_weights"].numpy(), lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R,
+                     C=w.C)
+    x2 = wl.bf16_bits(wl.activations(w.N, w.H, torch.Generator().manual_seed(5)))
+    fresh = orc.dispatch(x2, idx, None, lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R, C=w.C)
+    cached = orc.cached_dispatch(x2, d["send_head"], d["recv_rank_offset"], S=w.S, capacity=d["num_recv"])
+    assert np.array_equal(cached["recv_x"], fresh["recv_x"])
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_dispatch_fp8_kinds(orc, round_scale):
+    """Fused-cast dispatch == quantise then dispatch the codes; combine of the
+    dequantised identity experts returns the dequantised input."""
+    w = wl.NormalWorkload("t", S=4, T=16, H=256, E=32, R=16, K=4, C=5)
+    inp, idx, lay = _normal_case(orc, w)
+    x = wl.bf16_bits(inp["x"])
+    codes, sci, _ = orc.fp8_quantize(x, round_scale)
+    a = orc.dispatch(x, idx, None, lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R, C=w.C,
+                     x_kind=orc.X_BF16_CAST_FP8, round_scale=round_scale)
+    b = orc.dispatch(codes, idx, None, lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R, C=w.C,
+                     x_kind=orc.X_FP8, x_scales=sci)
+    assert np.array_equal(a["recv_x"], b["recv_x"]) and np.array_equal(a["recv_x_scales"], b["recv_x_scales"])
+    deq = orc.e4m3_decode(a["recv_x"]).reshape(a["recv_x"].shape) * np.repeat(a["recv_x_scales"], 128, axis=1)
+    y = brute.bf16_round_lib(deq).reshape(deq.shape)
+    c = orc.combine(y, None, a["send_head"], a["recv_rank_offset"], S=w.S)
+    ref = orc.e4m3_decode(codes).reshape(codes.shape) * np.repeat(sci, 128, axis=1)
+    ref = orc.bf16_to_f32(brute.bf16_round_lib(ref)).reshape(ref.shape).astype(np.float64)
+    cnt = lay["is_token_in_rank"].sum(axis=1).astype(np.float64)
+    got = orc.bf16_to_f32(c["combined_x"]).reshape(ref.shape).astype(np.float64)
+    ok = cnt > 0
+    assert orc.calc_diff(got[ok] / cnt[ok, None], ref[ok]) < 5e-6
+
+
+def test_calc_diff_definition(orc):
+    x = np.array([1.0, -2.0, 3.0])
+    assert orc.calc_diff(x, x) == 0.0
+    assert orc.calc_diff(x, -x) == 2.0
+    assert abs(orc.calc_diff(x, 2 * x) - (1 - 4 / 5)) < 1e-15
