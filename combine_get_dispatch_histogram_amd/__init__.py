@@ -1,0 +1,372 @@
+"""miep -- MI355X-native MoE expert-parallel core: layout, dispatch, handle, combine.
+
+A thin Python face over ``libmiep.so`` (C ABI in ``include/miep.h``).  This
+module only checks tensor shapes / dtypes / devices, allocates outputs with
+PyTorch and passes raw device pointers plus the current HIP stream; every step
+of the computation runs in the library's gfx950 kernels.  There is no
+fallback: without the built library every call raises.
+
+Calls (the API surface of "Chapter 4  V1: layout, dispatch and combine",
+sections 4.1-4.3, for ranks that are partitions of one GPU):
+  get_dispatch_layout(topk_idx, num_experts, num_ranks)            section 4.1
+  dispatch(x, topk_idx, topk_weights, <layout>, ...) -> (..., handle)  4.1
+  cached_dispatch(x, handle)                                        4.1 (cached)
+  combine(y, handle, topk_weights)                                  4.2, 4.4
+  low_latency_dispatch(x, topk_idx, max_tokens, num_experts, dest_rank, ...)  4.3
+The ``*_into`` variants take preallocated outputs and allocate nothing.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # noqa: F401
+
+__all__ = ["Handle", "MiepError", "get_dispatch_layout", "dispatch", "dispatch_into", "cached_dispatch",
+           "cached_dispatch_into", "combine", "combine_into", "low_latency_dispatch", "low_latency_dispatch_into",
+           "ll_msg_bytes", "version"]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("miep expects device tensors")
+    if not t.is_contiguous():
+        raise ValueError("miep expects contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _want(t: Optional[torch.Tensor], name: str, dtype, shape=None):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def version() -> str:
+    return _lib.load().miep_version().decode()
+
+
+def ll_msg_bytes(hidden: int, use_fp8: bool) -> int:
+    return int(_lib.load().miep_ll_msg_bytes(hidden, int(bool(use_fp8))))
+
+
+# --------------------------------------------------------------------------- handle
+@dataclass
+class Handle:
+    """The reverse-routing record of a normal dispatch (section 4.2).
+
+    rank_prefix_matrix [S,R], channel_prefix_matrix [S,R,C],
+    recv_channel_prefix_matrix [R,S,C], recv_rank_offset [R+1] (last = total
+    rows), recv_src_idx [cap], is_token_in_rank [N,R] bool, send_head [N,R].
+    Rank r's rows are receive rows recv_rank_offset[r] .. recv_rank_offset[r+1].
+    """
+    rank_prefix_matrix: torch.Tensor
+    channel_prefix_matrix: torch.Tensor
+    recv_channel_prefix_matrix: torch.Tensor
+    recv_rank_offset: torch.Tensor
+    recv_src_idx: torch.Tensor
+    is_token_in_rank: torch.Tensor
+    send_head: torch.Tensor
+    num_src: int
+    num_tokens: int
+    num_topk: int
+    num_experts: int
+    num_ranks: int
+    num_channels: int
+
+    @property
+    def recv_capacity(self) -> int:
+        return self.recv_src_idx.numel()
+
+    @staticmethod
+    def allocate(is_token_in_rank: torch.Tensor, num_src: int, num_topk: int, num_experts: int, num_channels: int,
+                 capacity: int) -> "Handle":
+        N, R = is_token_in_rank.shape
+        S = num_src
+        dev = is_token_in_rank.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        return Handle(torch.empty((S, R), **i32), torch.empty((S, R, num_channels), **i32),
+                      torch.empty((R, S, num_channels), **i32), torch.empty((R + 1,), **i32),
+                      torch.empty((capacity,), **i32), is_token_in_rank, torch.empty((N, R), **i32), S,
+                      N // S if S else 0, num_topk, num_experts, R, num_channels)
+
+    def c(self) -> _lib.HandleC:
+        return _lib.HandleC(self.rank_prefix_matrix.data_ptr(), self.channel_prefix_matrix.data_ptr(),
+                            self.recv_channel_prefix_matrix.data_ptr(), self.recv_rank_offset.data_ptr(),
+                            self.recv_src_idx.data_ptr(), self.is_token_in_rank.data_ptr(),
+                            self.send_head.data_ptr(), self.recv_capacity)
+
+    def problem(self, hidden: int, expert_alignment: int = 1) -> _lib.Problem:
+        return _lib.Problem(self.num_src, self.num_tokens, hidden, self.num_topk, self.num_experts, self.num_ranks,
+                            self.num_channels, expert_alignment)
+
+
+def _x_kind(x: torch.Tensor, cast_to_fp8: bool) -> int:
+    if x.dtype == torch.bfloat16:
+        return X_BF16_CAST_FP8 if cast_to_fp8 else X_BF16
+    if x.dtype in (torch.float8_e4m3fn, torch.uint8):
+        if cast_to_fp8:
+            raise ValueError("x is already FP8")
+        return X_FP8
+    raise TypeError("x must be bf16 or float8_e4m3fn/uint8 codes, got %s" % x.dtype)
+
+
+# --------------------------------------------------------------------------- layout
+def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, num_src: Optional[int] = None):
+    """Per-rank, per-RDMA-rank, per-expert token counts and the token-in-rank matrix.
+
+    topk_idx [N, K] int64 on the GPU (negative = masked); the N tokens are
+    ``num_src`` (default: num_ranks) consecutive source partitions.  Returns
+    (num_tokens_per_rank [S,R] i32, num_tokens_per_rdma_rank [S,R/8] i32 or
+    None when R <= 8, num_tokens_per_expert [S,E] i32, is_token_in_rank [N,R] bool).
+    """
+    _want(topk_idx, "topk_idx", torch.int64)
+    N, K = topk_idx.shape
+    S = num_ranks if num_src is None else num_src
+    if S <= 0 or N % S:
+        raise ValueError("the %d tokens do not split into %d source partitions" % (N, S))
+    dev = topk_idx.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    ntpr = torch.empty((S, num_ranks), **i32)
+    ntp_rdma = torch.empty((S, num_ranks // 8), **i32) if num_ranks > 8 else None
+    ntpe = torch.empty((S, num_experts), **i32)
+    itr = torch.empty((N, num_ranks), dtype=torch.bool, device=dev)
+    p = _lib.Problem(S, N // S, 8, K, num_experts, num_ranks, 1, 1)
+    _lib.check(_lib.load().miep_get_dispatch_layout(ctypes.byref(p), _ptr(topk_idx), _ptr(ntpr), _ptr(ntp_rdma),
+                                                    _ptr(ntpe), _ptr(itr), _stream(topk_idx)))
+    return ntpr, ntp_rdma, ntpe, itr
+
+
+# --------------------------------------------------------------------------- dispatch
+def dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_expert, handle: Handle, recv_x,
+                  recv_x_scales=None, recv_topk_idx=None, recv_topk_weights=None, num_recv_tokens_per_expert=None,
+                  x_scales=None, cast_to_fp8: bool = False, round_scale: bool = False,
+                  expert_alignment: int = 1) -> None:
+    """Fresh dispatch into preallocated outputs (allocates nothing)."""
+    kind = _x_kind(x, cast_to_fp8)
+    _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
+    N, S, R, K = x.shape[0], handle.num_src, handle.num_ranks, handle.num_topk
+    _want(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (S, R))
+    _want(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (S, handle.num_experts))
+    _want(topk_idx, "topk_idx", torch.int64, (N, K))
+    _want(topk_weights, "topk_weights", torch.float32, (N, K))
+    _want(recv_topk_idx, "recv_topk_idx", torch.int64)
+    _want(recv_topk_weights, "recv_topk_weights", torch.float32)
+    _want(num_recv_tokens_per_expert, "num_recv_tokens_per_expert", torch.int32, (R, handle.num_experts // R))
+    for t, name in ((recv_topk_idx, "recv_topk_idx"), (recv_topk_weights, "recv_topk_weights")):
+        if t is not None and (t.dim() != 2 or t.shape[0] < handle.recv_capacity or t.shape[1] != K):
+            raise ValueError("%s must be [>= %d, %d]" % (name, handle.recv_capacity, K))
+    p = handle.problem(x.shape[1], expert_alignment)
+    h = handle.c()
+    _lib.check(_lib.load().miep_dispatch(ctypes.byref(p), _ptr(x), kind, _ptr(x_scales), int(round_scale),
+                                         _ptr(topk_idx), _ptr(topk_weights), _ptr(num_tokens_per_rank),
+                                         _ptr(num_tokens_per_expert), _ptr(recv_x), _ptr(recv_x_scales),
+                                         _ptr(recv_topk_idx), _ptr(recv_topk_weights),
+                                         _ptr(num_recv_tokens_per_expert), ctypes.byref(h), _stream(x)))
+
+
+def _check_payload_shapes(x, kind, x_scales, handle: Handle, recv_x, recv_x_scales):
+    N, H = x.shape
+    if N != handle.send_head.shape[0] or N != handle.num_src * handle.num_tokens:
+        raise ValueError("x has %d tokens, the handle %d" % (N, handle.send_head.shape[0]))
+    if recv_x.dim() != 2 or recv_x.shape[1] != H or recv_x.shape[0] < handle.recv_capacity:
+        raise ValueError("recv_x must be [>= %d, %d]" % (handle.recv_capacity, H))
+    if kind == X_BF16:
+        _want(recv_x, "recv_x", torch.bfloat16)
+    else:
+        if recv_x.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError("recv_x must hold E4M3 codes for an FP8 dispatch")
+        if recv_x_scales is None or tuple(recv_x_scales.shape[1:]) != (H // 128,) or \
+                recv_x_scales.shape[0] < handle.recv_capacity:
+            raise ValueError("recv_x_scales must be [>= %d, %d]" % (handle.recv_capacity, H // 128))
+        _want(recv_x_scales, "recv_x_scales", torch.float32)
+    if kind == X_FP8:
+        _want(x_scales, "x_scales", torch.float32, (N, H // 128))
+        if x_scales is None:
+            raise ValueError("x_scales are required for pre-quantised FP8 x")
+    if handle.is_token_in_rank.shape != (N, handle.num_ranks):
+        raise ValueError("handle.is_token_in_rank must be [%d, %d]" % (N, handle.num_ranks))
+
+
+def _recv_buffers(x, kind, cap, dev):
+    H = x.shape[1]
+    if kind == X_BF16:
+        return torch.empty((cap, H), dtype=torch.bfloat16, device=dev), None
+    codes = torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev)
+    return codes, torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
+
+
+def dispatch(x: torch.Tensor, topk_idx: Optional[torch.Tensor], topk_weights: Optional[torch.Tensor],
+             num_tokens_per_rank: torch.Tensor, is_token_in_rank: torch.Tensor,
+             num_tokens_per_expert: Optional[torch.Tensor], num_experts: int, num_channels: int = 24,
+             expert_alignment: int = 1, num_worst_tokens: int = 0, x_scales: Optional[torch.Tensor] = None,
+             cast_to_fp8: bool = False, round_scale: bool = False):
+    """Normal-mode dispatch (section 4.1, fresh branch).
+
+    Receive buffers are sized exactly from num_tokens_per_rank (one host
+    read, the CPU-sync mode) unless ``num_worst_tokens`` > 0 gives a fixed
+    capacity.  Returns (recv_x, recv_x_scales, recv_topk_idx,
+    recv_topk_weights, num_recv_tokens_per_expert [R, E/R], handle).
+    """
+    kind = _x_kind(x, cast_to_fp8)
+    N, H = x.shape
+    S, R = num_tokens_per_rank.shape
+    _want(is_token_in_rank, "is_token_in_rank", torch.bool, (N, R))
+    _want(num_tokens_per_rank, "num_tokens_per_rank", torch.int32)
+    _want(topk_idx, "topk_idx", torch.int64)
+    _want(topk_weights, "topk_weights", torch.float32)
+    K = topk_idx.shape[1] if topk_idx is not None else 1
+    cap = int(num_worst_tokens) if num_worst_tokens > 0 else int(num_tokens_per_rank.sum().item())
+    dev = x.device
+    handle = Handle.allocate(is_token_in_rank, S, K, num_experts, num_channels, cap)
+    recv_x, recv_x_scales = _recv_buffers(x, kind, cap, dev)
+    recv_topk_idx = torch.empty((cap, K), dtype=torch.int64, device=dev) if topk_idx is not None else None
+    recv_topk_weights = torch.empty((cap, K), dtype=torch.float32, device=dev) if topk_weights is not None else None
+    nrte = torch.empty((R, num_experts // R), dtype=torch.int32, device=dev) if num_tokens_per_expert is not None \
+        else None
+    dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_expert, handle, recv_x,
+                  recv_x_scales, recv_topk_idx, recv_topk_weights, nrte, x_scales, cast_to_fp8, round_scale,
+                  expert_alignment)
+    return recv_x, recv_x_scales, recv_topk_idx, recv_topk_weights, nrte, handle
+
+
+def cached_dispatch_into(x, handle: Handle, recv_x, recv_x_scales=None, x_scales=None, cast_to_fp8: bool = False,
+                         round_scale: bool = False) -> None:
+    kind = _x_kind(x, cast_to_fp8)
+    _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
+    p = handle.problem(x.shape[1])
+    h = handle.c()
+    _lib.check(_lib.load().miep_cached_dispatch(ctypes.byref(p), _ptr(x), kind, _ptr(x_scales), int(round_scale),
+                                                ctypes.byref(h), _ptr(recv_x), _ptr(recv_x_scales), _stream(x)))
+
+
+def cached_dispatch(x: torch.Tensor, handle: Handle, x_scales: Optional[torch.Tensor] = None,
+                    cast_to_fp8: bool = False, round_scale: bool = False):
+    """Dispatch a new x along a handle's routing (section 4.1, cached branch): no top-k inputs."""
+    kind = _x_kind(x, cast_to_fp8)
+    recv_x, recv_x_scales = _recv_buffers(x, kind, handle.recv_capacity, x.device)
+    cached_dispatch_into(x, handle, recv_x, recv_x_scales, x_scales, cast_to_fp8, round_scale)
+    return recv_x, recv_x_scales
+
+
+# --------------------------------------------------------------------------- combine
+def combine_into(y, handle: Handle, combined_x, recv_topk_weights=None, combined_topk_weights=None) -> None:
+    N, H, K = handle.send_head.shape[0], y.shape[1], handle.num_topk
+    _want(y, "y", torch.bfloat16)
+    if y.dim() != 2 or y.shape[0] < handle.recv_capacity:
+        raise ValueError("y must be [>= %d, H]" % handle.recv_capacity)
+    _want(combined_x, "combined_x", torch.bfloat16, (N, H))
+    _want(recv_topk_weights, "recv_topk_weights", torch.float32)
+    if recv_topk_weights is not None and (recv_topk_weights.dim() != 2 or recv_topk_weights.shape[1] != K or
+                                          recv_topk_weights.shape[0] < handle.recv_capacity):
+        raise ValueError("recv_topk_weights must be [>= %d, %d]" % (handle.recv_capacity, K))
+    _want(combined_topk_weights, "combined_topk_weights", torch.float32, (N, K))
+    p = handle.problem(y.shape[1])
+    h = handle.c()
+    _lib.check(_lib.load().miep_combine(ctypes.byref(p), _ptr(y), _ptr(recv_topk_weights), ctypes.byref(h),
+                                        _ptr(combined_x), _ptr(combined_topk_weights), _stream(y)))
+
+
+def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None):
+    """Sum expert outputs back into source-token order (sections 4.2, 4.4).
+
+    y [cap, H] bf16 in the receive layout; ``topk_weights`` are the received
+    top-k weights [cap, K], reduced the same way.  Returns (combined_x [N, H]
+    bf16, combined_topk_weights [N, K] fp32 or None).
+    """
+    _want(y, "y", torch.bfloat16)
+    if y.shape[0] != handle.recv_capacity:
+        raise ValueError("y must have the handle's %d receive rows" % handle.recv_capacity)
+    N = handle.send_head.shape[0]
+    combined_x = torch.empty((N, y.shape[1]), dtype=torch.bfloat16, device=y.device)
+    cw = None
+    if topk_weights is not None:
+        _want(topk_weights, "topk_weights", torch.float32)
+        cw = torch.empty((N, topk_weights.shape[1]), dtype=torch.float32, device=y.device)
+        if topk_weights.shape[1] != handle.num_topk:
+            raise ValueError("topk_weights must have num_topk columns")
+    combine_into(y, handle, combined_x, topk_weights, cw)
+    return combined_x, cw
+
+
+# --------------------------------------------------------------------------- low-latency
+def low_latency_dispatch_into(x, topk_idx, num_ranks: int, max_tokens: int, num_experts: int, dest_rank: int,
+                              use_fp8: bool, round_scale: bool, use_ue8m0: bool, msg_buf, msg_count, packed_recv_x,
+                              packed_recv_x_scales, packed_recv_x_scales_ue8m0, packed_recv_src_info,
+                              packed_recv_layout_range, packed_recv_count,
+                              cumulative_local_expert_recv_stats=None) -> None:
+    N, H = x.shape
+    R, M, L, K = num_ranks, max_tokens, num_experts // num_ranks, topk_idx.shape[1]
+    if N % R:
+        raise ValueError("x rows must split evenly over the source ranks")
+    _want(x, "x", torch.bfloat16)
+    _want(topk_idx, "topk_idx", torch.int64, (N, K))
+    _want(msg_buf, "msg_buf", torch.uint8, (L, R, M, ll_msg_bytes(H, use_fp8)))
+    _want(msg_count, "msg_count", torch.int32, (L, R))
+    if use_fp8:
+        if packed_recv_x.dtype not in (torch.float8_e4m3fn, torch.uint8) or tuple(packed_recv_x.shape) != (L, R * M, H):
+            raise ValueError("packed_recv_x must be [%d, %d, %d] E4M3 codes" % (L, R * M, H))
+        _want(packed_recv_x_scales, "packed_recv_x_scales", torch.float32, (L, R * M, H // 128))
+        _want(packed_recv_x_scales_ue8m0, "packed_recv_x_scales_ue8m0", torch.uint8, (L, R * M, H // 128))
+    else:
+        _want(packed_recv_x, "packed_recv_x", torch.bfloat16, (L, R * M, H))
+    _want(packed_recv_src_info, "packed_recv_src_info", torch.int32, (L, R * M))
+    _want(packed_recv_layout_range, "packed_recv_layout_range", torch.int64, (L, R))
+    _want(packed_recv_count, "packed_recv_count", torch.int32, (L,))
+    _want(cumulative_local_expert_recv_stats, "cumulative_local_expert_recv_stats", torch.int32, (L,))
+    q = _lib.LLProblem(num_ranks, N // num_ranks, max_tokens, H, K, num_experts, dest_rank)
+    _lib.check(_lib.load().miep_ll_dispatch(
+        ctypes.byref(q), _ptr(x), _ptr(topk_idx), int(use_fp8), int(round_scale), int(use_ue8m0), _ptr(msg_buf),
+        _ptr(msg_count), _ptr(packed_recv_x), _ptr(packed_recv_x_scales), _ptr(packed_recv_x_scales_ue8m0),
+        _ptr(packed_recv_src_info), _ptr(packed_recv_layout_range), _ptr(packed_recv_count),
+        _ptr(cumulative_local_expert_recv_stats), _stream(x)))
+
+
+def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispatch_tokens_per_rank: int,
+                         num_experts: int, dest_rank: int, num_ranks: int, use_fp8: bool = True,
+                         round_scale: bool = False, use_ue8m0: bool = False,
+                         cumulative_local_expert_recv_stats: Optional[torch.Tensor] = None) -> dict:
+    """Low-latency dispatch received by rank ``dest_rank`` (section 4.3).
+
+    x [R*T, H] bf16 and topk_idx [R*T, K] int64 hold every source rank's
+    tokens.  Returns a dict with packed_recv_x [L, R*M, H] (E4M3 or bf16),
+    packed_recv_x_scales [L, R*M, H/128], packed_recv_x_scales_ue8m0 (or None),
+    packed_recv_src_info [L, R*M], packed_recv_layout_range [L, R] int64,
+    packed_recv_count [L], and the expert-major message buffer and counts.
+    """
+    _want(x, "x", torch.bfloat16)
+    _want(topk_idx, "topk_idx", torch.int64)
+    N, H = x.shape
+    R, M = num_ranks, num_max_dispatch_tokens_per_rank
+    L = num_experts // R
+    dev = x.device
+    mb = ll_msg_bytes(H, use_fp8)
+    msg_buf = torch.empty((L, R, M, mb), dtype=torch.uint8, device=dev)
+    msg_count = torch.empty((L, R), dtype=torch.int32, device=dev)
+    if use_fp8:
+        prx = torch.empty((L, R * M, H), dtype=torch.float8_e4m3fn, device=dev)
+        prs = torch.empty((L, R * M, H // 128), dtype=torch.float32, device=dev)
+        pue = torch.empty((L, R * M, H // 128), dtype=torch.uint8, device=dev) if use_ue8m0 else None
+    else:
+        prx = torch.empty((L, R * M, H), dtype=torch.bfloat16, device=dev)
+        prs = pue = None
+    src = torch.empty((L, R * M), dtype=torch.int32, device=dev)
+    lr = torch.empty((L, R), dtype=torch.int64, device=dev)
+    cnt = torch.empty((L,), dtype=torch.int32, device=dev)
+    low_latency_dispatch_into(x, topk_idx, R, M, num_experts, dest_rank, use_fp8, round_scale, use_ue8m0, msg_buf,
+                              msg_count, prx, prs, pue, src, lr, cnt, cumulative_local_expert_recv_stats)
+    return dict(packed_recv_x=prx, packed_recv_x_scales=prs, packed_recv_x_scales_ue8m0=pue,
+                packed_recv_src_info=src, packed_recv_layout_range=lr, packed_recv_count=cnt, msg_buf=msg_buf,
+                msg_count=msg_count, cumulative_local_expert_recv_stats=cumulative_local_expert_recv_stats)

@@ -1,0 +1,80 @@
+"""ctypes view of ``libmiep.so`` (the C ABI of ``include/miep.h``).
+
+Loading fails loudly: there is no fallback path.  If the library is missing the
+caller gets an ImportError telling them to run the build.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmiep.so")
+
+MIEP_OK, MIEP_EINVAL, MIEP_EUNSUPPORTED, MIEP_EHIP = 0, 1, 2, 3
+X_BF16, X_FP8, X_BF16_CAST_FP8 = 0, 1, 2
+
+# Every symbol the header declares (checked by the CPU ABI test).
+EXPORTS = ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine", "miep_ll_dispatch",
+           "miep_ll_msg_bytes", "miep_last_error", "miep_version")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("num_src", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32), ("num_ranks", ctypes.c_int32),
+                ("num_channels", ctypes.c_int32), ("expert_alignment", ctypes.c_int32)]
+
+
+class HandleC(ctypes.Structure):
+    _fields_ = [("rank_prefix_matrix", ctypes.c_void_p), ("channel_prefix_matrix", ctypes.c_void_p),
+                ("recv_channel_prefix_matrix", ctypes.c_void_p), ("recv_rank_offset", ctypes.c_void_p),
+                ("recv_src_idx", ctypes.c_void_p), ("is_token_in_rank", ctypes.c_void_p),
+                ("send_head", ctypes.c_void_p), ("recv_capacity", ctypes.c_int64)]
+
+
+class LLProblem(ctypes.Structure):
+    _fields_ = [("num_ranks", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("dest_rank", ctypes.c_int32)]
+
+
+class MiepError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("miep status %d: %s" % (status, msg))
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmiep.so is not built (%s); run `python -m combine_get_dispatch_histogram_amd.build`"
+                              % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.miep_get_dispatch_layout.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P]
+        lib.miep_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.POINTER(HandleC), _P]
+        lib.miep_cached_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, ctypes.POINTER(HandleC), _P,
+                                             _P, _P]
+        lib.miep_combine.argtypes = [ctypes.POINTER(Problem), _P, _P, ctypes.POINTER(HandleC), _P, _P, _P]
+        lib.miep_ll_dispatch.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                         _P, _P, _P, _P]
+        for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
+                  "miep_ll_dispatch"):
+            getattr(lib, f).restype = ctypes.c_int
+        lib.miep_ll_msg_bytes.argtypes = [_I32, _I32]
+        lib.miep_ll_msg_bytes.restype = ctypes.c_int64
+        lib.miep_last_error.restype = ctypes.c_char_p
+        lib.miep_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != MIEP_OK:
+        raise MiepError(status, load().miep_last_error().decode())

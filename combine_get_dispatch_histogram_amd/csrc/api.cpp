@@ -1,0 +1,322 @@
+// api.cpp -- the C ABI declared in include/miep.h: argument validation,
+// launch-geometry choice and the kernel launches.  Host code only.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/miep.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+miep_status fail(miep_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+miep_status ok() {
+  g_err[0] = '\0';
+  return MIEP_OK;
+}
+
+miep_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MIEP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+miep_status check_problem(const miep_problem* p) {
+  if (!p) return fail(MIEP_EINVAL, "problem is NULL");
+  if (p->num_src < 0 || p->num_tokens < 0) return fail(MIEP_EINVAL, "num_src and num_tokens must be >= 0");
+  if (p->hidden <= 0 || p->num_topk <= 0 || p->num_experts <= 0 || p->num_ranks <= 0 || p->num_channels <= 0)
+    return fail(MIEP_EINVAL, "hidden, num_topk, num_experts, num_ranks, num_channels must be > 0");
+  if (p->expert_alignment <= 0) return fail(MIEP_EINVAL, "expert_alignment must be >= 1");
+  if (p->num_experts % p->num_ranks != 0) return fail(MIEP_EINVAL, "num_experts must be a multiple of num_ranks");
+  if (p->num_ranks > 8 && p->num_ranks % 8 != 0)
+    return fail(MIEP_EINVAL, "num_ranks > 8 must be a multiple of 8 (RDMA groups of 8 ranks)");
+  if (p->num_ranks > miep::kMaxRanks) return fail(MIEP_EUNSUPPORTED, "num_ranks > %d", miep::kMaxRanks);
+  if (p->num_experts > miep::kMaxExperts) return fail(MIEP_EUNSUPPORTED, "num_experts > %d", miep::kMaxExperts);
+  if (p->num_topk > 64) return fail(MIEP_EUNSUPPORTED, "num_topk > 64");
+  if (static_cast<int64_t>(p->num_src) * p->num_tokens > (1ll << 31) - 1)
+    return fail(MIEP_EUNSUPPORTED, "more than 2^31-1 tokens");
+  return ok();
+}
+
+miep_status check_payload(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales) {
+  if (x_kind != MIEP_X_BF16 && x_kind != MIEP_X_FP8 && x_kind != MIEP_X_BF16_CAST_FP8)
+    return fail(MIEP_EINVAL, "unknown x_kind %d", x_kind);
+  const int64_t N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  if (N > 0 && !x) return fail(MIEP_EINVAL, "x is NULL");
+  if (!aligned16(x)) return fail(MIEP_EUNSUPPORTED, "x must be 16-byte aligned");
+  if (p->hidden % 8 != 0) return fail(MIEP_EUNSUPPORTED, "hidden must be a multiple of 8 (16-byte rows)");
+  if (x_kind != MIEP_X_BF16) {
+    if (p->hidden % miep::kFp8Group != 0) return fail(MIEP_EINVAL, "FP8 payloads need hidden % 128 == 0");
+    if (x_kind == MIEP_X_FP8 && N > 0 && !x_scales) return fail(MIEP_EINVAL, "x_scales is NULL for MIEP_X_FP8");
+  }
+  return ok();
+}
+
+// Arrays of zero elements may be NULL (empty tensors carry no storage).
+miep_status check_handle(const miep_problem* p, const miep_handle* h, bool full) {
+  if (!h) return fail(MIEP_EINVAL, "handle is NULL");
+  if (h->recv_capacity < 0 || h->recv_capacity > (1ll << 31) - 1)
+    return fail(MIEP_EINVAL, "recv_capacity must be in [0, 2^31-1]");
+  const int64_t N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  if (!h->recv_rank_offset) return fail(MIEP_EINVAL, "handle recv_rank_offset is NULL");
+  if (N > 0 && !h->send_head) return fail(MIEP_EINVAL, "handle send_head is NULL");
+  if (full) {
+    if (p->num_src > 0 && (!h->rank_prefix_matrix || !h->channel_prefix_matrix || !h->recv_channel_prefix_matrix))
+      return fail(MIEP_EINVAL, "handle prefix matrices are NULL");
+    if (h->recv_capacity > 0 && !h->recv_src_idx) return fail(MIEP_EINVAL, "handle recv_src_idx is NULL");
+    if (N > 0 && !h->is_token_in_rank) return fail(MIEP_EINVAL, "handle is_token_in_rank is NULL");
+  }
+  return ok();
+}
+
+miep::PackArgs pack_args(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                         int32_t round_scale, const miep_handle* h, void* recv_x, float* recv_x_scales) {
+  miep::PackArgs a{};
+  a.N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  a.T = p->num_tokens;
+  a.H = p->hidden;
+  a.K = p->num_topk;
+  a.E = p->num_experts;
+  a.R = p->num_ranks;
+  a.L = p->num_experts / p->num_ranks;
+  a.kind = x_kind;
+  a.round_scale = round_scale;
+  a.capacity = h->recv_capacity;
+  a.x = x;
+  a.x_scales = x_scales;
+  a.send_head = h->send_head;
+  a.off = h->recv_rank_offset;
+  a.recv_x = recv_x;
+  a.recv_x_scales = recv_x_scales;
+  return a;
+}
+
+}  // namespace
+
+namespace miep {
+const Tuning& tuning() {
+  static const Tuning t = {env_int("MIEP_PACK_VPL", 0), env_int("MIEP_PACK_SLICES", 0),
+                           env_int("MIEP_COMBINE_VPL", 0), env_int("MIEP_COMBINE_SLICES", 0), env_int("MIEP_NT", 1)};
+  return t;
+}
+}  // namespace miep
+
+extern "C" {
+
+const char* miep_last_error(void) { return g_err; }
+
+const char* miep_version(void) { return "miep 0.1 gfx950"; }
+
+int64_t miep_ll_msg_bytes(int32_t hidden, int32_t use_fp8) {
+  if (hidden <= 0) return -1;
+  return 16 + (use_fp8 ? static_cast<int64_t>(hidden) + 4ll * (hidden / miep::kFp8Group) : 2ll * hidden);
+}
+
+miep_status miep_get_dispatch_layout(const miep_problem* p, const int64_t* topk_idx, int32_t* num_tokens_per_rank,
+                                     int32_t* num_tokens_per_rdma_rank, int32_t* num_tokens_per_expert,
+                                     uint8_t* is_token_in_rank, void* stream) {
+  miep_status st = check_problem(p);
+  if (st != MIEP_OK) return st;
+  const int64_t N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  if (p->num_src > 0 && (!num_tokens_per_rank || !num_tokens_per_expert))
+    return fail(MIEP_EINVAL, "num_tokens_per_rank / num_tokens_per_expert NULL");
+  if (N > 0 && (!topk_idx || !is_token_in_rank)) return fail(MIEP_EINVAL, "topk_idx / is_token_in_rank NULL");
+  if (p->num_ranks > 8 && p->num_src > 0 && !num_tokens_per_rdma_rank)
+    return fail(MIEP_EINVAL, "num_tokens_per_rdma_rank required when num_ranks > 8");
+  if (p->num_ranks <= 8 && num_tokens_per_rdma_rank)
+    return fail(MIEP_EINVAL, "num_tokens_per_rdma_rank must be NULL when num_ranks <= 8");
+  if ((reinterpret_cast<uintptr_t>(is_token_in_rank) & 3u) != 0)
+    return fail(MIEP_EUNSUPPORTED, "is_token_in_rank must be 4-byte aligned");
+  miep::LayoutArgs a{};
+  a.S = p->num_src;
+  a.T = p->num_tokens;
+  a.K = p->num_topk;
+  a.E = p->num_experts;
+  a.R = p->num_ranks;
+  a.L = p->num_experts / p->num_ranks;
+  a.topk_idx = topk_idx;
+  a.ntpr = num_tokens_per_rank;
+  a.ntp_rdma = num_tokens_per_rdma_rank;
+  a.ntpe = num_tokens_per_expert;
+  a.in_rank = is_token_in_rank;
+  return hip_status(miep::launch_layout(a, static_cast<hipStream_t>(stream)), "layout launch");
+}
+
+miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                          int32_t round_scale, const int64_t* topk_idx, const float* topk_weights,
+                          const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_expert, void* recv_x,
+                          float* recv_x_scales, int64_t* recv_topk_idx, float* recv_topk_weights,
+                          int32_t* num_recv_tokens_per_expert, const miep_handle* h, void* stream) {
+  miep_status st = check_problem(p);
+  if (st != MIEP_OK) return st;
+  if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
+  if ((st = check_handle(p, h, true)) != MIEP_OK) return st;
+  if (p->num_src > 0 && !num_tokens_per_rank) return fail(MIEP_EINVAL, "num_tokens_per_rank is NULL");
+  if (h->recv_capacity > 0 && !recv_x) return fail(MIEP_EINVAL, "recv_x is NULL");
+  if (!aligned16(recv_x)) return fail(MIEP_EUNSUPPORTED, "recv_x must be 16-byte aligned");
+  if (x_kind != MIEP_X_BF16 && h->recv_capacity > 0 && !recv_x_scales)
+    return fail(MIEP_EINVAL, "recv_x_scales is NULL for an FP8 dispatch");
+  if (topk_idx && h->recv_capacity > 0 && !recv_topk_idx) return fail(MIEP_EINVAL, "recv_topk_idx is NULL");
+  if (topk_weights && !topk_idx) return fail(MIEP_EINVAL, "topk_weights given without topk_idx");
+  if (topk_weights && h->recv_capacity > 0 && !recv_topk_weights)
+    return fail(MIEP_EINVAL, "recv_topk_weights is NULL");
+  if (num_recv_tokens_per_expert && !num_tokens_per_expert)
+    return fail(MIEP_EINVAL, "num_recv_tokens_per_expert needs num_tokens_per_expert");
+  if (p->num_ranks % 4 == 0 && (reinterpret_cast<uintptr_t>(h->send_head) & 15u) != 0)
+    return fail(MIEP_EUNSUPPORTED, "send_head must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(h->is_token_in_rank) & 3u) != 0)
+    return fail(MIEP_EUNSUPPORTED, "is_token_in_rank must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  miep::NotifyArgs na{};
+  na.S = p->num_src;
+  na.T = p->num_tokens;
+  na.R = p->num_ranks;
+  na.C = p->num_channels;
+  na.E = p->num_experts;
+  na.L = p->num_experts / p->num_ranks;
+  na.align = p->expert_alignment;
+  na.in_rank = h->is_token_in_rank;
+  na.ntpr = num_tokens_per_rank;
+  na.ntpe = num_tokens_per_expert;
+  na.rpm = h->rank_prefix_matrix;
+  na.cpm = h->channel_prefix_matrix;
+  na.rcpm = h->recv_channel_prefix_matrix;
+  na.off = h->recv_rank_offset;
+  na.send_head = h->send_head;
+  na.nrte = num_recv_tokens_per_expert;
+  if (p->num_src == 0) {
+    // no sources: every receive offset is 0 and every expert count is 0
+    hipError_t e = miep::launch_fill_zero(h->recv_rank_offset, p->num_ranks + 1, s);
+    if (e == hipSuccess && num_recv_tokens_per_expert)
+      e = miep::launch_fill_zero(num_recv_tokens_per_expert, p->num_experts, s);
+    return hip_status(e, "dispatch (no sources)");
+  }
+  hipError_t e = miep::launch_notify(na, s);
+  if (e != hipSuccess) return hip_status(e, "notify launch");
+
+  miep::PackArgs a = pack_args(p, x, x_kind, x_scales, round_scale, h, recv_x, recv_x_scales);
+  a.meta = 1;
+  a.topk_idx = topk_idx;
+  a.topk_weights = topk_weights;
+  a.recv_topk_idx = topk_idx ? recv_topk_idx : nullptr;
+  a.recv_topk_weights = topk_weights ? recv_topk_weights : nullptr;
+  a.recv_src_idx = h->recv_src_idx;
+  if (!topk_idx) a.K = 0;
+  return hip_status(miep::launch_pack(a, s), "pack launch");
+}
+
+miep_status miep_cached_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                                 int32_t round_scale, const miep_handle* h, void* recv_x, float* recv_x_scales,
+                                 void* stream) {
+  miep_status st = check_problem(p);
+  if (st != MIEP_OK) return st;
+  if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
+  if ((st = check_handle(p, h, false)) != MIEP_OK) return st;
+  if (h->recv_capacity > 0 && !recv_x) return fail(MIEP_EINVAL, "recv_x is NULL");
+  if (!aligned16(recv_x)) return fail(MIEP_EUNSUPPORTED, "recv_x must be 16-byte aligned");
+  if (x_kind != MIEP_X_BF16 && h->recv_capacity > 0 && !recv_x_scales)
+    return fail(MIEP_EINVAL, "recv_x_scales is NULL for an FP8 dispatch");
+  miep::PackArgs a = pack_args(p, x, x_kind, x_scales, round_scale, h, recv_x, recv_x_scales);
+  a.meta = 0;
+  a.K = 0;
+  return hip_status(miep::launch_pack(a, static_cast<hipStream_t>(stream)), "cached pack launch");
+}
+
+miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
+                         const miep_handle* h, uint16_t* combined_x, float* combined_topk_weights, void* stream) {
+  miep_status st = check_problem(p);
+  if (st != MIEP_OK) return st;
+  if ((st = check_handle(p, h, false)) != MIEP_OK) return st;
+  const int64_t N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  if (p->hidden % 8 != 0) return fail(MIEP_EUNSUPPORTED, "hidden must be a multiple of 8 (16-byte rows)");
+  if (h->recv_capacity > 0 && !y) return fail(MIEP_EINVAL, "y is NULL");
+  if (N > 0 && !combined_x) return fail(MIEP_EINVAL, "combined_x is NULL");
+  if (!aligned16(y) || !aligned16(combined_x)) return fail(MIEP_EUNSUPPORTED, "y and combined_x must be 16-byte aligned");
+  if (recv_topk_weights && N > 0 && !combined_topk_weights)
+    return fail(MIEP_EINVAL, "combined_topk_weights is NULL while recv_topk_weights is given");
+  miep::CombineArgs a{};
+  a.N = N;
+  a.H = p->hidden;
+  a.K = p->num_topk;
+  a.R = p->num_ranks;
+  a.capacity = h->recv_capacity;
+  a.y = y;
+  a.w = recv_topk_weights;
+  a.send_head = h->send_head;
+  a.off = h->recv_rank_offset;
+  a.out = combined_x;
+  a.out_w = combined_topk_weights;
+  return hip_status(miep::launch_combine(a, static_cast<hipStream_t>(stream)), "combine launch");
+}
+
+miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,
+                             int32_t round_scale, int32_t use_ue8m0, void* msg_buf, int32_t* msg_count,
+                             void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
+                             int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
+                             int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats, void* stream) {
+  if (!q) return fail(MIEP_EINVAL, "problem is NULL");
+  const int R = q->num_ranks, T = q->num_tokens, M = q->max_tokens, H = q->hidden, K = q->num_topk,
+            E = q->num_experts, d = q->dest_rank;
+  if (R <= 0 || T < 0 || M <= 0 || H <= 0 || K <= 0 || E <= 0) return fail(MIEP_EINVAL, "sizes must be positive");
+  if (T > M) return fail(MIEP_EINVAL, "num_tokens > max_tokens");
+  if (E % R != 0) return fail(MIEP_EINVAL, "num_experts must be a multiple of num_ranks");
+  if (d < 0 || d >= R) return fail(MIEP_EINVAL, "dest_rank out of range");
+  if (use_ue8m0 && !round_scale) return fail(MIEP_EINVAL, "use_ue8m0 requires round_scale");
+  if (use_ue8m0 && !use_fp8) return fail(MIEP_EINVAL, "use_ue8m0 requires use_fp8");
+  if (R > 1024) return fail(MIEP_EUNSUPPORTED, "num_ranks > 1024");
+  if (M > 4096) return fail(MIEP_EUNSUPPORTED, "max_tokens > 4096");
+  if (H % 8 != 0) return fail(MIEP_EUNSUPPORTED, "hidden must be a multiple of 8");
+  if (use_fp8 && H % 512 != 0)
+    return fail(MIEP_EUNSUPPORTED, "FP8 low-latency messages need hidden % 512 == 0 (16-byte message stride)");
+  if (!x || !topk_idx || !msg_buf || !msg_count || !packed_recv_x || !packed_recv_src_info ||
+      !packed_recv_layout_range || !packed_recv_count)
+    return fail(MIEP_EINVAL, "a required pointer is NULL");
+  if (use_fp8 && !packed_recv_x_scales) return fail(MIEP_EINVAL, "packed_recv_x_scales is NULL with use_fp8");
+  if (!aligned16(x) || !aligned16(msg_buf) || !aligned16(packed_recv_x))
+    return fail(MIEP_EUNSUPPORTED, "x, msg_buf and packed_recv_x must be 16-byte aligned");
+  miep::LLArgs a{};
+  a.R = R;
+  a.T = T;
+  a.M = M;
+  a.H = H;
+  a.K = K;
+  a.E = E;
+  a.L = E / R;
+  a.d = d;
+  a.use_fp8 = use_fp8 ? 1 : 0;
+  a.round_scale = round_scale ? 1 : 0;
+  a.use_ue8m0 = use_ue8m0 ? 1 : 0;
+  a.msg_bytes = miep_ll_msg_bytes(H, use_fp8);
+  a.x = x;
+  a.topk_idx = topk_idx;
+  a.msg = static_cast<uint8_t*>(msg_buf);
+  a.msg_count = msg_count;
+  a.prx = packed_recv_x;
+  a.prs = packed_recv_x_scales;
+  a.prue = (use_fp8 && use_ue8m0) ? packed_recv_x_scales_ue8m0 : nullptr;
+  a.src_info = packed_recv_src_info;
+  a.layout_range = packed_recv_layout_range;
+  a.count = packed_recv_count;
+  a.cumulative = cumulative_local_expert_recv_stats;
+  return hip_status(miep::launch_ll(a, static_cast<hipStream_t>(stream)), "low-latency launch");
+}
+
+}  // extern "C"

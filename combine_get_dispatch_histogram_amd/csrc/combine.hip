@@ -1,0 +1,149 @@
+// combine.hip -- normal-mode combine on gfx950.
+//
+// "Chapter 4  V1: layout, dispatch and combine", section 4.2: combine uses
+// the dispatch handle to send expert outputs back without re-deriving the
+// routing; section 4.4: combine only adds the tokens (no gate weights are
+// applied in it), and the top-k weights are reduced separately.
+// Accumulation is fp32, the result is rounded once to bf16.
+//
+// Pull design: one wavefront per (token, row slice) gathers the rows that
+// the token's receiving ranks hold (send_head names them), adds them in
+// ascending rank order in fp32 registers, and writes the bf16 row once.
+// Every HBM byte is touched once: rho row reads + 1 row write per token.
+// No atomics: a token's sum lives in one wavefront's registers.
+#include "device.h"
+#include "kernels.h"
+
+namespace miep {
+
+template <int VPL, int MW, bool NT>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices) {
+  const int lane = lane_id();
+  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t n = gw / nslices;
+  const int slice = static_cast<int>(gw - n * nslices);
+  if (n >= a.N) return;
+  const int R = a.R;
+
+  int src[MW];
+  uint64_t smask[MW];
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    const int r = kWave * i + lane;
+    int row = -1;
+    if (r < R) {
+      const int sh = a.send_head[n * R + r];
+      if (sh >= 0) row = a.off[r] + sh;
+    }
+    const bool ok = row >= 0 && row < a.capacity;
+    src[i] = row;
+    smask[i] = ballot(ok);
+  }
+
+  // top-k weights: lane k sums its column over the receiving ranks
+  if (slice == 0 && a.out_w != nullptr) {
+    float acc = 0.0f;
+    bool have = false;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      uint64_t m = smask[i];
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        const int64_t row = readlane(src[i], b);
+        if (lane < a.K) {
+          const float v = a.w ? a.w[row * a.K + lane] : 0.0f;
+          acc = have ? acc + v : v;
+        }
+        have = true;
+      }
+    }
+    if (lane < a.K) a.out_w[n * a.K + lane] = have ? acc : 0.0f;
+  }
+
+  const int nv = a.H / 8;  // 16-byte vectors of 8 bf16
+  const uint8_t* y = reinterpret_cast<const uint8_t*>(a.y);
+  const int64_t row_bytes = 2 * static_cast<int64_t>(a.H);
+  uint8_t* orow = reinterpret_cast<uint8_t*>(a.out) + n * row_bytes;
+  const int span = kWave * VPL;
+  for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
+    float acc[VPL][8];
+    bool have = false;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      uint64_t m = smask[i];
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        const int64_t row = readlane(src[i], b);
+        const uint8_t* yrow = y + row * row_bytes;
+        v4u d[VPL];
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int v = v0 + j * kWave + lane;
+          if (v < nv) d[j] = ld16<NT>(yrow + static_cast<int64_t>(v) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const float f[8] = {bf16_lo(d[j].x), bf16_hi(d[j].x), bf16_lo(d[j].y), bf16_hi(d[j].y),
+                              bf16_lo(d[j].z), bf16_hi(d[j].z), bf16_lo(d[j].w), bf16_hi(d[j].w)};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[j][q] = have ? acc[j][q] + f[q] : f[q];
+        }
+        have = true;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + j * kWave + lane;
+      if (v < nv) {
+        v4u o;
+        if (have) {
+          o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+          o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+          o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+          o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+        } else {
+          o = v4u{0u, 0u, 0u, 0u};
+        }
+        st16<false>(orow + static_cast<int64_t>(v) * 16, o);
+      }
+    }
+  }
+}
+
+template <int VPL, bool NT>
+static hipError_t launch_combine_vpl(const CombineArgs& a, int nslices, hipStream_t st) {
+  const int64_t waves = a.N * nslices;
+  const int64_t blocks = (waves + 3) / 4;
+  if (a.R <= 64)
+    hipLaunchKernelGGL((combine_kernel<VPL, 1, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+                       nslices);
+  else
+    hipLaunchKernelGGL((combine_kernel<VPL, 4, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+                       nslices);
+  return hipGetLastError();
+}
+
+template <bool NT>
+static hipError_t launch_combine_nt(const CombineArgs& a, int vpl, int nslices, hipStream_t st) {
+  switch (vpl) {
+    case 2: return launch_combine_vpl<2, NT>(a, nslices, st);
+    case 4: return launch_combine_vpl<4, NT>(a, nslices, st);
+    case 7: return launch_combine_vpl<7, NT>(a, nslices, st);
+    default: return launch_combine_vpl<8, NT>(a, nslices, st);
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
+  if (a.N == 0) return hipSuccess;
+  const Tuning& tu = tuning();
+  const int nv = a.H / 8;
+  int vpl = tu.combine_vpl > 0 ? tu.combine_vpl : (nv % (7 * kWave) == 0 ? 7 : 8);
+  const int span = vpl * kWave;
+  int nslices = tu.combine_slices > 0 ? tu.combine_slices : (nv + span - 1) / span;
+  if (nslices < 1) nslices = 1;
+  return tu.nt ? launch_combine_nt<true>(a, vpl, nslices, st) : launch_combine_nt<false>(a, vpl, nslices, st);
+}
+
+}  // namespace miep

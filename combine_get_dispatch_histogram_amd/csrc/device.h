@@ -1,0 +1,191 @@
+// device.h -- gfx950 (CDNA4) device helpers shared by the miep kernels:
+// 64-lane wavefront primitives, 16-byte vector memory access, bf16 and
+// OCP E4M3 conversion, and the per-128-channel FP8 scale rule.
+//
+// The FP8 rule follows the low-latency dispatch of "DeepEP Normal vs
+// Low-Latency dual-mode analysis" (send-loop listing: per-group amax ->
+// scale / inverse scale, optionally rounded to a power of two, UE8M0).
+// The pages give only the call, so the exact steps are a reading:
+//   amax floored at 1e-4; plain: scale = 448/amax, scale_inv = amax/448
+//   (IEEE-rounded fp32 divisions); round_scale: scale_inv = 2^e with
+//   e = ceil(log2(amax/448)) taken from the bits of the quotient.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace miep {
+
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Uniform broadcast of lane `src` (src must be wave-uniform).
+__device__ __forceinline__ int readlane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+
+// Inclusive scan across the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- memory
+// 16-byte vector types.  Loads of data read once use the non-temporal hint
+// (streamed through, not kept in L2); stores of receive buffers likewise.
+struct alignas(16) v4u { uint32_t x, y, z, w; };
+struct alignas(8) v2u { uint32_t x, y; };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ v4u ld16(const void* p) {
+  if constexpr (NT) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return v4u{t.x, t.y, t.z, t.w};
+  } else {
+    return *reinterpret_cast<const v4u*>(p);
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(void* p, const v4u& v) {
+  if constexpr (NT) {
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+  } else {
+    *reinterpret_cast<v4u*>(p) = v;
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st8(void* p, const v2u& v) {
+  if constexpr (NT) {
+    const u32x2 t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+  } else {
+    *reinterpret_cast<v2u*>(p) = v;
+  }
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 round-to-nearest-even: gfx950 converts natively.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// ---------------------------------------------------------------- E4M3
+// fp32 -> OCP E4M3FN, round to nearest even, saturating at 448.
+// Bit-level: the normal range rounds the 23-bit fp32 mantissa to 3 bits
+// (a carry moves into the exponent field by itself); below 2^-6 the
+// value is a multiple of 2^-9 and rounds as the integer |a| * 2^9.
+__device__ __forceinline__ uint32_t e4m3_rne(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t m = u & 0x7FFFFFFFu;
+  if (m > 0x7F800000u) return 0x7Fu;                 // NaN
+  if (m >= 0x43E00000u) return sign | 0x7Eu;         // >= 448: saturate
+  if (m < 0x3C800000u) {                             // < 2^-6: subnormal grid
+    const float q = __builtin_rintf(__uint_as_float(m) * 512.0f);
+    return sign | static_cast<uint32_t>(q);          // 0..8 (8 = 2^-6, a normal code)
+  }
+  const uint32_t exp = (m >> 23) - 127u + 7u;        // 1..15
+  const uint32_t mant = m & 0x7FFFFFu;
+  uint32_t code = (exp << 3) | (mant >> 20);
+  const uint32_t rest = mant & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) code += 1u;
+  return sign | code;                                // <= 0x7E since |a| < 448
+}
+
+// Per-group scales.  Returns scale (multiplier) and writes scale_inv.
+__device__ __forceinline__ float fp8_scales(float amax, bool round_scale, float* scale_inv) {
+  amax = fmaxf(amax, 1e-4f);
+  if (round_scale) {
+    const uint32_t b = __float_as_uint(amax / 448.0f);
+    const int e = static_cast<int>((b >> 23) & 0xFFu) - 127 + ((b & 0x7FFFFFu) != 0u ? 1 : 0);
+    *scale_inv = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    return __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+  }
+  *scale_inv = amax / 448.0f;
+  return 448.0f / amax;
+}
+
+// Max over the 16 lanes that hold one 128-channel group (8 channels each).
+__device__ __forceinline__ float group16_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  v = fmaxf(v, __shfl_xor(v, 2, 16));
+  v = fmaxf(v, __shfl_xor(v, 4, 16));
+  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  return v;
+}
+
+// 8 bf16 channels (one 16-byte vector) -> amax of their magnitudes.
+__device__ __forceinline__ float absmax8(const v4u& v) {
+  float m = fabsf(bf16_lo(v.x));
+  m = fmaxf(m, fabsf(bf16_hi(v.x)));
+  m = fmaxf(m, fabsf(bf16_lo(v.y)));
+  m = fmaxf(m, fabsf(bf16_hi(v.y)));
+  m = fmaxf(m, fabsf(bf16_lo(v.z)));
+  m = fmaxf(m, fabsf(bf16_hi(v.z)));
+  m = fmaxf(m, fabsf(bf16_lo(v.w)));
+  m = fmaxf(m, fabsf(bf16_hi(v.w)));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  return e4m3_rne(a) | (e4m3_rne(b) << 8) | (e4m3_rne(c) << 16) | (e4m3_rne(d) << 24);
+}
+
+// 8 bf16 channels times `scale` -> 8 E4M3 codes (one fp32 multiply each).
+__device__ __forceinline__ v2u cast8(const v4u& v, float scale) {
+  v2u r;
+  r.x = e4m3x4(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale, bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
+  r.y = e4m3x4(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale, bf16_lo(v.w) * scale, bf16_hi(v.w) * scale);
+  return r;
+}
+
+// Rank set of one token (up to 64*MW ranks) held in registers; selects
+// instead of dynamic indexing keep it out of scratch memory.
+template <int MW>
+struct RankMask {
+  uint64_t w[MW];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < MW; ++i) w[i] = 0;
+  }
+  __device__ __forceinline__ void set(int r) {
+    const int q = r >> 6;
+    const uint64_t b = 1ull << (r & 63);
+#pragma unroll
+    for (int i = 0; i < MW; ++i) w[i] |= (q == i) ? b : 0ull;
+  }
+  __device__ __forceinline__ uint32_t get(int r) const {
+    const int q = r >> 6;
+    uint64_t v = w[0];
+#pragma unroll
+    for (int i = 1; i < MW; ++i) v = (q == i) ? w[i] : v;
+    return static_cast<uint32_t>((v >> (r & 63)) & 1ull);
+  }
+};
+
+}  // namespace miep

@@ -1,0 +1,95 @@
+// layout.hip -- get_dispatch_layout on gfx950.
+//
+// "Chapter 4  V1: layout, dispatch and combine", section 4.1: the layout
+// turns the top-k expert indices into per-rank, per-RDMA-rank and
+// per-expert token counts plus the token-in-rank membership matrix.
+// Expert e lives on rank e / (E/R) and negative entries are skipped ("DeepEP
+// Normal vs Low-Latency dual-mode analysis", low-latency send loop); ranks
+// group into RDMA ranks of 8 (same page, RDMA rank translation and the
+// 8-peer NVLink constant).
+//
+// One workgroup owns one source partition, so every count is produced by a
+// single workgroup: no global atomics, no zero-fill launch.  Each thread
+// reads one token's K indices, builds the rank bitmask in registers, writes
+// the membership row with 4-byte stores, and counts experts, ranks and
+// RDMA groups in LDS (integer adds, order-independent).
+#include "device.h"
+#include "kernels.h"
+
+namespace miep {
+
+template <int MW>
+__global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
+  extern __shared__ int32_t lds[];
+  const int G = a.R > 8 ? a.R / 8 : 0;
+  int32_t* hist = lds;            // [E]
+  int32_t* rcnt = hist + a.E;     // [R]
+  int32_t* gcnt = rcnt + a.R;     // [G]
+  const int s = blockIdx.x;
+  for (int i = threadIdx.x; i < a.E + a.R + G; i += blockDim.x) lds[i] = 0;
+  __syncthreads();
+
+  for (int t = threadIdx.x; t < a.T; t += blockDim.x) {
+    const int64_t n = static_cast<int64_t>(s) * a.T + t;
+    const int64_t* row = a.topk_idx + n * a.K;
+    RankMask<MW> m;
+    m.clear();
+    for (int k = 0; k < a.K; ++k) {
+      const int64_t e = row[k];
+      if (e < 0 || e >= a.E) continue;              // masked (or out of range)
+      atomicAdd(&hist[e], 1);
+      m.set(static_cast<int>(e) / a.L);
+    }
+    uint8_t* out = a.in_rank + n * a.R;
+    if ((a.R & 3) == 0) {
+      for (int r0 = 0; r0 < a.R; r0 += 4) {
+        const uint32_t b = m.get(r0) | (m.get(r0 + 1) << 8) | (m.get(r0 + 2) << 16) | (m.get(r0 + 3) << 24);
+        *reinterpret_cast<uint32_t*>(out + r0) = b;
+      }
+    } else {
+      for (int r = 0; r < a.R; ++r) out[r] = static_cast<uint8_t>(m.get(r));
+    }
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      uint64_t bits = m.w[i];
+      // RDMA groups: byte j of word i is ranks 64i+8j .. 64i+8j+7
+      uint64_t g = bits;
+      g |= g >> 4;
+      g |= g >> 2;
+      g |= g >> 1;
+      g &= 0x0101010101010101ull;
+      while (bits) {
+        const int b = __builtin_ctzll(bits);
+        bits &= bits - 1;
+        atomicAdd(&rcnt[64 * i + b], 1);
+      }
+      if (G) {
+        while (g) {
+          const int b = __builtin_ctzll(g);
+          g &= g - 1;
+          atomicAdd(&gcnt[8 * i + (b >> 3)], 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.ntpe[static_cast<int64_t>(s) * a.E + e] = hist[e];
+  for (int r = threadIdx.x; r < a.R; r += blockDim.x) a.ntpr[static_cast<int64_t>(s) * a.R + r] = rcnt[r];
+  if (a.ntp_rdma)
+    for (int g = threadIdx.x; g < G; g += blockDim.x) a.ntp_rdma[static_cast<int64_t>(s) * G + g] = gcnt[g];
+}
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t st) {
+  if (a.S == 0) return hipSuccess;
+  int threads = ((a.T + kWave - 1) / kWave) * kWave;
+  threads = threads < kWave ? kWave : (threads > 1024 ? 1024 : threads);
+  const int G = a.R > 8 ? a.R / 8 : 0;
+  const size_t lds = sizeof(int32_t) * static_cast<size_t>(a.E + a.R + G);
+  if (a.R <= 64)
+    hipLaunchKernelGGL(layout_kernel<1>, dim3(a.S), dim3(threads), lds, st, a);
+  else
+    hipLaunchKernelGGL(layout_kernel<4>, dim3(a.S), dim3(threads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace miep

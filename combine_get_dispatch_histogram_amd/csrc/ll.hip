@@ -1,0 +1,153 @@
+// ll.hip -- low-latency dispatch on one GPU, seen from one receiving rank.
+//
+// "DeepEP Normal vs Low-Latency dual-mode analysis", low-latency dispatch:
+// each token is cast (optionally to FP8 with per-128-channel scales) and
+// one message per top-k expert entry >= 0 goes straight to the rank owning
+// that expert; the receiver keeps messages expert-major, at slot
+// (local_expert, src_rank, i), and packs local expert l's rows from row
+// l * R * M.  "Normal vs Low-Latency: two communication philosophies in
+// DeepEP V1 / V2 / DeepGEMM": a message is one 16-byte header (the source
+// token index plus three reserved ints) and the payload (H E4M3 bytes and
+// H/128 fp32 scales, or 2H bf16 bytes).  "Chapter 4  V1: layout, dispatch
+// and combine", section 4.3: the call returns the packed rows, scales,
+// per-expert counts, source info and layout range.
+//
+// Where the transport fills slots in atomic arrival order, these kernels
+// fix the order: slot j of (l, s) is the j-th top-k entry of source s that
+// names expert d*L + l, in (token, k) order, so the output is
+// deterministic.  Two kernels, both one workgroup per (l, s):
+//   send: scan source s's top-k for the expert (LDS scan), then cast and
+//         write its messages (16-byte loads, 8/16-byte stores);
+//   recv: exclusive scan of the counts over s gives the packed range, then
+//         a 16-byte copy of payloads and scales.
+#include "device.h"
+#include "kernels.h"
+
+namespace miep {
+
+constexpr int kLLThreads = 256;
+constexpr int kLLMaxSlots = 4096;
+
+__global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
+  __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
+  __shared__ int32_t wsum[kLLThreads / kWave];
+  __shared__ int32_t carry_s;
+  const int l = blockIdx.x / a.R;
+  const int s = blockIdx.x % a.R;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int64_t target = static_cast<int64_t>(a.d) * a.L + l;
+  const int64_t* idx = a.topk_idx + static_cast<int64_t>(s) * a.T * a.K;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int t0 = 0; t0 < a.T; t0 += kLLThreads) {
+    const int t = t0 + tid;
+    int cnt = 0;
+    if (t < a.T)
+      for (int k = 0; k < a.K; ++k) cnt += idx[static_cast<int64_t>(t) * a.K + k] == target ? 1 : 0;
+    const int inc = wave_inclusive_scan(cnt);
+    if (lane == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    int before = carry_s;
+    for (int q = 0; q < w; ++q) before += wsum[q];
+    int j = before + inc - cnt;
+    if (t < a.T)
+      for (int k = 0; k < a.K && cnt > 0; ++k)
+        if (idx[static_cast<int64_t>(t) * a.K + k] == target) {
+          if (j < a.M) slot_tok[j] = t;
+          ++j;
+        }
+    __syncthreads();
+    if (tid == 0) {
+      int tot = carry_s;
+      for (int q = 0; q < kLLThreads / kWave; ++q) tot += wsum[q];
+      carry_s = tot;
+    }
+    __syncthreads();
+  }
+  const int n = carry_s < a.M ? carry_s : a.M;
+  if (tid == 0) a.msg_count[l * a.R + s] = n;
+
+  const int nv = a.H / 8;              // 16-byte vectors of 8 bf16
+  const int G = a.H / kFp8Group;
+  for (int j = w; j < n; j += kLLThreads / kWave) {
+    const int t = slot_tok[j];
+    uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
+    if (lane == 0) *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
+    const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.x) + (static_cast<int64_t>(s) * a.T + t) * 2 * a.H;
+    if (a.use_fp8) {
+      float* scales = reinterpret_cast<float*>(msg + 16 + a.H);
+      for (int v0 = 0; v0 < nv; v0 += kWave) {
+        const int v = v0 + lane;
+        v4u d{0u, 0u, 0u, 0u};
+        if (v < nv) d = ld16<false>(xrow + static_cast<int64_t>(v) * 16);
+        const float amax = group16_max(v < nv ? absmax8(d) : 0.0f);
+        float sci;
+        const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
+        if (v < nv) {
+          st8<false>(msg + 16 + static_cast<int64_t>(v) * 8, cast8(d, sc));
+          if ((lane & 15) == 0) scales[v / 16] = sci;
+        }
+      }
+      (void)G;
+    } else {
+      for (int v = lane; v < nv; v += kWave)
+        st16<false>(msg + 16 + static_cast<int64_t>(v) * 16, ld16<false>(xrow + static_cast<int64_t>(v) * 16));
+    }
+  }
+}
+
+__global__ __launch_bounds__(kLLThreads) void ll_recv_kernel(LLArgs a) {
+  __shared__ int32_t begin_s;
+  const int l = blockIdx.x / a.R;
+  const int s = blockIdx.x % a.R;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  if (w == 0) {
+    int part = 0;
+    for (int q = lane; q < s; q += kWave) part += a.msg_count[l * a.R + q];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, kWave);
+    if (lane == 0) begin_s = part;
+  }
+  __syncthreads();
+  const int begin = begin_s;
+  const int n = a.msg_count[l * a.R + s];
+  if (tid == 0) {
+    a.layout_range[l * a.R + s] = (static_cast<int64_t>(begin) << 32) | static_cast<int64_t>(static_cast<uint32_t>(n));
+    if (s == a.R - 1) {
+      a.count[l] = begin + n;
+      if (a.cumulative) a.cumulative[l] += begin + n;
+    }
+  }
+  const int64_t pb = a.use_fp8 ? a.H : 2 * static_cast<int64_t>(a.H);  // payload bytes
+  const int nv = static_cast<int>(pb / 16);
+  const int G = a.H / kFp8Group;
+  const int64_t rows_per_expert = static_cast<int64_t>(a.R) * a.M;
+  for (int j = w; j < n; j += kLLThreads / kWave) {
+    const uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
+    const int64_t row = l * rows_per_expert + begin + j;
+    if (lane == 0) a.src_info[row] = *reinterpret_cast<const int32_t*>(msg);
+    uint8_t* out = static_cast<uint8_t*>(a.prx) + row * pb;
+    for (int v = lane; v < nv; v += kWave)
+      st16<false>(out + static_cast<int64_t>(v) * 16, ld16<false>(msg + 16 + static_cast<int64_t>(v) * 16));
+    if (a.use_fp8) {
+      const uint32_t* sc = reinterpret_cast<const uint32_t*>(msg + 16 + a.H);
+      for (int g = lane; g < G; g += kWave) {
+        const uint32_t bits = sc[g];
+        reinterpret_cast<uint32_t*>(a.prs)[row * G + g] = bits;
+        if (a.prue) a.prue[row * G + g] = static_cast<uint8_t>((bits >> 23) & 0xFFu);
+      }
+    }
+  }
+}
+
+hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
+  const int blocks = a.L * a.R;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(ll_send_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ll_recv_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace miep

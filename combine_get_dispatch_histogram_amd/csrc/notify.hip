@@ -1,0 +1,184 @@
+// notify.hip -- the dispatch's notify step on one GPU: the handle's prefix
+// matrices, the receive offsets, send_head and the aligned per-expert
+// receive counts.
+//
+// "Chapter 4  V1: layout, dispatch and combine", sections 4.1-4.2: a fresh
+// dispatch returns the rank prefix matrix, the channel prefix matrix, the
+// receive-side channel prefix matrix, the source indices and send_head,
+// which together form the reverse-routing handle.  Channels hold
+// ceil(T/C) consecutive tokens of a source ("DeepEP Normal vs Low-Latency
+// dual-mode analysis", V2 channel constants).  Across GPUs this step is an
+// exchange of counts; with the ranks as partitions of one GPU it is a local
+// scan.
+//
+// One workgroup per source partition s.  Its rank bases (rows of rank r
+// before source s) come from the layout's num_tokens_per_rank, so the
+// workgroups never wait on each other.  The token scan is a 64-lane ballot
+// + popcount per rank and wavefront, then an LDS scan across the
+// workgroup's wavefronts; send_head rows leave as 16-byte stores.
+#include "device.h"
+#include "kernels.h"
+
+namespace miep {
+
+constexpr int kNotifyMaxWaves = 16;
+
+template <int MW>
+__global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
+  __shared__ int32_t base[kMaxRanks];                 // rows of rank r from sources < s
+  __shared__ int32_t total[kMaxRanks];                // rows of rank r from all sources
+  __shared__ int32_t run[kMaxRanks];                  // tokens of s already scanned that go to r
+  __shared__ int32_t wt[kNotifyMaxWaves][kMaxRanks];  // per-wavefront counts -> exclusive bases
+
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int nw = blockDim.x / kWave;
+  const int R = a.R, T = a.T, C = a.C, S = a.S;
+
+  for (int r = tid; r < R; r += blockDim.x) {
+    int b = 0, tot = 0;
+    for (int q = 0; q < S; ++q) {
+      const int v = a.ntpr[static_cast<int64_t>(q) * R + r];
+      tot += v;
+      b += q < s ? v : 0;
+    }
+    base[r] = b;
+    total[r] = tot;
+    run[r] = 0;
+  }
+  __syncthreads();
+
+  // receive offsets: exclusive scan of the per-rank totals (workgroup 0)
+  if (s == 0 && w == 0) {
+    int carry = 0;
+    for (int r0 = 0; r0 < R; r0 += kWave) {
+      const int r = r0 + lane;
+      const int v = r < R ? total[r] : 0;
+      const int inc = wave_inclusive_scan(v);
+      if (r < R) a.off[r] = carry + inc - v;
+      carry += readlane(inc, kWave - 1);
+    }
+    if (lane == 0) a.off[R] = carry;
+  }
+
+  // per-expert receive counts, rounded up to the expert alignment
+  if (a.nrte != nullptr && a.ntpe != nullptr) {
+    for (int e = s * blockDim.x + tid; e < a.E; e += gridDim.x * blockDim.x) {
+      int64_t sum = 0;
+      for (int q = 0; q < S; ++q) sum += a.ntpe[static_cast<int64_t>(q) * a.E + e];
+      a.nrte[e] = static_cast<int32_t>((sum + a.align - 1) / a.align * a.align);
+    }
+  }
+
+  const int tc = T > 0 ? (T + C - 1) / C : 1;
+  for (int t0 = 0; t0 < T; t0 += blockDim.x) {
+    const int t = t0 + tid;
+    const bool valid = t < T;
+    const int64_t n = static_cast<int64_t>(s) * T + t;
+    RankMask<MW> m;
+    m.clear();
+    if (valid) {
+      const uint8_t* row = a.in_rank + n * R;
+      if ((R & 3) == 0) {
+        for (int r0 = 0; r0 < R; r0 += 4) {
+          const uint32_t b = *reinterpret_cast<const uint32_t*>(row + r0);
+          if (b & 0xFFu) m.set(r0);
+          if (b & 0xFF00u) m.set(r0 + 1);
+          if (b & 0xFF0000u) m.set(r0 + 2);
+          if (b & 0xFF000000u) m.set(r0 + 3);
+        }
+      } else {
+        for (int r = 0; r < R; ++r)
+          if (row[r]) m.set(r);
+      }
+    }
+    // pass 1: per-wavefront counts, lane j of the wave keeps rank r0 + j
+    for (int r0 = 0; r0 < R; r0 += kWave) {
+      const int rend = R - r0 < kWave ? R - r0 : kWave;
+      int mine = 0;
+      for (int j = 0; j < rend; ++j) {
+        const int c = __popcll(ballot(m.get(r0 + j) != 0));
+        mine = lane == j ? c : mine;
+      }
+      if (lane < rend) wt[w][r0 + lane] = mine;
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += blockDim.x) {
+      int acc = run[r];
+      for (int q = 0; q < nw; ++q) {
+        const int v = wt[q][r];
+        wt[q][r] = acc;
+        acc += v;
+      }
+      run[r] = acc;
+    }
+    __syncthreads();
+    // pass 2: exclusive rank within source s -> send_head, channel prefixes
+    const bool last_in_channel = valid && ((t % tc) == tc - 1 || t == T - 1);
+    const int c = t / tc;
+    for (int r0 = 0; r0 < R; r0 += 4) {
+      int v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = r0 + j;
+        v[j] = -1;
+        if (r < R) {
+          const bool bit = m.get(r) != 0;
+          const uint64_t b = ballot(bit);
+          const int pre = wt[w][r] + __popcll(b & lanemask_lt());
+          if (bit) v[j] = base[r] + pre;
+          if (last_in_channel) {
+            const int inc = pre + (bit ? 1 : 0);
+            a.cpm[(static_cast<int64_t>(s) * R + r) * C + c] = inc;
+            a.rcpm[(static_cast<int64_t>(r) * S + s) * C + c] = base[r] + inc;
+          }
+        }
+      }
+      if (valid) {
+        int32_t* dst = a.send_head + n * R + r0;
+        if ((R & 3) == 0) {
+          *reinterpret_cast<int4*>(dst) = make_int4(v[0], v[1], v[2], v[3]);
+        } else {
+          for (int j = 0; j < 4 && r0 + j < R; ++j) dst[j] = v[j];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // rank prefix row of this source; channels past the last token hold the total
+  const int nonempty = T > 0 ? (T + tc - 1) / tc : 0;
+  for (int r = tid; r < R; r += blockDim.x) {
+    a.rpm[static_cast<int64_t>(s) * R + r] = base[r] + run[r];
+    for (int c = nonempty; c < C; ++c) {
+      a.cpm[(static_cast<int64_t>(s) * R + r) * C + c] = run[r];
+      a.rcpm[(static_cast<int64_t>(r) * S + s) * C + c] = base[r] + run[r];
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(int32_t* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
+  if (a.S == 0) return hipSuccess;
+  int threads = ((a.T + kWave - 1) / kWave) * kWave;
+  threads = threads < kWave ? kWave : (threads > kNotifyMaxWaves * kWave ? kNotifyMaxWaves * kWave : threads);
+  if (a.R <= 64)
+    hipLaunchKernelGGL(notify_kernel<1>, dim3(a.S), dim3(threads), 0, st, a);
+  else
+    hipLaunchKernelGGL(notify_kernel<4>, dim3(a.S), dim3(threads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace miep

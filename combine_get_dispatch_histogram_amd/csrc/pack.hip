@@ -1,0 +1,192 @@
+// pack.hip -- normal-mode dispatch payload movement (fresh and cached).
+//
+// "Chapter 4  V1: layout, dispatch and combine", section 4.1: every token
+// goes to every rank whose experts it selected, rank-major, together with
+// its source index and the top-k entries that rank owns; the cached branch
+// moves only x (and its scales) along the same placement.  The optional
+// per-128-channel FP8 cast is the one of the low-latency send loop ("DeepEP
+// Normal vs Low-Latency dual-mode analysis").
+//
+// Push design: one wavefront per (token, row slice).  The slice is read
+// from HBM once into registers (16-byte loads) and written to each of the
+// rho receiving ranks' rows (16-byte stores), so HBM sees 1 read + rho
+// writes per token -- the minimum.  Destinations come from send_head: lane
+// r holds rank r's row, a ballot gives the destination set, and the wave
+// walks it with scalar find-first-set + readlane, so every store is a fully
+// coalesced 1 KiB wavefront store.  No atomics anywhere: placement was
+// fixed by the notify scan.
+#include "device.h"
+#include "kernels.h"
+
+namespace miep {
+
+template <int KIND, int VPL, int MW, bool NT>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
+  const int lane = lane_id();
+  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t n = gw / nslices;
+  const int slice = static_cast<int>(gw - n * nslices);
+  if (n >= a.N) return;
+  const int R = a.R;
+
+  // destination rows: lane holds rank (64*i + lane)
+  int dst[MW];
+  uint64_t dmask[MW];
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    const int r = kWave * i + lane;
+    int row = -1;
+    if (r < R) {
+      const int sh = a.send_head[n * R + r];
+      if (sh >= 0) row = a.off[r] + sh;
+    }
+    const bool ok = row >= 0 && row < a.capacity;
+    dst[i] = row;
+    dmask[i] = ballot(ok);
+  }
+
+  const int G = a.H / kFp8Group;
+  // top-k entries, source index and pre-quantised scales: once per token
+  if (slice == 0 && (a.meta || KIND == kPackFp8)) {
+    int64_t e = -1;
+    float wk = 0.0f;
+    if (a.meta && lane < a.K) {
+      e = a.topk_idx[n * a.K + lane];
+      if (a.topk_weights) wk = a.topk_weights[n * a.K + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      uint64_t m = dmask[i];
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        const int r = kWave * i + b;
+        const int64_t row = readlane(dst[i], b);
+        if (a.meta) {
+          if (lane < a.K) {
+            const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;
+            if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
+            if (a.recv_topk_weights) a.recv_topk_weights[row * a.K + lane] = mine ? wk : 0.0f;
+          }
+          if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(n % a.T);
+        }
+        if constexpr (KIND == kPackFp8) {
+          for (int g = lane; g < G; g += kWave) a.recv_x_scales[row * G + g] = a.x_scales[n * G + g];
+        }
+      }
+    }
+  }
+
+  // payload: input vectors are 16 bytes (8 bf16 or 16 E4M3 codes)
+  const int nv = KIND == kPackFp8 ? a.H / 16 : a.H / 8;
+  const int64_t in_row_bytes = KIND == kPackFp8 ? a.H : 2 * static_cast<int64_t>(a.H);
+  const int64_t out_row_bytes = KIND == kPackBf16 ? 2 * static_cast<int64_t>(a.H) : a.H;
+  const uint8_t* xrow = static_cast<const uint8_t*>(a.x) + n * in_row_bytes;
+  uint8_t* recv = static_cast<uint8_t*>(a.recv_x);
+  const int span = kWave * VPL;
+  for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
+    v4u d[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + j * kWave + lane;
+      if (v < nv) d[j] = ld16<NT>(xrow + static_cast<int64_t>(v) * 16);
+    }
+    if constexpr (KIND == kPackCastFp8) {
+      // 16 lanes hold one 128-channel group; nv is a multiple of 16, so a
+      // group is either entirely in range or entirely out.
+      v2u q[VPL];
+      float sci[VPL];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + j * kWave + lane;
+        const float amax = group16_max(v < nv ? absmax8(d[j]) : 0.0f);
+        const float sc = fp8_scales(amax, a.round_scale != 0, &sci[j]);
+        if (v < nv) q[j] = cast8(d[j], sc);
+      }
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        uint64_t m = dmask[i];
+        while (m) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          const int64_t row = readlane(dst[i], b);
+          uint8_t* orow = recv + row * out_row_bytes;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int v = v0 + j * kWave + lane;
+            if (v < nv) {
+              st8<NT>(orow + static_cast<int64_t>(v) * 8, q[j]);
+              if ((lane & 15) == 0) a.recv_x_scales[row * G + v / 16] = sci[j];
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        uint64_t m = dmask[i];
+        while (m) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          const int64_t row = readlane(dst[i], b);
+          uint8_t* orow = recv + row * out_row_bytes;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int v = v0 + j * kWave + lane;
+            if (v < nv) st16<NT>(orow + static_cast<int64_t>(v) * 16, d[j]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int KIND, int VPL, bool NT>
+static hipError_t launch_pack_vpl(const PackArgs& a, int nslices, hipStream_t st) {
+  const int64_t waves = a.N * nslices;
+  const int64_t blocks = (waves + 3) / 4;
+  if (a.R <= 64)
+    hipLaunchKernelGGL((pack_kernel<KIND, VPL, 1, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+                       nslices);
+  else
+    hipLaunchKernelGGL((pack_kernel<KIND, VPL, 4, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+                       nslices);
+  return hipGetLastError();
+}
+
+template <int KIND, bool NT>
+static hipError_t launch_pack_kind(const PackArgs& a, int vpl, int nslices, hipStream_t st) {
+  switch (vpl) {
+    case 2: return launch_pack_vpl<KIND, 2, NT>(a, nslices, st);
+    case 4: return launch_pack_vpl<KIND, 4, NT>(a, nslices, st);
+    case 7: return launch_pack_vpl<KIND, 7, NT>(a, nslices, st);
+    case 14: return launch_pack_vpl<KIND, 14, NT>(a, nslices, st);
+    default: return launch_pack_vpl<KIND, 8, NT>(a, nslices, st);
+  }
+}
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
+  if (a.N == 0) return hipSuccess;
+  const Tuning& tu = tuning();
+  const int nv = a.kind == kPackFp8 ? a.H / 16 : a.H / 8;
+  // default geometry: 7 vectors per lane when the row splits into 448-vector
+  // slices (hidden 7168 bf16 -> 2 slices), else 8 vectors per lane
+  int vpl = tu.pack_vpl > 0 ? tu.pack_vpl : (nv % (7 * kWave) == 0 ? 7 : 8);
+  int span = vpl * kWave;
+  int nslices = tu.pack_slices > 0 ? tu.pack_slices : (nv + span - 1) / span;
+  if (nslices < 1) nslices = 1;
+  const bool nt = tu.nt != 0;
+  switch (a.kind) {
+    case kPackFp8:
+      return nt ? launch_pack_kind<kPackFp8, true>(a, vpl, nslices, st)
+                : launch_pack_kind<kPackFp8, false>(a, vpl, nslices, st);
+    case kPackCastFp8:
+      return nt ? launch_pack_kind<kPackCastFp8, true>(a, vpl, nslices, st)
+                : launch_pack_kind<kPackCastFp8, false>(a, vpl, nslices, st);
+    default:
+      return nt ? launch_pack_kind<kPackBf16, true>(a, vpl, nslices, st)
+                : launch_pack_kind<kPackBf16, false>(a, vpl, nslices, st);
+  }
+}
+
+}  // namespace miep

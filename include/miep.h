@@ -1,0 +1,197 @@
+/*
+ * miep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel core:
+ * layout histogram, normal-mode dispatch with its handle, cached dispatch,
+ * combine, and low-latency (expert-major, optionally FP8) dispatch.
+ *
+ * One GPU plays every rank: the R logical ranks are partitions of one
+ * device's HBM, and the S source partitions are the token blocks that the
+ * R ranks would each send.  No inter-GPU transport is involved.
+ *
+ * Pages the calls follow (titles as published):
+ *   [Ch4]  "Chapter 4  V1: layout, dispatch and combine", sections 4.1-4.5
+ *   [NvLL] "DeepEP Normal vs Low-Latency dual-mode analysis"
+ *   [Phil] "Normal vs Low-Latency: two communication philosophies in
+ *          DeepEP V1 / V2 / DeepGEMM"
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless a parameter says "host", owned by
+ *     the caller; the library keeps no pointer after the call returns and
+ *     allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; the caller orders and synchronises.
+ *   - Integer matrices are row-major int32 unless noted; booleans are one
+ *     byte, 0 or 1.  bf16 data is passed as its 16-bit patterns.
+ *   - Every call returns miep_status; on failure nothing was enqueued and
+ *     miep_last_error() describes the reason (thread-local, host memory
+ *     owned by the library).  No call aborts, traps or prints.
+ *   - Device-side bounds: rows at or past `recv_capacity` are never
+ *     written; top-k entries outside [0, num_experts) are treated as masked.
+ */
+#ifndef MIEP_H
+#define MIEP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum miep_status {
+  MIEP_OK = 0,
+  MIEP_EINVAL = 1,       /* a bad argument: null pointer, size or flag */
+  MIEP_EUNSUPPORTED = 2, /* valid, but outside what the kernels handle (e.g. R > 256, misaligned x) */
+  MIEP_EHIP = 3          /* the HIP runtime refused a launch */
+} miep_status;
+
+/* Payload kinds of a normal-mode dispatch. */
+typedef enum miep_xkind {
+  MIEP_X_BF16 = 0,          /* x: [N][H] bf16; rows travel as 2H bytes                         */
+  MIEP_X_FP8 = 1,           /* x: [N][H] E4M3 codes + x_scales [N][H/128] fp32 (pre-quantised)  */
+  MIEP_X_BF16_CAST_FP8 = 2  /* x: [N][H] bf16, cast per 128 channels to E4M3 + fp32 scales      */
+} miep_xkind;
+
+/* Sizes of one normal-mode problem.  N = num_src * num_tokens tokens. */
+typedef struct miep_problem {
+  int32_t num_src;          /* S: source partitions (the sending ranks)                  */
+  int32_t num_tokens;       /* T: tokens per source partition                             */
+  int32_t hidden;           /* H: channels per token                                      */
+  int32_t num_topk;         /* K: experts per token                                       */
+  int32_t num_experts;      /* E: experts; expert e lives on rank e / (E / R)              */
+  int32_t num_ranks;        /* R: receiving ranks, 1..256; R > 8 needs R % 8 == 0          */
+  int32_t num_channels;     /* C: channels splitting each source's tokens (ceil(T/C) each) */
+  int32_t expert_alignment; /* a >= 1: per-expert receive counts rounded up to a multiple  */
+} miep_problem;
+
+/* The normal-mode handle ([Ch4] 4.2: a reverse-routing record, reused by
+ * cached dispatch and combine).  All arrays are caller-owned device memory;
+ * miep_dispatch fills every non-const member, is_token_in_rank is its input.
+ *   rank_prefix_matrix[s][r]            inclusive over sources: rows rank r receives from sources 0..s
+ *   channel_prefix_matrix[s][r][c]      inclusive over channels: tokens of source s, channels 0..c, sent to r
+ *   recv_channel_prefix_matrix[r][s][c] rank r's row count before source s plus channel_prefix_matrix[s][r][c]
+ *   recv_rank_offset[r]                 first receive row of rank r; [R] = total rows (may exceed capacity)
+ *   recv_src_idx[row]                   token index t (within its source) of each receive row
+ *   is_token_in_rank[n][r]              layout membership, n = s*T + t
+ *   send_head[n][r]                     row of token n inside rank r's block, or -1
+ * Rank r's rows are recv rows [recv_rank_offset[r], recv_rank_offset[r+1]),
+ * ordered by (source, token).  The handle stays valid while the arrays live
+ * and the routing is unchanged. */
+typedef struct miep_handle {
+  int32_t* rank_prefix_matrix;         /* [S][R]    */
+  int32_t* channel_prefix_matrix;      /* [S][R][C] */
+  int32_t* recv_channel_prefix_matrix; /* [R][S][C] */
+  int32_t* recv_rank_offset;           /* [R + 1]   */
+  int32_t* recv_src_idx;               /* [recv_capacity] */
+  const uint8_t* is_token_in_rank;     /* [N][R]    */
+  int32_t* send_head;                  /* [N][R]    */
+  int64_t recv_capacity;               /* rows allocated in every receive-side array */
+} miep_handle;
+
+/* get_dispatch_layout -- [Ch4] 4.1: from the top-k routing compute the
+ * tokens per rank, per RDMA rank (groups of 8 ranks, [NvLL] RDMA rank
+ * translation), per expert, and the token-in-rank membership.
+ *   topk_idx                 [N][K] int64, negative = masked
+ *   num_tokens_per_rank      [S][R]   out
+ *   num_tokens_per_rdma_rank [S][R/8] out; must be NULL when R <= 8, non-NULL when R > 8
+ *   num_tokens_per_expert    [S][E]   out (counts top-k entries)
+ *   is_token_in_rank         [N][R]   out (0/1 bytes)
+ * Errors: EINVAL for a null required pointer or bad sizes (E % R != 0,
+ * R > 8 with R % 8 != 0); EUNSUPPORTED for R > 256 or E > 8192. */
+miep_status miep_get_dispatch_layout(const miep_problem* p, const int64_t* topk_idx,
+                                     int32_t* num_tokens_per_rank, int32_t* num_tokens_per_rdma_rank,
+                                     int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank, void* stream);
+
+/* dispatch -- [Ch4] 4.1 fresh branch: notify (the prefix matrices) then
+ * pack every token into each rank that receives it, rank-major.
+ *   x                  [N][H] per x_kind (16-byte aligned; H % 8 == 0, FP8 kinds H % 128 == 0)
+ *   x_scales           [N][H/128] fp32 for MIEP_X_FP8, else ignored
+ *   round_scale        for MIEP_X_BF16_CAST_FP8: power-of-two scales
+ *   topk_idx           [N][K] int64, nullable (then no recv_topk_* output)
+ *   topk_weights       [N][K] fp32, nullable
+ *   num_tokens_per_rank   [S][R] from get_dispatch_layout (source of the rank prefixes)
+ *   num_tokens_per_expert [S][E] from get_dispatch_layout, nullable
+ *   recv_x             [cap][H] bf16, or [cap][H] E4M3 codes for the FP8 kinds
+ *   recv_x_scales      [cap][H/128] fp32 for the FP8 kinds
+ *   recv_topk_idx      [cap][K] int64: local expert id (e - r*E/R) where expert e is on the row's rank, else -1
+ *   recv_topk_weights  [cap][K] fp32: the weight there, else 0
+ *   num_recv_tokens_per_expert [R][E/R] out, nullable: per-expert receive count rounded up to expert_alignment
+ *   h                  the handle (all members required; cap = h->recv_capacity)
+ * Size the receive side exactly with sum(num_tokens_per_rank), or with a
+ * worst case (the num_worst_tokens mode): recv_rank_offset[R] reports the
+ * true total either way. */
+miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                          int32_t round_scale, const int64_t* topk_idx, const float* topk_weights,
+                          const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_expert, void* recv_x,
+                          float* recv_x_scales, int64_t* recv_topk_idx, float* recv_topk_weights,
+                          int32_t* num_recv_tokens_per_expert, const miep_handle* h, void* stream);
+
+/* cached_dispatch -- [Ch4] 4.1 cached branch: with a handle from an earlier
+ * dispatch of the same routing, move only x (and its scales); there are no
+ * top-k arguments.  Arguments as in miep_dispatch; only h->send_head,
+ * h->recv_rank_offset and h->recv_capacity are read. */
+miep_status miep_cached_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                                 int32_t round_scale, const miep_handle* h, void* recv_x, float* recv_x_scales,
+                                 void* stream);
+
+/* combine -- [Ch4] 4.2 and 4.4: send expert outputs back through the handle
+ * and add them per source token in fp32 (no gate weights applied), and
+ * separately add the received top-k weights.  Contributions are added in
+ * ascending rank order; a token no rank received combines to zero.
+ *   y                     [cap][H] bf16 expert outputs in the receive layout
+ *   recv_topk_weights     [cap][K] fp32, nullable
+ *   combined_x            [N][H] bf16 out (round to nearest even)
+ *   combined_topk_weights [N][K] fp32 out, nullable (required if recv_topk_weights is given)
+ * Reads h->send_head, h->recv_rank_offset, h->recv_capacity. */
+miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
+                         const miep_handle* h, uint16_t* combined_x, float* combined_topk_weights, void* stream);
+
+/* Sizes of one low-latency problem, seen from the receiving rank dest_rank. */
+typedef struct miep_ll_problem {
+  int32_t num_ranks;   /* R: source ranks (all ranks send), 1..1024          */
+  int32_t num_tokens;  /* T: tokens per source rank, T <= max_tokens          */
+  int32_t max_tokens;  /* M: num_max_dispatch_tokens_per_rank (slot capacity) */
+  int32_t hidden;      /* H: H % 8 == 0; with FP8, H % 128 == 0               */
+  int32_t num_topk;    /* K */
+  int32_t num_experts; /* E: E % R == 0; L = E / R local experts per rank     */
+  int32_t dest_rank;   /* d: the receiving rank modelled                      */
+} miep_ll_problem;
+
+/* Bytes of one low-latency message ([Phil] message format): a 16-byte
+ * header (int32 source token index + 3 reserved int32, zero here), then
+ * either H E4M3 bytes and H/128 fp32 scales, or 2H bf16 bytes.  Host-only. */
+int64_t miep_ll_msg_bytes(int32_t hidden, int32_t use_fp8);
+
+/* low_latency_dispatch -- [NvLL] low-latency dispatch (send loop, receive
+ * layout) and [Ch4] 4.3 outputs.  Send side: every top-k entry of a source
+ * token that names one of rank d's local experts becomes one message,
+ * written expert-major to slot (l, s, j) of msg_buf; j counts such entries
+ * of source s in (token, k) order.  Receive side: for each local expert l
+ * the (l, s) blocks are packed in ascending s.
+ *   x              [R*T][H] bf16;  topk_idx [R*T][K] int64 (negative = masked)
+ *   use_fp8        cast per 128 channels (round_scale: power-of-two scales;
+ *                  use_ue8m0 additionally emits exponent bytes, requires round_scale)
+ *   msg_buf        [L][R][M] messages of miep_ll_msg_bytes() (16-byte aligned) -- scratch standing in for the transport
+ *   msg_count      [L][R] int32 out: messages per (local expert, source), capped at M
+ *   packed_recv_x  [L][R*M][H] E4M3 codes, or bf16 without FP8 (rows past the count untouched)
+ *   packed_recv_x_scales [L][R*M][H/128] fp32 (FP8 only)
+ *   packed_recv_x_scales_ue8m0 [L][R*M][H/128] uint8 exponent + 127, nullable (FP8 + use_ue8m0 only)
+ *   packed_recv_src_info [L][R*M] int32: source token index of each row
+ *   packed_recv_layout_range [L][R] int64: (first row << 32) | count
+ *   packed_recv_count [L] int32: rows per local expert
+ *   cumulative_local_expert_recv_stats [L] int32, nullable: += packed_recv_count */
+miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,
+                             int32_t round_scale, int32_t use_ue8m0, void* msg_buf, int32_t* msg_count,
+                             void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
+                             int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
+                             int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats, void* stream);
+
+/* Description of the last failure on this thread ("" if none). Host-only. */
+const char* miep_last_error(void);
+
+/* Library version string. Host-only. */
+const char* miep_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIEP_H */

@@ -1,0 +1,150 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/miep.h declares, and its host-only helpers and argument validation
+behave as documented.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from combine_get_dispatch_histogram_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miep.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(miep_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from combine_get_dispatch_histogram_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
+              "miep_ll_dispatch"):
+        assert f in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(miep_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_host_helpers(lib):
+    assert lib.miep_ll_msg_bytes(7168, 1) == 7408
+    assert lib.miep_ll_msg_bytes(7168, 0) == 14352
+    assert lib.miep_ll_msg_bytes(0, 1) == -1
+    assert b"gfx950" in lib.miep_version()
+
+
+def _problem(**kw):
+    d = dict(num_src=8, num_tokens=512, hidden=7168, num_topk=8, num_experts=256, num_ranks=8, num_channels=24,
+             expert_alignment=1)
+    d.update(kw)
+    return _lib.Problem(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_experts=250), _lib.MIEP_EINVAL),          # E % R != 0
+    (dict(num_ranks=12, num_experts=240), _lib.MIEP_EINVAL),   # R > 8, R % 8 != 0
+    (dict(num_ranks=512, num_experts=512), _lib.MIEP_EUNSUPPORTED),
+    (dict(num_experts=16384, num_ranks=8), _lib.MIEP_EUNSUPPORTED),
+    (dict(expert_alignment=0), _lib.MIEP_EINVAL),
+    (dict(num_channels=0), _lib.MIEP_EINVAL),
+    (dict(num_tokens=-1), _lib.MIEP_EINVAL),
+    (dict(num_topk=65), _lib.MIEP_EUNSUPPORTED),
+])
+def test_layout_rejects_bad_problems(lib, kw, status):
+    p = _problem(**kw)
+    rc = lib.miep_get_dispatch_layout(ctypes.byref(p), 16, 16, None, 16, 16, None)
+    assert rc == status, lib.miep_last_error()
+    assert lib.miep_last_error()
+
+
+def test_layout_rejects_null_and_rdma_mismatch(lib):
+    p = _problem()
+    assert lib.miep_get_dispatch_layout(None, 16, 16, None, 16, 16, None) == _lib.MIEP_EINVAL
+    assert lib.miep_get_dispatch_layout(ctypes.byref(p), None, 16, None, 16, 16, None) == _lib.MIEP_EINVAL
+    # R = 8: the RDMA counts must be NULL; R = 16: they are required
+    assert lib.miep_get_dispatch_layout(ctypes.byref(p), 16, 16, 16, 16, 16, None) == _lib.MIEP_EINVAL
+    p16 = _problem(num_ranks=16)
+    assert lib.miep_get_dispatch_layout(ctypes.byref(p16), 16, 16, None, 16, 16, None) == _lib.MIEP_EINVAL
+
+
+def test_dispatch_validation(lib):
+    p = _problem()
+    h = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, 100)
+    # misaligned x
+    rc = lib.miep_dispatch(ctypes.byref(p), 8, 0, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None, ctypes.byref(h),
+                           None)
+    assert rc == _lib.MIEP_EUNSUPPORTED
+    # FP8 payload without scales
+    rc = lib.miep_dispatch(ctypes.byref(p), 16, 1, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None, ctypes.byref(h),
+                           None)
+    assert rc == _lib.MIEP_EINVAL
+    # unknown kind
+    rc = lib.miep_dispatch(ctypes.byref(p), 16, 7, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None, ctypes.byref(h),
+                           None)
+    assert rc == _lib.MIEP_EINVAL
+    # handle missing arrays
+    hbad = _lib.HandleC(None, 16, 16, 16, 16, 16, 16, 100)
+    rc = lib.miep_dispatch(ctypes.byref(p), 16, 0, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None,
+                           ctypes.byref(hbad), None)
+    assert rc == _lib.MIEP_EINVAL
+    # FP8 cast needs hidden % 128 == 0
+    p2 = _problem(hidden=200)
+    rc = lib.miep_dispatch(ctypes.byref(p2), 16, 2, None, 0, 16, 16, 16, 16, 16, 16, 16, 16, None, ctypes.byref(h),
+                           None)
+    assert rc == _lib.MIEP_EINVAL
+    # negative capacity
+    hneg = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, -1)
+    rc = lib.miep_cached_dispatch(ctypes.byref(p), 16, 0, None, 0, ctypes.byref(hneg), 16, None, None)
+    assert rc == _lib.MIEP_EINVAL
+
+
+def test_combine_validation(lib):
+    p = _problem()
+    h = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, 100)
+    assert lib.miep_combine(ctypes.byref(p), None, None, ctypes.byref(h), 16, None, None) == _lib.MIEP_EINVAL
+    assert lib.miep_combine(ctypes.byref(p), 16, 16, ctypes.byref(h), 16, None, None) == _lib.MIEP_EINVAL
+    assert lib.miep_combine(ctypes.byref(p), 8, None, ctypes.byref(h), 16, None, None) == _lib.MIEP_EUNSUPPORTED
+
+
+def test_ll_validation(lib):
+    def q(**kw):
+        d = dict(num_ranks=32, num_tokens=128, max_tokens=128, hidden=7168, num_topk=8, num_experts=256, dest_rank=0)
+        d.update(kw)
+        return _lib.LLProblem(**d)
+
+    args = [16, 16, 1, 1, 1, 16, 16, 16, 16, 16, 16, 16, 16, None, None]
+    assert lib.miep_ll_dispatch(ctypes.byref(q(num_tokens=129)), *args) == _lib.MIEP_EINVAL
+    assert lib.miep_ll_dispatch(ctypes.byref(q(dest_rank=32)), *args) == _lib.MIEP_EINVAL
+    assert lib.miep_ll_dispatch(ctypes.byref(q(hidden=7040)), *args) == _lib.MIEP_EUNSUPPORTED
+    bad = list(args)
+    bad[3], bad[4] = 0, 1                      # ue8m0 without round_scale
+    assert lib.miep_ll_dispatch(ctypes.byref(q()), *bad) == _lib.MIEP_EINVAL
+    nul = list(args)
+    nul[5] = None                              # msg_buf NULL
+    assert lib.miep_ll_dispatch(ctypes.byref(q()), *nul) == _lib.MIEP_EINVAL
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,471 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact for the layout, the handle (prefix matrices, offsets,
+send_head, recv_src_idx), the received rows and top-k metadata, the FP8
+codes and scales, and the low-latency messages and packed outputs.  Combine
+is compared bit-exactly too (same summation order), and additionally held to
+the stated tolerances: max relative error < 1e-2 against the fp32 reference
+and, for identity experts, calc_diff < 5e-6 after dividing by the number of
+receiving ranks.  Full-size workloads compare every output the oracle can
+produce in seconds and sampled rows for the FP8 payloads.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_get_dispatch_histogram_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import combine_get_dispatch_histogram_amd as miep  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def u16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def u8(t):
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def npy(t):
+    return t.detach().cpu().numpy()
+
+
+def _inputs(w, seed=0):
+    inp = wl.normal_inputs(w, seed)
+    return inp["x"], inp["topk_idx"], inp["topk_weights"]
+
+
+def _ref_dispatch(w, x_bits, idx, wts, lay, **kw):
+    return oracle.dispatch(x_bits, idx, wts, lay["is_token_in_rank"], lay["num_tokens_per_expert"], S=w.S, E=w.E,
+                           R=w.R, C=w.C, expert_alignment=w.expert_alignment, **kw)
+
+
+def _check_layout(w, idx_t, got):
+    ntpr, ntp_rdma, ntpe, itr = got
+    ref = oracle.layout(npy(idx_t), w.S, w.E, w.R)
+    assert np.array_equal(npy(ntpr), ref["num_tokens_per_rank"])
+    assert np.array_equal(npy(ntpe), ref["num_tokens_per_expert"])
+    assert np.array_equal(npy(itr).astype(np.uint8), ref["is_token_in_rank"])
+    if w.R > 8:
+        assert np.array_equal(npy(ntp_rdma), ref["num_tokens_per_rdma_rank"])
+    else:
+        assert ntp_rdma is None
+    return ref
+
+
+def _check_handle(h, ref):
+    assert np.array_equal(npy(h.rank_prefix_matrix), ref["rank_prefix_matrix"])
+    assert np.array_equal(npy(h.channel_prefix_matrix), ref["channel_prefix_matrix"])
+    assert np.array_equal(npy(h.recv_channel_prefix_matrix), ref["recv_channel_prefix_matrix"])
+    assert np.array_equal(npy(h.recv_rank_offset), ref["recv_rank_offset"])
+    assert np.array_equal(npy(h.send_head), ref["send_head"])
+    n = min(ref["num_recv"], h.recv_capacity)
+    assert np.array_equal(npy(h.recv_src_idx)[:n], ref["recv_src_idx"][:n])
+
+
+SMALL = [
+    # name, S, T, H, E, R, K, C, align
+    ("tiny", 4, 32, 256, 16, 4, 4, 24, 1),
+    ("ragged", 3, 1500, 2056, 48, 6, 5, 7, 4),       # 2 token tiles, R % 4 != 0, ragged row tail
+    ("one-src", 1, 700, 7168, 64, 8, 8, 24, 1),
+    ("r16", 4, 96, 512, 64, 16, 6, 24, 2),            # two RDMA groups
+    ("r128", 2, 100, 256, 1024, 128, 8, 5, 1),        # 2-word rank masks
+    ("r256", 2, 64, 264, 2048, 256, 9, 3, 1),
+    ("r1", 2, 40, 128, 8, 1, 2, 4, 1),
+]
+
+
+def _small_workload(name, S, T, H, E, R, K, C, align, **kw):
+    return wl.NormalWorkload(name, S=S, T=T, H=H, E=E, R=R, K=K, C=C, expert_alignment=align, **kw)
+
+
+def _masked_inputs(w, seed, mask_p=0.0, dup_p=0.0, oob_p=0.0):
+    x, idx, wts = _inputs(w, seed)
+    rng = np.random.default_rng(seed)
+    idx = idx.numpy().copy()
+    if dup_p and w.K > 1:
+        d = rng.random(w.N) < dup_p
+        idx[d, 1] = idx[d, 0]
+    if mask_p:
+        idx[rng.random(idx.shape) < mask_p] = -1
+    if oob_p:
+        idx[rng.random(idx.shape) < oob_p] = w.E + 3
+    return x, torch.from_numpy(idx), wts
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("variant", ["plain", "masked-dup-oob"])
+def test_layout_dispatch_combine_small(case, variant):
+    w = _small_workload(*case)
+    say("layout/dispatch/combine", case, variant)
+    if variant == "plain":
+        x, idx, wts = _inputs(w, 1)
+    else:
+        x, idx, wts = _masked_inputs(w, 2, mask_p=0.2, dup_p=0.2, oob_p=0.05)
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    lay = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    ref_lay = _check_layout(w, idx, lay)
+    ntpr, _, ntpe, itr = lay
+    recv_x, _, rti, rtw, nrte, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, w.expert_alignment)
+    ref = _ref_dispatch(w, wl.bf16_bits(x), idx.numpy(), wts.numpy(), ref_lay)
+    torch.cuda.synchronize()
+    _check_handle(h, ref)
+    assert np.array_equal(u16(recv_x), ref["recv_x"])
+    assert np.array_equal(npy(rti), ref["recv_topk_idx"])
+    assert np.array_equal(npy(rtw).view(np.uint32), ref["recv_topk_weights"].view(np.uint32))
+    assert np.array_equal(npy(nrte), ref["num_recv_tokens_per_expert"])
+    # combine of random expert outputs: bit-exact against the oracle (same order)
+    y = wl.expert_outputs(h.recv_capacity, w.H, seed=5)
+    cx, cw = miep.combine(y.to(DEV), h, rtw)
+    rc = oracle.combine(wl.bf16_bits(y), ref["recv_topk_weights"], ref["send_head"], ref["recv_rank_offset"], S=w.S,
+                        want_f32=True)
+    assert np.array_equal(u16(cx), rc["combined_x"])
+    assert np.array_equal(npy(cw).view(np.uint32), rc["combined_topk_weights"].view(np.uint32))
+
+
+@pytest.mark.parametrize("wname", ["tiny", "normal", "skewed"])
+def test_full_workload_bf16(wname):
+    """Full-size normal / skewed workloads: every output bit-exact, identity
+    round trip and random-y combine within the stated tolerances."""
+    w = wl.WORKLOADS[wname]
+    say("full bf16", wname)
+    x, idx, wts = _inputs(w, 0)
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    lay = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    ref_lay = _check_layout(w, idx, lay)
+    if wname != "skewed":
+        # per-expert counts sum to the valid top-k entries
+        assert int(lay[2].sum()) == int((idx >= 0).sum())
+    ntpr, _, ntpe, itr = lay
+    recv_x, _, rti, rtw, nrte, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C)
+    x_bits = wl.bf16_bits(x)
+    ref = _ref_dispatch(w, x_bits, idx.numpy(), wts.numpy(), ref_lay)
+    torch.cuda.synchronize()
+    _check_handle(h, ref)
+    assert np.array_equal(u16(recv_x), ref["recv_x"])
+    assert np.array_equal(npy(rti), ref["recv_topk_idx"])
+    assert np.array_equal(npy(rtw).view(np.uint32), ref["recv_topk_weights"].view(np.uint32))
+    assert np.array_equal(npy(nrte), ref["num_recv_tokens_per_expert"])
+
+    # identity experts: combined / (#ranks that received the token) == x
+    cx, cw = miep.combine(recv_x, h, rtw)
+    rc = oracle.combine(ref["recv_x"], ref["recv_topk_weights"], ref["send_head"], ref["recv_rank_offset"], S=w.S)
+    assert np.array_equal(u16(cx), rc["combined_x"])
+    cnt = ref_lay["is_token_in_rank"].sum(axis=1).astype(np.float64)
+    got = cx.float().cpu().numpy().astype(np.float64)
+    xf = x.float().numpy().astype(np.float64)
+    ok = cnt > 0
+    assert oracle.calc_diff(got[ok] / cnt[ok, None], xf[ok]) < 5e-6
+    assert np.all(got[~ok] == 0)
+    valid = (idx.numpy() >= 0) & ok[:, None]
+    assert np.array_equal(npy(cw)[valid], wts.numpy()[valid])
+
+    # random expert outputs: max relative error vs the fp32 reference < 1e-2
+    y = wl.expert_outputs(h.recv_capacity, w.H, seed=3)
+    cy, _ = miep.combine(y.to(DEV), h)
+    ry = oracle.combine(wl.bf16_bits(y), None, ref["send_head"], ref["recv_rank_offset"], S=w.S, want_f32=True)
+    assert np.array_equal(u16(cy), ry["combined_x"])
+    g = cy.float().cpu().numpy().astype(np.float64)
+    f = ry["combined_f32"].astype(np.float64)
+    assert (np.abs(g - f) / np.maximum(np.abs(f), 1e-6)).max() < 1e-2
+
+
+def test_cached_dispatch_normal():
+    w = wl.NORMAL
+    say("cached dispatch", w.name)
+    x, idx, wts = _inputs(w, 0)
+    idxd = idx.to(DEV)
+    ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    _, _, _, _, _, h = miep.dispatch(x.to(DEV), idxd, wts.to(DEV), ntpr, itr, ntpe, w.E, w.C)
+    x2 = wl.activations(w.N, w.H, torch.Generator().manual_seed(9))
+    recv2, _ = miep.cached_dispatch(x2.to(DEV), h)
+    ref = oracle.cached_dispatch(wl.bf16_bits(x2), npy(h.send_head), npy(h.recv_rank_offset), S=w.S,
+                                 capacity=h.recv_capacity)
+    assert np.array_equal(u16(recv2), ref["recv_x"])
+
+
+def test_capacity_guard_and_worst_case_mode():
+    """Worst-case capacity: the true total is reported, rows past the
+    capacity are never written (guard rows stay intact)."""
+    w = _small_workload("cap", 2, 300, 512, 32, 4, 4, 6, 1)
+    say("capacity guard", w)
+    x, idx, wts = _inputs(w, 4)
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    total = int(ntpr.sum())
+    ref = oracle.dispatch(wl.bf16_bits(x), idx.numpy(), wts.numpy(), npy(itr).astype(np.uint8), npy(ntpe), S=w.S,
+                          E=w.E, R=w.R, C=w.C)
+    for cap in (total // 2, total, w.N * w.R):
+        guard = 64
+        h = miep.Handle.allocate(itr, w.S, w.K, w.E, w.C, cap)
+        recv_x = torch.full((cap + guard, w.H), 7.0, dtype=torch.bfloat16, device=DEV)
+        rti = torch.full((cap + guard, w.K), 123, dtype=torch.int64, device=DEV)
+        rtw = torch.full((cap + guard, w.K), 5.0, dtype=torch.float32, device=DEV)
+        miep.dispatch_into(xd, idxd, wd, ntpr, ntpe, h, recv_x, None, rti, rtw, None)
+        torch.cuda.synchronize()
+        n = min(cap, total)
+        assert int(h.recv_rank_offset[-1]) == total
+        assert np.array_equal(u16(recv_x[:n]), ref["recv_x"][:n])
+        assert np.array_equal(npy(rti[:n]), ref["recv_topk_idx"][:n])
+        assert bool((recv_x[cap:] == 7.0).all()) and bool((rti[cap:] == 123).all()) and bool((rtw[cap:] == 5).all())
+        if cap > total:
+            assert bool((recv_x[total:] == 7.0).all())
+        assert np.array_equal(npy(h.send_head), ref["send_head"])
+
+
+def test_empty_inputs():
+    say("empty: T = 0")
+    w = _small_workload("empty", 4, 0, 256, 16, 4, 4, 24, 1)
+    idx = torch.empty((0, w.K), dtype=torch.int64, device=DEV)
+    ntpr, _, ntpe, itr = miep.get_dispatch_layout(idx, w.E, w.R, w.S)
+    assert int(ntpr.abs().sum()) == 0 and int(ntpe.abs().sum()) == 0
+    x = torch.empty((0, w.H), dtype=torch.bfloat16, device=DEV)
+    recv_x, _, rti, rtw, nrte, h = miep.dispatch(x, idx, torch.empty((0, w.K), device=DEV), ntpr, itr, ntpe, w.E,
+                                                 w.C)
+    torch.cuda.synchronize()
+    assert recv_x.shape[0] == 0
+    assert npy(h.recv_rank_offset).tolist() == [0] * (w.R + 1)
+    assert int(h.channel_prefix_matrix.abs().sum()) == 0 and int(h.rank_prefix_matrix.abs().sum()) == 0
+    assert int(nrte.abs().sum()) == 0
+    cx, cw = miep.combine(torch.empty((0, w.H), dtype=torch.bfloat16, device=DEV), h, rtw)
+    assert cx.shape == (0, w.H)
+
+
+def test_all_masked_tokens_combine_to_zero():
+    w = _small_workload("masked", 2, 64, 256, 16, 4, 4, 3, 1)
+    say("all masked", w)
+    x, idx, wts = _inputs(w, 6)
+    idx = idx.clone()
+    idx[::2] = -1                          # every other token goes nowhere
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    recv_x, _, rti, rtw, _, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C)
+    cx, cw = miep.combine(recv_x, h, rtw)
+    torch.cuda.synchronize()
+    assert bool((cx[::2] == 0).all()) and bool((cw[::2] == 0).all())
+    assert not bool(torch.signbit(cx[::2]).any())
+
+
+# --------------------------------------------------------------------------- FP8
+def _exhaustive_bf16_rows(H=7168):
+    """Every finite bf16 pattern, in 128-channel groups that each hold one
+    448: the plain and the power-of-two scales are then exactly 1, so the
+    codes are the E4M3 encodings of the bf16 values themselves."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = (pats.astype(np.uint32) << 16).view(np.float32)
+    pats = pats[np.isfinite(f) & (np.abs(f) <= 448.0)]
+    per = 127
+    ngroups = -(-pats.size // per)
+    groups = np.zeros((ngroups, 128), np.uint16)
+    flat = np.zeros(ngroups * per, np.uint16)
+    flat[:pats.size] = pats
+    groups[:, :per] = flat.reshape(ngroups, per)
+    groups[:, per] = 0x43E0                # 448.0 in bf16
+    G = H // 128
+    rows = -(-ngroups // G)
+    out = np.zeros((rows * G, 128), np.uint16)
+    out[:, 127] = 0x43E0
+    out[:ngroups] = groups
+    return out.reshape(rows, H)
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_fp8_cast_exhaustive_bf16(round_scale):
+    say("fp8 cast exhaustive bf16", round_scale)
+    xb = _exhaustive_bf16_rows()
+    N, H = xb.shape
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16)
+    idx = torch.zeros((N, 1), dtype=torch.int64)          # every token to expert 0 on rank 0
+    xd, idxd = x.to(DEV), idx.to(DEV)
+    ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, 1, 1, 1)
+    rx, rs, _, _, _, h = miep.dispatch(xd, idxd, None, ntpr, itr, ntpe, 1, 1, cast_to_fp8=True,
+                                       round_scale=round_scale)
+    codes, sci, _ = oracle.fp8_quantize(xb, round_scale)
+    assert np.array_equal(npy(rs).view(np.uint32), sci.view(np.uint32))
+    assert np.all(sci == 1.0)
+    got = u8(rx)
+    bad = np.nonzero(got != codes)
+    assert bad[0].size == 0, (xb[bad][:8], got[bad][:8], codes[bad][:8])
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_fp8_dispatch_kinds_small(round_scale):
+    """Fused cast and pre-quantised FP8 dispatch on a ragged multi-tile case,
+    with magnitudes that exercise subnormal codes and saturation edges."""
+    w = _small_workload("fp8", 3, 200, 1152, 48, 16, 4, 5, 1)
+    say("fp8 kinds", w, round_scale)
+    x, idx, wts = _inputs(w, 8)
+    scale = torch.tensor(np.random.default_rng(0).choice([1e-6, 1e-3, 1.0, 300.0, 3e4], (w.N, 1)),
+                         dtype=torch.float32)
+    x = (x.float() * scale).to(torch.bfloat16)
+    x[5, :128] = 0.0
+    xb = wl.bf16_bits(x)
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    ref_lay = oracle.layout(idx.numpy(), w.S, w.E, w.R)
+    ref = _ref_dispatch(w, xb, idx.numpy(), wts.numpy(), ref_lay, x_kind=oracle.X_BF16_CAST_FP8,
+                        round_scale=round_scale)
+    rx, rs, rti, rtw, _, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True,
+                                           round_scale=round_scale)
+    torch.cuda.synchronize()
+    _check_handle(h, ref)
+    assert np.array_equal(u8(rx), ref["recv_x"])
+    assert np.array_equal(npy(rs).view(np.uint32), ref["recv_x_scales"].view(np.uint32))
+    # pre-quantised codes + scales travel unchanged
+    codes, sci, _ = oracle.fp8_quantize(xb, round_scale)
+    cd = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(DEV)
+    rx2, rs2 = miep.cached_dispatch(cd, h, x_scales=torch.from_numpy(sci).to(DEV))
+    assert np.array_equal(u8(rx2), ref["recv_x"])
+    assert np.array_equal(npy(rs2).view(np.uint32), ref["recv_x_scales"].view(np.uint32))
+    # cached dispatch with the fused cast reproduces the fresh result
+    rx3, rs3 = miep.cached_dispatch(xd, h, cast_to_fp8=True, round_scale=round_scale)
+    assert torch.equal(rx3.view(torch.uint8), rx.view(torch.uint8)) and torch.equal(rs3, rs)
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_large_two_level_fp8_roundtrip(round_scale):
+    """Large workload: 16384 tokens, 64 ranks in 8 RDMA groups, FP8-cast
+    dispatch, bf16 combine of the dequantised identity experts.  The layout
+    and the handle are compared in full; the FP8 rows of 512 sampled source
+    tokens are compared bit-exactly against the oracle's quantiser."""
+    w = wl.LARGE
+    say("large fp8", round_scale)
+    x, idx, wts = _inputs(w, 0)
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    lay = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    ref_lay = _check_layout(w, idx, lay)
+    ntpr, _, ntpe, itr = lay
+    rx, rs, rti, rtw, nrte, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True,
+                                              round_scale=round_scale)
+    # handle and metadata: oracle run on a narrow payload (placement does not depend on H)
+    ref = oracle.dispatch(np.zeros((w.N, 8), np.uint16), idx.numpy(), wts.numpy(), ref_lay["is_token_in_rank"],
+                          ref_lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R, C=w.C)
+    torch.cuda.synchronize()
+    _check_handle(h, ref)
+    assert np.array_equal(npy(rti), ref["recv_topk_idx"])
+    assert np.array_equal(npy(nrte), ref["num_recv_tokens_per_expert"])
+    # sampled payload rows
+    rng = np.random.default_rng(1)
+    sample = rng.choice(w.N, 512, replace=False)
+    xb = wl.bf16_bits(x)
+    codes, sci, _ = oracle.fp8_quantize(xb[sample], round_scale)
+    send_head = ref["send_head"]
+    off = ref["recv_rank_offset"]
+    rows, srcs = [], []
+    for i, n in enumerate(sample):
+        for r in np.nonzero(send_head[n] >= 0)[0]:
+            rows.append(off[r] + send_head[n, r])
+            srcs.append(i)
+    rows = torch.tensor(rows, device=DEV)
+    assert np.array_equal(u8(rx[rows]), codes[srcs])
+    assert np.array_equal(npy(rs[rows]).view(np.uint32), sci[srcs].view(np.uint32))
+    # identity expert on the dequantised rows, bf16 combine
+    y = (rx.float() * rs.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+    cx, cw = miep.combine(y, h, rtw)
+    deq = (torch.from_numpy(codes).view(torch.float8_e4m3fn).float() *
+           torch.from_numpy(sci).repeat_interleave(128, dim=1)).to(torch.bfloat16).float().numpy().astype(np.float64)
+    cnt = ref_lay["is_token_in_rank"].sum(axis=1).astype(np.float64)[sample]
+    got = cx[torch.from_numpy(sample).to(DEV)].float().cpu().numpy().astype(np.float64)
+    ok = cnt > 0
+    assert oracle.calc_diff(got[ok] / cnt[ok, None], deq[ok]) < 5e-6
+    valid = (idx.numpy() >= 0)
+    assert np.array_equal(npy(cw)[valid], wts.numpy()[valid])
+
+
+# --------------------------------------------------------------------------- low-latency
+def _check_ll(out, ref, use_fp8, use_ue8m0, L, S, M):
+    cnt = ref["msg_count"]
+    assert np.array_equal(npy(out["msg_count"]), cnt)
+    assert np.array_equal(npy(out["packed_recv_count"]), ref["packed_recv_count"])
+    assert np.array_equal(npy(out["packed_recv_layout_range"]), ref["packed_recv_layout_range"])
+    msg = u8(out["msg_buf"])
+    for l in range(L):
+        for s in range(S):
+            n = cnt[l, s]
+            assert np.array_equal(msg[l, s, :n], ref["msg_buf"][l, s, :n]), (l, s)
+        n = ref["packed_recv_count"][l]
+        assert np.array_equal(npy(out["packed_recv_src_info"])[l, :n], ref["packed_recv_src_info"][l, :n])
+        if use_fp8:
+            assert np.array_equal(u8(out["packed_recv_x"][l, :n]), ref["packed_recv_x"][l, :n])
+            assert np.array_equal(npy(out["packed_recv_x_scales"][l, :n]).view(np.uint32),
+                                  ref["packed_recv_x_scales"][l, :n].view(np.uint32))
+            if use_ue8m0:
+                assert np.array_equal(npy(out["packed_recv_x_scales_ue8m0"][l, :n]),
+                                      ref["packed_recv_x_scales_ue8m0"][l, :n])
+        else:
+            assert np.array_equal(u16(out["packed_recv_x"][l, :n]), ref["packed_recv_x"][l, :n])
+
+
+LL_SMALL = [
+    # name, R, T, M, H, E, K, d
+    ("ll-tiny", 4, 6, 8, 512, 16, 3, 1),
+    ("ll-ragged", 6, 300, 320, 1536, 24, 4, 5),
+]
+
+
+@pytest.mark.parametrize("case", LL_SMALL, ids=[c[0] for c in LL_SMALL])
+@pytest.mark.parametrize("flags", [(False, False, False), (True, False, False), (True, True, False),
+                                   (True, True, True)], ids=["bf16", "fp8", "fp8-pow2", "fp8-ue8m0"])
+def test_ll_small(case, flags):
+    name, R, T, M, H, E, K, d = case
+    use_fp8, round_scale, use_ue8m0 = flags
+    say("ll", case, flags)
+    g = torch.Generator().manual_seed(11)
+    idx = wl.topk_uniform(R * T, E, K, g)
+    idx[::7, 0] = -1
+    if K > 1:
+        idx[::5, 1] = idx[::5, 0]          # duplicated expert: two messages
+    x = wl.activations(R * T, H, g)
+    stats = torch.full((E // R,), 3, dtype=torch.int32)
+    out = miep.low_latency_dispatch(x.to(DEV), idx.to(DEV), M, E, d, R, use_fp8, round_scale, use_ue8m0,
+                                    stats.to(DEV))
+    ref = oracle.ll_dispatch(wl.bf16_bits(x), idx.numpy(), S=R, M=M, E=E, R=R, dest_rank=d, use_fp8=use_fp8,
+                             round_scale=round_scale, use_ue8m0=use_ue8m0, cumulative_stats=stats.numpy())
+    torch.cuda.synchronize()
+    _check_ll(out, ref, use_fp8, use_ue8m0, E // R, R, M)
+    assert np.array_equal(npy(out["cumulative_local_expert_recv_stats"]), ref["cumulative_local_expert_recv_stats"])
+
+
+@pytest.mark.parametrize("flags", [(True, False, False), (True, True, True), (False, False, False)],
+                         ids=["fp8", "fp8-ue8m0", "bf16"])
+def test_ll_full_workload(flags):
+    w = wl.LL
+    use_fp8, round_scale, use_ue8m0 = flags
+    say("ll full", flags)
+    inp = wl.ll_inputs(w, 0)
+    out = miep.low_latency_dispatch(inp["x"].to(DEV), inp["topk_idx"].to(DEV), w.M, w.E, w.dest_rank, w.R, use_fp8,
+                                    round_scale, use_ue8m0)
+    ref = oracle.ll_dispatch(wl.bf16_bits(inp["x"]), inp["topk_idx"].numpy(), S=w.S, M=w.M, E=w.E, R=w.R,
+                             dest_rank=w.dest_rank, use_fp8=use_fp8, round_scale=round_scale, use_ue8m0=use_ue8m0)
+    torch.cuda.synchronize()
+    _check_ll(out, ref, use_fp8, use_ue8m0, w.L, w.S, w.M)
+
+
+def test_repeat_is_deterministic():
+    w = wl.NORMAL
+    say("determinism", w.name)
+    x, idx, wts = _inputs(w, 0)
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    outs = []
+    for _ in range(2):
+        ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+        recv_x, _, rti, rtw, _, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C)
+        cx, cw = miep.combine(recv_x, h, rtw)
+        outs.append((recv_x.clone(), h.send_head.clone(), cx.clone(), cw.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
