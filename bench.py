@@ -1,0 +1,382 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE expert-parallel core on one MI355X.
+
+Headline workload ("normal"): 4096 tokens as 8 source partitions of 512,
+hidden 7168 bf16, 256 experts on 8 logical ranks, top-8, 24 channels.  One
+step = get_dispatch_layout -> dispatch (notify + pack) -> combine of
+synthetic expert outputs, all inputs resident in HBM.  The JSON line reports
+tokens/s for the whole step, the HBM roofline of the dominant kernel (HIP
+events on the stream the kernels run on), the other hot-path stages measured
+separately (cached dispatch, FP8 low-latency dispatch, the large FP8
+two-level workload, the skewed workload) and the CPU oracle timed on the host.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# --------------------------------------------------------------------------- algorithmic bytes
+# Bytes each kernel must move at minimum (every input read once, every output
+# written once), per launch.  rows = receive rows written (sum over tokens of
+# the number of ranks that receive the token).
+def bytes_layout(N, K, R, E, S):
+    G = R // 8 if R > 8 else 0
+    return N * K * 8 + N * R + S * (R + E + G) * 4
+
+
+def bytes_notify(N, R, S, C, E):
+    return N * R + N * R * 4 + S * R * 4 + 2 * S * R * C * 4 + (R + 1) * 4 + S * E * 4 + E * 4
+
+
+def bytes_pack(N, H, K, R, rows, kind="bf16", meta=True):
+    row_in = 2 * H if kind in ("bf16", "cast") else H
+    row_out = 2 * H if kind == "bf16" else H + 4 * (H // 128)
+    b = N * row_in + N * R * 4 + rows * row_out
+    if kind == "fp8":
+        b += N * 4 * (H // 128)
+    if meta:
+        b += N * K * 12 + rows * (4 + 12 * K)
+    return b
+
+
+def bytes_combine(N, H, K, R, rows, weights=True):
+    b = N * R * 4 + rows * 2 * H + N * 2 * H
+    if weights:
+        b += rows * 4 * K + N * 4 * K
+    return b
+
+
+def bytes_ll(msgs, distinct_tokens, H, use_fp8, R, L):
+    mb = 16 + (H + 4 * (H // 128) if use_fp8 else 2 * H)
+    pb = mb - 16
+    return distinct_tokens * 2 * H + 2 * msgs * mb + msgs * (pb + 4) + L * R * (4 + 8)
+
+
+# --------------------------------------------------------------------------- helpers
+def src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "combine_get_dispatch_histogram_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, kernel_src, launches_bytes_key=None):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = d.get("kernels", {}).get(kernel_key)
+    if not k or k.get("src_hash") != src_hash(*kernel_src):
+        return None
+    return k.get("traffic_bytes_per_launch")
+
+
+class Timer:
+    """HIP events recorded on the current stream around each call."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        self.i = 0
+
+    def __enter__(self):
+        self.ev[self.i][0].record()
+        return self
+
+    def __exit__(self, *a):
+        self.ev[self.i][1].record()
+        self.i += 1
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev[:self.i]]
+
+
+def med(xs):
+    s = sorted(xs)
+    return s[len(s) // 2] if s else float("nan")
+
+
+def mean(xs):
+    return sum(xs) / len(xs) if xs else float("nan")
+
+
+# --------------------------------------------------------------------------- GPU legs
+def run_normal(torch, miep, wl, steps, warmup):
+    w = wl.NORMAL
+    dev = torch.device("cuda:0")
+    inp = wl.normal_inputs(w, 0)
+    x = inp["x"].to(dev)
+    idx = inp["topk_idx"].to(dev)
+    wts = inp["topk_weights"].to(dev)
+    S, R, E, K, H, N, C = w.S, w.R, w.E, w.K, w.H, w.N, w.C
+    i32 = dict(dtype=torch.int32, device=dev)
+    ntpr = torch.empty((S, R), **i32)
+    ntpe = torch.empty((S, E), **i32)
+    itr = torch.empty((N, R), dtype=torch.bool, device=dev)
+    miep.get_dispatch_layout_into(idx, E, R, S, ntpr, None, ntpe, itr)
+    rows = int(ntpr.sum().item())              # exact receive size (routing is fixed across steps)
+    h = miep.Handle.allocate(itr, S, K, E, C, rows)
+    recv_x = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    rti = torch.empty((rows, K), dtype=torch.int64, device=dev)
+    rtw = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    nrte = torch.empty((R, E // R), **i32)
+    y = wl.expert_outputs(rows, H, seed=1).to(dev)   # synthetic expert outputs in the receive layout
+    cx = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    cw = torch.empty((N, K), dtype=torch.float32, device=dev)
+
+    def step(tl=None, td=None, tc=None):
+        if tl:
+            with tl:
+                miep.get_dispatch_layout_into(idx, E, R, S, ntpr, None, ntpe, itr)
+            with td:
+                miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, None, rti, rtw, nrte)
+            with tc:
+                miep.combine_into(y, h, cx, rtw, cw)
+        else:
+            miep.get_dispatch_layout_into(idx, E, R, S, ntpr, None, ntpe, itr)
+            miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, None, rti, rtw, nrte)
+            miep.combine_into(y, h, cx, rtw, cw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # (1) the timed region: exactly `steps` steps, no events inside
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # (2) the same steps again with HIP events around every call
+    tl, td, tc = Timer(torch, steps), Timer(torch, steps), Timer(torch, steps)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        step(tl, td, tc)
+    torch.cuda.synchronize()
+    # (3) cached dispatch on the same handle (the pack kernel alone)
+    tcd = Timer(torch, steps)
+    for _ in range(steps):
+        with tcd:
+            miep.cached_dispatch_into(x, h, recv_x)
+    torch.cuda.synchronize()
+    return dict(w=w, rows=rows, wall=wall, layout_ms=tl.ms(), dispatch_ms=td.ms(), combine_ms=tc.ms(),
+                cached_ms=tcd.ms())
+
+
+def run_ll(torch, miep, wl, iters):
+    w = wl.LL
+    dev = torch.device("cuda:0")
+    inp = wl.ll_inputs(w, 0)
+    x = inp["x"].to(dev)
+    idx = inp["topk_idx"].to(dev)
+    L, R, M, H = w.L, w.R, w.M, w.H
+    out = {}
+    for name, fp8, rs, ue in (("fp8", True, False, False), ("fp8_ue8m0", True, True, True)):
+        mb = miep.ll_msg_bytes(H, fp8)
+        bufs = dict(msg_buf=torch.empty((L, R, M, mb), dtype=torch.uint8, device=dev),
+                    msg_count=torch.empty((L, R), dtype=torch.int32, device=dev),
+                    packed_recv_x=torch.empty((L, R * M, H), dtype=torch.float8_e4m3fn, device=dev),
+                    packed_recv_x_scales=torch.empty((L, R * M, H // 128), dtype=torch.float32, device=dev),
+                    packed_recv_x_scales_ue8m0=torch.empty((L, R * M, H // 128), dtype=torch.uint8, device=dev)
+                    if ue else None,
+                    packed_recv_src_info=torch.empty((L, R * M), dtype=torch.int32, device=dev),
+                    packed_recv_layout_range=torch.empty((L, R), dtype=torch.int64, device=dev),
+                    packed_recv_count=torch.empty((L,), dtype=torch.int32, device=dev))
+
+        def call():
+            miep.low_latency_dispatch_into(x, idx, R, M, w.E, w.dest_rank, fp8, rs, ue, **bufs)
+
+        for _ in range(5):
+            call()
+        t = Timer(torch, iters)
+        for _ in range(iters):
+            with t:
+                call()
+        torch.cuda.synchronize()
+        msgs = int(bufs["packed_recv_count"].sum().item())
+        local = (idx >= w.dest_rank * L) & (idx < (w.dest_rank + 1) * L)
+        distinct = int(local.any(dim=1).sum().item())
+        ms = med(t.ms())
+        out[name] = dict(us=round(ms * 1e3, 2), messages=msgs, tokens=distinct,
+                         tokens_per_s=round(distinct / (ms / 1e3), 1),
+                         gbs=round(bytes_ll(msgs, distinct, H, fp8, R, L) / (ms / 1e3) / 1e9, 1))
+    return out
+
+
+def run_normal_variant(torch, miep, wl, w, iters, cast_fp8):
+    dev = torch.device("cuda:0")
+    inp = wl.normal_inputs(w, 0)
+    x = inp["x"].to(dev)
+    idx = inp["topk_idx"].to(dev)
+    wts = inp["topk_weights"].to(dev)
+    lay = miep.get_dispatch_layout(idx, w.E, w.R, w.S)
+    ntpr, ntp_rdma, ntpe, itr = lay
+    recv_x, recv_s, rti, rtw, nrte, h = miep.dispatch(x, idx, wts, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=cast_fp8)
+    rows = h.recv_capacity
+    if cast_fp8:
+        y = (recv_x.float() * recv_s.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+    else:
+        y = wl.expert_outputs(rows, w.H, seed=1).to(dev)
+    cx = torch.empty((w.N, w.H), dtype=torch.bfloat16, device=dev)
+    cw = torch.empty((w.N, w.K), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, recv_s, rti, rtw, nrte, cast_to_fp8=cast_fp8)
+        miep.combine_into(y, h, cx, rtw, cw)
+    td, tc, tcd = Timer(torch, iters), Timer(torch, iters), Timer(torch, iters)
+    for _ in range(iters):
+        with td:
+            miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, recv_s, rti, rtw, nrte, cast_to_fp8=cast_fp8)
+        with tc:
+            miep.combine_into(y, h, cx, rtw, cw)
+        with tcd:
+            miep.cached_dispatch_into(x, h, recv_x, recv_s, cast_to_fp8=cast_fp8)
+    torch.cuda.synchronize()
+    d_ms, c_ms, cd_ms = med(td.ms()), med(tc.ms()), med(tcd.ms())
+    kind = "cast" if cast_fp8 else "bf16"
+    db = bytes_notify(w.N, w.R, w.S, w.C, w.E) + bytes_pack(w.N, w.H, w.K, w.R, rows, kind)
+    cb = bytes_combine(w.N, w.H, w.K, w.R, rows)
+    return dict(rows=rows, rho=round(rows / w.N, 4), dispatch_us=round(d_ms * 1e3, 1),
+                combine_us=round(c_ms * 1e3, 1), cached_dispatch_us=round(cd_ms * 1e3, 1),
+                tokens_per_s=round(w.N / ((d_ms + c_ms) / 1e3), 1),
+                dispatch_gbs=round(db / (d_ms / 1e3) / 1e9, 1), combine_gbs=round(cb / (c_ms / 1e3) / 1e9, 1),
+                cached_dispatch_gbs=round(bytes_pack(w.N, w.H, w.K, w.R, rows, kind, meta=False) / (cd_ms / 1e3) / 1e9,
+                                          1))
+
+
+# --------------------------------------------------------------------------- CPU oracle leg
+def cpu_baseline(wl, budget_s):
+    import numpy as np  # noqa: F401
+
+    import oracle
+    w = wl.NORMAL
+    inp = wl.normal_inputs(w, 0)
+    x = wl.bf16_bits(inp["x"])
+    idx = inp["topk_idx"].numpy()
+    wts = inp["topk_weights"].numpy()
+    y = None
+    runs, t_total = 0, 0.0
+    while runs < 1 or (t_total < budget_s and runs < 20):
+        t0 = time.perf_counter()
+        lay = oracle.layout(idx, w.S, w.E, w.R)
+        d = oracle.dispatch(x, idx, wts, lay["is_token_in_rank"], lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R,
+                            C=w.C)
+        if y is None:
+            t_gen = time.perf_counter()
+            y = wl.bf16_bits(wl.expert_outputs(d["num_recv"], w.H, seed=1))
+            t0 += time.perf_counter() - t_gen          # input generation is not oracle work
+        oracle.combine(y, d["recv_topk_weights"], d["send_head"], d["recv_rank_offset"], S=w.S)
+        t_total += time.perf_counter() - t0
+        runs += 1
+    return dict(value=round(w.N * runs / t_total, 1), unit="tokens/s", cores=1, kind="oracle",
+                sample="the full normal workload (4096 tokens, layout + dispatch + combine), %d run(s), %.1f s, "
+                       "single-threaded C oracle (gcc -O2), host has %d cores" % (runs, t_total, os.cpu_count()))
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-secondary", action="store_true", help="skip the separately measured stages")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain copy of this many MiB first (reference for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the logical ranks are partitions of one GPU's HBM and nothing here "
+              "uses a second GPU (asked for --gpus %d)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_get_dispatch_histogram_amd as miep
+    from combine_get_dispatch_histogram_amd import workloads as wl
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    r = run_normal(torch, miep, wl, args.steps, args.warmup)
+    w, rows = r["w"], r["rows"]
+    N, H, K, R, S, C, E = w.N, w.H, w.K, w.R, w.S, w.C, w.E
+    ms_step = r["wall"] * 1e3 / args.steps
+    lay_ms, dis_ms, com_ms, cd_ms = (mean(r[k]) for k in ("layout_ms", "dispatch_ms", "combine_ms", "cached_ms"))
+    b_lay = bytes_layout(N, K, R, E, S)
+    b_dis = bytes_notify(N, R, S, C, E) + bytes_pack(N, H, K, R, rows)
+    b_com = bytes_combine(N, H, K, R, rows)
+    b_cd = bytes_pack(N, H, K, R, rows, meta=False)
+    step_bytes = b_lay + b_dis + b_com
+
+    # dominant kernel: the combine is a single-kernel call; the pack kernel is
+    # timed alone through cached dispatch (the fresh dispatch adds notify).
+    cand = {"combine": (com_ms, b_com, ("combine.hip", "device.h")),
+            "pack": (cd_ms, b_cd, ("pack.hip", "device.h"))}
+    dom = max(cand, key=lambda k: cand[k][0])
+    d_ms, d_bytes, d_src = cand[dom]
+    achieved = d_bytes / (d_ms / 1e3) / 1e9
+    traffic = load_traffic(dom, d_src)
+    line = {
+        "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(N / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "normal", "tokens": N, "sources": S, "hidden": H, "experts": E, "ranks": R, "topk": K,
+                   "channels": C, "routing": "uniform top-8 distinct", "recv_rows": rows,
+                   "step": "layout + dispatch (notify + pack) + combine"},
+        "achieved_gbs_step": round(step_bytes / (ms_step / 1e3) / 1e9, 1),
+        "frac_of_hbm_peak_step": round(step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tokens_per_s_dispatch_plus_combine": round(N / ((dis_ms + com_ms) / 1e3), 1),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": d_bytes, "avg_launch_us": round(d_ms * 1e3, 2)},
+        "stages_us": {"layout": round(lay_ms * 1e3, 2), "dispatch": round(dis_ms * 1e3, 2),
+                      "combine": round(com_ms * 1e3, 2), "cached_dispatch": round(cd_ms * 1e3, 2)},
+        "stages_gbs": {"layout": round(b_lay / (lay_ms / 1e3) / 1e9, 1),
+                       "dispatch": round(b_dis / (dis_ms / 1e3) / 1e9, 1),
+                       "combine": round(b_com / (com_ms / 1e3) / 1e9, 1),
+                       "cached_dispatch": round(b_cd / (cd_ms / 1e3) / 1e9, 1)},
+    }
+    if not args.no_secondary:
+        sec = {"ll": run_ll(torch, miep, wl, 20),
+               "skewed": run_normal_variant(torch, miep, wl, wl.SKEWED, 20, False),
+               "large_fp8": run_normal_variant(torch, miep, wl, wl.LARGE, 10, True)}
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

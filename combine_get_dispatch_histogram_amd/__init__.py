@@ -26,7 +26,7 @@ import torch
 from . import _lib
 from ._lib import MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # noqa: F401
 
-__all__ = ["Handle", "MiepError", "get_dispatch_layout", "dispatch", "dispatch_into", "cached_dispatch",
+__all__ = ["Handle", "MiepError", "get_dispatch_layout", "get_dispatch_layout_into", "dispatch", "dispatch_into", "cached_dispatch",
            "cached_dispatch_into", "combine", "combine_into", "low_latency_dispatch", "low_latency_dispatch_into",
            "ll_msg_bytes", "version"]
 
@@ -143,10 +143,27 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
     ntp_rdma = torch.empty((S, num_ranks // 8), **i32) if num_ranks > 8 else None
     ntpe = torch.empty((S, num_experts), **i32)
     itr = torch.empty((N, num_ranks), dtype=torch.bool, device=dev)
-    p = _lib.Problem(S, N // S, 8, K, num_experts, num_ranks, 1, 1)
-    _lib.check(_lib.load().miep_get_dispatch_layout(ctypes.byref(p), _ptr(topk_idx), _ptr(ntpr), _ptr(ntp_rdma),
-                                                    _ptr(ntpe), _ptr(itr), _stream(topk_idx)))
+    get_dispatch_layout_into(topk_idx, num_experts, num_ranks, S, ntpr, ntp_rdma, ntpe, itr)
     return ntpr, ntp_rdma, ntpe, itr
+
+
+def get_dispatch_layout_into(topk_idx, num_experts: int, num_ranks: int, num_src: int, num_tokens_per_rank,
+                             num_tokens_per_rdma_rank, num_tokens_per_expert, is_token_in_rank) -> None:
+    """get_dispatch_layout into preallocated outputs (allocates nothing)."""
+    N, K = topk_idx.shape
+    S, R = num_src, num_ranks
+    if S <= 0 or N % S:
+        raise ValueError("the %d tokens do not split into %d source partitions" % (N, S))
+    _want(topk_idx, "topk_idx", torch.int64)
+    _want(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (S, R))
+    _want(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (S, num_experts))
+    _want(is_token_in_rank, "is_token_in_rank", torch.bool, (N, R))
+    if R > 8:
+        _want(num_tokens_per_rdma_rank, "num_tokens_per_rdma_rank", torch.int32, (S, R // 8))
+    p = _lib.Problem(S, N // S, 8, K, num_experts, R, 1, 1)
+    _lib.check(_lib.load().miep_get_dispatch_layout(ctypes.byref(p), _ptr(topk_idx), _ptr(num_tokens_per_rank),
+                                                    _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert),
+                                                    _ptr(is_token_in_rank), _stream(topk_idx)))
 
 
 # --------------------------------------------------------------------------- dispatch

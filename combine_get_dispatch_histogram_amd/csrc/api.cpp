@@ -112,8 +112,9 @@ miep::PackArgs pack_args(const miep_problem* p, const void* x, int32_t x_kind, c
 
 namespace miep {
 const Tuning& tuning() {
-  static const Tuning t = {env_int("MIEP_PACK_VPL", 0), env_int("MIEP_PACK_SLICES", 0),
-                           env_int("MIEP_COMBINE_VPL", 0), env_int("MIEP_COMBINE_SLICES", 0), env_int("MIEP_NT", 1)};
+  static const Tuning t = {env_int("MIEP_PACK_VPL", 0),     env_int("MIEP_PACK_SLICES", 0),
+                           env_int("MIEP_COMBINE_VPL", 0),  env_int("MIEP_COMBINE_SLICES", 0),
+                           env_int("MIEP_PACK_NT", 2) & 3, env_int("MIEP_COMBINE_NT", 1) != 0 ? 1 : 0};
   return t;
 }
 }  // namespace miep

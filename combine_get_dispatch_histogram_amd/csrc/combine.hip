@@ -33,7 +33,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
     int row = -1;
     if (r < R) {
       const int sh = a.send_head[n * R + r];
-      if (sh >= 0) row = a.off[r] + sh;
+      const int o = a.off[r];                        // independent of sh: both loads in flight
+      row = sh >= 0 ? o + sh : -1;
     }
     const bool ok = row >= 0 && row < a.capacity;
     src[i] = row;
@@ -143,7 +144,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int span = vpl * kWave;
   int nslices = tu.combine_slices > 0 ? tu.combine_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
-  return tu.nt ? launch_combine_nt<true>(a, vpl, nslices, st) : launch_combine_nt<false>(a, vpl, nslices, st);
+  return tu.combine_nt ? launch_combine_nt<true>(a, vpl, nslices, st) : launch_combine_nt<false>(a, vpl, nslices, st);
 }
 
 }  // namespace miep

@@ -18,7 +18,6 @@
 
 namespace miep {
 
-
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -95,28 +94,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- E4M3
-// fp32 -> OCP E4M3FN, round to nearest even, saturating at 448.
-// Bit-level: the normal range rounds the 23-bit fp32 mantissa to 3 bits
-// (a carry moves into the exponent field by itself); below 2^-6 the
-// value is a multiple of 2^-9 and rounds as the integer |a| * 2^9.
-__device__ __forceinline__ uint32_t e4m3_rne(float a) {
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t m = u & 0x7FFFFFFFu;
-  if (m > 0x7F800000u) return 0x7Fu;                 // NaN
-  if (m >= 0x43E00000u) return sign | 0x7Eu;         // >= 448: saturate
-  if (m < 0x3C800000u) {                             // < 2^-6: subnormal grid
-    const float q = __builtin_rintf(__uint_as_float(m) * 512.0f);
-    return sign | static_cast<uint32_t>(q);          // 0..8 (8 = 2^-6, a normal code)
-  }
-  const uint32_t exp = (m >> 23) - 127u + 7u;        // 1..15
-  const uint32_t mant = m & 0x7FFFFFu;
-  uint32_t code = (exp << 3) | (mant >> 20);
-  const uint32_t rest = mant & 0xFFFFFu;
-  if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) code += 1u;
-  return sign | code;                                // <= 0x7E since |a| < 448
-}
-
 // Per-group scales.  Returns scale (multiplier) and writes scale_inv.
 __device__ __forceinline__ float fp8_scales(float amax, bool round_scale, float* scale_inv) {
   amax = fmaxf(amax, 1e-4f);
@@ -152,8 +129,16 @@ __device__ __forceinline__ float absmax8(const v4u& v) {
   return m;
 }
 
+// Four fp32 -> four E4M3 codes (byte i = value i).  gfx950 converts two
+// values per v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even).  Every
+// caller feeds finite |v| <= 448 (amax * (448 / amax) rounds to at most
+// 448 in fp32), a range where no saturation rule is involved; the parity
+// tests compare the codes with the oracle over every bf16 value and over
+// millions of scaled products.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  return e4m3_rne(a) | (e4m3_rne(b) << 8) | (e4m3_rne(c) << 16) | (e4m3_rne(d) << 24);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return static_cast<uint32_t>(r);
 }
 
 // 8 bf16 channels times `scale` -> 8 E4M3 codes (one fp32 multiply each).
@@ -187,5 +172,40 @@ struct RankMask {
     return static_cast<uint32_t>((v >> (r & 63)) & 1ull);
   }
 };
+
+// Membership row (R bytes, nonzero = member) -> RankMask.  All loads of a
+// 64-rank chunk are issued before any is consumed (4-byte loads when
+// R % 4 == 0 and the row is 4-byte aligned, else bytes for R < 8).
+template <int MW>
+__device__ __forceinline__ RankMask<MW> load_rank_row(const uint8_t* row, int R) {
+  RankMask<MW> m;
+  m.clear();
+  if ((R & 3) == 0) {
+    for (int c0 = 0; c0 < R; c0 += 64) {
+      uint32_t v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = c0 + 4 * i < R ? *reinterpret_cast<const uint32_t*>(row + c0 + 4 * i) : 0u;
+      uint64_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w |= static_cast<uint64_t>(((v[i] >> (8 * j)) & 0xFFu) != 0u) << (4 * i + j);
+      const int q = c0 >> 6;
+#pragma unroll
+      for (int k = 0; k < MW; ++k) m.w[k] = (k == q) ? w : m.w[k];
+    }
+  } else {
+    uint8_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = i < R ? row[i] : 0;
+    uint64_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= static_cast<uint64_t>(v[i] != 0) << i;
+    m.w[0] = w;
+  }
+  return m;
+}
 
 }  // namespace miep

@@ -99,9 +99,11 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st);
 
 // Optional launch-geometry overrides read once from the environment
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
-// MIEP_NT): used by the benchmark's sweeps, never required.
+// MIEP_PACK_NT, MIEP_COMBINE_NT): used by geometry sweeps, never required.
+// pack_nt: bit 0 = non-temporal payload loads, bit 1 = non-temporal stores;
+// combine_nt: non-temporal loads of the expert outputs.
 struct Tuning {
-  int pack_vpl, pack_slices, combine_vpl, combine_slices, nt;
+  int pack_vpl, pack_slices, combine_vpl, combine_slices, pack_nt, combine_nt;
 };
 const Tuning& tuning();
 

@@ -34,11 +34,17 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
     const int64_t* row = a.topk_idx + n * a.K;
     RankMask<MW> m;
     m.clear();
-    for (int k = 0; k < a.K; ++k) {
-      const int64_t e = row[k];
-      if (e < 0 || e >= a.E) continue;              // masked (or out of range)
-      atomicAdd(&hist[e], 1);
-      m.set(static_cast<int>(e) / a.L);
+    for (int k0 = 0; k0 < a.K; k0 += 8) {         // 8 independent loads in flight
+      int64_t e8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e8[j] = k0 + j < a.K ? row[k0 + j] : -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t e = e8[j];
+        if (e < 0 || e >= a.E) continue;            // masked (or out of range)
+        atomicAdd(&hist[e], 1);
+        m.set(static_cast<int>(e) / a.L);
+      }
     }
     uint8_t* out = a.in_rank + n * a.R;
     if ((a.R & 3) == 0) {

@@ -15,7 +15,8 @@
 // Where the transport fills slots in atomic arrival order, these kernels
 // fix the order: slot j of (l, s) is the j-th top-k entry of source s that
 // names expert d*L + l, in (token, k) order, so the output is
-// deterministic.  Two kernels, both one workgroup per (l, s):
+// deterministic.  Two kernels, both kLLSplit workgroups per (l, s) block that
+// share its messages (the slot scan is repeated by each; it is tiny):
 //   send: scan source s's top-k for the expert (LDS scan), then cast and
 //         write its messages (16-byte loads, 8/16-byte stores);
 //   recv: exclusive scan of the counts over s gives the packed range, then
@@ -26,8 +27,10 @@
 namespace miep {
 
 constexpr int kLLThreads = 256;
+constexpr int kLLSplit = 4;  // workgroups sharing one (l, s) block's messages
 constexpr int kLLMaxSlots = 4096;
 
+template <int VPL>
 __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
   __shared__ int32_t wsum[kLLThreads / kWave];
@@ -41,21 +44,28 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   __syncthreads();
   for (int t0 = 0; t0 < a.T; t0 += kLLThreads) {
     const int t = t0 + tid;
-    int cnt = 0;
-    if (t < a.T)
-      for (int k = 0; k < a.K; ++k) cnt += idx[static_cast<int64_t>(t) * a.K + k] == target ? 1 : 0;
+    uint64_t kmask = 0;                           // entries k of token t that name the expert
+    if (t < a.T) {
+      const int64_t* row = idx + static_cast<int64_t>(t) * a.K;
+      for (int k0 = 0; k0 < a.K; k0 += 8) {       // 8 independent loads in flight
+        int64_t e8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e8[j] = k0 + j < a.K ? row[k0 + j] : -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kmask |= static_cast<uint64_t>(e8[j] == target) << (k0 + j);
+      }
+    }
+    const int cnt = __popcll(kmask);
     const int inc = wave_inclusive_scan(cnt);
     if (lane == kWave - 1) wsum[w] = inc;
     __syncthreads();
     int before = carry_s;
     for (int q = 0; q < w; ++q) before += wsum[q];
     int j = before + inc - cnt;
-    if (t < a.T)
-      for (int k = 0; k < a.K && cnt > 0; ++k)
-        if (idx[static_cast<int64_t>(t) * a.K + k] == target) {
-          if (j < a.M) slot_tok[j] = t;
-          ++j;
-        }
+    for (uint64_t km = kmask; km != 0; km &= km - 1) {   // one slot per matching entry, k ascending
+      if (j < a.M) slot_tok[j] = t;
+      ++j;
+    }
     __syncthreads();
     if (tid == 0) {
       int tot = carry_s;
@@ -65,37 +75,50 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
     __syncthreads();
   }
   const int n = carry_s < a.M ? carry_s : a.M;
-  if (tid == 0) a.msg_count[l * a.R + s] = n;
+  if (tid == 0 && blockIdx.y == 0) a.msg_count[l * a.R + s] = n;
 
+  // messages: one wavefront per (message, row slice); the slice's 16-byte
+  // loads are all issued before any of its stores
   const int nv = a.H / 8;              // 16-byte vectors of 8 bf16
-  const int G = a.H / kFp8Group;
-  for (int j = w; j < n; j += kLLThreads / kWave) {
+  const int span = kWave * VPL;
+  const int nsl = (nv + span - 1) / span;
+  for (int task = blockIdx.y * (kLLThreads / kWave) + w; task < n * nsl; task += gridDim.y * (kLLThreads / kWave)) {
+    const int j = task / nsl;
+    const int v0 = (task - j * nsl) * span;
     const int t = slot_tok[j];
     uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
-    if (lane == 0) *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
+    if (v0 == 0 && lane == 0) *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
     const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.x) + (static_cast<int64_t>(s) * a.T + t) * 2 * a.H;
+    v4u d[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int v = v0 + i * kWave + lane;
+      if (v < nv) d[i] = ld16<false>(xrow + static_cast<int64_t>(v) * 16);
+    }
     if (a.use_fp8) {
       float* scales = reinterpret_cast<float*>(msg + 16 + a.H);
-      for (int v0 = 0; v0 < nv; v0 += kWave) {
-        const int v = v0 + lane;
-        v4u d{0u, 0u, 0u, 0u};
-        if (v < nv) d = ld16<false>(xrow + static_cast<int64_t>(v) * 16);
-        const float amax = group16_max(v < nv ? absmax8(d) : 0.0f);
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int v = v0 + i * kWave + lane;
+        const float amax = group16_max(v < nv ? absmax8(d[i]) : 0.0f);
         float sci;
         const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
         if (v < nv) {
-          st8<false>(msg + 16 + static_cast<int64_t>(v) * 8, cast8(d, sc));
+          st8<false>(msg + 16 + static_cast<int64_t>(v) * 8, cast8(d[i], sc));
           if ((lane & 15) == 0) scales[v / 16] = sci;
         }
       }
-      (void)G;
     } else {
-      for (int v = lane; v < nv; v += kWave)
-        st16<false>(msg + 16 + static_cast<int64_t>(v) * 16, ld16<false>(xrow + static_cast<int64_t>(v) * 16));
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int v = v0 + i * kWave + lane;
+        if (v < nv) st16<false>(msg + 16 + static_cast<int64_t>(v) * 16, d[i]);
+      }
     }
   }
 }
 
+template <int VPL>
 __global__ __launch_bounds__(kLLThreads) void ll_recv_kernel(LLArgs a) {
   __shared__ int32_t begin_s;
   const int l = blockIdx.x / a.R;
@@ -111,7 +134,7 @@ __global__ __launch_bounds__(kLLThreads) void ll_recv_kernel(LLArgs a) {
   __syncthreads();
   const int begin = begin_s;
   const int n = a.msg_count[l * a.R + s];
-  if (tid == 0) {
+  if (tid == 0 && blockIdx.y == 0) {          // once per (l, s), not per split workgroup
     a.layout_range[l * a.R + s] = (static_cast<int64_t>(begin) << 32) | static_cast<int64_t>(static_cast<uint32_t>(n));
     if (s == a.R - 1) {
       a.count[l] = begin + n;
@@ -122,32 +145,54 @@ __global__ __launch_bounds__(kLLThreads) void ll_recv_kernel(LLArgs a) {
   const int nv = static_cast<int>(pb / 16);
   const int G = a.H / kFp8Group;
   const int64_t rows_per_expert = static_cast<int64_t>(a.R) * a.M;
-  for (int j = w; j < n; j += kLLThreads / kWave) {
+  const int span = kWave * VPL;
+  const int nsl = (nv + span - 1) / span;
+  for (int task = blockIdx.y * (kLLThreads / kWave) + w; task < n * nsl; task += gridDim.y * (kLLThreads / kWave)) {
+    const int j = task / nsl;
+    const int sl = task - j * nsl;
+    const int v0 = sl * span;
     const uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
     const int64_t row = l * rows_per_expert + begin + j;
-    if (lane == 0) a.src_info[row] = *reinterpret_cast<const int32_t*>(msg);
+    v4u d[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int v = v0 + i * kWave + lane;
+      if (v < nv) d[i] = ld16<false>(msg + 16 + static_cast<int64_t>(v) * 16);
+    }
     uint8_t* out = static_cast<uint8_t*>(a.prx) + row * pb;
-    for (int v = lane; v < nv; v += kWave)
-      st16<false>(out + static_cast<int64_t>(v) * 16, ld16<false>(msg + 16 + static_cast<int64_t>(v) * 16));
-    if (a.use_fp8) {
-      const uint32_t* sc = reinterpret_cast<const uint32_t*>(msg + 16 + a.H);
-      for (int g = lane; g < G; g += kWave) {
-        const uint32_t bits = sc[g];
-        reinterpret_cast<uint32_t*>(a.prs)[row * G + g] = bits;
-        if (a.prue) a.prue[row * G + g] = static_cast<uint8_t>((bits >> 23) & 0xFFu);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int v = v0 + i * kWave + lane;
+      if (v < nv) st16<false>(out + static_cast<int64_t>(v) * 16, d[i]);
+    }
+    if (sl == 0) {
+      if (lane == 0) a.src_info[row] = *reinterpret_cast<const int32_t*>(msg);
+      if (a.use_fp8) {
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(msg + 16 + a.H);
+        for (int g = lane; g < G; g += kWave) {
+          const uint32_t bits = sc[g];
+          reinterpret_cast<uint32_t*>(a.prs)[row * G + g] = bits;
+          if (a.prue) a.prue[row * G + g] = static_cast<uint8_t>((bits >> 23) & 0xFFu);
+        }
       }
     }
   }
 }
 
+template <int VPL>
+static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, hipStream_t st) {
+  hipLaunchKernelGGL(ll_send_kernel<VPL>, dim3(blocks, kLLSplit), dim3(kLLThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ll_recv_kernel<VPL>, dim3(blocks, kLLSplit), dim3(kLLThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
   const int blocks = a.L * a.R;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(ll_send_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ll_recv_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
-  return hipGetLastError();
+  // 7 vectors per lane when a bf16 row splits into 448-vector slices (hidden 7168)
+  return (a.H / 8) % (7 * kWave) == 0 ? launch_ll_vpl<7>(a, blocks, st) : launch_ll_vpl<8>(a, blocks, st);
 }
 
 }  // namespace miep

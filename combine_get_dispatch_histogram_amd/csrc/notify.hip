@@ -37,16 +37,29 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   const int nw = blockDim.x / kWave;
   const int R = a.R, T = a.T, C = a.C, S = a.S;
 
+  extern __shared__ int32_t eacc[];                   // per-expert sums of the experts this workgroup owns
+  const int ne = a.E > s ? (a.E - s + S - 1) / S : 0; // experts e = s + k*S
   for (int r = tid; r < R; r += blockDim.x) {
-    int b = 0, tot = 0;
-    for (int q = 0; q < S; ++q) {
-      const int v = a.ntpr[static_cast<int64_t>(q) * R + r];
-      tot += v;
-      b += q < s ? v : 0;
-    }
-    base[r] = b;
-    total[r] = tot;
+    base[r] = 0;
+    total[r] = 0;
     run[r] = 0;
+  }
+  for (int k = tid; k < ne; k += blockDim.x) eacc[k] = 0;
+  __syncthreads();
+  // rank totals and bases: every (source, rank) entry loaded by one thread,
+  // summed with LDS integer atomics (order-free), so no thread walks a
+  // dependent chain of S loads
+  for (int i = tid; i < S * R; i += blockDim.x) {
+    const int q = i / R, r = i - q * R;
+    const int v = a.ntpr[i];
+    atomicAdd(&total[r], v);
+    if (q < s) atomicAdd(&base[r], v);
+  }
+  if (a.nrte != nullptr && a.ntpe != nullptr) {
+    for (int i = tid; i < ne * S; i += blockDim.x) {
+      const int k = i / S, q = i - k * S;
+      atomicAdd(&eacc[k], a.ntpe[static_cast<int64_t>(q) * a.E + s + k * S]);
+    }
   }
   __syncthreads();
 
@@ -65,10 +78,9 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
 
   // per-expert receive counts, rounded up to the expert alignment
   if (a.nrte != nullptr && a.ntpe != nullptr) {
-    for (int e = s * blockDim.x + tid; e < a.E; e += gridDim.x * blockDim.x) {
-      int64_t sum = 0;
-      for (int q = 0; q < S; ++q) sum += a.ntpe[static_cast<int64_t>(q) * a.E + e];
-      a.nrte[e] = static_cast<int32_t>((sum + a.align - 1) / a.align * a.align);
+    for (int k = tid; k < ne; k += blockDim.x) {
+      const int64_t sum = eacc[k];
+      a.nrte[s + k * S] = static_cast<int32_t>((sum + a.align - 1) / a.align * a.align);
     }
   }
 
@@ -79,21 +91,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     const int64_t n = static_cast<int64_t>(s) * T + t;
     RankMask<MW> m;
     m.clear();
-    if (valid) {
-      const uint8_t* row = a.in_rank + n * R;
-      if ((R & 3) == 0) {
-        for (int r0 = 0; r0 < R; r0 += 4) {
-          const uint32_t b = *reinterpret_cast<const uint32_t*>(row + r0);
-          if (b & 0xFFu) m.set(r0);
-          if (b & 0xFF00u) m.set(r0 + 1);
-          if (b & 0xFF0000u) m.set(r0 + 2);
-          if (b & 0xFF000000u) m.set(r0 + 3);
-        }
-      } else {
-        for (int r = 0; r < R; ++r)
-          if (row[r]) m.set(r);
-      }
-    }
+    if (valid) m = load_rank_row<MW>(a.in_rank + n * R, R);
     // pass 1: per-wavefront counts, lane j of the wave keeps rank r0 + j
     for (int r0 = 0; r0 < R; r0 += kWave) {
       const int rend = R - r0 < kWave ? R - r0 : kWave;
@@ -174,10 +172,12 @@ hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
   if (a.S == 0) return hipSuccess;
   int threads = ((a.T + kWave - 1) / kWave) * kWave;
   threads = threads < kWave ? kWave : (threads > kNotifyMaxWaves * kWave ? kNotifyMaxWaves * kWave : threads);
+  const int ne_max = (a.E + a.S - 1) / a.S;  // experts owned by workgroup 0 (the most)
+  const size_t lds = sizeof(int32_t) * static_cast<size_t>(ne_max > 0 ? ne_max : 1);
   if (a.R <= 64)
-    hipLaunchKernelGGL(notify_kernel<1>, dim3(a.S), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL(notify_kernel<1>, dim3(a.S), dim3(threads), lds, st, a);
   else
-    hipLaunchKernelGGL(notify_kernel<4>, dim3(a.S), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL(notify_kernel<4>, dim3(a.S), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@
 
 namespace miep {
 
-template <int KIND, int VPL, int MW, bool NT>
+template <int KIND, int VPL, int MW, int NT>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   const int lane = lane_id();
   const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
     int row = -1;
     if (r < R) {
       const int sh = a.send_head[n * R + r];
-      if (sh >= 0) row = a.off[r] + sh;
+      const int o = a.off[r];                        // independent of sh: both loads in flight
+      row = sh >= 0 ? o + sh : -1;
     }
     const bool ok = row >= 0 && row < a.capacity;
     dst[i] = row;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int v = v0 + j * kWave + lane;
-      if (v < nv) d[j] = ld16<NT>(xrow + static_cast<int64_t>(v) * 16);
+      if (v < nv) d[j] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(v) * 16);
     }
     if constexpr (KIND == kPackCastFp8) {
       // 16 lanes hold one 128-channel group; nv is a multiple of 16, so a
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
           for (int j = 0; j < VPL; ++j) {
             const int v = v0 + j * kWave + lane;
             if (v < nv) {
-              st8<NT>(orow + static_cast<int64_t>(v) * 8, q[j]);
+              st8<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 8, q[j]);
               if ((lane & 15) == 0) a.recv_x_scales[row * G + v / 16] = sci[j];
             }
           }
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
 #pragma unroll
           for (int j = 0; j < VPL; ++j) {
             const int v = v0 + j * kWave + lane;
-            if (v < nv) st16<NT>(orow + static_cast<int64_t>(v) * 16, d[j]);
+            if (v < nv) st16<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 16, d[j]);
           }
         }
       }
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   }
 }
 
-template <int KIND, int VPL, bool NT>
+template <int KIND, int VPL, int NT>
 static hipError_t launch_pack_vpl(const PackArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
   const int64_t blocks = (waves + 3) / 4;
@@ -154,14 +155,22 @@ static hipError_t launch_pack_vpl(const PackArgs& a, int nslices, hipStream_t st
   return hipGetLastError();
 }
 
-template <int KIND, bool NT>
+template <int KIND, int NT>
 static hipError_t launch_pack_kind(const PackArgs& a, int vpl, int nslices, hipStream_t st) {
   switch (vpl) {
-    case 2: return launch_pack_vpl<KIND, 2, NT>(a, nslices, st);
     case 4: return launch_pack_vpl<KIND, 4, NT>(a, nslices, st);
     case 7: return launch_pack_vpl<KIND, 7, NT>(a, nslices, st);
-    case 14: return launch_pack_vpl<KIND, 14, NT>(a, nslices, st);
     default: return launch_pack_vpl<KIND, 8, NT>(a, nslices, st);
+  }
+}
+
+template <int KIND>
+static hipError_t launch_pack_nt(const PackArgs& a, int vpl, int nslices, int nt, hipStream_t st) {
+  switch (nt) {
+    case 0: return launch_pack_kind<KIND, 0>(a, vpl, nslices, st);
+    case 1: return launch_pack_kind<KIND, 1>(a, vpl, nslices, st);
+    case 2: return launch_pack_kind<KIND, 2>(a, vpl, nslices, st);
+    default: return launch_pack_kind<KIND, 3>(a, vpl, nslices, st);
   }
 }
 
@@ -175,17 +184,10 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   int span = vpl * kWave;
   int nslices = tu.pack_slices > 0 ? tu.pack_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
-  const bool nt = tu.nt != 0;
   switch (a.kind) {
-    case kPackFp8:
-      return nt ? launch_pack_kind<kPackFp8, true>(a, vpl, nslices, st)
-                : launch_pack_kind<kPackFp8, false>(a, vpl, nslices, st);
-    case kPackCastFp8:
-      return nt ? launch_pack_kind<kPackCastFp8, true>(a, vpl, nslices, st)
-                : launch_pack_kind<kPackCastFp8, false>(a, vpl, nslices, st);
-    default:
-      return nt ? launch_pack_kind<kPackBf16, true>(a, vpl, nslices, st)
-                : launch_pack_kind<kPackBf16, false>(a, vpl, nslices, st);
+    case kPackFp8: return launch_pack_nt<kPackFp8>(a, vpl, nslices, tu.pack_nt, st);
+    case kPackCastFp8: return launch_pack_nt<kPackCastFp8>(a, vpl, nslices, tu.pack_nt, st);
+    default: return launch_pack_nt<kPackBf16>(a, vpl, nslices, tu.pack_nt, st);
   }
 }
 

@@ -304,6 +304,33 @@ def test_fp8_cast_exhaustive_bf16(round_scale):
 
 
 @pytest.mark.parametrize("round_scale", [False, True])
+def test_fp8_cast_random_magnitudes(round_scale):
+    """14.7M scaled products: rows and 128-channel groups spanning 1e-8 .. 1e4,
+    some groups with one dominant outlier, every code and scale compared."""
+    say("fp8 cast random magnitudes", round_scale)
+    N, H = 2048, 7168
+    g = torch.Generator().manual_seed(21)
+    x = torch.randn((N, H), generator=g)
+    G = H // 128
+    mag = 10.0 ** (torch.rand((N, G), generator=g) * 12 - 8)
+    x = (x.view(N, G, 128) * mag.unsqueeze(2))
+    out = torch.rand((N, G), generator=g) < 0.2
+    x[:, :, 0] = torch.where(out, x[:, :, 0] * 1000.0, x[:, :, 0])
+    x = x.view(N, H).to(torch.bfloat16)
+    xb = wl.bf16_bits(x)
+    idx = torch.zeros((N, 1), dtype=torch.int64)
+    xd, idxd = x.to(DEV), idx.to(DEV)
+    ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, 1, 1, 1)
+    rx, rs, _, _, _, h = miep.dispatch(xd, idxd, None, ntpr, itr, ntpe, 1, 1, cast_to_fp8=True,
+                                       round_scale=round_scale)
+    codes, sci, _ = oracle.fp8_quantize(xb, round_scale)
+    assert np.array_equal(npy(rs).view(np.uint32), sci.view(np.uint32))
+    got = u8(rx)
+    bad = np.nonzero(got != codes)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], codes[bad][:5])
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
 def test_fp8_dispatch_kinds_small(round_scale):
     """Fused cast and pre-quantised FP8 dispatch on a ragged multi-tile case,
     with magnitudes that exercise subnormal codes and saturation edges."""
