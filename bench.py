@@ -77,7 +77,7 @@ def src_hash(*names):
 def load_traffic(kernel_key, kernel_src, launches_bytes_key=None):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, "pmc_traffic.json")
+    path = os.path.join(PROFILES, "normal_hbm_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -289,6 +289,88 @@ def cpu_baseline(wl, budget_s):
                        "single-threaded C oracle (gcc -O2), host has %d cores" % (runs, t_total, os.cpu_count()))
 
 
+# --------------------------------------------------------------------------- profile summaries
+KERNEL_SRC = {"combine": ("combine.hip", "device.h"), "pack": ("pack.hip", "device.h"),
+              "notify": ("notify.hip", "device.h"), "layout": ("layout.hip", "device.h")}
+
+
+def _kernel_key(name):
+    for k in ("combine_kernel", "pack_kernel", "notify_kernel", "layout_kernel", "ll_send_kernel", "ll_recv_kernel"):
+        if "miep::" + k in name:
+            return k.replace("_kernel", "")
+    return None
+
+
+def summarize_stats(stats_dir, out_md, command):
+    """rocprofv3 --kernel-trace --stats CSV -> a short markdown table of the miep kernels."""
+    import csv
+    import glob
+    path = glob.glob(os.path.join(stats_dir, "*_kernel_stats.csv"))[0]
+    lines = ["# Kernel durations: normal workload step (rocprofv3 --kernel-trace --stats)", "",
+             "Command (from the repo root on the GPU box; `R` = repo root):", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(path)):
+        if "miep::" not in r["Name"]:
+            continue
+        lines.append("| `%s` | %s | %.2f | %.2f | %.2f |" % (r["Name"].split("(")[0], r["Calls"],
+                                                            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                                                            float(r["MaxNs"]) / 1e3))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_pmc(fetch_dir, write_dir, out_json, out_md, commands, copy_mib):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each miep kernel, scaled by
+    what the same counters read for the runtime's plain copy kernel of known size."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def per_kernel(d, counter):
+        path = glob.glob(os.path.join(d, "*_counter_collection.csv"))[0]
+        vals = defaultdict(list)
+        copy = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if r["Kernel_Name"] == "__amd_rocclr_copyBuffer" and v > 0:
+                copy.append(v)
+            k = _kernel_key(r["Kernel_Name"])
+            if k:
+                vals[k].append(v)
+        return vals, max(copy)
+
+    fetch, copy_f = per_kernel(fetch_dir, "FETCH_SIZE")
+    write, copy_w = per_kernel(write_dir, "WRITE_SIZE")
+    true_kib = copy_mib * 1024.0
+    sf, sw = copy_f / true_kib, copy_w / true_kib
+    out = {"copy_probe_mib": copy_mib, "fetch_scale": round(sf, 5), "write_scale": round(sw, 5),
+           "commands": commands, "kernels": {}}
+    lines = ["# HBM traffic per launch: normal workload (rocprofv3 --pmc)", "",
+             "Counters are KiB per dispatch.  Scale factors come from the runtime's plain copy kernel "
+             "(`__amd_rocclr_copyBuffer`) of %d MiB run in the same process: FETCH_SIZE reads %.5f x its true bytes, "
+             "WRITE_SIZE %.5f x." % (copy_mib, sf, sw), "", "Commands:", "", "```"] + commands + ["```", "",
+             "| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic MB (scaled) | source hash |",
+             "|---|---|---|---|---|---|"]
+    for k in sorted(set(fetch) & set(write)):
+        f = sum(fetch[k]) / len(fetch[k])
+        w = sum(write[k]) / len(write[k])
+        traffic = (f / sf + w / sw) * 1024.0
+        entry = {"launches": len(fetch[k]), "fetch_kib": round(f, 1), "write_kib": round(w, 1),
+                 "traffic_bytes_per_launch": int(traffic)}
+        if k in KERNEL_SRC:
+            entry["src_hash"] = src_hash(*KERNEL_SRC[k])
+        out["kernels"][k] = entry
+        lines.append("| %s | %d | %.1f | %.1f | %.2f | %s |" % (k, len(fetch[k]), f, w, traffic / 1e6,
+                                                               entry.get("src_hash", "-")))
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 # --------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -300,7 +382,19 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy of this many MiB first (reference for HBM counter scaling)")
+    ap.add_argument("--summarize-stats", metavar="DIR", help="write profiles/ summary of a rocprofv3 --stats run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)")
+    ap.add_argument("--command", action="append", default=[], help="command line(s) recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, os.path.join(PROFILES, "normal_step_kernels.md"),
+                        "\n".join(args.command))
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], os.path.join(PROFILES, "normal_hbm_traffic.json"),
+                      os.path.join(PROFILES, "normal_hbm_traffic.md"), args.command, args.copy_probe_mib or 512)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the logical ranks are partitions of one GPU's HBM and nothing here "
               "uses a second GPU (asked for --gpus %d)." % args.gpus, file=sys.stderr)
