@@ -114,6 +114,7 @@ namespace miep {
 const Tuning& tuning() {
   static const Tuning t = {env_int("MIEP_PACK_VPL", 0),     env_int("MIEP_PACK_SLICES", 0),
                            env_int("MIEP_COMBINE_VPL", 0),  env_int("MIEP_COMBINE_SLICES", 0),
+                           env_int("MIEP_COMBINE_MAXR", 0),
                            env_int("MIEP_PACK_NT", 2) & 3, env_int("MIEP_COMBINE_NT", 1) != 0 ? 1 : 0};
   return t;
 }

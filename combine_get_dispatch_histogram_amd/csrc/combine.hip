@@ -16,7 +16,7 @@
 
 namespace miep {
 
-template <int VPL, int MW, bool NT>
+template <int VPL, int MAXR, int MW, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices) {
   const int lane = lane_id();
   const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
@@ -74,24 +74,45 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
     for (int i = 0; i < MW; ++i) {
       uint64_t m = smask[i];
       while (m) {
-        const int b = __builtin_ctzll(m);
-        m &= m - 1;
-        const int64_t row = readlane(src[i], b);
-        const uint8_t* yrow = y + row * row_bytes;
-        v4u d[VPL];
+        // a batch of up to MAXR source rows: every load issued, then the adds
+        // in ascending rank order (the order the oracle fixes)
+        int64_t rows[MAXR];
+        int nb = 0;
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const int v = v0 + j * kWave + lane;
-          if (v < nv) d[j] = ld16<NT>(yrow + static_cast<int64_t>(v) * 16);
+        for (int q = 0; q < MAXR; ++q) {
+          rows[q] = 0;
+          if (m) {
+            const int b = __builtin_ctzll(m);
+            m &= m - 1;
+            rows[q] = readlane(src[i], b);
+            nb = q + 1;
+          }
+        }
+        v4u d[MAXR][VPL];
+#pragma unroll
+        for (int q = 0; q < MAXR; ++q) {
+          if (q < nb) {
+            const uint8_t* yrow = y + rows[q] * row_bytes;
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+              const int v = v0 + j * kWave + lane;
+              if (v < nv) d[q][j] = ld16<NT>(yrow + static_cast<int64_t>(v) * 16);
+            }
+          }
         }
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const float f[8] = {bf16_lo(d[j].x), bf16_hi(d[j].x), bf16_lo(d[j].y), bf16_hi(d[j].y),
-                              bf16_lo(d[j].z), bf16_hi(d[j].z), bf16_lo(d[j].w), bf16_hi(d[j].w)};
+        for (int q = 0; q < MAXR; ++q) {
+          if (q < nb) {
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc[j][q] = have ? acc[j][q] + f[q] : f[q];
+            for (int j = 0; j < VPL; ++j) {
+              const float f[8] = {bf16_lo(d[q][j].x), bf16_hi(d[q][j].x), bf16_lo(d[q][j].y), bf16_hi(d[q][j].y),
+                                  bf16_lo(d[q][j].z), bf16_hi(d[q][j].z), bf16_lo(d[q][j].w), bf16_hi(d[q][j].w)};
+#pragma unroll
+              for (int k = 0; k < 8; ++k) acc[j][k] = have ? acc[j][k] + f[k] : f[k];
+            }
+            have = true;
+          }
         }
-        have = true;
       }
     }
 #pragma unroll
@@ -113,38 +134,46 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
   }
 }
 
-template <int VPL, bool NT>
-static hipError_t launch_combine_vpl(const CombineArgs& a, int nslices, hipStream_t st) {
+template <int VPL, int MAXR, bool NT>
+static hipError_t launch_combine_cfg(const CombineArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
   const int64_t blocks = (waves + 3) / 4;
   if (a.R <= 64)
-    hipLaunchKernelGGL((combine_kernel<VPL, 1, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+    hipLaunchKernelGGL((combine_kernel<VPL, MAXR, 1, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                        nslices);
   else
-    hipLaunchKernelGGL((combine_kernel<VPL, 4, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+    hipLaunchKernelGGL((combine_kernel<VPL, MAXR, 4, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                        nslices);
   return hipGetLastError();
 }
 
+// (vectors per lane, rows loaded per batch) pairs compiled in; register use
+// grows with their product, so large rows-per-batch go with short slices.
 template <bool NT>
-static hipError_t launch_combine_nt(const CombineArgs& a, int vpl, int nslices, hipStream_t st) {
-  switch (vpl) {
-    case 2: return launch_combine_vpl<2, NT>(a, nslices, st);
-    case 4: return launch_combine_vpl<4, NT>(a, nslices, st);
-    case 7: return launch_combine_vpl<7, NT>(a, nslices, st);
-    default: return launch_combine_vpl<8, NT>(a, nslices, st);
-  }
+static hipError_t launch_combine_nt(const CombineArgs& a, int vpl, int maxr, int nslices, hipStream_t st) {
+  if (vpl == 1) return launch_combine_cfg<1, 8, NT>(a, nslices, st);
+  if (vpl == 2) return maxr <= 4 ? launch_combine_cfg<2, 4, NT>(a, nslices, st)
+                                 : launch_combine_cfg<2, 8, NT>(a, nslices, st);
+  if (vpl == 4) return maxr <= 2 ? launch_combine_cfg<4, 2, NT>(a, nslices, st)
+                                 : launch_combine_cfg<4, 4, NT>(a, nslices, st);
+  if (vpl == 7) return maxr <= 1 ? launch_combine_cfg<7, 1, NT>(a, nslices, st)
+                                 : launch_combine_cfg<7, 2, NT>(a, nslices, st);
+  return maxr <= 1 ? launch_combine_cfg<8, 1, NT>(a, nslices, st) : launch_combine_cfg<8, 2, NT>(a, nslices, st);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
   const Tuning& tu = tuning();
   const int nv = a.H / 8;
-  int vpl = tu.combine_vpl > 0 ? tu.combine_vpl : (nv % (7 * kWave) == 0 ? 7 : 8);
+  // default: one 16-byte vector per lane per row and 8 rows' loads in flight
+  // (hidden 7168 -> 14 waves per token); ragged rows keep 8 vectors x 2 rows
+  int vpl = tu.combine_vpl > 0 ? tu.combine_vpl : (nv % kWave == 0 ? 1 : 8);
+  int maxr = tu.combine_maxr > 0 ? tu.combine_maxr : (vpl <= 2 ? 8 : 2);
   const int span = vpl * kWave;
   int nslices = tu.combine_slices > 0 ? tu.combine_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
-  return tu.combine_nt ? launch_combine_nt<true>(a, vpl, nslices, st) : launch_combine_nt<false>(a, vpl, nslices, st);
+  return tu.combine_nt ? launch_combine_nt<true>(a, vpl, maxr, nslices, st)
+                       : launch_combine_nt<false>(a, vpl, maxr, nslices, st);
 }
 
 }  // namespace miep

@@ -99,11 +99,12 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st);
 
 // Optional launch-geometry overrides read once from the environment
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
-// MIEP_PACK_NT, MIEP_COMBINE_NT): used by geometry sweeps, never required.
+// MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT): used by geometry sweeps,
+// never required.  combine_maxr: source rows whose loads are issued together.
 // pack_nt: bit 0 = non-temporal payload loads, bit 1 = non-temporal stores;
 // combine_nt: non-temporal loads of the expert outputs.
 struct Tuning {
-  int pack_vpl, pack_slices, combine_vpl, combine_slices, pack_nt, combine_nt;
+  int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt;
 };
 const Tuning& tuning();
 
