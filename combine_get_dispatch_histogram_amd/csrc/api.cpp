@@ -115,7 +115,8 @@ const Tuning& tuning() {
   static const Tuning t = {env_int("MIEP_PACK_VPL", 0),     env_int("MIEP_PACK_SLICES", 0),
                            env_int("MIEP_COMBINE_VPL", 0),  env_int("MIEP_COMBINE_SLICES", 0),
                            env_int("MIEP_COMBINE_MAXR", 0),
-                           env_int("MIEP_PACK_NT", 2) & 3, env_int("MIEP_COMBINE_NT", 1) != 0 ? 1 : 0};
+                           env_int("MIEP_PACK_NT", 2) & 3, env_int("MIEP_COMBINE_NT", 1) & 3,
+                           env_int("MIEP_LL_SPLIT", 0),     env_int("MIEP_LL_VPL", 0)};
   return t;
 }
 }  // namespace miep

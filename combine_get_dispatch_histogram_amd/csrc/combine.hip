@@ -16,7 +16,7 @@
 
 namespace miep {
 
-template <int VPL, int MAXR, int MW, bool NT>
+template <int VPL, int MAXR, int MW, int NT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices) {
   const int lane = lane_id();
   const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
               const int v = v0 + j * kWave + lane;
-              if (v < nv) d[q][j] = ld16<NT>(yrow + static_cast<int64_t>(v) * 16);
+              if (v < nv) d[q][j] = ld16<(NT & 1) != 0>(yrow + static_cast<int64_t>(v) * 16);
             }
           }
         }
@@ -128,13 +128,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
         } else {
           o = v4u{0u, 0u, 0u, 0u};
         }
-        st16<false>(orow + static_cast<int64_t>(v) * 16, o);
+        st16<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 16, o);
       }
     }
   }
 }
 
-template <int VPL, int MAXR, bool NT>
+template <int VPL, int MAXR, int NT>
 static hipError_t launch_combine_cfg(const CombineArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
   const int64_t blocks = (waves + 3) / 4;
@@ -149,9 +149,11 @@ static hipError_t launch_combine_cfg(const CombineArgs& a, int nslices, hipStrea
 
 // (vectors per lane, rows loaded per batch) pairs compiled in; register use
 // grows with their product, so large rows-per-batch go with short slices.
-template <bool NT>
+template <int NT>
 static hipError_t launch_combine_nt(const CombineArgs& a, int vpl, int maxr, int nslices, hipStream_t st) {
-  if (vpl == 1) return launch_combine_cfg<1, 8, NT>(a, nslices, st);
+  if (vpl == 1) return maxr <= 4 ? launch_combine_cfg<1, 4, NT>(a, nslices, st)
+                                 : maxr <= 8 ? launch_combine_cfg<1, 8, NT>(a, nslices, st)
+                                             : launch_combine_cfg<1, 16, NT>(a, nslices, st);
   if (vpl == 2) return maxr <= 4 ? launch_combine_cfg<2, 4, NT>(a, nslices, st)
                                  : launch_combine_cfg<2, 8, NT>(a, nslices, st);
   if (vpl == 4) return maxr <= 2 ? launch_combine_cfg<4, 2, NT>(a, nslices, st)
@@ -172,8 +174,12 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int span = vpl * kWave;
   int nslices = tu.combine_slices > 0 ? tu.combine_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
-  return tu.combine_nt ? launch_combine_nt<true>(a, vpl, maxr, nslices, st)
-                       : launch_combine_nt<false>(a, vpl, maxr, nslices, st);
+  switch (tu.combine_nt) {
+    case 0: return launch_combine_nt<0>(a, vpl, maxr, nslices, st);
+    case 2: return launch_combine_nt<2>(a, vpl, maxr, nslices, st);
+    case 3: return launch_combine_nt<3>(a, vpl, maxr, nslices, st);
+    default: return launch_combine_nt<1>(a, vpl, maxr, nslices, st);
+  }
 }
 
 }  // namespace miep

@@ -102,9 +102,10 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st);
 // MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT): used by geometry sweeps,
 // never required.  combine_maxr: source rows whose loads are issued together.
 // pack_nt: bit 0 = non-temporal payload loads, bit 1 = non-temporal stores;
-// combine_nt: non-temporal loads of the expert outputs.
+// combine_nt: bit 0 = non-temporal loads of the expert outputs, bit 1 =
+// non-temporal stores of the combined rows.
 struct Tuning {
-  int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt;
+  int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl;
 };
 const Tuning& tuning();
 

@@ -27,7 +27,7 @@
 namespace miep {
 
 constexpr int kLLThreads = 256;
-constexpr int kLLSplit = 4;  // workgroups sharing one (l, s) block's messages
+constexpr int kLLSplit = 8;  // default workgroups sharing one (l, s) block's messages
 constexpr int kLLMaxSlots = 4096;
 
 template <int VPL>
@@ -180,19 +180,28 @@ __global__ __launch_bounds__(kLLThreads) void ll_recv_kernel(LLArgs a) {
 }
 
 template <int VPL>
-static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, hipStream_t st) {
-  hipLaunchKernelGGL(ll_send_kernel<VPL>, dim3(blocks, kLLSplit), dim3(kLLThreads), 0, st, a);
+static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, int split, hipStream_t st) {
+  hipLaunchKernelGGL(ll_send_kernel<VPL>, dim3(blocks, split), dim3(kLLThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ll_recv_kernel<VPL>, dim3(blocks, kLLSplit), dim3(kLLThreads), 0, st, a);
+  hipLaunchKernelGGL(ll_recv_kernel<VPL>, dim3(blocks, split), dim3(kLLThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
   const int blocks = a.L * a.R;
   if (blocks == 0) return hipSuccess;
-  // one 16-byte vector per lane per task when a bf16 row is a multiple of 64 vectors
-  return (a.H / 8) % kWave == 0 ? launch_ll_vpl<1>(a, blocks, st) : launch_ll_vpl<8>(a, blocks, st);
+  const Tuning& tu = tuning();
+  const int split = tu.ll_split > 0 ? tu.ll_split : kLLSplit;
+  // two 16-byte vectors per lane per task when a bf16 row is a multiple of
+  // 128 vectors (measured best with 8 workgroups per (l, s) block)
+  const int vpl = tu.ll_vpl > 0 ? tu.ll_vpl : ((a.H / 8) % (2 * kWave) == 0 ? 2 : 8);
+  switch (vpl) {
+    case 1: return launch_ll_vpl<1>(a, blocks, split, st);
+    case 2: return launch_ll_vpl<2>(a, blocks, split, st);
+    case 4: return launch_ll_vpl<4>(a, blocks, split, st);
+    default: return launch_ll_vpl<8>(a, blocks, split, st);
+  }
 }
 
 }  // namespace miep

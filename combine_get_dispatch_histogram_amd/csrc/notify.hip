@@ -45,6 +45,11 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     run[r] = 0;
   }
   for (int k = tid; k < ne; k += blockDim.x) eacc[k] = 0;
+  // the first token tile's membership rows are loaded now, so their latency
+  // overlaps the rank-total reduction below
+  RankMask<MW> first;
+  first.clear();
+  if (tid < T) first = load_rank_row<MW>(a.in_rank + (static_cast<int64_t>(s) * T + tid) * R, R);
   __syncthreads();
   // rank totals and bases: every (source, rank) entry loaded by one thread,
   // summed with LDS integer atomics (order-free), so no thread walks a
@@ -89,9 +94,11 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     const int t = t0 + tid;
     const bool valid = t < T;
     const int64_t n = static_cast<int64_t>(s) * T + t;
-    RankMask<MW> m;
-    m.clear();
-    if (valid) m = load_rank_row<MW>(a.in_rank + n * R, R);
+    RankMask<MW> m = first;
+    if (t0 > 0) {
+      m.clear();
+      if (valid) m = load_rank_row<MW>(a.in_rank + n * R, R);
+    }
     // pass 1: per-wavefront counts, lane j of the wave keeps rank r0 + j
     for (int r0 = 0; r0 < R; r0 += kWave) {
       const int rend = R - r0 < kWave ? R - r0 : kWave;
