@@ -6,7 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/miep.h"
+#include "miep.h"
 #include "kernels.h"
 
 namespace {
@@ -64,6 +64,8 @@ miep_status check_payload(const miep_problem* p, const void* x, int32_t x_kind, 
   if (p->hidden % 8 != 0) return fail(MIEP_EUNSUPPORTED, "hidden must be a multiple of 8 (16-byte rows)");
   if (x_kind != MIEP_X_BF16) {
     if (p->hidden % miep::kFp8Group != 0) return fail(MIEP_EINVAL, "FP8 payloads need hidden % 128 == 0");
+    if (x_kind == MIEP_X_BF16_CAST_FP8 && p->hidden > 65536)
+      return fail(MIEP_EUNSUPPORTED, "the fused FP8 cast supports hidden <= 65536");
     if (x_kind == MIEP_X_FP8 && N > 0 && !x_scales) return fail(MIEP_EINVAL, "x_scales is NULL for MIEP_X_FP8");
   }
   return ok();
@@ -116,7 +118,8 @@ const Tuning& tuning() {
                            env_int("MIEP_COMBINE_VPL", 0),  env_int("MIEP_COMBINE_SLICES", 0),
                            env_int("MIEP_COMBINE_MAXR", 0),
                            env_int("MIEP_PACK_NT", 2) & 3, env_int("MIEP_COMBINE_NT", 1) & 3,
-                           env_int("MIEP_LL_SPLIT", 0),     env_int("MIEP_LL_VPL", 0)};
+                           env_int("MIEP_LL_SPLIT", 0),     env_int("MIEP_LL_VPL", 0),
+                           env_int("MIEP_CAST_TPB", -1)};
   return t;
 }
 }  // namespace miep

@@ -99,13 +99,17 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st);
 
 // Optional launch-geometry overrides read once from the environment
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
-// MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT): used by geometry sweeps,
-// never required.  combine_maxr: source rows whose loads are issued together.
+// MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT, MIEP_LL_SPLIT,
+// MIEP_LL_VPL, MIEP_CAST_TPB): used by geometry sweeps, never required.
+// combine_maxr: source rows whose loads are issued together.
 // pack_nt: bit 0 = non-temporal payload loads, bit 1 = non-temporal stores;
 // combine_nt: bit 0 = non-temporal loads of the expert outputs, bit 1 =
-// non-temporal stores of the combined rows.
+// non-temporal stores of the combined rows.  ll_split: workgroups per
+// low-latency (expert, source) block.  cast_tpb: fused FP8 cast with one
+// token per workgroup (1), 1 KiB slices (0), or chosen per call (-1).
 struct Tuning {
-  int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl;
+  int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl,
+      cast_tpb;
 };
 const Tuning& tuning();
 

@@ -142,6 +142,134 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   }
 }
 
+// Fused FP8 cast, one token per workgroup: wavefront w casts row slice w
+// (64 lanes x VPL 16-byte vectors) and stores its codes to every
+// destination; the row's H/128 scales are gathered in LDS and leave as one
+// contiguous store per destination (scattered 16-byte scale pieces written
+// by separate wavefronts cost a quarter of the kernel's time).
+constexpr int kCastMaxGroups = 512;  // H <= 65536
+
+template <int VPL, int MW, int NT>
+__global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
+  __shared__ float row_scales[kCastMaxGroups];
+  const int lane = lane_id();
+  const int slice = threadIdx.x / kWave;
+  const int64_t n = blockIdx.x;
+  const int R = a.R;
+  int dst[MW];
+  uint64_t dmask[MW];
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    const int r = kWave * i + lane;
+    int row = -1;
+    if (r < R) {
+      const int sh = a.send_head[n * R + r];
+      const int o = a.off[r];
+      row = sh >= 0 ? o + sh : -1;
+    }
+    dst[i] = row;
+    dmask[i] = ballot(row >= 0 && row < a.capacity);
+  }
+  const int G = a.H / kFp8Group;
+  if (slice == 0 && a.meta) {
+    int64_t e = -1;
+    float wk = 0.0f;
+    if (lane < a.K) {
+      e = a.topk_idx[n * a.K + lane];
+      if (a.topk_weights) wk = a.topk_weights[n * a.K + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      uint64_t m = dmask[i];
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        const int r = kWave * i + b;
+        const int64_t row = readlane(dst[i], b);
+        if (lane < a.K) {
+          const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;
+          if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
+          if (a.recv_topk_weights) a.recv_topk_weights[row * a.K + lane] = mine ? wk : 0.0f;
+        }
+        if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(n % a.T);
+      }
+    }
+  }
+  const int nv = a.H / 8;
+  const uint8_t* xrow = static_cast<const uint8_t*>(a.x) + n * 2 * static_cast<int64_t>(a.H);
+  uint8_t* recv = static_cast<uint8_t*>(a.recv_x);
+  const int v0 = slice * kWave * VPL;
+  v4u d[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int v = v0 + j * kWave + lane;
+    if (v < nv) d[j] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(v) * 16);
+  }
+  v2u q[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int v = v0 + j * kWave + lane;
+    const float amax = group16_max(v < nv ? absmax8(d[j]) : 0.0f);
+    float sci;
+    const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
+    if (v < nv) {
+      q[j] = cast8(d[j], sc);
+      if ((lane & 15) == 0) row_scales[v / 16] = sci;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    uint64_t m = dmask[i];
+    while (m) {
+      const int b = __builtin_ctzll(m);
+      m &= m - 1;
+      uint8_t* orow = recv + static_cast<int64_t>(readlane(dst[i], b)) * a.H;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + j * kWave + lane;
+        if (v < nv) st8<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 8, q[j]);
+      }
+    }
+  }
+  __syncthreads();
+  if (slice == 0) {
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      uint64_t m = dmask[i];
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        float* srow = a.recv_x_scales + static_cast<int64_t>(readlane(dst[i], b)) * G;
+        for (int g = lane; g < G; g += kWave) srow[g] = row_scales[g];
+      }
+    }
+  }
+}
+
+template <int VPL, int NT>
+static hipError_t launch_pack_cast_vpl(const PackArgs& a, hipStream_t st) {
+  const int nv = a.H / 8;
+  const int waves = (nv + kWave * VPL - 1) / (kWave * VPL);
+  if (a.R <= 64)
+    hipLaunchKernelGGL((pack_cast_kernel<VPL, 1, NT>), dim3(static_cast<unsigned>(a.N)), dim3(waves * kWave), 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((pack_cast_kernel<VPL, 4, NT>), dim3(static_cast<unsigned>(a.N)), dim3(waves * kWave), 0, st,
+                       a);
+  return hipGetLastError();
+}
+
+// Smallest vectors-per-lane (at least `vpl_hint`) that fits the row in 16
+// wavefronts.
+template <int NT>
+static hipError_t launch_pack_cast(const PackArgs& a, int vpl_hint, hipStream_t st) {
+  const int nv = a.H / 8;
+  if (vpl_hint <= 1 && nv <= 16 * kWave) return launch_pack_cast_vpl<1, NT>(a, st);
+  if (vpl_hint <= 2 && nv <= 32 * kWave) return launch_pack_cast_vpl<2, NT>(a, st);
+  if (vpl_hint <= 4 && nv <= 64 * kWave) return launch_pack_cast_vpl<4, NT>(a, st);
+  return launch_pack_cast_vpl<8, NT>(a, st);
+}
+
 template <int KIND, int VPL, int NT>
 static hipError_t launch_pack_vpl(const PackArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
@@ -191,7 +319,20 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   if (nslices < 1) nslices = 1;
   switch (a.kind) {
     case kPackFp8: return launch_pack_nt<kPackFp8>(a, vpl, nslices, tu.pack_nt, st);
-    case kPackCastFp8: return launch_pack_nt<kPackCastFp8>(a, vpl, nslices, tu.pack_nt, st);
+    case kPackCastFp8:
+      // Measured on the 16384-token workload: with the top-k metadata (fresh
+      // dispatch) one token per workgroup at 2 vectors per lane is fastest
+      // (229 vs 264 us); without it (cached) the 1 KiB slices are (247 vs 262).
+      if (tu.cast_tpb > 0 || (tu.cast_tpb < 0 && a.meta)) {
+        const int hint = tu.pack_vpl > 0 ? tu.pack_vpl : 2;
+        switch (tu.pack_nt) {
+          case 0: return launch_pack_cast<0>(a, hint, st);
+          case 1: return launch_pack_cast<1>(a, hint, st);
+          case 3: return launch_pack_cast<3>(a, hint, st);
+          default: return launch_pack_cast<2>(a, hint, st);
+        }
+      }
+      return launch_pack_nt<kPackCastFp8>(a, vpl, nslices, tu.pack_nt, st);
     default: return launch_pack_nt<kPackBf16>(a, vpl, nslices, tu.pack_nt, st);
   }
 }
