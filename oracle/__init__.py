@@ -69,13 +69,15 @@ def _declare(lib):
     lib.oracle_dispatch.restype = _I
     lib.oracle_cached_dispatch.argtypes = [_I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I64, _P, _P]
     lib.oracle_cached_dispatch.restype = _I
-    lib.oracle_combine.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _P, _P, _P, _P]
+    lib.oracle_combine.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P]
     lib.oracle_combine.restype = _I
     lib.oracle_fp8_quantize.argtypes = [_I64, _I, _P, _I, _P, _P, _P]
     lib.oracle_fp8_quantize.restype = _I
     lib.oracle_ll_msg_bytes.argtypes = [_I, _I]
     lib.oracle_ll_msg_bytes.restype = _I64
-    lib.oracle_ll_dispatch.argtypes = [_I] * 8 + [_P, _P, _I, _I, _I] + [_P] * 9
+    lib.oracle_ll_dispatch.argtypes = [_I] * 8 + [_P, _P, _I, _I, _I] + [_P] * 10
+    lib.oracle_ll_combine.argtypes = [_I] * 8 + [_P] * 7
+    lib.oracle_ll_combine.restype = _I
     lib.oracle_ll_dispatch.restype = _I
     lib.oracle_e4m3_encode_n.argtypes = [_I64, _P, _P]
     lib.oracle_e4m3_decode_n.argtypes = [_I64, _P, _P]
@@ -224,8 +226,8 @@ def cached_dispatch(x: np.ndarray, send_head: np.ndarray, recv_rank_offset: np.n
 
 # --------------------------------------------------------------------------- O4
 def combine(y: np.ndarray, recv_topk_weights, send_head: np.ndarray, recv_rank_offset: np.ndarray, S: int,
-            K: int = 0, want_f64: bool = False, want_f32: bool = False) -> dict:
-    """y: uint16 bf16 bits [capacity][H] in the receive layout."""
+            K: int = 0, want_f64: bool = False, want_f32: bool = False, bias0=None, bias1=None) -> dict:
+    """y: uint16 bf16 bits [capacity][H] in the receive layout; bias0/bias1: uint16 [N][H] or None."""
     y = _c(y, np.uint16)
     cap, H = y.shape
     sh = _c(send_head, np.int32)
@@ -239,8 +241,10 @@ def combine(y: np.ndarray, recv_topk_weights, send_head: np.ndarray, recv_rank_o
     out_w = np.empty((N, K), np.float32) if w is not None else None
     out32 = np.empty((N, H), np.float32) if want_f32 else None
     out64 = np.empty((N, H), np.float64) if want_f64 else None
-    _check(_load().oracle_combine(S, T, H, K, R, _ptr(y), _ptr(w), _ptr(sh), _ptr(off), cap, _ptr(out), _ptr(out_w),
-                                  _ptr(out32), _ptr(out64)), "combine")
+    b0 = _c(bias0, np.uint16) if bias0 is not None else None
+    b1 = _c(bias1, np.uint16) if bias1 is not None else None
+    _check(_load().oracle_combine(S, T, H, K, R, _ptr(y), _ptr(w), _ptr(b0), _ptr(b1), _ptr(sh), _ptr(off), cap,
+                                  _ptr(out), _ptr(out_w), _ptr(out32), _ptr(out64)), "combine")
     return dict(combined_x=out, combined_topk_weights=out_w, combined_f32=out32, combined_f64=out64)
 
 
@@ -251,7 +255,7 @@ def ll_msg_bytes(H: int, use_fp8: bool) -> int:
 
 def ll_dispatch(x: np.ndarray, topk_idx: np.ndarray, S: int, M: int, E: int, R: int, dest_rank: int,
                 use_fp8: bool, round_scale: bool = False, use_ue8m0: bool = False,
-                cumulative_stats: np.ndarray | None = None) -> dict:
+                cumulative_stats: np.ndarray | None = None, mask: np.ndarray | None = None) -> dict:
     """Low-latency dispatch seen from rank ``dest_rank``.  x: uint16 bf16 bits [S*T][H]."""
     x = _c(x, np.uint16)
     idx = _c(topk_idx, np.int64)
@@ -275,12 +279,32 @@ def ll_dispatch(x: np.ndarray, topk_idx: np.ndarray, S: int, M: int, E: int, R: 
     lr = np.zeros((L, S), np.int64)
     pc = np.zeros((L,), np.int32)
     cs = _c(cumulative_stats, np.int32).copy() if cumulative_stats is not None else None
+    mk = _c(mask, np.int32) if mask is not None else None
     _check(_load().oracle_ll_dispatch(S, T, M, H, K, E, R, dest_rank, _ptr(x), _ptr(idx), int(use_fp8),
                                       int(round_scale), int(use_ue8m0), _ptr(msg), _ptr(cnt), _ptr(prx), _ptr(prs),
-                                      _ptr(pue), _ptr(src), _ptr(lr), _ptr(pc), _ptr(cs)), "ll_dispatch")
+                                      _ptr(pue), _ptr(src), _ptr(lr), _ptr(pc), _ptr(cs), _ptr(mk)), "ll_dispatch")
     return dict(msg_buf=msg, msg_count=cnt, packed_recv_x=prx, packed_recv_x_scales=prs,
                 packed_recv_x_scales_ue8m0=pue, packed_recv_src_info=src, packed_recv_layout_range=lr,
                 packed_recv_count=pc, cumulative_local_expert_recv_stats=cs)
+
+
+def ll_combine(y: np.ndarray, src_info: np.ndarray, layout_range: np.ndarray, topk_idx: np.ndarray, S: int, M: int,
+               E: int, R: int, dest_rank: int, topk_weights=None, want_f64: bool = False) -> dict:
+    """Low-latency combine seen from rank ``dest_rank``: y uint16 bf16 bits [L][S*M][H] (the local experts'
+    outputs in the packed layout) -> combined [S*T][H] bf16 bits (this rank's contribution per source token)."""
+    y = _c(y, np.uint16)
+    L, SM, H = y.shape
+    idx = _c(topk_idx, np.int64)
+    N, K = idx.shape
+    T = N // S
+    si = _c(src_info, np.int32)
+    lr = _c(layout_range, np.int64)
+    w = _c(topk_weights, np.float32) if topk_weights is not None else None
+    out = np.empty((N, H), np.uint16)
+    out64 = np.empty((N, H), np.float64) if want_f64 else None
+    _check(_load().oracle_ll_combine(S, T, M, H, K, E, R, dest_rank, _ptr(y), _ptr(si), _ptr(lr), _ptr(idx), _ptr(w),
+                                     _ptr(out), _ptr(out64)), "ll_combine")
+    return dict(combined_x=out, combined_f64=out64)
 
 
 def calc_diff(x: np.ndarray, y: np.ndarray) -> float:

@@ -387,11 +387,17 @@ int oracle_cached_dispatch(int S, int T, int H, int R, int x_kind, const void* x
  * Reading: contributions are added in ascending rank order, the sum is
  * started from the first contribution (so a lone -0.0 stays -0.0), and a
  * token that no rank received combines to +0.0.
+ * [Ch4] 4.2 also unpacks a bias into bias_0 and bias_1 for the combine; the
+ * pages give no formula.  Reading: each bias is a [S*T][H] bf16 row per
+ * source token added after the received contributions, bias_0 then bias_1,
+ * in fp32 (an empty contribution sum counts as +0.0 then).
  *   y [capacity][H] bf16 in the receive layout, w [capacity][K] f32
- *   (nullable) -> out [S*T][H] bf16, out_w [S*T][K] f32 (nullable),
+ *   (nullable), bias0/bias1 [S*T][H] bf16 (nullable)
+ *   -> out [S*T][H] bf16, out_w [S*T][K] f32 (nullable),
  *   out_f32 [S*T][H] (nullable): the fp32 sums before the bf16 rounding;
  *   out_f64 [S*T][H] (nullable): the same sums in fp64, for accuracy checks. */
 int oracle_combine(int S, int T, int H, int K, int R, const uint16_t* y, const float* w,
+                   const uint16_t* bias0, const uint16_t* bias1,
                    const int32_t* send_head, const int32_t* recv_rank_offset, int64_t capacity,
                    uint16_t* out, float* out_w, float* out_f32, double* out_f64) {
     if (S < 0 || T < 0 || H <= 0 || R <= 0 || K < 0) return ORC_EINVAL;
@@ -416,10 +422,17 @@ int oracle_combine(int S, int T, int H, int K, int R, const uint16_t* y, const f
             }
             have = 1;
         }
+        const int biased = bias0 != NULL || bias1 != NULL;
         for (int h = 0; h < H; ++h) {
-            out[n * H + h] = have ? oracle_bf16_round(acc[h]) : 0;
-            if (out_f32) out_f32[n * H + h] = have ? acc[h] : 0.0f;
-            if (out_f64) out_f64[n * H + h] = have ? acc64[h] : 0.0;
+            if (biased) {
+                if (!have) { acc[h] = 0.0f; acc64[h] = 0.0; }
+                if (bias0) { acc[h] += oracle_bf16_to_f32(bias0[n * H + h]); acc64[h] += oracle_bf16_to_f32(bias0[n * H + h]); }
+                if (bias1) { acc[h] += oracle_bf16_to_f32(bias1[n * H + h]); acc64[h] += oracle_bf16_to_f32(bias1[n * H + h]); }
+            }
+            const int any = have || biased;
+            out[n * H + h] = any ? oracle_bf16_round(acc[h]) : 0;
+            if (out_f32) out_f32[n * H + h] = any ? acc[h] : 0.0f;
+            if (out_f64) out_f64[n * H + h] = any ? acc64[h] : 0.0;
         }
         if (out_w)
             for (int k = 0; k < K; ++k) out_w[n * K + k] = have ? wacc[k] : 0.0f;
@@ -445,7 +458,12 @@ int oracle_combine(int S, int T, int H, int K, int R, const uint16_t* y, const f
  * instead of the atomic arrival order; reserved header ints are 0; the
  * (l, s) blocks are packed in ascending s; layout_range[l][s] =
  * (begin << 32) | count; slots past M are dropped (count capped at M);
- * with use_ue8m0 the scales also come out as exponent bytes (e + 127).  */
+ * with use_ue8m0 the scales also come out as exponent bytes (e + 127).
+ * Rank masking ([NvLL] low-latency send loop and receive wait: a masked
+ * destination is not sent to, a masked source is not waited for): with a
+ * mask array [R] (nonzero = masked), nothing travels to rank d if d is
+ * masked, and nothing from a masked source s -- its (l, s) blocks hold 0
+ * messages.  */
 int64_t oracle_ll_msg_bytes(int H, int use_fp8) {
     return 16 + (use_fp8 ? (int64_t)H + 4LL * (H / ORC_FP8_GROUP) : 2LL * H);
 }
@@ -456,7 +474,7 @@ int oracle_ll_dispatch(int S, int T, int M, int H, int K, int E, int R, int d,
                        uint8_t* msg_buf, int32_t* msg_count,
                        void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_ue8m0,
                        int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
-                       int32_t* packed_recv_count, int32_t* cumulative_stats) {
+                       int32_t* packed_recv_count, int32_t* cumulative_stats, const int32_t* mask) {
     if (S <= 0 || T < 0 || M <= 0 || T > M || H <= 0 || K <= 0 || E <= 0 || R <= 0 || E % R != 0) return ORC_EINVAL;
     if (S != R || d < 0 || d >= R) return ORC_EINVAL;
     if (use_fp8 && H % ORC_FP8_GROUP != 0) return ORC_EINVAL;
@@ -474,7 +492,8 @@ int oracle_ll_dispatch(int S, int T, int M, int H, int K, int E, int R, int d,
     for (int l = 0; l < L; ++l)
         for (int s = 0; s < S; ++s) {
             int j = 0;
-            for (int t = 0; t < T; ++t)
+            const int masked = mask != NULL && (mask[d] != 0 || mask[s] != 0);
+            for (int t = 0; t < (masked ? 0 : T); ++t)
                 for (int k = 0; k < K; ++k) {
                     if (topk_idx[((int64_t)s * T + t) * K + k] != (int64_t)d * L + l) continue;
                     if (j < M) {
@@ -528,6 +547,70 @@ int oracle_ll_dispatch(int S, int T, int M, int H, int K, int E, int R, int d,
     }
     free(codes); free(sci); free(ue);
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Low-latency combine                                                        */
+/* ------------------------------------------------------------------------ */
+/* [Ch4] 4.3 names a low-latency combine beside the low-latency dispatch
+ * (with a deferred-receive hook and a zero-copy option) and [NvLL] lists it
+ * among the low-latency kernels; neither gives its arithmetic.
+ * Reading: it is the reverse of the low-latency dispatch seen from rank d.
+ * Every packed row of local expert l that came from source token (s, t)
+ * returns to that token.  For each source token, its top-k entries that name
+ * one of d's local experts are visited in ascending k; the entry's row is
+ * the dispatch's slot rule (the j-th such entry of source s in (token, k)
+ * order is row l*S*M + begin(l, s) + j); the row is multiplied by the
+ * entry's gate weight when weights are given (one fp32 multiply), else taken
+ * as is like the normal combine; contributions are summed in fp32 from the
+ * first one and rounded once to bf16; a token with no entry on rank d (or
+ * only dropped ones) combines to +0.0.  A row whose src_info does not name
+ * the token means the handle does not belong to this routing: error.
+ *   y [L][S*M][H] bf16, src_info [L][S*M], layout_range [L][S], topk_idx
+ *   [S*T][K], w [S*T][K] (nullable) -> out [S*T][H] bf16, out_f64 (nullable). */
+int oracle_ll_combine(int S, int T, int M, int H, int K, int E, int R, int d,
+                      const uint16_t* y, const int32_t* src_info, const int64_t* layout_range,
+                      const int64_t* topk_idx, const float* w, uint16_t* out, double* out_f64) {
+    if (S <= 0 || T < 0 || M <= 0 || T > M || H <= 0 || K <= 0 || E <= 0 || R <= 0 || E % R != 0) return ORC_EINVAL;
+    if (S != R || d < 0 || d >= R) return ORC_EINVAL;
+    const int L = E / R;
+    float* acc = (float*)malloc(sizeof(float) * (size_t)H);
+    double* acc64 = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!acc || !acc64) { free(acc); free(acc64); return ORC_EINVAL; }
+    int rc = ORC_OK;
+    for (int s = 0; s < S && rc == ORC_OK; ++s)
+        for (int t = 0; t < T && rc == ORC_OK; ++t) {
+            const int64_t n = (int64_t)s * T + t;
+            int have = 0;
+            for (int k = 0; k < K; ++k) {
+                const int64_t e = topk_idx[n * K + k];
+                if (e < (int64_t)d * L || e >= (int64_t)(d + 1) * L) continue;
+                const int l = (int)(e - (int64_t)d * L);
+                int64_t j = 0;                                   /* slot of entry (t, k) */
+                for (int t2 = 0; t2 < t; ++t2)
+                    for (int k2 = 0; k2 < K; ++k2) j += topk_idx[((int64_t)s * T + t2) * K + k2] == e;
+                for (int k2 = 0; k2 < k; ++k2) j += topk_idx[n * K + k2] == e;
+                const int64_t lr = layout_range[l * S + s];
+                const int64_t begin = lr >> 32, cnt = lr & 0xFFFFFFFFLL;
+                if (j >= cnt) continue;                          /* dropped at the slot cap, or masked */
+                const int64_t row = (int64_t)l * S * M + begin + j;
+                if (src_info[row] != t) { rc = ORC_EINVAL; break; }
+                const float wk = w ? w[n * K + k] : 1.0f;
+                for (int h = 0; h < H; ++h) {
+                    const float yv = oracle_bf16_to_f32(y[row * H + h]);
+                    const float v = w ? yv * wk : yv;
+                    const double v64 = (double)yv * (double)wk;     /* exact product, fp64 reference */
+                    if (!have) { acc[h] = v; acc64[h] = v64; } else { acc[h] += v; acc64[h] += v64; }
+                }
+                have = 1;
+            }
+            for (int h = 0; h < H; ++h) {
+                out[n * H + h] = have ? oracle_bf16_round(acc[h]) : 0;
+                if (out_f64) out_f64[n * H + h] = have ? acc64[h] : 0.0;
+            }
+        }
+    free(acc); free(acc64);
+    return rc;
 }
 
 /* ------------------------------------------------------------------------ */

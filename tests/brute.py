@@ -152,3 +152,41 @@ def expected_groups_hit(E: int, K: int, G: int) -> float:
     """Expected number of distinct groups (of E/G experts each) hit by K distinct
     uniformly chosen experts: G * (1 - C(E - E/G, K) / C(E, K))."""
     return G * (1 - math.comb(E - E // G, K) / math.comb(E, K))
+
+
+# ----------------------------------------------------------------- low-latency combine
+def ll_combine(y_bits, src_info, layout_range, topk_idx, S, M, E, R, d, weights=None):
+    """For each source token, walk its top-k entries on rank d's experts in k order; the entry's row is
+    found by scanning the (expert, source) block for rows naming the token (its occurrence among the
+    token's entries for that expert picks among duplicates); fp32 sum from the first contribution."""
+    L = E // R
+    N, K = topk_idx.shape
+    T = N // S
+    H = y_bits.shape[2]
+    out = np.zeros((N, H), np.float32)
+    have = np.zeros(N, bool)
+    for s in range(S):
+        for t in range(T):
+            n = s * T + t
+            acc = None
+            seen = {}
+            for k in range(K):
+                e = int(topk_idx[n, k])
+                if not (d * L <= e < (d + 1) * L):
+                    continue
+                l = e - d * L
+                occ = seen.get(e, 0)
+                seen[e] = occ + 1
+                begin, cnt = int(layout_range[l, s]) >> 32, int(layout_range[l, s]) & 0xFFFFFFFF
+                rows = [begin + i for i in range(cnt) if src_info[l, begin + i] == t]
+                if occ >= len(rows):
+                    continue
+                row = rows[occ]
+                v = (y_bits[l, row].astype(np.uint32) << 16).view(np.float32)
+                if weights is not None:
+                    v = (v * np.float32(weights[n, k])).astype(np.float32)
+                acc = v.copy() if acc is None else (acc + v).astype(np.float32)
+            if acc is not None:
+                out[n] = acc
+                have[n] = True
+    return out, have
