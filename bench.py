@@ -65,6 +65,12 @@ def bytes_ll(msgs, distinct_tokens, H, use_fp8, R, L):
     return distinct_tokens * 2 * H + 2 * msgs * mb + msgs * (pb + 4) + L * R * (4 + 8)
 
 
+def bytes_ll_combine(msgs, N, H, K, weighted):
+    """Low-latency combine: every packed row read once (and its src_info), every
+    token's top-k row (and weights) read and its combined row written."""
+    return msgs * (2 * H + 4) + N * (2 * H + K * (8 + (4 if weighted else 0)))
+
+
 # --------------------------------------------------------------------------- helpers
 def src_hash(*names):
     h = hashlib.sha256()
@@ -217,6 +223,26 @@ def run_ll(torch, miep, wl, iters):
         out[name] = dict(us=round(ms * 1e3, 2), messages=msgs, tokens=distinct,
                          tokens_per_s=round(distinct / (ms / 1e3), 1),
                          gbs=round(bytes_ll(msgs, distinct, H, fp8, R, L) / (ms / 1e3) / 1e9, 1))
+
+    # low-latency combine of bf16 expert outputs in the packed layout, gate-weighted
+    y = wl.expert_outputs(L * R * M, H, seed=1).view(L, R * M, H).to(dev)
+    wts = wl.gate_weights(w.N, w.K, torch.Generator().manual_seed(2)).to(dev)
+    cx = torch.empty((w.N, H), dtype=torch.bfloat16, device=dev)
+
+    def ccall():
+        miep.low_latency_combine_into(y, idx, wts, bufs["packed_recv_src_info"], bufs["packed_recv_layout_range"], R, M,
+                                      w.E, w.dest_rank, cx)
+
+    for _ in range(5):
+        ccall()
+    t = Timer(torch, iters)
+    for _ in range(iters):
+        with t:
+            ccall()
+    torch.cuda.synchronize()
+    ms = med(t.ms())
+    out["combine"] = dict(us=round(ms * 1e3, 2), messages=msgs, tokens=w.N,
+                          gbs=round(bytes_ll_combine(msgs, w.N, H, w.K, True) / (ms / 1e3) / 1e9, 1))
     return out
 
 
@@ -295,7 +321,8 @@ KERNEL_SRC = {"combine": ("combine.hip", "device.h"), "pack": ("pack.hip", "devi
 
 
 def _kernel_key(name):
-    for k in ("combine_kernel", "pack_kernel", "notify_kernel", "layout_kernel", "ll_send_kernel", "ll_recv_kernel"):
+    for k in ("ll_combine_kernel", "combine_kernel", "pack_kernel", "notify_kernel", "layout_kernel", "ll_send_kernel",
+              "ll_recv_kernel"):
         if "miep::" + k in name:
             return k.replace("_kernel", "")
     return None

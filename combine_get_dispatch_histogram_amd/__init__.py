@@ -11,8 +11,10 @@ sections 4.1-4.3, for ranks that are partitions of one GPU):
   get_dispatch_layout(topk_idx, num_experts, num_ranks)            section 4.1
   dispatch(x, topk_idx, topk_weights, <layout>, ...) -> (..., handle)  4.1
   cached_dispatch(x, handle)                                        4.1 (cached)
-  combine(y, handle, topk_weights)                                  4.2, 4.4
+  combine(y, handle, topk_weights, bias)                            4.2, 4.4
   low_latency_dispatch(x, topk_idx, max_tokens, num_experts, dest_rank, ...)  4.3
+  low_latency_combine(y, topk_idx, topk_weights, <dispatch outputs>, ...)     4.3
+  update_mask_buffer / clean_mask_buffer / query_mask_buffer        rank masking
 The ``*_into`` variants take preallocated outputs and allocate nothing.
 """
 from __future__ import annotations
@@ -28,7 +30,8 @@ from ._lib import MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # noqa: F401
 
 __all__ = ["Handle", "MiepError", "get_dispatch_layout", "get_dispatch_layout_into", "dispatch", "dispatch_into", "cached_dispatch",
            "cached_dispatch_into", "combine", "combine_into", "low_latency_dispatch", "low_latency_dispatch_into",
-           "ll_msg_bytes", "version"]
+           "low_latency_combine", "low_latency_combine_into", "update_mask_buffer", "clean_mask_buffer",
+           "query_mask_buffer", "ll_msg_bytes", "version"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -279,7 +282,19 @@ def cached_dispatch(x: torch.Tensor, handle: Handle, x_scales: Optional[torch.Te
 
 
 # --------------------------------------------------------------------------- combine
-def combine_into(y, handle: Handle, combined_x, recv_topk_weights=None, combined_topk_weights=None) -> None:
+def _unpack_bias(bias):
+    """``bias`` is None, one [N, H] bf16 tensor, or a pair (bias_0, bias_1) with None allowed in either place."""
+    if bias is None:
+        return None, None
+    if isinstance(bias, torch.Tensor):
+        return bias, None
+    if isinstance(bias, (tuple, list)) and len(bias) == 2:
+        return bias[0], bias[1]
+    raise TypeError("bias must be a tensor or a pair of tensors")
+
+
+def combine_into(y, handle: Handle, combined_x, recv_topk_weights=None, combined_topk_weights=None,
+                 bias=None) -> None:
     N, H, K = handle.send_head.shape[0], y.shape[1], handle.num_topk
     _want(y, "y", torch.bfloat16)
     if y.dim() != 2 or y.shape[0] < handle.recv_capacity:
@@ -290,18 +305,22 @@ def combine_into(y, handle: Handle, combined_x, recv_topk_weights=None, combined
                                           recv_topk_weights.shape[0] < handle.recv_capacity):
         raise ValueError("recv_topk_weights must be [>= %d, %d]" % (handle.recv_capacity, K))
     _want(combined_topk_weights, "combined_topk_weights", torch.float32, (N, K))
+    b0, b1 = _unpack_bias(bias)
+    _want(b0, "bias_0", torch.bfloat16, (N, H))
+    _want(b1, "bias_1", torch.bfloat16, (N, H))
     p = handle.problem(y.shape[1])
     h = handle.c()
-    _lib.check(_lib.load().miep_combine(ctypes.byref(p), _ptr(y), _ptr(recv_topk_weights), ctypes.byref(h),
-                                        _ptr(combined_x), _ptr(combined_topk_weights), _stream(y)))
+    _lib.check(_lib.load().miep_combine(ctypes.byref(p), _ptr(y), _ptr(recv_topk_weights), _ptr(b0), _ptr(b1),
+                                        ctypes.byref(h), _ptr(combined_x), _ptr(combined_topk_weights), _stream(y)))
 
 
-def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None):
+def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None, bias=None):
     """Sum expert outputs back into source-token order (sections 4.2, 4.4).
 
     y [cap, H] bf16 in the receive layout; ``topk_weights`` are the received
-    top-k weights [cap, K], reduced the same way.  Returns (combined_x [N, H]
-    bf16, combined_topk_weights [N, K] fp32 or None).
+    top-k weights [cap, K], reduced the same way; ``bias`` (one [N, H] bf16
+    tensor or a pair) is added to each token's sum after the received rows.
+    Returns (combined_x [N, H] bf16, combined_topk_weights [N, K] fp32 or None).
     """
     _want(y, "y", torch.bfloat16)
     if y.shape[0] != handle.recv_capacity:
@@ -314,7 +333,7 @@ def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor
         cw = torch.empty((N, topk_weights.shape[1]), dtype=torch.float32, device=y.device)
         if topk_weights.shape[1] != handle.num_topk:
             raise ValueError("topk_weights must have num_topk columns")
-    combine_into(y, handle, combined_x, topk_weights, cw)
+    combine_into(y, handle, combined_x, topk_weights, cw, bias)
     return combined_x, cw
 
 
@@ -323,7 +342,7 @@ def low_latency_dispatch_into(x, topk_idx, num_ranks: int, max_tokens: int, num_
                               use_fp8: bool, round_scale: bool, use_ue8m0: bool, msg_buf, msg_count, packed_recv_x,
                               packed_recv_x_scales, packed_recv_x_scales_ue8m0, packed_recv_src_info,
                               packed_recv_layout_range, packed_recv_count,
-                              cumulative_local_expert_recv_stats=None) -> None:
+                              cumulative_local_expert_recv_stats=None, mask_buffer=None) -> None:
     N, H = x.shape
     R, M, L, K = num_ranks, max_tokens, num_experts // num_ranks, topk_idx.shape[1]
     if N % R:
@@ -343,18 +362,20 @@ def low_latency_dispatch_into(x, topk_idx, num_ranks: int, max_tokens: int, num_
     _want(packed_recv_layout_range, "packed_recv_layout_range", torch.int64, (L, R))
     _want(packed_recv_count, "packed_recv_count", torch.int32, (L,))
     _want(cumulative_local_expert_recv_stats, "cumulative_local_expert_recv_stats", torch.int32, (L,))
+    _want(mask_buffer, "mask_buffer", torch.int32, (R,))
     q = _lib.LLProblem(num_ranks, N // num_ranks, max_tokens, H, K, num_experts, dest_rank)
     _lib.check(_lib.load().miep_ll_dispatch(
         ctypes.byref(q), _ptr(x), _ptr(topk_idx), int(use_fp8), int(round_scale), int(use_ue8m0), _ptr(msg_buf),
         _ptr(msg_count), _ptr(packed_recv_x), _ptr(packed_recv_x_scales), _ptr(packed_recv_x_scales_ue8m0),
         _ptr(packed_recv_src_info), _ptr(packed_recv_layout_range), _ptr(packed_recv_count),
-        _ptr(cumulative_local_expert_recv_stats), _stream(x)))
+        _ptr(cumulative_local_expert_recv_stats), _ptr(mask_buffer), _stream(x)))
 
 
 def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispatch_tokens_per_rank: int,
                          num_experts: int, dest_rank: int, num_ranks: int, use_fp8: bool = True,
                          round_scale: bool = False, use_ue8m0: bool = False,
-                         cumulative_local_expert_recv_stats: Optional[torch.Tensor] = None) -> dict:
+                         cumulative_local_expert_recv_stats: Optional[torch.Tensor] = None,
+                         mask_buffer: Optional[torch.Tensor] = None) -> dict:
     """Low-latency dispatch received by rank ``dest_rank`` (section 4.3).
 
     x [R*T, H] bf16 and topk_idx [R*T, K] int64 hold every source rank's
@@ -362,6 +383,8 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
     packed_recv_x_scales [L, R*M, H/128], packed_recv_x_scales_ue8m0 (or None),
     packed_recv_src_info [L, R*M], packed_recv_layout_range [L, R] int64,
     packed_recv_count [L], and the expert-major message buffer and counts.
+    ``mask_buffer`` [R] int32 (nonzero = masked rank) stops every message from
+    or to a masked rank.
     """
     _want(x, "x", torch.bfloat16)
     _want(topk_idx, "topk_idx", torch.int64)
@@ -383,7 +406,80 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
     lr = torch.empty((L, R), dtype=torch.int64, device=dev)
     cnt = torch.empty((L,), dtype=torch.int32, device=dev)
     low_latency_dispatch_into(x, topk_idx, R, M, num_experts, dest_rank, use_fp8, round_scale, use_ue8m0, msg_buf,
-                              msg_count, prx, prs, pue, src, lr, cnt, cumulative_local_expert_recv_stats)
+                              msg_count, prx, prs, pue, src, lr, cnt, cumulative_local_expert_recv_stats, mask_buffer)
     return dict(packed_recv_x=prx, packed_recv_x_scales=prs, packed_recv_x_scales_ue8m0=pue,
                 packed_recv_src_info=src, packed_recv_layout_range=lr, packed_recv_count=cnt, msg_buf=msg_buf,
                 msg_count=msg_count, cumulative_local_expert_recv_stats=cumulative_local_expert_recv_stats)
+
+
+def low_latency_combine_into(y, topk_idx, topk_weights, packed_recv_src_info, packed_recv_layout_range,
+                             num_ranks: int, max_tokens: int, num_experts: int, dest_rank: int, combined_x) -> None:
+    R, M = num_ranks, max_tokens
+    L = num_experts // R if R > 0 else 0
+    _want(topk_idx, "topk_idx", torch.int64)
+    if topk_idx.dim() != 2 or R <= 0 or topk_idx.shape[0] % R:
+        raise ValueError("topk_idx must be [R*T, K]")
+    N, K = topk_idx.shape
+    _want(y, "y", torch.bfloat16)
+    if y.dim() != 3 or tuple(y.shape[:2]) != (L, R * M):
+        raise ValueError("y must be [%d, %d, H]" % (L, R * M))
+    H = y.shape[2]
+    _want(topk_weights, "topk_weights", torch.float32, (N, K))
+    _want(packed_recv_src_info, "packed_recv_src_info", torch.int32, (L, R * M))
+    _want(packed_recv_layout_range, "packed_recv_layout_range", torch.int64, (L, R))
+    _want(combined_x, "combined_x", torch.bfloat16, (N, H))
+    q = _lib.LLProblem(R, N // R, M, H, K, num_experts, dest_rank)
+    _lib.check(_lib.load().miep_ll_combine(ctypes.byref(q), _ptr(y), _ptr(packed_recv_src_info),
+                                           _ptr(packed_recv_layout_range), _ptr(topk_idx), _ptr(topk_weights),
+                                           _ptr(combined_x), _stream(y)))
+
+
+def low_latency_combine(y: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                        packed_recv_src_info: torch.Tensor, packed_recv_layout_range: torch.Tensor,
+                        num_max_dispatch_tokens_per_rank: int, num_experts: int, dest_rank: int,
+                        num_ranks: int) -> torch.Tensor:
+    """Low-latency combine: rank ``dest_rank``'s expert outputs back to token order (section 4.3).
+
+    y [L, R*M, H] bf16 in the packed layout of ``low_latency_dispatch``;
+    topk_idx [R*T, K] is the routing that dispatch was given and
+    packed_recv_src_info / packed_recv_layout_range are its outputs.  Each
+    token sums, in ascending k, the rows its entries on d's experts were sent
+    to, times the entry's weight when ``topk_weights`` is given.  Returns
+    combined_x [R*T, H] bf16 (zero for tokens without a row on rank d).
+    """
+    _want(y, "y", torch.bfloat16)
+    combined_x = torch.empty((topk_idx.shape[0], y.shape[-1]), dtype=torch.bfloat16, device=y.device)
+    low_latency_combine_into(y, topk_idx, topk_weights, packed_recv_src_info, packed_recv_layout_range, num_ranks,
+                             num_max_dispatch_tokens_per_rank, num_experts, dest_rank, combined_x)
+    return combined_x
+
+
+# --------------------------------------------------------------------------- rank mask
+def _mask_check(mask_buffer):
+    _want(mask_buffer, "mask_buffer", torch.int32)
+    if mask_buffer.dim() != 1:
+        raise ValueError("mask_buffer must be [num_ranks] int32")
+
+
+def update_mask_buffer(mask_buffer: torch.Tensor, rank: int, mask: bool) -> None:
+    """Set (mask=True) or clear rank ``rank``'s entry of the [R] int32 mask."""
+    _mask_check(mask_buffer)
+    _lib.check(_lib.load().miep_mask_update(_ptr(mask_buffer), mask_buffer.shape[0], int(rank), int(bool(mask)),
+                                            _stream(mask_buffer)))
+
+
+def clean_mask_buffer(mask_buffer: torch.Tensor) -> None:
+    """Clear every entry of the [R] int32 mask."""
+    _mask_check(mask_buffer)
+    _lib.check(_lib.load().miep_mask_clean(_ptr(mask_buffer), mask_buffer.shape[0], _stream(mask_buffer)))
+
+
+def query_mask_buffer(mask_buffer: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Copy the [R] int32 mask into ``out`` (allocated when None) and return it."""
+    _mask_check(mask_buffer)
+    if out is None:
+        out = torch.empty_like(mask_buffer)
+    _want(out, "out", torch.int32, tuple(mask_buffer.shape))
+    _lib.check(_lib.load().miep_mask_query(_ptr(mask_buffer), mask_buffer.shape[0], _ptr(out),
+                                           _stream(mask_buffer)))
+    return out

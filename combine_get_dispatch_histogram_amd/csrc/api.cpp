@@ -110,6 +110,23 @@ miep::PackArgs pack_args(const miep_problem* p, const void* x, int32_t x_kind, c
   return a;
 }
 
+// Sizes of a low-latency problem (shared by dispatch and combine).
+miep_status check_ll_problem(const miep_ll_problem* q) {
+  if (!q) return fail(MIEP_EINVAL, "problem is NULL");
+  const int R = q->num_ranks, T = q->num_tokens, M = q->max_tokens, H = q->hidden, K = q->num_topk,
+            E = q->num_experts, d = q->dest_rank;
+  if (R <= 0 || T < 0 || M <= 0 || H <= 0 || K <= 0 || E <= 0) return fail(MIEP_EINVAL, "sizes must be positive");
+  if (T > M) return fail(MIEP_EINVAL, "num_tokens > max_tokens");
+  if (E % R != 0) return fail(MIEP_EINVAL, "num_experts must be a multiple of num_ranks");
+  if (d < 0 || d >= R) return fail(MIEP_EINVAL, "dest_rank out of range");
+  if (R > 1024) return fail(MIEP_EUNSUPPORTED, "num_ranks > 1024");
+  if (M > 4096) return fail(MIEP_EUNSUPPORTED, "max_tokens > 4096");
+  if (K > 64) return fail(MIEP_EUNSUPPORTED, "num_topk > 64");
+  if (H % 8 != 0) return fail(MIEP_EUNSUPPORTED, "hidden must be a multiple of 8");
+  if (static_cast<int64_t>(E) * M > (1ll << 31) - 1) return fail(MIEP_EUNSUPPORTED, "num_experts * max_tokens >= 2^31");
+  return MIEP_OK;
+}
+
 }  // namespace
 
 namespace miep {
@@ -119,7 +136,8 @@ const Tuning& tuning() {
                            env_int("MIEP_COMBINE_MAXR", 0),
                            env_int("MIEP_PACK_NT", 2) & 3, env_int("MIEP_COMBINE_NT", 1) & 3,
                            env_int("MIEP_LL_SPLIT", 0),     env_int("MIEP_LL_VPL", 0),
-                           env_int("MIEP_CAST_TPB", -1)};
+                           env_int("MIEP_CAST_TPB", -1),    env_int("MIEP_LLC_VPL", 0),
+                           env_int("MIEP_LLC_SLICES", 0)};
   return t;
 }
 }  // namespace miep
@@ -247,7 +265,8 @@ miep_status miep_cached_dispatch(const miep_problem* p, const void* x, int32_t x
 }
 
 miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
-                         const miep_handle* h, uint16_t* combined_x, float* combined_topk_weights, void* stream) {
+                         const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
+                         uint16_t* combined_x, float* combined_topk_weights, void* stream) {
   miep_status st = check_problem(p);
   if (st != MIEP_OK) return st;
   if ((st = check_handle(p, h, false)) != MIEP_OK) return st;
@@ -256,6 +275,7 @@ miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* 
   if (h->recv_capacity > 0 && !y) return fail(MIEP_EINVAL, "y is NULL");
   if (N > 0 && !combined_x) return fail(MIEP_EINVAL, "combined_x is NULL");
   if (!aligned16(y) || !aligned16(combined_x)) return fail(MIEP_EUNSUPPORTED, "y and combined_x must be 16-byte aligned");
+  if (!aligned16(bias_0) || !aligned16(bias_1)) return fail(MIEP_EUNSUPPORTED, "bias rows must be 16-byte aligned");
   if (recv_topk_weights && N > 0 && !combined_topk_weights)
     return fail(MIEP_EINVAL, "combined_topk_weights is NULL while recv_topk_weights is given");
   miep::CombineArgs a{};
@@ -266,6 +286,8 @@ miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* 
   a.capacity = h->recv_capacity;
   a.y = y;
   a.w = recv_topk_weights;
+  a.bias0 = N > 0 ? bias_0 : nullptr;
+  a.bias1 = N > 0 ? bias_1 : nullptr;
   a.send_head = h->send_head;
   a.off = h->recv_rank_offset;
   a.out = combined_x;
@@ -277,22 +299,17 @@ miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const 
                              int32_t round_scale, int32_t use_ue8m0, void* msg_buf, int32_t* msg_count,
                              void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
                              int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
-                             int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats, void* stream) {
-  if (!q) return fail(MIEP_EINVAL, "problem is NULL");
+                             int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats,
+                             const int32_t* mask_buffer, void* stream) {
+  miep_status st = check_ll_problem(q);
+  if (st != MIEP_OK) return st;
   const int R = q->num_ranks, T = q->num_tokens, M = q->max_tokens, H = q->hidden, K = q->num_topk,
             E = q->num_experts, d = q->dest_rank;
-  if (R <= 0 || T < 0 || M <= 0 || H <= 0 || K <= 0 || E <= 0) return fail(MIEP_EINVAL, "sizes must be positive");
-  if (T > M) return fail(MIEP_EINVAL, "num_tokens > max_tokens");
-  if (E % R != 0) return fail(MIEP_EINVAL, "num_experts must be a multiple of num_ranks");
-  if (d < 0 || d >= R) return fail(MIEP_EINVAL, "dest_rank out of range");
   if (use_ue8m0 && !round_scale) return fail(MIEP_EINVAL, "use_ue8m0 requires round_scale");
   if (use_ue8m0 && !use_fp8) return fail(MIEP_EINVAL, "use_ue8m0 requires use_fp8");
-  if (R > 1024) return fail(MIEP_EUNSUPPORTED, "num_ranks > 1024");
-  if (M > 4096) return fail(MIEP_EUNSUPPORTED, "max_tokens > 4096");
-  if (H % 8 != 0) return fail(MIEP_EUNSUPPORTED, "hidden must be a multiple of 8");
   if (use_fp8 && H % 512 != 0)
     return fail(MIEP_EUNSUPPORTED, "FP8 low-latency messages need hidden % 512 == 0 (16-byte message stride)");
-  if (!x || !topk_idx || !msg_buf || !msg_count || !packed_recv_x || !packed_recv_src_info ||
+  if ((T > 0 && (!x || !topk_idx)) || !msg_buf || !msg_count || !packed_recv_x || !packed_recv_src_info ||
       !packed_recv_layout_range || !packed_recv_count)
     return fail(MIEP_EINVAL, "a required pointer is NULL");
   if (use_fp8 && !packed_recv_x_scales) return fail(MIEP_EINVAL, "packed_recv_x_scales is NULL with use_fp8");
@@ -322,7 +339,50 @@ miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const 
   a.layout_range = packed_recv_layout_range;
   a.count = packed_recv_count;
   a.cumulative = cumulative_local_expert_recv_stats;
+  a.mask = mask_buffer;
   return hip_status(miep::launch_ll(a, static_cast<hipStream_t>(stream)), "low-latency launch");
+}
+
+miep_status miep_ll_combine(const miep_ll_problem* q, const uint16_t* y, const int32_t* packed_recv_src_info,
+                            const int64_t* packed_recv_layout_range, const int64_t* topk_idx,
+                            const float* topk_weights, uint16_t* combined_x, void* stream) {
+  miep_status st = check_ll_problem(q);
+  if (st != MIEP_OK) return st;
+  if (!y || !packed_recv_src_info || !packed_recv_layout_range || (q->num_tokens > 0 && (!topk_idx || !combined_x)))
+    return fail(MIEP_EINVAL, "a required pointer is NULL");
+  if (!aligned16(y) || !aligned16(combined_x)) return fail(MIEP_EUNSUPPORTED, "y and combined_x must be 16-byte aligned");
+  miep::LLCombineArgs a{};
+  a.R = q->num_ranks;
+  a.T = q->num_tokens;
+  a.M = q->max_tokens;
+  a.H = q->hidden;
+  a.K = q->num_topk;
+  a.E = q->num_experts;
+  a.L = q->num_experts / q->num_ranks;
+  a.d = q->dest_rank;
+  a.y = y;
+  a.src_info = packed_recv_src_info;
+  a.layout_range = packed_recv_layout_range;
+  a.topk_idx = topk_idx;
+  a.w = topk_weights;
+  a.out = combined_x;
+  return hip_status(miep::launch_ll_combine(a, static_cast<hipStream_t>(stream)), "low-latency combine launch");
+}
+
+miep_status miep_mask_update(int32_t* mask_buffer, int32_t num_ranks, int32_t rank, int32_t value, void* stream) {
+  if (!mask_buffer || num_ranks <= 0) return fail(MIEP_EINVAL, "mask_buffer is NULL or num_ranks <= 0");
+  if (rank < 0 || rank >= num_ranks) return fail(MIEP_EINVAL, "rank out of range");
+  return hip_status(miep::launch_mask_set(mask_buffer, rank, value, static_cast<hipStream_t>(stream)), "mask launch");
+}
+
+miep_status miep_mask_clean(int32_t* mask_buffer, int32_t num_ranks, void* stream) {
+  if (!mask_buffer || num_ranks <= 0) return fail(MIEP_EINVAL, "mask_buffer is NULL or num_ranks <= 0");
+  return hip_status(miep::launch_fill_zero(mask_buffer, num_ranks, static_cast<hipStream_t>(stream)), "mask launch");
+}
+
+miep_status miep_mask_query(const int32_t* mask_buffer, int32_t num_ranks, int32_t* out, void* stream) {
+  if (!mask_buffer || !out || num_ranks <= 0) return fail(MIEP_EINVAL, "a pointer is NULL or num_ranks <= 0");
+  return hip_status(miep::launch_copy_i32(mask_buffer, out, num_ranks, static_cast<hipStream_t>(stream)), "mask launch");
 }
 
 }  // extern "C"

@@ -115,6 +115,29 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
         }
       }
     }
+    // bias rows: added after the received contributions, bias_0 then bias_1
+    const bool biased = a.bias0 != nullptr || a.bias1 != nullptr;
+    if (biased) {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + j * kWave + lane;
+        if (v >= nv) continue;
+        if (!have) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[j][k] = 0.0f;
+        }
+        for (int b = 0; b < 2; ++b) {
+          const uint16_t* bias = b == 0 ? a.bias0 : a.bias1;
+          if (bias == nullptr) continue;
+          const v4u t = ld16<false>(reinterpret_cast<const uint8_t*>(bias) + n * row_bytes + static_cast<int64_t>(v) * 16);
+          const float f[8] = {bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y),
+                              bf16_lo(t.z), bf16_hi(t.z), bf16_lo(t.w), bf16_hi(t.w)};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[j][k] += f[k];
+        }
+      }
+      have = true;
+    }
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int v = v0 + j * kWave + lane;

@@ -71,6 +71,8 @@ struct CombineArgs {
   int64_t capacity;
   const uint16_t* y;
   const float* w;            // [cap][K] or null
+  const uint16_t* bias0;     // [N][H] or null
+  const uint16_t* bias1;     // [N][H] or null
   const int32_t* send_head;
   const int32_t* off;
   uint16_t* out;             // [N][H]
@@ -94,22 +96,43 @@ struct LLArgs {
   int64_t* layout_range;     // [L][R]
   int32_t* count;            // [L]
   int32_t* cumulative;       // [L] or null
+  const int32_t* mask;       // [R] nonzero = masked rank, or null
 };
 hipError_t launch_ll(const LLArgs& a, hipStream_t st);
+
+// ---- low-latency combine: rank d's expert outputs back to source-token order
+struct LLCombineArgs {
+  int R, T, M, H, K, E, L, d;
+  const uint16_t* y;             // [L][R*M][H]
+  const int32_t* src_info;       // [L][R*M]
+  const int64_t* layout_range;   // [L][R]
+  const int64_t* topk_idx;       // [R*T][K]
+  const float* w;                // [R*T][K] or null
+  uint16_t* out;                 // [R*T][H]
+};
+hipError_t launch_ll_combine(const LLCombineArgs& a, hipStream_t st);
+
+// ---- rank mask helpers: set one entry (launch_mask_set), clear all
+// (launch_fill_zero), copy out (launch_copy_i32); tiny kernels
+hipError_t launch_mask_set(int32_t* mask, int rank, int value, hipStream_t st);
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t st);
 
 // Optional launch-geometry overrides read once from the environment
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
 // MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT, MIEP_LL_SPLIT,
-// MIEP_LL_VPL, MIEP_CAST_TPB): used by geometry sweeps, never required.
+// MIEP_LL_VPL, MIEP_CAST_TPB, MIEP_LLC_VPL, MIEP_LLC_SLICES): used by
+// geometry sweeps, never required.
 // combine_maxr: source rows whose loads are issued together.
 // pack_nt: bit 0 = non-temporal payload loads, bit 1 = non-temporal stores;
 // combine_nt: bit 0 = non-temporal loads of the expert outputs, bit 1 =
 // non-temporal stores of the combined rows.  ll_split: workgroups per
 // low-latency (expert, source) block.  cast_tpb: fused FP8 cast with one
 // token per workgroup (1), 1 KiB slices (0), or chosen per call (-1).
+// llc_vpl / llc_slices: low-latency combine vectors per lane and slices per
+// token.
 struct Tuning {
   int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl,
-      cast_tpb;
+      cast_tpb, llc_vpl, llc_slices;
 };
 const Tuning& tuning();
 

@@ -40,12 +40,14 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int64_t target = static_cast<int64_t>(a.d) * a.L + l;
   const int64_t* idx = a.topk_idx + static_cast<int64_t>(s) * a.T * a.K;
+  // a masked destination is not sent to, a masked source is not received from
+  const bool masked = a.mask != nullptr && (a.mask[a.d] != 0 || a.mask[s] != 0);
   if (tid == 0) carry_s = 0;
   __syncthreads();
   for (int t0 = 0; t0 < a.T; t0 += kLLThreads) {
     const int t = t0 + tid;
     uint64_t kmask = 0;                           // entries k of token t that name the expert
-    if (t < a.T) {
+    if (t < a.T && !masked) {
       const int64_t* row = idx + static_cast<int64_t>(t) * a.K;
       for (int k0 = 0; k0 < a.K; k0 += 8) {       // 8 independent loads in flight
         int64_t e8[8];
@@ -202,6 +204,192 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
     case 4: return launch_ll_vpl<4>(a, blocks, split, st);
     default: return launch_ll_vpl<8>(a, blocks, split, st);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Low-latency combine, the reverse of the dispatch above seen from rank d:
+// every source token (s, t) gets back the rows of d's experts that its top-k
+// entries were sent to, summed in fp32 in ascending k (each row times the
+// entry's gate weight when weights are given) and rounded once to bf16.
+//
+// One wavefront per (token, row slice).  Lane k holds top-k entry k; for
+// each entry on a local expert l the wavefront finds the entry's slot in the
+// (l, s) block from the dispatch's slot rule: rows of the block hold source
+// tokens in (token, k) order, so the slot is the number of rows naming an
+// earlier token (one ballot count over the block's src_info, 64 rows per
+// load) plus the entry's rank among the token's earlier entries for the same
+// expert.  A slot at or past the block's count was dropped at the cap (or
+// the rank was masked) and is skipped; so is a row whose src_info does not
+// name the token (a handle from another routing).  Then the rows are
+// gathered like the normal combine: up to MAXR rows' loads in flight, adds
+// in k order.  A token with no row writes +0.0.
+template <int VPL, int MAXR>
+__global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int nslices) {
+  const int lane = lane_id();
+  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t n = gw / nslices;
+  const int slice = static_cast<int>(gw - n * nslices);
+  if (n >= static_cast<int64_t>(a.R) * a.T) return;
+  const int s = static_cast<int>(n / a.T);
+  const int t = static_cast<int>(n - static_cast<int64_t>(s) * a.T);
+  const int64_t lo = static_cast<int64_t>(a.d) * a.L;
+  const int64_t block_rows = static_cast<int64_t>(a.R) * a.M;
+
+  int le = -1;        // lane k: local expert of entry k, or -1
+  float wk = 1.0f;    // lane k: gate weight of entry k
+  if (lane < a.K) {
+    const int64_t e = a.topk_idx[n * a.K + lane];
+    if (e >= lo && e < lo + a.L) le = static_cast<int>(e - lo);
+    if (a.w) wk = a.w[n * a.K + lane];
+  }
+  int occ = 0;        // earlier entries of this token naming the same local expert
+  for (int k2 = 0; k2 < a.K; ++k2) {
+    const int e2 = readlane(le, k2);
+    occ += (k2 < lane && le >= 0 && e2 == le) ? 1 : 0;
+  }
+
+  int row = -1;       // lane k: packed row of entry k, or -1
+  for (uint64_t m = ballot(le >= 0); m != 0; m &= m - 1) {
+    const int k = __builtin_ctzll(m);
+    const int l = readlane(le, k);
+    const int o = readlane(occ, k);
+    const int64_t lr = a.layout_range[static_cast<int64_t>(l) * a.R + s];
+    const int64_t begin = lr >> 32;
+    int64_t cnt = lr & 0xFFFFFFFFll;
+    if (begin < 0 || begin + cnt > block_rows) cnt = 0;   // not a range this dispatch writes
+    const int32_t* si = a.src_info + l * block_rows + begin;
+    int before = 0;
+    for (int64_t c0 = 0; c0 < cnt; c0 += kWave) {
+      const int64_t i = c0 + lane;
+      before += __popcll(ballot(i < cnt && si[i] < t));
+    }
+    const int64_t j = before + o;
+    int r = -1;
+    if (j < cnt && si[j] == t) r = static_cast<int>(l * block_rows + begin + j);
+    if (lane == k) row = r;
+  }
+
+  const int nv = a.H / 8;
+  const int64_t row_bytes = 2 * static_cast<int64_t>(a.H);
+  const uint8_t* y = reinterpret_cast<const uint8_t*>(a.y);
+  uint8_t* orow = reinterpret_cast<uint8_t*>(a.out) + n * row_bytes;
+  const uint64_t valid = ballot(row >= 0);
+  const bool weighted = a.w != nullptr;
+  const int span = kWave * VPL;
+  for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
+    float acc[VPL][8];
+    bool have = false;
+    uint64_t m = valid;
+    while (m) {
+      int64_t rows[MAXR];
+      float ws[MAXR];
+      int nb = 0;
+#pragma unroll
+      for (int q = 0; q < MAXR; ++q) {
+        rows[q] = 0;
+        ws[q] = 1.0f;
+        if (m) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          rows[q] = readlane(row, b);
+          ws[q] = __int_as_float(readlane(__float_as_int(wk), b));
+          nb = q + 1;
+        }
+      }
+      v4u dv[MAXR][VPL];
+#pragma unroll
+      for (int q = 0; q < MAXR; ++q) {
+        if (q < nb) {
+          const uint8_t* yrow = y + rows[q] * row_bytes;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int v = v0 + j * kWave + lane;
+            if (v < nv) dv[q][j] = ld16<false>(yrow + static_cast<int64_t>(v) * 16);
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < MAXR; ++q) {
+        if (q < nb) {
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            float f[8] = {bf16_lo(dv[q][j].x), bf16_hi(dv[q][j].x), bf16_lo(dv[q][j].y), bf16_hi(dv[q][j].y),
+                          bf16_lo(dv[q][j].z), bf16_hi(dv[q][j].z), bf16_lo(dv[q][j].w), bf16_hi(dv[q][j].w)};
+            if (weighted) {
+#pragma unroll
+              for (int k = 0; k < 8; ++k) f[k] = f[k] * ws[q];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[j][k] = have ? acc[j][k] + f[k] : f[k];
+          }
+          have = true;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int v = v0 + j * kWave + lane;
+      if (v < nv) {
+        v4u o = v4u{0u, 0u, 0u, 0u};
+        if (have) {
+          o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+          o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+          o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+          o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+        }
+        st16<false>(orow + static_cast<int64_t>(v) * 16, o);
+      }
+    }
+  }
+}
+
+template <int VPL, int MAXR>
+static hipError_t launch_ll_combine_cfg(const LLCombineArgs& a, int nslices, hipStream_t st) {
+  const int64_t waves = static_cast<int64_t>(a.R) * a.T * nslices;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((ll_combine_kernel<VPL, MAXR>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+                     nslices);
+  return hipGetLastError();
+}
+
+hipError_t launch_ll_combine(const LLCombineArgs& a, hipStream_t st) {
+  if (static_cast<int64_t>(a.R) * a.T == 0) return hipSuccess;
+  const Tuning& tu = tuning();
+  const int nv = a.H / 8;
+  const int vpl = tu.llc_vpl > 0 ? tu.llc_vpl : (nv % kWave == 0 ? 1 : 8);
+  const int span = vpl * kWave;
+  int nslices = tu.llc_slices > 0 ? tu.llc_slices : (nv + span - 1) / span;
+  if (nslices < 1) nslices = 1;
+  switch (vpl) {
+    case 1: return launch_ll_combine_cfg<1, 8>(a, nslices, st);
+    case 2: return launch_ll_combine_cfg<2, 8>(a, nslices, st);
+    case 4: return launch_ll_combine_cfg<4, 4>(a, nslices, st);
+    default: return launch_ll_combine_cfg<8, 2>(a, nslices, st);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rank mask helpers: one entry set, all entries cleared, or the mask copied
+// out.  Tiny kernels rather than memset/memcpy nodes so that a captured
+// stream replays them faithfully.
+__global__ void mask_set_kernel(int32_t* mask, int rank, int value) {
+  if (threadIdx.x == 0) mask[rank] = value;
+}
+
+__global__ void copy_i32_kernel(const int32_t* src, int32_t* dst, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = src[i];
+}
+
+hipError_t launch_mask_set(int32_t* mask, int rank, int value, hipStream_t st) {
+  hipLaunchKernelGGL(mask_set_kernel, dim3(1), dim3(kWave), 0, st, mask, rank, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(copy_i32_kernel, dim3(blocks), dim3(256), 0, st, src, dst, n);
+  return hipGetLastError();
 }
 
 }  // namespace miep

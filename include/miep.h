@@ -1,7 +1,8 @@
 /*
  * miep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel core:
  * layout histogram, normal-mode dispatch with its handle, cached dispatch,
- * combine, and low-latency (expert-major, optionally FP8) dispatch.
+ * combine (with optional bias rows), low-latency (expert-major, optionally
+ * FP8) dispatch and combine, and the low-latency rank mask.
  *
  * One GPU plays every rank: the R logical ranks are partitions of one
  * device's HBM, and the S source partitions are the token blocks that the
@@ -136,13 +137,19 @@ miep_status miep_cached_dispatch(const miep_problem* p, const void* x, int32_t x
  * and add them per source token in fp32 (no gate weights applied), and
  * separately add the received top-k weights.  Contributions are added in
  * ascending rank order; a token no rank received combines to zero.
+ * [Ch4] 4.2 also unpacks a bias into two rows for the combine without a
+ * formula; here each given bias row is added to its token's fp32 sum after
+ * the received contributions, bias_0 first (a token no rank received then
+ * combines to its bias).
  *   y                     [cap][H] bf16 expert outputs in the receive layout
  *   recv_topk_weights     [cap][K] fp32, nullable
+ *   bias_0, bias_1        [N][H] bf16 each, nullable, 16-byte aligned
  *   combined_x            [N][H] bf16 out (round to nearest even)
  *   combined_topk_weights [N][K] fp32 out, nullable (required if recv_topk_weights is given)
  * Reads h->send_head, h->recv_rank_offset, h->recv_capacity. */
 miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
-                         const miep_handle* h, uint16_t* combined_x, float* combined_topk_weights, void* stream);
+                         const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
+                         uint16_t* combined_x, float* combined_topk_weights, void* stream);
 
 /* Sizes of one low-latency problem, seen from the receiving rank dest_rank. */
 typedef struct miep_ll_problem {
@@ -177,12 +184,55 @@ int64_t miep_ll_msg_bytes(int32_t hidden, int32_t use_fp8);
  *   packed_recv_src_info [L][R*M] int32: source token index of each row
  *   packed_recv_layout_range [L][R] int64: (first row << 32) | count
  *   packed_recv_count [L] int32: rows per local expert
- *   cumulative_local_expert_recv_stats [L] int32, nullable: += packed_recv_count */
+ *   cumulative_local_expert_recv_stats [L] int32, nullable: += packed_recv_count
+ *   mask_buffer    [R] int32, nullable: rank masking ([NvLL] low-latency
+ *                  send loop and receive wait), nonzero = masked.  If rank d
+ *                  or source s is masked, no message travels from s to d:
+ *                  the (l, s) blocks hold 0 rows.
+ * Errors: EINVAL for bad sizes or flags or a null required pointer;
+ * EUNSUPPORTED for R > 1024, M > 4096, K > 64, H % 8 != 0, FP8 with
+ * H % 512 != 0, or misaligned x / msg_buf / packed_recv_x. */
 miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,
                              int32_t round_scale, int32_t use_ue8m0, void* msg_buf, int32_t* msg_count,
                              void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
                              int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
-                             int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats, void* stream);
+                             int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats,
+                             const int32_t* mask_buffer, void* stream);
+
+/* low_latency_combine -- [Ch4] 4.3 and [NvLL] name it beside the
+ * low-latency dispatch without its arithmetic.  Here it is the reverse of
+ * miep_ll_dispatch seen from rank d: each source token (s, t) gets back the
+ * rows of d's local experts that its top-k entries were sent to (the slot
+ * rule of the dispatch: the j-th entry of source s naming expert d*L + l,
+ * in (token, k) order, is row l*R*M + begin(l, s) + j), each multiplied by
+ * the entry's gate weight when topk_weights is given, summed in fp32 in
+ * ascending k and rounded once to bf16.  Entries dropped at the slot cap or
+ * by rank masking (slot >= count) contribute nothing; a token without a row
+ * combines to +0.0.
+ *   y                       [L][R*M][H] bf16 expert outputs, packed like packed_recv_x (16-byte aligned)
+ *   packed_recv_src_info    [L][R*M] int32 from miep_ll_dispatch
+ *   packed_recv_layout_range [L][R] int64 from miep_ll_dispatch
+ *   topk_idx                [R*T][K] int64, the routing given to miep_ll_dispatch
+ *   topk_weights            [R*T][K] fp32, nullable (then rows are summed unweighted)
+ *   combined_x              [R*T][H] bf16 out (16-byte aligned)
+ * A handle from another routing is not detected: a row whose src_info does
+ * not name the token is skipped, and every access stays inside y.
+ * Errors: as miep_ll_dispatch for sizes; EINVAL for a null required pointer. */
+miep_status miep_ll_combine(const miep_ll_problem* q, const uint16_t* y, const int32_t* packed_recv_src_info,
+                            const int64_t* packed_recv_layout_range, const int64_t* topk_idx,
+                            const float* topk_weights, uint16_t* combined_x, void* stream);
+
+/* Rank mask buffer helpers ([NvLL]: the low-latency buffer's mask can be
+ * queried, updated and cleaned; a rank is masked when it stops answering).
+ * mask_buffer is [num_ranks] int32 device memory owned by the caller.
+ *   update: mask_buffer[rank] = value (nonzero = masked)
+ *   clean:  every entry = 0
+ *   query:  out[r] = mask_buffer[r] for every r (out: [num_ranks] int32 device)
+ * Small kernels (no memset or copy nodes), enqueued on `stream`.
+ * Errors: EINVAL for a null pointer, num_ranks <= 0 or rank out of range. */
+miep_status miep_mask_update(int32_t* mask_buffer, int32_t num_ranks, int32_t rank, int32_t value, void* stream);
+miep_status miep_mask_clean(int32_t* mask_buffer, int32_t num_ranks, void* stream);
+miep_status miep_mask_query(const int32_t* mask_buffer, int32_t num_ranks, int32_t* out, void* stream);
 
 /* Description of the last failure on this thread ("" if none). Host-only. */
 const char* miep_last_error(void);

@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
-              "miep_ll_dispatch"):
+              "miep_ll_dispatch", "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query"):
         assert f in names
     assert set(names) == set(_lib.EXPORTS)
 
@@ -120,9 +120,14 @@ def test_dispatch_validation(lib):
 def test_combine_validation(lib):
     p = _problem()
     h = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, 100)
-    assert lib.miep_combine(ctypes.byref(p), None, None, ctypes.byref(h), 16, None, None) == _lib.MIEP_EINVAL
-    assert lib.miep_combine(ctypes.byref(p), 16, 16, ctypes.byref(h), 16, None, None) == _lib.MIEP_EINVAL
-    assert lib.miep_combine(ctypes.byref(p), 8, None, ctypes.byref(h), 16, None, None) == _lib.MIEP_EUNSUPPORTED
+    def c(y, w, b0, b1, out, cw):
+        return lib.miep_combine(ctypes.byref(p), y, w, b0, b1, ctypes.byref(h), out, cw, None)
+
+    assert c(None, None, None, None, 16, None) == _lib.MIEP_EINVAL        # y NULL
+    assert c(16, 16, None, None, 16, None) == _lib.MIEP_EINVAL            # weights without their output
+    assert c(8, None, None, None, 16, None) == _lib.MIEP_EUNSUPPORTED     # misaligned y
+    assert c(16, None, 8, None, 16, None) == _lib.MIEP_EUNSUPPORTED       # misaligned bias_0
+    assert c(16, None, None, 24, 16, None) == _lib.MIEP_EUNSUPPORTED      # misaligned bias_1
 
 
 def test_ll_validation(lib):
@@ -131,8 +136,10 @@ def test_ll_validation(lib):
         d.update(kw)
         return _lib.LLProblem(**d)
 
-    args = [16, 16, 1, 1, 1, 16, 16, 16, 16, 16, 16, 16, 16, None, None]
+    args = [16, 16, 1, 1, 1, 16, 16, 16, 16, 16, 16, 16, 16, None, None, None]
     assert lib.miep_ll_dispatch(ctypes.byref(q(num_tokens=129)), *args) == _lib.MIEP_EINVAL
+    assert lib.miep_ll_dispatch(ctypes.byref(q(num_topk=65)), *args) == _lib.MIEP_EUNSUPPORTED
+    assert lib.miep_ll_dispatch(ctypes.byref(q(num_experts=250)), *args) == _lib.MIEP_EINVAL
     assert lib.miep_ll_dispatch(ctypes.byref(q(dest_rank=32)), *args) == _lib.MIEP_EINVAL
     assert lib.miep_ll_dispatch(ctypes.byref(q(hidden=7040)), *args) == _lib.MIEP_EUNSUPPORTED
     bad = list(args)
@@ -141,6 +148,28 @@ def test_ll_validation(lib):
     nul = list(args)
     nul[5] = None                              # msg_buf NULL
     assert lib.miep_ll_dispatch(ctypes.byref(q()), *nul) == _lib.MIEP_EINVAL
+
+    cargs = [16, 16, 16, 16, None, 16, None]   # y, src_info, layout_range, topk_idx, weights, out, stream
+    assert lib.miep_ll_combine(None, *cargs) == _lib.MIEP_EINVAL
+    assert lib.miep_ll_combine(ctypes.byref(q(dest_rank=-1)), *cargs) == _lib.MIEP_EINVAL
+    assert lib.miep_ll_combine(ctypes.byref(q(max_tokens=8192, num_tokens=8)), *cargs) == _lib.MIEP_EUNSUPPORTED
+    bad = list(cargs)
+    bad[1] = None                              # src_info NULL
+    assert lib.miep_ll_combine(ctypes.byref(q()), *bad) == _lib.MIEP_EINVAL
+    bad = list(cargs)
+    bad[0] = 8                                 # misaligned y
+    assert lib.miep_ll_combine(ctypes.byref(q()), *bad) == _lib.MIEP_EUNSUPPORTED
+
+
+def test_mask_validation(lib):
+    assert lib.miep_mask_update(None, 8, 0, 1, None) == _lib.MIEP_EINVAL
+    assert lib.miep_mask_update(16, 8, 8, 1, None) == _lib.MIEP_EINVAL
+    assert lib.miep_mask_update(16, 8, -1, 1, None) == _lib.MIEP_EINVAL
+    assert lib.miep_mask_update(16, 0, 0, 1, None) == _lib.MIEP_EINVAL
+    assert lib.miep_mask_clean(None, 8, None) == _lib.MIEP_EINVAL
+    assert lib.miep_mask_clean(16, 0, None) == _lib.MIEP_EINVAL
+    assert lib.miep_mask_query(16, 8, None, None) == _lib.MIEP_EINVAL
+    assert lib.miep_mask_query(None, 8, 16, None) == _lib.MIEP_EINVAL
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
