@@ -95,15 +95,26 @@ def load_traffic(kernel_key, kernel_src, launches_bytes_key=None):
     return k.get("traffic_bytes_per_launch")
 
 
-class Timer:
-    """HIP events recorded on the current stream around each call."""
+LEAD_CYCLES = 200000   # GPU spin ahead of a short timed call (about 0.1 ms)
 
-    def __init__(self, torch, n):
+
+class Timer:
+    """HIP events recorded on the current stream around each call.
+
+    ``lead_cycles`` > 0 first enqueues a short GPU spin (torch.cuda._sleep) so
+    that the host has queued the call before the start event runs: for calls
+    shorter than their host-side launch cost the interval is then device time
+    rather than host overhead."""
+
+    def __init__(self, torch, n, lead_cycles=0):
         self.torch = torch
         self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         self.i = 0
+        self.lead = lead_cycles
 
     def __enter__(self):
+        if self.lead:
+            self.torch.cuda._sleep(self.lead)
         self.ev[self.i][0].record()
         return self
 
@@ -113,6 +124,22 @@ class Timer:
 
     def ms(self):
         return [a.elapsed_time(b) for a, b in self.ev[:self.i]]
+
+
+def time_batched(torch, fn, iters, batch=16, warm=5):
+    """Device time per call of a short call: ``batch`` calls back to back
+    between two events, behind a GPU spin long enough for the host to queue
+    them all, so neither host launch cost nor event overhead enters the
+    per-call figure; median over ``iters`` batches, in ms."""
+    for _ in range(warm):
+        fn()
+    t = Timer(torch, iters, LEAD_CYCLES * batch)
+    for _ in range(iters):
+        with t:
+            for _ in range(batch):
+                fn()
+    torch.cuda.synchronize()
+    return med(t.ms()) / batch
 
 
 def med(xs):
@@ -182,8 +209,13 @@ def run_normal(torch, miep, wl, steps, warmup):
         with tcd:
             miep.cached_dispatch_into(x, h, recv_x)
     torch.cuda.synchronize()
+    # (4) per-launch device time of the two big kernels for the roofline: 16
+    # launches back to back between two events on the launch stream
+    it = max(3, min(steps, 10))
+    combine_launch_ms = time_batched(torch, lambda: miep.combine_into(y, h, cx, rtw, cw), it)
+    pack_launch_ms = time_batched(torch, lambda: miep.cached_dispatch_into(x, h, recv_x), it)
     return dict(w=w, rows=rows, wall=wall, layout_ms=tl.ms(), dispatch_ms=td.ms(), combine_ms=tc.ms(),
-                cached_ms=tcd.ms())
+                cached_ms=tcd.ms(), combine_launch_ms=combine_launch_ms, pack_launch_ms=pack_launch_ms)
 
 
 def run_ll(torch, miep, wl, iters):
@@ -209,17 +241,10 @@ def run_ll(torch, miep, wl, iters):
         def call():
             miep.low_latency_dispatch_into(x, idx, R, M, w.E, w.dest_rank, fp8, rs, ue, **bufs)
 
-        for _ in range(5):
-            call()
-        t = Timer(torch, iters)
-        for _ in range(iters):
-            with t:
-                call()
-        torch.cuda.synchronize()
+        ms = time_batched(torch, call, iters)
         msgs = int(bufs["packed_recv_count"].sum().item())
         local = (idx >= w.dest_rank * L) & (idx < (w.dest_rank + 1) * L)
         distinct = int(local.any(dim=1).sum().item())
-        ms = med(t.ms())
         out[name] = dict(us=round(ms * 1e3, 2), messages=msgs, tokens=distinct,
                          tokens_per_s=round(distinct / (ms / 1e3), 1),
                          gbs=round(bytes_ll(msgs, distinct, H, fp8, R, L) / (ms / 1e3) / 1e9, 1))
@@ -233,14 +258,7 @@ def run_ll(torch, miep, wl, iters):
         miep.low_latency_combine_into(y, idx, wts, bufs["packed_recv_src_info"], bufs["packed_recv_layout_range"], R, M,
                                       w.E, w.dest_rank, cx)
 
-    for _ in range(5):
-        ccall()
-    t = Timer(torch, iters)
-    for _ in range(iters):
-        with t:
-            ccall()
-    torch.cuda.synchronize()
-    ms = med(t.ms())
+    ms = time_batched(torch, ccall, iters)
     out["combine"] = dict(us=round(ms * 1e3, 2), messages=msgs, tokens=w.N,
                           gbs=round(bytes_ll_combine(msgs, w.N, H, w.K, True) / (ms / 1e3) / 1e9, 1))
     return out
@@ -328,12 +346,12 @@ def _kernel_key(name):
     return None
 
 
-def summarize_stats(stats_dir, out_md, command):
+def summarize_stats(stats_dir, out_md, command, title="normal workload step"):
     """rocprofv3 --kernel-trace --stats CSV -> a short markdown table of the miep kernels."""
     import csv
     import glob
     path = glob.glob(os.path.join(stats_dir, "*_kernel_stats.csv"))[0]
-    lines = ["# Kernel durations: normal workload step (rocprofv3 --kernel-trace --stats)", "",
+    lines = ["# Kernel durations: %s (rocprofv3 --kernel-trace --stats)" % title, "",
              "Command (from the repo root on the GPU box; `R` = repo root):", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(path)):
@@ -413,10 +431,15 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)")
     ap.add_argument("--command", action="append", default=[], help="command line(s) recorded in a summary")
+    ap.add_argument("--stats-name", default="normal_step_kernels",
+                    help="file name (without .md) of the --summarize-stats output under profiles/")
+    ap.add_argument("--stats-title", default="normal workload step", help="workload named in that summary's title")
+    ap.add_argument("--ll-only", action="store_true",
+                    help="run only the low-latency dispatch and combine measurement (for a kernel profile)")
     args = ap.parse_args()
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, os.path.join(PROFILES, "normal_step_kernels.md"),
-                        "\n".join(args.command))
+        summarize_stats(args.summarize_stats, os.path.join(PROFILES, args.stats_name + ".md"),
+                        "\n".join(args.command), args.stats_title)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], os.path.join(PROFILES, "normal_hbm_traffic.json"),
@@ -431,6 +454,10 @@ def main():
 
     import combine_get_dispatch_histogram_amd as miep
     from combine_get_dispatch_histogram_amd import workloads as wl
+
+    if args.ll_only:
+        print(json.dumps({"ll": run_ll(torch, miep, wl, 20)}), flush=True)
+        return
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -454,8 +481,8 @@ def main():
 
     # dominant kernel: the combine is a single-kernel call; the pack kernel is
     # timed alone through cached dispatch (the fresh dispatch adds notify).
-    cand = {"combine": (com_ms, b_com, ("combine.hip", "device.h")),
-            "pack": (cd_ms, b_cd, ("pack.hip", "device.h"))}
+    cand = {"combine": (r["combine_launch_ms"], b_com, ("combine.hip", "device.h")),
+            "pack": (r["pack_launch_ms"], b_cd, ("pack.hip", "device.h"))}
     dom = max(cand, key=lambda k: cand[k][0])
     d_ms, d_bytes, d_src = cand[dom]
     achieved = d_bytes / (d_ms / 1e3) / 1e9

@@ -212,87 +212,149 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
 // entries were sent to, summed in fp32 in ascending k (each row times the
 // entry's gate weight when weights are given) and rounded once to bf16.
 //
-// One wavefront per (token, row slice).  Lane k holds top-k entry k; for
-// each entry on a local expert l the wavefront finds the entry's slot in the
-// (l, s) block from the dispatch's slot rule: rows of the block hold source
-// tokens in (token, k) order, so the slot is the number of rows naming an
-// earlier token (one ballot count over the block's src_info, 64 rows per
-// load) plus the entry's rank among the token's earlier entries for the same
-// expert.  A slot at or past the block's count was dropped at the cap (or
-// the rank was masked) and is skipped; so is a row whose src_info does not
-// name the token (a handle from another routing).  Then the rows are
-// gathered like the normal combine: up to MAXR rows' loads in flight, adds
-// in k order.  A token with no row writes +0.0.
+// One wavefront per (group of P = 64 / K tokens, row slice); lane p*K + k
+// holds entry k of the group's token p, so one load brings in the routing
+// of P tokens.  Most tokens have no entry on rank d: their zero rows are
+// stored at once.  For an entry on local expert l the lane finds its slot in
+// the (l, s) block from the dispatch's slot rule: the block's rows hold
+// source tokens in (token, k) order, so the slot is the number of rows that
+// name an earlier token (a binary search of the block's src_info) plus the
+// number of the token's earlier entries for the same expert.  A slot at or
+// past the block's count was dropped at the cap (or the rank was masked) and
+// is skipped; so is a row whose src_info does not name the token (a handle
+// from another routing).  The rows are then gathered in lane order, which is
+// (token, k) order, MAXR rows' loads in flight, and each token's sum is
+// stored when the walk moves past it.
+// bf16 (round to nearest even) of one token's fp32 sums for the slice at v0
+template <int VPL>
+__device__ __forceinline__ void store_sum(uint8_t* orow, const float (&acc)[VPL][8], int v0, int nv, int lane) {
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int v = v0 + j * kWave + lane;
+    if (v < nv) {
+      v4u o;
+      o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+      o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+      o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+      o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+      st16<false>(orow + static_cast<int64_t>(v) * 16, o);
+    }
+  }
+}
+
 template <int VPL, int MAXR>
 __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int nslices) {
   const int lane = lane_id();
   const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
-  const int64_t n = gw / nslices;
-  const int slice = static_cast<int>(gw - n * nslices);
-  if (n >= static_cast<int64_t>(a.R) * a.T) return;
-  const int s = static_cast<int>(n / a.T);
-  const int t = static_cast<int>(n - static_cast<int64_t>(s) * a.T);
+  const int K = a.K;
+  const int P = kWave / K;                                 // tokens per group
+  const int64_t N = static_cast<int64_t>(a.R) * a.T;
+  const int64_t g = gw / nslices;
+  const int slice = static_cast<int>(gw - g * nslices);
+  const int64_t n0 = g * P;
+  if (n0 >= N) return;
+  const int np = N - n0 < P ? static_cast<int>(N - n0) : P;   // tokens in this group
   const int64_t lo = static_cast<int64_t>(a.d) * a.L;
   const int64_t block_rows = static_cast<int64_t>(a.R) * a.M;
+  const uint64_t seg = K == kWave ? ~0ull : ((1ull << K) - 1);
 
-  int le = -1;        // lane k: local expert of entry k, or -1
-  float wk = 1.0f;    // lane k: gate weight of entry k
-  if (lane < a.K) {
-    const int64_t e = a.topk_idx[n * a.K + lane];
+  // routing of the group: lane p*K + k <- entry k of token n0 + p
+  const int p = lane / K;
+  const int k = lane - p * K;
+  const bool mine = p < np;
+  const int64_t n = n0 + p;
+  int le = -1;                     // local expert of the entry, or -1
+  float wk = 1.0f;                 // its gate weight
+  if (mine) {
+    const int64_t e = a.topk_idx[n * K + k];
     if (e >= lo && e < lo + a.L) le = static_cast<int>(e - lo);
-    if (a.w) wk = a.w[n * a.K + lane];
+    if (a.w) wk = a.w[n * K + k];
   }
-  int occ = 0;        // earlier entries of this token naming the same local expert
-  for (int k2 = 0; k2 < a.K; ++k2) {
-    const int e2 = readlane(le, k2);
-    occ += (k2 < lane && le >= 0 && e2 == le) ? 1 : 0;
-  }
-
-  int row = -1;       // lane k: packed row of entry k, or -1
-  for (uint64_t m = ballot(le >= 0); m != 0; m &= m - 1) {
-    const int k = __builtin_ctzll(m);
-    const int l = readlane(le, k);
-    const int o = readlane(occ, k);
-    const int64_t lr = a.layout_range[static_cast<int64_t>(l) * a.R + s];
-    const int64_t begin = lr >> 32;
-    int64_t cnt = lr & 0xFFFFFFFFll;
-    if (begin < 0 || begin + cnt > block_rows) cnt = 0;   // not a range this dispatch writes
-    const int32_t* si = a.src_info + l * block_rows + begin;
-    int before = 0;
-    for (int64_t c0 = 0; c0 < cnt; c0 += kWave) {
-      const int64_t i = c0 + lane;
-      before += __popcll(ballot(i < cnt && si[i] < t));
-    }
-    const int64_t j = before + o;
-    int r = -1;
-    if (j < cnt && si[j] == t) r = static_cast<int>(l * block_rows + begin + j);
-    if (lane == k) row = r;
-  }
+  const uint64_t local = ballot(le >= 0);
+  uint64_t tok_local = 0;          // tokens with an entry on rank d
+  for (int q = 0; q < np; ++q)
+    if ((local >> (q * K)) & seg) tok_local |= 1ull << q;
 
   const int nv = a.H / 8;
   const int64_t row_bytes = 2 * static_cast<int64_t>(a.H);
-  const uint8_t* y = reinterpret_cast<const uint8_t*>(a.y);
-  uint8_t* orow = reinterpret_cast<uint8_t*>(a.out) + n * row_bytes;
-  const uint64_t valid = ballot(row >= 0);
-  const bool weighted = a.w != nullptr;
+  uint8_t* out = reinterpret_cast<uint8_t*>(a.out);
   const int span = kWave * VPL;
+
+  // zero rows of the tokens without an entry on rank d
+  for (int v0 = slice * span; v0 < nv; v0 += nslices * span)
+    for (int q = 0; q < np; ++q) {
+      if ((tok_local >> q) & 1ull) continue;
+      uint8_t* orow = out + (n0 + q) * row_bytes;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + j * kWave + lane;
+        if (v < nv) st16<false>(orow + static_cast<int64_t>(v) * 16, v4u{0u, 0u, 0u, 0u});
+      }
+    }
+  if (tok_local == 0) return;
+
+  // slot of every local entry: earlier entries of the token naming the same
+  // expert, plus rows of the (l, s) block naming an earlier token
+  int occ = 0;
+  for (int j = 1; j < K; ++j) {
+    const int other = __shfl(le, lane - j < 0 ? 0 : lane - j, kWave);
+    occ += (j <= k && le >= 0 && other == le) ? 1 : 0;
+  }
+  int row = -1;                    // packed row of the entry, or -1
+  if (le >= 0) {
+    const int s = static_cast<int>(n / a.T);
+    const int t = static_cast<int>(n - static_cast<int64_t>(s) * a.T);
+    const int64_t lr = a.layout_range[static_cast<int64_t>(le) * a.R + s];
+    const int64_t begin = lr >> 32;
+    int64_t cnt = lr & 0xFFFFFFFFll;
+    if (begin < 0 || begin + cnt > block_rows) cnt = 0;   // not a range the dispatch writes
+    const int32_t* si = a.src_info + le * block_rows + begin;
+    int64_t b = 0, e = cnt;                               // first row naming a token >= t
+    while (b < e) {
+      const int64_t mid = (b + e) >> 1;
+      if (si[mid] < t) b = mid + 1; else e = mid;
+    }
+    const int64_t j = b + occ;
+    if (j < cnt && si[j] == t) row = static_cast<int>(le * block_rows + begin + j);
+  }
+  const uint64_t valid = ballot(row >= 0);
+  uint64_t tok_valid = 0;
+  for (int q = 0; q < np; ++q)
+    if ((valid >> (q * K)) & seg) tok_valid |= 1ull << q;
+
+  const uint8_t* y = reinterpret_cast<const uint8_t*>(a.y);
+  const bool weighted = a.w != nullptr;
   for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
+    // tokens whose every local entry was dropped combine to zero
+    for (int q = 0; q < np; ++q) {
+      if (((tok_local & ~tok_valid) >> q) & 1ull) {
+        uint8_t* orow = out + (n0 + q) * row_bytes;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int v = v0 + j * kWave + lane;
+          if (v < nv) st16<false>(orow + static_cast<int64_t>(v) * 16, v4u{0u, 0u, 0u, 0u});
+        }
+      }
+    }
     float acc[VPL][8];
-    bool have = false;
+    int cur = -1;                  // token whose sum is in acc
     uint64_t m = valid;
     while (m) {
       int64_t rows[MAXR];
       float ws[MAXR];
+      int tq[MAXR];
       int nb = 0;
 #pragma unroll
       for (int q = 0; q < MAXR; ++q) {
         rows[q] = 0;
         ws[q] = 1.0f;
+        tq[q] = 0;
         if (m) {
-          const int b = __builtin_ctzll(m);
+          const int bl = __builtin_ctzll(m);
           m &= m - 1;
-          rows[q] = readlane(row, b);
-          ws[q] = __int_as_float(readlane(__float_as_int(wk), b));
+          rows[q] = readlane(row, bl);
+          ws[q] = __int_as_float(readlane(__float_as_int(wk), bl));
+          tq[q] = bl / K;
           nb = q + 1;
         }
       }
@@ -311,42 +373,32 @@ __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int ns
 #pragma unroll
       for (int q = 0; q < MAXR; ++q) {
         if (q < nb) {
+          const bool first = tq[q] != cur;
+          if (first && cur >= 0) store_sum<VPL>(out + (n0 + cur) * row_bytes, acc, v0, nv, lane);
+          cur = tq[q];
 #pragma unroll
           for (int j = 0; j < VPL; ++j) {
             float f[8] = {bf16_lo(dv[q][j].x), bf16_hi(dv[q][j].x), bf16_lo(dv[q][j].y), bf16_hi(dv[q][j].y),
                           bf16_lo(dv[q][j].z), bf16_hi(dv[q][j].z), bf16_lo(dv[q][j].w), bf16_hi(dv[q][j].w)};
             if (weighted) {
 #pragma unroll
-              for (int k = 0; k < 8; ++k) f[k] = f[k] * ws[q];
+              for (int c = 0; c < 8; ++c) f[c] = f[c] * ws[q];
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc[j][k] = have ? acc[j][k] + f[k] : f[k];
+            for (int c = 0; c < 8; ++c) acc[j][c] = first ? f[c] : acc[j][c] + f[c];
           }
-          have = true;
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int v = v0 + j * kWave + lane;
-      if (v < nv) {
-        v4u o = v4u{0u, 0u, 0u, 0u};
-        if (have) {
-          o.x = pack_bf16x2(acc[j][0], acc[j][1]);
-          o.y = pack_bf16x2(acc[j][2], acc[j][3]);
-          o.z = pack_bf16x2(acc[j][4], acc[j][5]);
-          o.w = pack_bf16x2(acc[j][6], acc[j][7]);
-        }
-        st16<false>(orow + static_cast<int64_t>(v) * 16, o);
-      }
-    }
+    if (cur >= 0) store_sum<VPL>(out + (n0 + cur) * row_bytes, acc, v0, nv, lane);
   }
 }
 
 template <int VPL, int MAXR>
 static hipError_t launch_ll_combine_cfg(const LLCombineArgs& a, int nslices, hipStream_t st) {
-  const int64_t waves = static_cast<int64_t>(a.R) * a.T * nslices;
-  const int64_t blocks = (waves + 3) / 4;
+  const int P = kWave / a.K;
+  const int64_t groups = (static_cast<int64_t>(a.R) * a.T + P - 1) / P;
+  const int64_t blocks = (groups * nslices + 3) / 4;
   hipLaunchKernelGGL((ll_combine_kernel<VPL, MAXR>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                      nslices);
   return hipGetLastError();
@@ -356,15 +408,15 @@ hipError_t launch_ll_combine(const LLCombineArgs& a, hipStream_t st) {
   if (static_cast<int64_t>(a.R) * a.T == 0) return hipSuccess;
   const Tuning& tu = tuning();
   const int nv = a.H / 8;
-  const int vpl = tu.llc_vpl > 0 ? tu.llc_vpl : (nv % kWave == 0 ? 1 : 8);
+  // default: one 16-byte vector per lane per token (1 KiB row pieces)
+  const int vpl = tu.llc_vpl > 0 ? tu.llc_vpl : 1;
   const int span = vpl * kWave;
   int nslices = tu.llc_slices > 0 ? tu.llc_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
   switch (vpl) {
-    case 1: return launch_ll_combine_cfg<1, 8>(a, nslices, st);
     case 2: return launch_ll_combine_cfg<2, 8>(a, nslices, st);
     case 4: return launch_ll_combine_cfg<4, 4>(a, nslices, st);
-    default: return launch_ll_combine_cfg<8, 2>(a, nslices, st);
+    default: return launch_ll_combine_cfg<1, 8>(a, nslices, st);
   }
 }
 
