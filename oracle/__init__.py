@@ -79,6 +79,13 @@ def _declare(lib):
     lib.oracle_ll_combine.argtypes = [_I] * 8 + [_P] * 7
     lib.oracle_ll_combine.restype = _I
     lib.oracle_ll_dispatch.restype = _I
+    # S T H K E R C, x_kind x x_scales round_scale, topk_idx topk_weights in_rank,
+    # rdma_capacity + 9 pointers, capacity + 6 pointers
+    lib.oracle_relay_dispatch.argtypes = [_I] * 7 + [_I, _P, _P, _I, _P, _P, _P, _I64] + [_P] * 9 + [_I64] + [_P] * 6
+    lib.oracle_relay_dispatch.restype = _I
+    # S T H K R, y w bias0 bias1, capacity off, rdma_capacity roff nvl_head rdma_head, 5 outputs
+    lib.oracle_relay_combine.argtypes = [_I] * 5 + [_P] * 4 + [_I64, _P, _I64, _P, _P, _P] + [_P] * 5
+    lib.oracle_relay_combine.restype = _I
     lib.oracle_e4m3_encode_n.argtypes = [_I64, _P, _P]
     lib.oracle_e4m3_decode_n.argtypes = [_I64, _P, _P]
     lib.oracle_bf16_round_n.argtypes = [_I64, _P, _P]
@@ -305,6 +312,86 @@ def ll_combine(y: np.ndarray, src_info: np.ndarray, layout_range: np.ndarray, to
     _check(_load().oracle_ll_combine(S, T, M, H, K, E, R, dest_rank, _ptr(y), _ptr(si), _ptr(lr), _ptr(idx), _ptr(w),
                                      _ptr(out), _ptr(out64)), "ll_combine")
     return dict(combined_x=out, combined_f64=out64)
+
+
+# --------------------------------------------------------------------------- two-level relay
+def relay_dispatch(x: np.ndarray, topk_idx, topk_weights, is_token_in_rank: np.ndarray, S: int, E: int, R: int,
+                   C: int, x_kind: int = X_BF16, x_scales=None, round_scale: bool = False,
+                   rdma_capacity: int | None = None, capacity: int | None = None) -> dict:
+    """Dispatch through one RDMA buffer per group of 8 ranks, then forwarding to the group's ranks."""
+    in_rank = _c(is_token_in_rank, np.uint8)
+    N, R_ = in_rank.shape
+    assert R_ == R and N % S == 0 and R % 8 == 0
+    T = N // S
+    G8 = R // 8
+    H = x.shape[1]
+    x = _c(x, np.uint8 if x_kind == X_FP8 else np.uint16)
+    K = topk_idx.shape[1] if topk_idx is not None else 0
+    idx = _c(topk_idx, np.int64) if topk_idx is not None else None
+    w = _c(topk_weights, np.float32) if topk_weights is not None else None
+    xs = _c(x_scales, np.float32) if x_scales is not None else None
+    grp = in_rank.reshape(N, G8, 8).any(axis=2)
+    rtotal = int(grp.sum())
+    total = int(in_rank.astype(np.int64).sum())
+    rcap = rtotal if rdma_capacity is None else int(rdma_capacity)
+    cap = total if capacity is None else int(capacity)
+    G = H // FP8_GROUP
+    fp8 = x_kind != X_BF16
+    dt = np.uint8 if fp8 else np.uint16
+    rdma_x = np.zeros((rcap, H), dt)
+    rdma_sc = np.zeros((rcap, G), np.float32) if fp8 else None
+    rdma_src = np.full((rcap,), -1, np.int32)
+    rdma_rpm = np.empty((S, G8), np.int32)
+    rdma_cpm = np.empty((S, G8, C), np.int32)
+    rdma_rcpm = np.empty((G8, S, C), np.int32)
+    roff = np.empty((G8 + 1,), np.int32)
+    srh = np.empty((N, G8), np.int32)
+    snh = np.full((rcap, 8), -1, np.int32)
+    recv_x = np.zeros((cap, H), dt)
+    recv_sc = np.zeros((cap, G), np.float32) if fp8 else None
+    recv_src = np.full((cap,), -1, np.int32)
+    recv_idx = np.full((cap, K), -1, np.int64) if idx is not None else None
+    recv_w = np.zeros((cap, K), np.float32) if (idx is not None and w is not None) else None
+    off = np.empty((R + 1,), np.int32)
+    _check(_load().oracle_relay_dispatch(S, T, H, K, E, R, C, x_kind, _ptr(x), _ptr(xs), int(round_scale), _ptr(idx),
+                                         _ptr(w), _ptr(in_rank), rcap, _ptr(rdma_x), _ptr(rdma_sc), _ptr(rdma_src),
+                                         _ptr(rdma_rpm), _ptr(rdma_cpm), _ptr(rdma_rcpm), _ptr(roff), _ptr(srh),
+                                         _ptr(snh), cap, _ptr(recv_x), _ptr(recv_sc), _ptr(recv_src), _ptr(recv_idx),
+                                         _ptr(recv_w), _ptr(off)), "relay_dispatch")
+    return dict(rdma_x=rdma_x, rdma_x_scales=rdma_sc, rdma_src_idx=rdma_src, rdma_rank_prefix_matrix=rdma_rpm,
+                rdma_channel_prefix_matrix=rdma_cpm, recv_rdma_channel_prefix_matrix=rdma_rcpm,
+                recv_rdma_offset=roff, send_rdma_head=srh, send_nvl_head=snh, num_rdma_recv=int(roff[G8]),
+                recv_x=recv_x, recv_x_scales=recv_sc, recv_src_idx=recv_src, recv_topk_idx=recv_idx,
+                recv_topk_weights=recv_w, recv_rank_offset=off, num_recv=int(off[R]))
+
+
+def relay_combine(y: np.ndarray, recv_topk_weights, recv_rank_offset, recv_rdma_offset, send_nvl_head, send_rdma_head,
+                  S: int, K: int = 0, bias0=None, bias1=None, want_f64: bool = False) -> dict:
+    """Two-level combine: y uint16 bf16 bits [capacity][H] -> partials per RDMA row, then per source token."""
+    y = _c(y, np.uint16)
+    cap, H = y.shape
+    off = _c(recv_rank_offset, np.int32)
+    roff = _c(recv_rdma_offset, np.int32)
+    snh = _c(send_nvl_head, np.int32)
+    srh = _c(send_rdma_head, np.int32)
+    R = off.shape[0] - 1
+    N = srh.shape[0]
+    T = N // S if S else 0
+    rcap = snh.shape[0]
+    w = _c(recv_topk_weights, np.float32) if recv_topk_weights is not None else None
+    if w is not None:
+        K = w.shape[1]
+    b0 = _c(bias0, np.uint16) if bias0 is not None else None
+    b1 = _c(bias1, np.uint16) if bias1 is not None else None
+    rdma_y = np.zeros((rcap, H), np.uint16)
+    rdma_w = np.zeros((rcap, K), np.float32) if w is not None else None
+    out = np.empty((N, H), np.uint16)
+    out_w = np.zeros((N, K), np.float32) if w is not None else None
+    out64 = np.empty((N, H), np.float64) if want_f64 else None
+    _check(_load().oracle_relay_combine(S, T, H, K, R, _ptr(y), _ptr(w), _ptr(b0), _ptr(b1), cap, _ptr(off), rcap,
+                                        _ptr(roff), _ptr(snh), _ptr(srh), _ptr(rdma_y), _ptr(rdma_w), _ptr(out),
+                                        _ptr(out_w), _ptr(out64)), "relay_combine")
+    return dict(rdma_y=rdma_y, rdma_w=rdma_w, combined_x=out, combined_topk_weights=out_w, combined_f64=out64)
 
 
 def calc_diff(x: np.ndarray, y: np.ndarray) -> float:

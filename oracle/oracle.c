@@ -614,6 +614,230 @@ int oracle_ll_combine(int S, int T, int M, int H, int K, int E, int R, int d,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Two-level relay: dispatch through one buffer per RDMA group, and the     */
+/* two-level combine                                                        */
+/* ------------------------------------------------------------------------ */
+/* [NvLL] normal-mode internode dispatch: a token crosses the RDMA network
+ * once per destination node (RDMA rank = rank / 8, the RDMA rank
+ * translation), lands in that node's RDMA receive buffer together with its
+ * source metadata (which of the node's 8 NVLink ranks want it), and a
+ * forwarder copies it from the RDMA buffer into the NVLink buffer of each
+ * of those ranks, from which the receivers fill recv_x.  [Ch4] 4.2: the
+ * internode handle adds RDMA / global channel prefixes, rank prefixes and
+ * the source metadata.  On one GPU both hops are HBM copies.
+ * Readings (the pages give the pipeline, not the layouts):
+ *   - group g = ranks 8g..8g+7 (G = R/8 groups); token n goes to group g
+ *     when it goes to any of those ranks;
+ *   - the RDMA buffer of group g holds one row per such token, in (source,
+ *     token) order, at rows [roff[g], roff[g+1]) of one [rdma_capacity]
+ *     array; a row carries the payload as it travels (bf16, or E4M3 codes +
+ *     fp32 scales: the FP8 cast happens once, before the first hop);
+ *     rdma_src_idx[row] = n (source token s*T + t);
+ *   - send_rdma_head[n][g] = the row of n within group g's block, or -1;
+ *     rdma prefix matrices as O2 with groups in place of ranks:
+ *     rdma_cpm[s][g][c], rdma_rpm[s][g], rdma_rcpm[g][s][c];
+ *   - the forwarder walks group g's rows in order and appends each to the
+ *     receive block of every rank g*8+j whose bit is set, so rank r's rows
+ *     are again in (source, token) order (the same recv side as O3);
+ *     send_nvl_head[row][j] = the row within rank g*8+j's block, or -1;
+ *     recv_src_idx and recv_topk_* as O3.
+ * Rows at or past a capacity are not written.                              */
+int oracle_relay_dispatch(int S, int T, int H, int K, int E, int R, int C,
+                          int x_kind, const void* x, const float* x_scales, int round_scale,
+                          const int64_t* topk_idx, const float* topk_weights, const uint8_t* in_rank,
+                          int64_t rdma_capacity, void* rdma_x, float* rdma_x_scales, int32_t* rdma_src_idx,
+                          int32_t* rdma_rpm, int32_t* rdma_cpm, int32_t* rdma_rcpm, int32_t* recv_rdma_offset,
+                          int32_t* send_rdma_head, int32_t* send_nvl_head,
+                          int64_t capacity, void* recv_x, float* recv_x_scales, int32_t* recv_src_idx,
+                          int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* recv_rank_offset) {
+    if (S < 0 || T < 0 || H <= 0 || E <= 0 || R <= 0 || C <= 0 || E % R != 0 || R % 8 != 0) return ORC_EINVAL;
+    if (x_kind != ORC_X_BF16 && (H % ORC_FP8_GROUP != 0 || H / ORC_FP8_GROUP > 1024)) return ORC_EINVAL;
+    const int L = E / R, NG = R / 8;
+    const int tc = (T + C - 1) / C;
+    const int G = H / ORC_FP8_GROUP;
+    const int64_t rb = orc_row_bytes(x_kind, H);
+    const int fp8 = x_kind != ORC_X_BF16;
+
+    /* group membership, counted per (source, group, channel) */
+    for (int s = 0; s < S; ++s)
+        for (int g = 0; g < NG; ++g) {
+            int run = 0;
+            for (int c = 0; c < C; ++c) {
+                int t0 = c * tc, t1 = (c + 1) * tc < T ? (c + 1) * tc : T;
+                for (int t = t0; t < t1; ++t) {
+                    int hit = 0;
+                    for (int j = 0; j < 8; ++j) hit |= in_rank[((int64_t)s * T + t) * R + g * 8 + j] != 0;
+                    run += hit;
+                }
+                rdma_cpm[((int64_t)s * NG + g) * C + c] = run;
+            }
+        }
+    for (int g = 0; g < NG; ++g) {
+        int run = 0;
+        for (int s = 0; s < S; ++s) {
+            int before = run;
+            run += rdma_cpm[((int64_t)s * NG + g) * C + (C - 1)];
+            rdma_rpm[s * NG + g] = run;
+            for (int c = 0; c < C; ++c)
+                rdma_rcpm[((int64_t)g * S + s) * C + c] = before + rdma_cpm[((int64_t)s * NG + g) * C + c];
+        }
+    }
+    recv_rdma_offset[0] = 0;
+    for (int g = 0; g < NG; ++g)
+        recv_rdma_offset[g + 1] = recv_rdma_offset[g] + (S > 0 ? rdma_rpm[(S - 1) * NG + g] : 0);
+
+    /* first hop: each token once per destination group, cast once */
+    for (int g = 0; g < NG; ++g) {
+        int row = 0;
+        for (int s = 0; s < S; ++s)
+            for (int t = 0; t < T; ++t) {
+                int64_t n = (int64_t)s * T + t;
+                int hit = 0;
+                for (int j = 0; j < 8; ++j) hit |= in_rank[n * R + g * 8 + j] != 0;
+                if (!hit) { send_rdma_head[n * NG + g] = -1; continue; }
+                send_rdma_head[n * NG + g] = row;
+                int64_t i = (int64_t)recv_rdma_offset[g] + row;
+                row++;
+                if (i >= rdma_capacity) continue;
+                orc_write_payload(x_kind, H, x, x_scales, round_scale, n, (uint8_t*)rdma_x + i * rb,
+                                  fp8 ? rdma_x_scales + i * G : NULL);
+                rdma_src_idx[i] = (int32_t)n;
+            }
+    }
+
+    /* receive blocks of the final ranks */
+    recv_rank_offset[0] = 0;
+    for (int r = 0; r < R; ++r) {
+        int n_r = 0;
+        for (int64_t n = 0; n < (int64_t)S * T; ++n) n_r += in_rank[n * R + r] != 0;
+        recv_rank_offset[r + 1] = recv_rank_offset[r] + n_r;
+    }
+
+    /* second hop: the forwarder of group g walks its rows in order */
+    for (int g = 0; g < NG; ++g) {
+        int row_of[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int64_t total = (int64_t)recv_rdma_offset[g + 1] - recv_rdma_offset[g];
+        for (int64_t q = 0; q < total; ++q) {
+            int64_t i = (int64_t)recv_rdma_offset[g] + q;
+            if (i >= rdma_capacity) break;
+            int64_t n = rdma_src_idx[i];
+            for (int j = 0; j < 8; ++j) {
+                int r = g * 8 + j;
+                if (!in_rank[n * R + r]) { send_nvl_head[i * 8 + j] = -1; continue; }
+                send_nvl_head[i * 8 + j] = row_of[j];
+                int64_t dst = (int64_t)recv_rank_offset[r] + row_of[j];
+                row_of[j]++;
+                if (dst >= capacity) continue;
+                memcpy((uint8_t*)recv_x + dst * rb, (const uint8_t*)rdma_x + i * rb, (size_t)rb);
+                if (fp8 && recv_x_scales) memcpy(recv_x_scales + dst * G, rdma_x_scales + i * G, sizeof(float) * G);
+                recv_src_idx[dst] = (int32_t)(n % T);
+                if (topk_idx && recv_topk_idx) {
+                    for (int k = 0; k < K; ++k) {
+                        int64_t e = topk_idx[n * K + k];
+                        int mine = e >= 0 && e < E && e / L == r;
+                        recv_topk_idx[dst * K + k] = mine ? e - (int64_t)r * L : -1;
+                        if (topk_weights && recv_topk_weights)
+                            recv_topk_weights[dst * K + k] = mine ? topk_weights[n * K + k] : 0.0f;
+                    }
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* Two-level combine, the reverse of the relay ([NvLL] normal mode: the
+ * combine reduces inside the node over NVLink first, then sends one row
+ * per node back over RDMA; [Ch4] 4.4: only additions, weights reduced
+ * separately).  Readings:
+ *   - first level: every RDMA row of group g sums, in fp32 from its first
+ *     term, the expert outputs of the group's ranks j ascending with
+ *     send_nvl_head[row][j] >= 0, and is rounded to bf16 -- the type a
+ *     partial travels in; the top-k weights are summed the same way in fp32;
+ *     a row no rank holds is +0.0;
+ *   - second level: every source token sums, in fp32 from its first term,
+ *     its groups' partial rows g ascending (send_rdma_head >= 0), then the
+ *     bias rows as in O4, and is rounded once more to bf16; weights as fp32.
+ *   y [capacity][H] bf16, w [capacity][K] (nullable) -> rdma_y
+ *   [rdma_capacity][H] bf16 partials, rdma_w (nullable), out [S*T][H] bf16,
+ *   out_w [S*T][K] (nullable), out_f64: every contribution and bias summed
+ *   in fp64 without the intermediate rounding (accuracy reference).        */
+int oracle_relay_combine(int S, int T, int H, int K, int R,
+                         const uint16_t* y, const float* w, const uint16_t* bias0, const uint16_t* bias1,
+                         int64_t capacity, const int32_t* recv_rank_offset,
+                         int64_t rdma_capacity, const int32_t* recv_rdma_offset, const int32_t* send_nvl_head,
+                         const int32_t* send_rdma_head,
+                         uint16_t* rdma_y, float* rdma_w, uint16_t* out, float* out_w, double* out_f64) {
+    if (S < 0 || T < 0 || H <= 0 || R <= 0 || R % 8 != 0 || K < 0) return ORC_EINVAL;
+    const int NG = R / 8;
+    float* acc = (float*)malloc(sizeof(float) * (size_t)H);
+    double* acc64 = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!acc || !acc64) { free(acc); free(acc64); return ORC_EINVAL; }
+    float wacc[64];
+    if (K > 64) { free(acc); free(acc64); return ORC_EINVAL; }
+
+    /* first level: inside each group */
+    for (int g = 0; g < NG; ++g)
+        for (int64_t i = recv_rdma_offset[g]; i < recv_rdma_offset[g + 1] && i < rdma_capacity; ++i) {
+            int have = 0;
+            for (int j = 0; j < 8; ++j) {
+                int32_t h = send_nvl_head[i * 8 + j];
+                if (h < 0) continue;
+                int64_t row = (int64_t)recv_rank_offset[g * 8 + j] + h;
+                if (row >= capacity) continue;
+                for (int c = 0; c < H; ++c) {
+                    float v = oracle_bf16_to_f32(y[row * H + c]);
+                    acc[c] = have ? acc[c] + v : v;
+                }
+                if (w) for (int k = 0; k < K; ++k) wacc[k] = have ? wacc[k] + w[row * K + k] : w[row * K + k];
+                have = 1;
+            }
+            for (int c = 0; c < H; ++c) rdma_y[i * H + c] = have ? oracle_bf16_round(acc[c]) : 0;
+            if (w && rdma_w) for (int k = 0; k < K; ++k) rdma_w[i * K + k] = have ? wacc[k] : 0.0f;
+        }
+
+    /* second level: across groups, per source token */
+    for (int64_t n = 0; n < (int64_t)S * T; ++n) {
+        int have = 0;
+        for (int c = 0; c < H; ++c) acc64[c] = 0.0;
+        for (int g = 0; g < NG; ++g) {
+            int32_t h = send_rdma_head[n * NG + g];
+            if (h < 0) continue;
+            int64_t i = (int64_t)recv_rdma_offset[g] + h;
+            if (i >= rdma_capacity) continue;
+            for (int c = 0; c < H; ++c) {
+                float v = oracle_bf16_to_f32(rdma_y[i * H + c]);
+                acc[c] = have ? acc[c] + v : v;
+            }
+            if (w && rdma_w) for (int k = 0; k < K; ++k) wacc[k] = have ? wacc[k] + rdma_w[i * K + k] : rdma_w[i * K + k];
+            have = 1;
+            if (out_f64) {
+                for (int j = 0; j < 8; ++j) {
+                    int32_t hh = send_nvl_head[i * 8 + j];
+                    if (hh < 0) continue;
+                    int64_t row = (int64_t)recv_rank_offset[g * 8 + j] + hh;
+                    if (row >= capacity) continue;
+                    for (int c = 0; c < H; ++c) acc64[c] += oracle_bf16_to_f32(y[row * H + c]);
+                }
+            }
+        }
+        const int biased = bias0 != NULL || bias1 != NULL;
+        for (int c = 0; c < H; ++c) {
+            if (biased) {
+                if (!have) acc[c] = 0.0f;
+                if (bias0) { acc[c] += oracle_bf16_to_f32(bias0[n * H + c]); acc64[c] += oracle_bf16_to_f32(bias0[n * H + c]); }
+                if (bias1) { acc[c] += oracle_bf16_to_f32(bias1[n * H + c]); acc64[c] += oracle_bf16_to_f32(bias1[n * H + c]); }
+            }
+            out[n * H + c] = (have || biased) ? oracle_bf16_round(acc[c]) : 0;
+            if (out_f64) out_f64[n * H + c] = acc64[c];
+        }
+        if (out_w) for (int k = 0; k < K; ++k) out_w[n * K + k] = (have && w && rdma_w) ? wacc[k] : 0.0f;
+    }
+    free(acc); free(acc64);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Batch forms of the scalar encoders (for exhaustive tests)                 */
 /* ------------------------------------------------------------------------ */
 void oracle_e4m3_encode_n(int64_t n, const float* a, uint8_t* out) {

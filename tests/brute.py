@@ -190,3 +190,59 @@ def ll_combine(y_bits, src_info, layout_range, topk_idx, S, M, E, R, d, weights=
                 out[n] = acc
                 have[n] = True
     return out, have
+
+
+# ----------------------------------------------------------------- two-level relay
+def relay_plan(in_rank, S: int):
+    """Group buffers of the relay: for every group of 8 ranks, the ordered list of source tokens n that
+    go to any of its ranks; per RDMA row, the row it takes in each of the group's ranks (or -1)."""
+    in_rank = np.asarray(in_rank)
+    N, R = in_rank.shape
+    G = R // 8
+    rows = {g: [n for n in range(N) if any(in_rank[n, 8 * g + j] for j in range(8))] for g in range(G)}
+    send_rdma_head = np.full((N, G), -1, np.int64)
+    for g in range(G):
+        for i, n in enumerate(rows[g]):
+            send_rdma_head[n, g] = i
+    nvl = {}
+    for g in range(G):
+        taken = [0] * 8
+        for i, n in enumerate(rows[g]):
+            heads = []
+            for j in range(8):
+                if in_rank[n, 8 * g + j]:
+                    heads.append(taken[j])
+                    taken[j] += 1
+                else:
+                    heads.append(-1)
+            nvl[(g, i)] = heads
+    return rows, send_rdma_head, nvl
+
+
+def relay_combine(y_bits, recv_rank_offset, rows, send_rdma_head, nvl, S: int):
+    """Two-level sum: per group row, fp32 over the group's ranks then one bf16 rounding (torch's cast);
+    per token, fp32 over its groups' rounded partials, then bf16 again."""
+    N, G = send_rdma_head.shape
+    H = y_bits.shape[1]
+    partial = {}
+    for g in range(G):
+        for i, n in enumerate(rows[g]):
+            acc = None
+            for j, h in enumerate(nvl[(g, i)]):
+                if h < 0:
+                    continue
+                v = (y_bits[int(recv_rank_offset[8 * g + j]) + h].astype(np.uint32) << 16).view(np.float32)
+                acc = v.copy() if acc is None else (acc + v).astype(np.float32)
+            partial[(g, i)] = np.zeros(H, np.uint16) if acc is None else bf16_round_lib(acc)
+    out = np.zeros((N, H), np.uint16)
+    for n in range(N):
+        acc = None
+        for g in range(G):
+            i = int(send_rdma_head[n, g])
+            if i < 0:
+                continue
+            v = (partial[(g, i)].astype(np.uint32) << 16).view(np.float32)
+            acc = v.copy() if acc is None else (acc + v).astype(np.float32)
+        if acc is not None:
+            out[n] = bf16_round_lib(acc)
+    return out, partial
