@@ -12,6 +12,8 @@ sections 4.1-4.3, for ranks that are partitions of one GPU):
   dispatch(x, topk_idx, topk_weights, <layout>, ...) -> (..., handle)  4.1
   cached_dispatch(x, handle)                                        4.1 (cached)
   combine(y, handle, topk_weights, bias)                            4.2, 4.4
+  relay_dispatch / relay_combine: the same through one buffer per group of 8
+  ranks (the two-level RDMA + NVLink relay), with a RelayHandle
   low_latency_dispatch(x, topk_idx, max_tokens, num_experts, dest_rank, ...)  4.3
   low_latency_combine(y, topk_idx, topk_weights, <dispatch outputs>, ...)     4.3
   update_mask_buffer / clean_mask_buffer / query_mask_buffer        rank masking
@@ -31,6 +33,7 @@ from ._lib import MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # noqa: F401
 __all__ = ["Handle", "MiepError", "get_dispatch_layout", "get_dispatch_layout_into", "dispatch", "dispatch_into", "cached_dispatch",
            "cached_dispatch_into", "combine", "combine_into", "low_latency_dispatch", "low_latency_dispatch_into",
            "low_latency_combine", "low_latency_combine_into", "update_mask_buffer", "clean_mask_buffer",
+           "RelayHandle", "relay_dispatch", "relay_dispatch_into", "relay_combine", "relay_combine_into",
            "query_mask_buffer", "ll_msg_bytes", "version"]
 
 
@@ -483,3 +486,178 @@ def query_mask_buffer(mask_buffer: torch.Tensor, out: Optional[torch.Tensor] = N
     _lib.check(_lib.load().miep_mask_query(_ptr(mask_buffer), mask_buffer.shape[0], _ptr(out),
                                            _stream(mask_buffer)))
     return out
+
+
+# --------------------------------------------------------------------------- two-level relay
+@dataclass
+class RelayHandle:
+    """The group rows of a relay dispatch (groups of 8 ranks standing for the nodes).
+
+    rdma_rank_prefix_matrix [S,G], rdma_channel_prefix_matrix [S,G,C],
+    recv_rdma_channel_prefix_matrix [G,S,C], recv_rdma_offset [G+1] (last =
+    total group rows), send_rdma_head [N,G], rdma_src_idx [rcap] (source token
+    of each group row), send_nvl_head [rcap, 8] (its row in each of the group's
+    ranks, or -1).
+    """
+    rdma_rank_prefix_matrix: torch.Tensor
+    rdma_channel_prefix_matrix: torch.Tensor
+    recv_rdma_channel_prefix_matrix: torch.Tensor
+    recv_rdma_offset: torch.Tensor
+    send_rdma_head: torch.Tensor
+    rdma_src_idx: torch.Tensor
+    send_nvl_head: torch.Tensor
+
+    @property
+    def rdma_capacity(self) -> int:
+        return self.rdma_src_idx.numel()
+
+    @staticmethod
+    def allocate(num_tokens: int, num_src: int, num_ranks: int, num_channels: int, rdma_capacity: int,
+                 device) -> "RelayHandle":
+        G = num_ranks // 8
+        i32 = dict(dtype=torch.int32, device=device)
+        return RelayHandle(torch.empty((num_src, G), **i32), torch.empty((num_src, G, num_channels), **i32),
+                           torch.empty((G, num_src, num_channels), **i32), torch.empty((G + 1,), **i32),
+                           torch.empty((num_tokens, G), **i32), torch.empty((rdma_capacity,), **i32),
+                           torch.empty((rdma_capacity, 8), **i32))
+
+    def c(self) -> _lib.RelayHandleC:
+        return _lib.RelayHandleC(self.rdma_rank_prefix_matrix.data_ptr(), self.rdma_channel_prefix_matrix.data_ptr(),
+                                 self.recv_rdma_channel_prefix_matrix.data_ptr(), self.recv_rdma_offset.data_ptr(),
+                                 self.send_rdma_head.data_ptr(), self.rdma_src_idx.data_ptr(),
+                                 self.send_nvl_head.data_ptr(), self.rdma_capacity)
+
+
+def relay_dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                        num_tokens_per_expert, handle: Handle, relay: RelayHandle, rdma_x, recv_x,
+                        rdma_x_scales=None, recv_x_scales=None, recv_topk_idx=None, recv_topk_weights=None,
+                        num_recv_tokens_per_expert=None, x_scales=None, cast_to_fp8: bool = False,
+                        round_scale: bool = False, expert_alignment: int = 1) -> None:
+    """Relay dispatch into preallocated outputs (allocates nothing)."""
+    kind = _x_kind(x, cast_to_fp8)
+    _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
+    N, H = x.shape
+    S, R, K = handle.num_src, handle.num_ranks, handle.num_topk
+    G = R // 8
+    if R % 8 or R <= 8:
+        raise ValueError("the relay needs num_ranks > 8 and a multiple of 8")
+    _want(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (S, R))
+    _want(num_tokens_per_rdma_rank, "num_tokens_per_rdma_rank", torch.int32, (S, G))
+    _want(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (S, handle.num_experts))
+    _want(topk_idx, "topk_idx", torch.int64, (N, K))
+    _want(topk_weights, "topk_weights", torch.float32, (N, K))
+    _want(num_recv_tokens_per_expert, "num_recv_tokens_per_expert", torch.int32, (R, handle.num_experts // R))
+    for t, name in ((recv_topk_idx, "recv_topk_idx"), (recv_topk_weights, "recv_topk_weights")):
+        if t is not None and (t.dim() != 2 or t.shape[0] < handle.recv_capacity or t.shape[1] != K):
+            raise ValueError("%s must be [>= %d, %d]" % (name, handle.recv_capacity, K))
+    _want(recv_topk_idx, "recv_topk_idx", torch.int64)
+    _want(recv_topk_weights, "recv_topk_weights", torch.float32)
+    rc = relay.rdma_capacity
+    if rdma_x.dim() != 2 or rdma_x.shape[0] < rc or rdma_x.shape[1] != H:
+        raise ValueError("rdma_x must be [>= %d, %d]" % (rc, H))
+    if kind == X_BF16:
+        _want(rdma_x, "rdma_x", torch.bfloat16)
+    else:
+        if rdma_x.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError("rdma_x must hold E4M3 codes for an FP8 dispatch")
+        if rdma_x_scales is None or rdma_x_scales.dim() != 2 or rdma_x_scales.shape[0] < rc or \
+                rdma_x_scales.shape[1] != H // 128:
+            raise ValueError("rdma_x_scales must be [>= %d, %d]" % (rc, H // 128))
+        _want(rdma_x_scales, "rdma_x_scales", torch.float32)
+    if relay.send_rdma_head.shape != (N, G):
+        raise ValueError("relay.send_rdma_head must be [%d, %d]" % (N, G))
+    p = handle.problem(H, expert_alignment)
+    h = handle.c()
+    rh = relay.c()
+    _lib.check(_lib.load().miep_relay_dispatch(
+        ctypes.byref(p), _ptr(x), kind, _ptr(x_scales), int(round_scale), _ptr(topk_idx), _ptr(topk_weights),
+        _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert), _ptr(rdma_x),
+        _ptr(rdma_x_scales), _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_topk_idx), _ptr(recv_topk_weights),
+        _ptr(num_recv_tokens_per_expert), ctypes.byref(h), ctypes.byref(rh), _stream(x)))
+
+
+def relay_dispatch(x: torch.Tensor, topk_idx: Optional[torch.Tensor], topk_weights: Optional[torch.Tensor],
+                   num_tokens_per_rank: torch.Tensor, num_tokens_per_rdma_rank: torch.Tensor,
+                   is_token_in_rank: torch.Tensor, num_tokens_per_expert: Optional[torch.Tensor], num_experts: int,
+                   num_channels: int = 24, expert_alignment: int = 1, x_scales: Optional[torch.Tensor] = None,
+                   cast_to_fp8: bool = False, round_scale: bool = False):
+    """Dispatch through the two-level relay: each token once per destination group of 8 ranks (the FP8 cast,
+    if any, happens once before this hop), then forwarded to the group's receiving ranks.
+
+    The receive side equals ``dispatch``'s.  Buffers are sized exactly (one host read of the rank and group
+    counts).  Returns (recv_x, recv_x_scales, recv_topk_idx, recv_topk_weights, num_recv_tokens_per_expert,
+    handle, relay_handle, rdma_x, rdma_x_scales).
+    """
+    kind = _x_kind(x, cast_to_fp8)
+    N, H = x.shape
+    S, R = num_tokens_per_rank.shape
+    _want(is_token_in_rank, "is_token_in_rank", torch.bool, (N, R))
+    _want(num_tokens_per_rank, "num_tokens_per_rank", torch.int32)
+    _want(num_tokens_per_rdma_rank, "num_tokens_per_rdma_rank", torch.int32)
+    _want(topk_idx, "topk_idx", torch.int64)
+    _want(topk_weights, "topk_weights", torch.float32)
+    K = topk_idx.shape[1] if topk_idx is not None else 1
+    cap = int(num_tokens_per_rank.sum().item())
+    rcap = int(num_tokens_per_rdma_rank.sum().item())
+    dev = x.device
+    handle = Handle.allocate(is_token_in_rank, S, K, num_experts, num_channels, cap)
+    relay = RelayHandle.allocate(N, S, R, num_channels, rcap, dev)
+    recv_x, recv_x_scales = _recv_buffers(x, kind, cap, dev)
+    rdma_x, rdma_x_scales = _recv_buffers(x, kind, rcap, dev)
+    recv_topk_idx = torch.empty((cap, K), dtype=torch.int64, device=dev) if topk_idx is not None else None
+    recv_topk_weights = torch.empty((cap, K), dtype=torch.float32, device=dev) if topk_weights is not None else None
+    nrte = torch.empty((R, num_experts // R), dtype=torch.int32, device=dev) if num_tokens_per_expert is not None \
+        else None
+    relay_dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                        num_tokens_per_expert, handle, relay, rdma_x, recv_x, rdma_x_scales, recv_x_scales,
+                        recv_topk_idx, recv_topk_weights, nrte, x_scales, cast_to_fp8, round_scale, expert_alignment)
+    return recv_x, recv_x_scales, recv_topk_idx, recv_topk_weights, nrte, handle, relay, rdma_x, rdma_x_scales
+
+
+def relay_combine_into(y, handle: Handle, relay: RelayHandle, rdma_y, combined_x, recv_topk_weights=None,
+                       rdma_w=None, combined_topk_weights=None, bias=None) -> None:
+    N, H, K = handle.send_head.shape[0], y.shape[1], handle.num_topk
+    _want(y, "y", torch.bfloat16)
+    if y.dim() != 2 or y.shape[0] < handle.recv_capacity:
+        raise ValueError("y must be [>= %d, H]" % handle.recv_capacity)
+    _want(rdma_y, "rdma_y", torch.bfloat16)
+    if rdma_y.dim() != 2 or rdma_y.shape[0] < relay.rdma_capacity or rdma_y.shape[1] != H:
+        raise ValueError("rdma_y must be [>= %d, %d]" % (relay.rdma_capacity, H))
+    _want(combined_x, "combined_x", torch.bfloat16, (N, H))
+    _want(recv_topk_weights, "recv_topk_weights", torch.float32)
+    if recv_topk_weights is not None:
+        if recv_topk_weights.dim() != 2 or recv_topk_weights.shape[1] != K or \
+                recv_topk_weights.shape[0] < handle.recv_capacity:
+            raise ValueError("recv_topk_weights must be [>= %d, %d]" % (handle.recv_capacity, K))
+        if rdma_w is None or rdma_w.dim() != 2 or rdma_w.shape[0] < relay.rdma_capacity or rdma_w.shape[1] != K:
+            raise ValueError("rdma_w must be [>= %d, %d] when weights are combined" % (relay.rdma_capacity, K))
+    _want(rdma_w, "rdma_w", torch.float32)
+    _want(combined_topk_weights, "combined_topk_weights", torch.float32, (N, K))
+    b0, b1 = _unpack_bias(bias)
+    _want(b0, "bias_0", torch.bfloat16, (N, H))
+    _want(b1, "bias_1", torch.bfloat16, (N, H))
+    p = handle.problem(H)
+    h = handle.c()
+    rh = relay.c()
+    _lib.check(_lib.load().miep_relay_combine(ctypes.byref(p), _ptr(y), _ptr(recv_topk_weights), _ptr(b0), _ptr(b1),
+                                              ctypes.byref(h), ctypes.byref(rh), _ptr(rdma_y), _ptr(rdma_w),
+                                              _ptr(combined_x), _ptr(combined_topk_weights), _stream(y)))
+
+
+def relay_combine(y: torch.Tensor, handle: Handle, relay: RelayHandle, topk_weights: Optional[torch.Tensor] = None,
+                  bias=None):
+    """Two-level combine: each group row sums its group's ranks (rounded to bf16, the partial's travel type),
+    then each token sums its groups' partials and the bias.  Returns (combined_x [N, H] bf16,
+    combined_topk_weights [N, K] fp32 or None)."""
+    _want(y, "y", torch.bfloat16)
+    N, H = handle.send_head.shape[0], y.shape[1]
+    dev = y.device
+    rdma_y = torch.empty((relay.rdma_capacity, H), dtype=torch.bfloat16, device=dev)
+    combined_x = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    rdma_w = cw = None
+    if topk_weights is not None:
+        K = topk_weights.shape[1]
+        rdma_w = torch.empty((relay.rdma_capacity, K), dtype=torch.float32, device=dev)
+        cw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    relay_combine_into(y, handle, relay, rdma_y, combined_x, topk_weights, rdma_w, cw, bias)
+    return combined_x, cw

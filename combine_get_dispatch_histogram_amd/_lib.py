@@ -15,7 +15,8 @@ MIEP_OK, MIEP_EINVAL, MIEP_EUNSUPPORTED, MIEP_EHIP = 0, 1, 2, 3
 X_BF16, X_FP8, X_BF16_CAST_FP8 = 0, 1, 2
 
 # Every symbol the header declares (checked by the CPU ABI test).
-EXPORTS = ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine", "miep_ll_dispatch",
+EXPORTS = ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
+           "miep_relay_dispatch", "miep_relay_combine", "miep_ll_dispatch",
            "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query", "miep_ll_msg_bytes",
            "miep_last_error", "miep_version")
 
@@ -31,6 +32,13 @@ class HandleC(ctypes.Structure):
                 ("recv_channel_prefix_matrix", ctypes.c_void_p), ("recv_rank_offset", ctypes.c_void_p),
                 ("recv_src_idx", ctypes.c_void_p), ("is_token_in_rank", ctypes.c_void_p),
                 ("send_head", ctypes.c_void_p), ("recv_capacity", ctypes.c_int64)]
+
+
+class RelayHandleC(ctypes.Structure):
+    _fields_ = [("rdma_rank_prefix_matrix", ctypes.c_void_p), ("rdma_channel_prefix_matrix", ctypes.c_void_p),
+                ("recv_rdma_channel_prefix_matrix", ctypes.c_void_p), ("recv_rdma_offset", ctypes.c_void_p),
+                ("send_rdma_head", ctypes.c_void_p), ("rdma_src_idx", ctypes.c_void_p),
+                ("send_nvl_head", ctypes.c_void_p), ("rdma_capacity", ctypes.c_int64)]
 
 
 class LLProblem(ctypes.Structure):
@@ -63,6 +71,10 @@ def load() -> ctypes.CDLL:
         lib.miep_cached_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, ctypes.POINTER(HandleC), _P,
                                              _P, _P]
         lib.miep_combine.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.POINTER(HandleC), _P, _P, _P]
+        lib.miep_relay_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32] + [_P] * 12 + \
+            [ctypes.POINTER(HandleC), ctypes.POINTER(RelayHandleC), _P]
+        lib.miep_relay_combine.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.POINTER(HandleC),
+                                           ctypes.POINTER(RelayHandleC), _P, _P, _P, _P, _P]
         lib.miep_ll_dispatch.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P]
         lib.miep_ll_combine.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _P, _P, _P, _P, _P]
@@ -70,6 +82,7 @@ def load() -> ctypes.CDLL:
         lib.miep_mask_clean.argtypes = [_P, _I32, _P]
         lib.miep_mask_query.argtypes = [_P, _I32, _P, _P]
         for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
+                  "miep_relay_dispatch", "miep_relay_combine",
                   "miep_ll_dispatch", "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query"):
             getattr(lib, f).restype = ctypes.c_int
         lib.miep_ll_msg_bytes.argtypes = [_I32, _I32]

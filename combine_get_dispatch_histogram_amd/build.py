@@ -22,7 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "miep")
 LIB = os.path.join(HERE, "libmiep.so")
 
-SOURCES = ["api.cpp", "layout.hip", "notify.hip", "pack.hip", "combine.hip", "ll.hip"]
+SOURCES = ["api.cpp", "layout.hip", "notify.hip", "pack.hip", "combine.hip", "ll.hip", "relay.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -110,6 +110,45 @@ miep::PackArgs pack_args(const miep_problem* p, const void* x, int32_t x_kind, c
   return a;
 }
 
+// The relay's group-row arrays (G = R / 8 groups).
+miep_status check_relay(const miep_problem* p, const miep_relay_handle* rh) {
+  if (!rh) return fail(MIEP_EINVAL, "relay handle is NULL");
+  if (p->num_ranks % 8 != 0 || p->num_ranks <= 8)
+    return fail(MIEP_EUNSUPPORTED, "the relay needs num_ranks > 8 and a multiple of 8");
+  if (rh->rdma_capacity < 0 || rh->rdma_capacity > (1ll << 31) - 1)
+    return fail(MIEP_EINVAL, "rdma_capacity out of range");
+  const int64_t N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  if (!rh->recv_rdma_offset) return fail(MIEP_EINVAL, "relay recv_rdma_offset is NULL");
+  if (N > 0 && !rh->send_rdma_head) return fail(MIEP_EINVAL, "relay send_rdma_head is NULL");
+  if (rh->rdma_capacity > 0 && (!rh->send_nvl_head || !rh->rdma_src_idx))
+    return fail(MIEP_EINVAL, "relay send_nvl_head / rdma_src_idx is NULL");
+  if (!aligned16(rh->send_nvl_head) || !aligned16(rh->send_rdma_head))
+    return fail(MIEP_EUNSUPPORTED, "send_nvl_head and send_rdma_head must be 16-byte aligned");
+  return MIEP_OK;
+}
+
+miep::NotifyArgs notify_args(const miep_problem* p, const miep_handle* h, const int32_t* ntpr, const int32_t* ntpe,
+                             int32_t* nrte) {
+  miep::NotifyArgs na{};
+  na.S = p->num_src;
+  na.T = p->num_tokens;
+  na.R = p->num_ranks;
+  na.C = p->num_channels;
+  na.E = p->num_experts;
+  na.L = p->num_experts / p->num_ranks;
+  na.align = p->expert_alignment;
+  na.in_rank = h->is_token_in_rank;
+  na.ntpr = ntpr;
+  na.ntpe = ntpe;
+  na.rpm = h->rank_prefix_matrix;
+  na.cpm = h->channel_prefix_matrix;
+  na.rcpm = h->recv_channel_prefix_matrix;
+  na.off = h->recv_rank_offset;
+  na.send_head = h->send_head;
+  na.nrte = nrte;
+  return na;
+}
+
 // Sizes of a low-latency problem (shared by dispatch and combine).
 miep_status check_ll_problem(const miep_ll_problem* q) {
   if (!q) return fail(MIEP_EINVAL, "problem is NULL");
@@ -209,23 +248,7 @@ miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, 
     return fail(MIEP_EUNSUPPORTED, "is_token_in_rank must be 4-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  miep::NotifyArgs na{};
-  na.S = p->num_src;
-  na.T = p->num_tokens;
-  na.R = p->num_ranks;
-  na.C = p->num_channels;
-  na.E = p->num_experts;
-  na.L = p->num_experts / p->num_ranks;
-  na.align = p->expert_alignment;
-  na.in_rank = h->is_token_in_rank;
-  na.ntpr = num_tokens_per_rank;
-  na.ntpe = num_tokens_per_expert;
-  na.rpm = h->rank_prefix_matrix;
-  na.cpm = h->channel_prefix_matrix;
-  na.rcpm = h->recv_channel_prefix_matrix;
-  na.off = h->recv_rank_offset;
-  na.send_head = h->send_head;
-  na.nrte = num_recv_tokens_per_expert;
+  miep::NotifyArgs na = notify_args(p, h, num_tokens_per_rank, num_tokens_per_expert, num_recv_tokens_per_expert);
   if (p->num_src == 0) {
     // no sources: every receive offset is 0 and every expert count is 0
     hipError_t e = miep::launch_fill_zero(h->recv_rank_offset, p->num_ranks + 1, s);
@@ -293,6 +316,160 @@ miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* 
   a.out = combined_x;
   a.out_w = combined_topk_weights;
   return hip_status(miep::launch_combine(a, static_cast<hipStream_t>(stream)), "combine launch");
+}
+
+miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                                int32_t round_scale, const int64_t* topk_idx, const float* topk_weights,
+                                const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_rdma_rank,
+                                const int32_t* num_tokens_per_expert, void* rdma_x, float* rdma_x_scales,
+                                void* recv_x, float* recv_x_scales, int64_t* recv_topk_idx,
+                                float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
+                                const miep_handle* h, const miep_relay_handle* rh, void* stream) {
+  miep_status st = check_problem(p);
+  if (st != MIEP_OK) return st;
+  if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
+  if ((st = check_handle(p, h, true)) != MIEP_OK) return st;
+  if ((st = check_relay(p, rh)) != MIEP_OK) return st;
+  const int G = p->num_ranks / 8;
+  if (p->num_src > 0 && (!num_tokens_per_rank || !num_tokens_per_rdma_rank))
+    return fail(MIEP_EINVAL, "num_tokens_per_rank / num_tokens_per_rdma_rank is NULL");
+  if (h->recv_capacity > 0 && !recv_x) return fail(MIEP_EINVAL, "recv_x is NULL");
+  if (rh->rdma_capacity > 0 && !rdma_x) return fail(MIEP_EINVAL, "rdma_x is NULL");
+  if (!aligned16(recv_x) || !aligned16(rdma_x)) return fail(MIEP_EUNSUPPORTED, "recv_x and rdma_x must be 16-byte aligned");
+  if (x_kind != MIEP_X_BF16 && ((h->recv_capacity > 0 && !recv_x_scales) || (rh->rdma_capacity > 0 && !rdma_x_scales)))
+    return fail(MIEP_EINVAL, "recv_x_scales / rdma_x_scales is NULL for an FP8 dispatch");
+  if (topk_idx && h->recv_capacity > 0 && !recv_topk_idx) return fail(MIEP_EINVAL, "recv_topk_idx is NULL");
+  if (topk_weights && !topk_idx) return fail(MIEP_EINVAL, "topk_weights given without topk_idx");
+  if (topk_weights && h->recv_capacity > 0 && !recv_topk_weights)
+    return fail(MIEP_EINVAL, "recv_topk_weights is NULL");
+  if (num_recv_tokens_per_expert && !num_tokens_per_expert)
+    return fail(MIEP_EINVAL, "num_recv_tokens_per_expert needs num_tokens_per_expert");
+  if (!aligned16(h->send_head)) return fail(MIEP_EUNSUPPORTED, "send_head must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(h->is_token_in_rank) & 3u) != 0)
+    return fail(MIEP_EUNSUPPORTED, "is_token_in_rank must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->num_src == 0) {
+    hipError_t e = miep::launch_fill_zero(h->recv_rank_offset, p->num_ranks + 1, s);
+    if (e == hipSuccess) e = miep::launch_fill_zero(rh->recv_rdma_offset, G + 1, s);
+    if (e == hipSuccess && num_recv_tokens_per_expert)
+      e = miep::launch_fill_zero(num_recv_tokens_per_expert, p->num_experts, s);
+    return hip_status(e, "relay dispatch (no sources)");
+  }
+  // the ranks' handle (the receive side is the direct dispatch's)
+  miep::NotifyArgs na = notify_args(p, h, num_tokens_per_rank, num_tokens_per_expert, num_recv_tokens_per_expert);
+  hipError_t e = miep::launch_notify(na, s);
+  if (e != hipSuccess) return hip_status(e, "notify launch");
+  // the groups' prefix matrices, offsets and send_rdma_head
+  miep::NotifyArgs ng = na;
+  ng.R = G;
+  ng.group_w = 8;
+  ng.E = 0;
+  ng.ntpr = num_tokens_per_rdma_rank;
+  ng.ntpe = nullptr;
+  ng.nrte = nullptr;
+  ng.rpm = rh->rdma_rank_prefix_matrix;
+  ng.cpm = rh->rdma_channel_prefix_matrix;
+  ng.rcpm = rh->recv_rdma_channel_prefix_matrix;
+  ng.off = rh->recv_rdma_offset;
+  ng.send_head = rh->send_rdma_head;
+  e = miep::launch_notify(ng, s);
+  if (e != hipSuccess) return hip_status(e, "group notify launch");
+  miep::RelayMetaArgs rm{};
+  rm.N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  rm.G = G;
+  rm.R = p->num_ranks;
+  rm.rdma_capacity = rh->rdma_capacity;
+  rm.send_rdma_head = rh->send_rdma_head;
+  rm.rdma_off = rh->recv_rdma_offset;
+  rm.send_head = h->send_head;
+  rm.rdma_src_idx = rh->rdma_src_idx;
+  rm.send_nvl_head = rh->send_nvl_head;
+  e = miep::launch_relay_meta(rm, s);
+  if (e != hipSuccess) return hip_status(e, "relay meta launch");
+  // first hop: every token once into each destination group's rows
+  miep::PackArgs a1 = pack_args(p, x, x_kind, x_scales, round_scale, h, rdma_x, rdma_x_scales);
+  a1.R = G;
+  a1.send_head = rh->send_rdma_head;
+  a1.off = rh->recv_rdma_offset;
+  a1.capacity = rh->rdma_capacity;
+  a1.meta = 0;
+  e = miep::launch_pack(a1, s);
+  if (e != hipSuccess) return hip_status(e, "relay pack launch");
+  // second hop: every group row to the group's receiving ranks, with metadata
+  const int fwd_kind = x_kind == MIEP_X_BF16 ? MIEP_X_BF16 : MIEP_X_FP8;
+  miep::PackArgs a2 = pack_args(p, rdma_x, fwd_kind, rdma_x_scales, 0, h, recv_x, recv_x_scales);
+  a2.N = rh->rdma_capacity;
+  a2.R = 8;
+  a2.send_head = rh->send_nvl_head;
+  a2.meta = 1;
+  a2.topk_idx = topk_idx;
+  a2.topk_weights = topk_weights;
+  a2.recv_topk_idx = topk_idx ? recv_topk_idx : nullptr;
+  a2.recv_topk_weights = topk_weights ? recv_topk_weights : nullptr;
+  a2.recv_src_idx = h->recv_src_idx;
+  if (!topk_idx) a2.K = 0;
+  a2.count = rh->recv_rdma_offset + G;
+  a2.group_off = rh->recv_rdma_offset;
+  a2.groups = G;
+  a2.group_w = 8;
+  a2.src_tok = rh->rdma_src_idx;
+  return hip_status(miep::launch_pack(a2, s), "relay forward launch");
+}
+
+miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
+                               const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
+                               const miep_relay_handle* rh, uint16_t* rdma_y, float* rdma_w, uint16_t* combined_x,
+                               float* combined_topk_weights, void* stream) {
+  miep_status st = check_problem(p);
+  if (st != MIEP_OK) return st;
+  if ((st = check_handle(p, h, false)) != MIEP_OK) return st;
+  if ((st = check_relay(p, rh)) != MIEP_OK) return st;
+  const int G = p->num_ranks / 8;
+  const int64_t N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  if (p->hidden % 8 != 0) return fail(MIEP_EUNSUPPORTED, "hidden must be a multiple of 8 (16-byte rows)");
+  if (h->recv_capacity > 0 && !y) return fail(MIEP_EINVAL, "y is NULL");
+  if (rh->rdma_capacity > 0 && !rdma_y) return fail(MIEP_EINVAL, "rdma_y is NULL");
+  if (N > 0 && !combined_x) return fail(MIEP_EINVAL, "combined_x is NULL");
+  if (!aligned16(y) || !aligned16(rdma_y) || !aligned16(combined_x) || !aligned16(bias_0) || !aligned16(bias_1))
+    return fail(MIEP_EUNSUPPORTED, "y, rdma_y, combined_x and bias rows must be 16-byte aligned");
+  if (recv_topk_weights && ((rh->rdma_capacity > 0 && !rdma_w) || (N > 0 && !combined_topk_weights)))
+    return fail(MIEP_EINVAL, "rdma_w / combined_topk_weights is NULL while recv_topk_weights is given");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // first level: each group row sums its group's ranks' rows
+  miep::CombineArgs c1{};
+  c1.N = rh->rdma_capacity;
+  c1.H = p->hidden;
+  c1.K = p->num_topk;
+  c1.R = 8;
+  c1.capacity = h->recv_capacity;
+  c1.y = y;
+  c1.w = recv_topk_weights;
+  c1.send_head = rh->send_nvl_head;
+  c1.off = h->recv_rank_offset;
+  c1.out = rdma_y;
+  c1.out_w = recv_topk_weights ? rdma_w : nullptr;
+  c1.count = rh->recv_rdma_offset + G;
+  c1.group_off = rh->recv_rdma_offset;
+  c1.groups = G;
+  c1.group_w = 8;
+  hipError_t e = miep::launch_combine(c1, s);
+  if (e != hipSuccess) return hip_status(e, "relay combine (group level) launch");
+  // second level: each token sums its groups' partial rows, then the bias
+  miep::CombineArgs c2{};
+  c2.N = N;
+  c2.H = p->hidden;
+  c2.K = p->num_topk;
+  c2.R = G;
+  c2.capacity = rh->rdma_capacity;
+  c2.y = rdma_y;
+  c2.w = recv_topk_weights ? rdma_w : nullptr;
+  c2.bias0 = N > 0 ? bias_0 : nullptr;
+  c2.bias1 = N > 0 ? bias_1 : nullptr;
+  c2.send_head = rh->send_rdma_head;
+  c2.off = rh->recv_rdma_offset;
+  c2.out = combined_x;
+  c2.out_w = combined_topk_weights;
+  return hip_status(miep::launch_combine(c2, s), "relay combine (token level) launch");
 }
 
 miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,

@@ -23,7 +23,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
   const int64_t n = gw / nslices;
   const int slice = static_cast<int>(gw - n * nslices);
   if (n >= a.N) return;
+  if (a.count != nullptr && n >= *a.count) return;   // past the group rows
   const int R = a.R;
+  // group-level reduction: lane j of row n's group g reads rank g*group_w + j
+  int rbase = 0;
+  if (a.group_off != nullptr) {
+    const bool le = lane <= a.groups && a.group_off[lane] <= n;
+    rbase = (__popcll(ballot(le)) - 1) * a.group_w;
+  }
 
   int src[MW];
   uint64_t smask[MW];
@@ -33,7 +40,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
     int row = -1;
     if (r < R) {
       const int sh = a.send_head[n * R + r];
-      const int o = a.off[r];                        // independent of sh: both loads in flight
+      const int o = a.off[rbase + r];                // independent of sh: both loads in flight
       row = sh >= 0 ? o + sh : -1;
     }
     const bool ok = row >= 0 && row < a.capacity;

@@ -25,9 +25,13 @@ struct LayoutArgs {
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t st);
 
 // ---- notify: prefix matrices, receive offsets, send_head (one workgroup per source)
+// group_w == 0: the destinations are the R ranks of in_rank's rows.
+// group_w == 8: the destinations are R groups of 8 ranks (rows of R*8
+// bytes); a token goes to a group when it goes to any of its ranks.
 struct NotifyArgs {
   int S, T, R, C, E, L, align;
-  const uint8_t* in_rank;   // [S*T][R]
+  int group_w;
+  const uint8_t* in_rank;   // [S*T][R] (or [S*T][R*group_w])
   const int32_t* ntpr;      // [S][R]
   const int32_t* ntpe;      // [S][E] or null
   int32_t* rpm;             // [S][R]
@@ -61,6 +65,11 @@ struct PackArgs {
   int64_t* recv_topk_idx;
   float* recv_topk_weights;
   int32_t* recv_src_idx;
+  // Forwarding from group rows (all null / 0 for a direct dispatch):
+  const int32_t* count;      // device row count; rows n >= *count are skipped
+  const int32_t* group_off;  // [groups+1] first row of each group; lane j of row n's group g is rank g*group_w + j
+  int groups, group_w;
+  const int32_t* src_tok;    // [N] source token of row n (top-k metadata, recv_src_idx)
 };
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 
@@ -77,8 +86,26 @@ struct CombineArgs {
   const int32_t* off;
   uint16_t* out;             // [N][H]
   float* out_w;              // [N][K] or null
+  // Group-level reduction (all null / 0 for a direct combine): rows n >=
+  // *count are skipped; lane j of row n's group g reads rank g*group_w + j.
+  const int32_t* count;
+  const int32_t* group_off;  // [groups+1]
+  int groups, group_w;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+// ---- relay: per group row, its source token and its rows in the group's ranks
+struct RelayMetaArgs {
+  int64_t N;                  // source tokens
+  int G, R;                   // groups of 8, ranks
+  int64_t rdma_capacity;
+  const int32_t* send_rdma_head;  // [N][G]
+  const int32_t* rdma_off;        // [G+1]
+  const int32_t* send_head;       // [N][R]
+  int32_t* rdma_src_idx;          // [rdma_capacity]
+  int32_t* send_nvl_head;         // [rdma_capacity][8]
+};
+hipError_t launch_relay_meta(const RelayMetaArgs& a, hipStream_t st);
 
 // ---- low-latency: expert-major send, then receive-side unpack
 struct LLArgs {

@@ -23,6 +23,25 @@ namespace miep {
 
 constexpr int kNotifyMaxWaves = 16;
 
+// Destination set of token n: its rank row, or with group_w == 8 one bit
+// per group of 8 ranks (set when any of the group's bytes is set).
+template <int MW>
+__device__ __forceinline__ RankMask<MW> load_member(const NotifyArgs& a, int64_t n) {
+  if (a.group_w == 0) return load_rank_row<MW>(a.in_rank + n * a.R, a.R);
+  const int W = a.R * 8;                               // ranks per row, <= kMaxRanks
+  const RankMask<4> full = load_rank_row<4>(a.in_rank + n * W, W);
+  RankMask<MW> m;
+  m.clear();
+  for (int g = 0; g < a.R; ++g) {
+    const int q = g >> 3;                              // 64-bit word holding ranks 8g..8g+7
+    uint64_t word = full.w[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) word = q == i ? full.w[i] : word;
+    if ((word >> ((g & 7) * 8)) & 0xFFull) m.set(g);
+  }
+  return m;
+}
+
 template <int MW>
 __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   __shared__ int32_t base[kMaxRanks];                 // rows of rank r from sources < s
@@ -49,7 +68,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   // overlaps the rank-total reduction below
   RankMask<MW> first;
   first.clear();
-  if (tid < T) first = load_rank_row<MW>(a.in_rank + (static_cast<int64_t>(s) * T + tid) * R, R);
+  if (tid < T) first = load_member<MW>(a, static_cast<int64_t>(s) * T + tid);
   __syncthreads();
   // rank totals and bases: every (source, rank) entry loaded by one thread,
   // summed with LDS integer atomics (order-free), so no thread walks a
@@ -97,7 +116,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     RankMask<MW> m = first;
     if (t0 > 0) {
       m.clear();
-      if (valid) m = load_rank_row<MW>(a.in_rank + n * R, R);
+      if (valid) m = load_member<MW>(a, n);
     }
     // pass 1: per-wavefront counts, lane j of the wave keeps rank r0 + j
     for (int r0 = 0; r0 < R; r0 += kWave) {

@@ -20,6 +20,17 @@
 
 namespace miep {
 
+// First rank of the group that row n belongs to, for rows forwarded from
+// group rows (group_off[g] <= n < group_off[g+1]); 0 for a direct dispatch.
+// Wave-uniform: lane g loads group_off[g] and a ballot counts the groups
+// that start at or before n.
+__device__ __forceinline__ int group_rank_base(const int32_t* group_off, int groups, int group_w, int64_t n) {
+  if (group_off == nullptr) return 0;
+  const int lane = lane_id();
+  const bool le = lane <= groups && group_off[lane] <= n;
+  return (__popcll(ballot(le)) - 1) * group_w;
+}
+
 template <int KIND, int VPL, int MW, int NT>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   const int lane = lane_id();
@@ -27,9 +38,11 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   const int64_t n = gw / nslices;
   const int slice = static_cast<int>(gw - n * nslices);
   if (n >= a.N) return;
+  if (a.count != nullptr && n >= *a.count) return;   // past the forwarded rows
   const int R = a.R;
+  const int rbase = group_rank_base(a.group_off, a.groups, a.group_w, n);
 
-  // destination rows: lane holds rank (64*i + lane)
+  // destination rows: lane holds rank (rbase + 64*i + lane)
   int dst[MW];
   uint64_t dmask[MW];
 #pragma unroll
@@ -38,7 +51,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
     int row = -1;
     if (r < R) {
       const int sh = a.send_head[n * R + r];
-      const int o = a.off[r];                        // independent of sh: both loads in flight
+      const int o = a.off[rbase + r];                // independent of sh: both loads in flight
       row = sh >= 0 ? o + sh : -1;
     }
     const bool ok = row >= 0 && row < a.capacity;
@@ -49,11 +62,12 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   const int G = a.H / kFp8Group;
   // top-k entries, source index and pre-quantised scales: once per token
   if (slice == 0 && (a.meta || KIND == kPackFp8)) {
+    const int64_t tok = a.src_tok != nullptr ? a.src_tok[n] : n;   // the source token the row carries
     int64_t e = -1;
     float wk = 0.0f;
     if (a.meta && lane < a.K) {
-      e = a.topk_idx[n * a.K + lane];
-      if (a.topk_weights) wk = a.topk_weights[n * a.K + lane];
+      e = a.topk_idx[tok * a.K + lane];
+      if (a.topk_weights) wk = a.topk_weights[tok * a.K + lane];
     }
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
@@ -61,7 +75,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
       while (m) {
         const int b = __builtin_ctzll(m);
         m &= m - 1;
-        const int r = kWave * i + b;
+        const int r = rbase + kWave * i + b;
         const int64_t row = readlane(dst[i], b);
         if (a.meta) {
           if (lane < a.K) {
@@ -69,7 +83,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
             if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
             if (a.recv_topk_weights) a.recv_topk_weights[row * a.K + lane] = mine ? wk : 0.0f;
           }
-          if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(n % a.T);
+          if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(tok % a.T);
         }
         if constexpr (KIND == kPackFp8) {
           for (int g = lane; g < G; g += kWave) a.recv_x_scales[row * G + g] = a.x_scales[n * G + g];
@@ -323,7 +337,9 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
       // Measured on the 16384-token workload: with the top-k metadata (fresh
       // dispatch) one token per workgroup at 2 vectors per lane is fastest
       // (229 vs 264 us); without it (cached) the 1 KiB slices are (247 vs 262).
-      if (tu.cast_tpb > 0 || (tu.cast_tpb < 0 && a.meta)) {
+      // The token-per-workgroup kernel has no forwarding mode.
+      if ((tu.cast_tpb > 0 || (tu.cast_tpb < 0 && a.meta)) && a.group_off == nullptr && a.count == nullptr &&
+          a.src_tok == nullptr) {
         const int hint = tu.pack_vpl > 0 ? tu.pack_vpl : 2;
         switch (tu.pack_nt) {
           case 0: return launch_pack_cast<0>(a, hint, st);

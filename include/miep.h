@@ -1,8 +1,10 @@
 /*
  * miep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel core:
  * layout histogram, normal-mode dispatch with its handle, cached dispatch,
- * combine (with optional bias rows), low-latency (expert-major, optionally
- * FP8) dispatch and combine, and the low-latency rank mask.
+ * combine (with optional bias rows), the two-level relay (dispatch through
+ * one buffer per group of 8 ranks and the two-level combine), low-latency
+ * (expert-major, optionally FP8) dispatch and combine, and the low-latency
+ * rank mask.
  *
  * One GPU plays every rank: the R logical ranks are partitions of one
  * device's HBM, and the S source partitions are the token blocks that the
@@ -150,6 +152,78 @@ miep_status miep_cached_dispatch(const miep_problem* p, const void* x, int32_t x
 miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
                          const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
                          uint16_t* combined_x, float* combined_topk_weights, void* stream);
+
+/* The two-level relay's handle ([NvLL] normal-mode internode dispatch:
+ * RDMA to the destination node, then forwarding over NVLink inside it;
+ * [Ch4] 4.2: the internode handle adds RDMA prefixes and source metadata).
+ * Groups g = 0..G-1 of 8 ranks (ranks 8g..8g+7, the RDMA rank translation)
+ * stand for the nodes.  All arrays are caller-owned device memory filled by
+ * miep_relay_dispatch:
+ *   rdma_rank_prefix_matrix[s][g]            inclusive over sources: group rows group g receives from sources 0..s
+ *   rdma_channel_prefix_matrix[s][g][c]      inclusive over channels: tokens of source s, channels 0..c, sent to group g
+ *   recv_rdma_channel_prefix_matrix[g][s][c] group g's row count before source s plus rdma_channel_prefix_matrix[s][g][c]
+ *   recv_rdma_offset[g]                      first group row of group g; [G] = total group rows
+ *   send_rdma_head[n][g]                     row of token n inside group g's block, or -1
+ *   rdma_src_idx[row]                        source token n = s*T + t of each group row
+ *   send_nvl_head[row][j]                    row of the group row inside rank 8g+j's receive block, or -1
+ * A token goes to group g when it goes to any of the group's ranks; group
+ * g's rows are [recv_rdma_offset[g], recv_rdma_offset[g+1]), in (source,
+ * token) order.  send_head, send_nvl_head and rdma_src_idx must be 16-byte
+ * aligned. */
+typedef struct miep_relay_handle {
+  int32_t* rdma_rank_prefix_matrix;         /* [S][G]    */
+  int32_t* rdma_channel_prefix_matrix;      /* [S][G][C] */
+  int32_t* recv_rdma_channel_prefix_matrix; /* [G][S][C] */
+  int32_t* recv_rdma_offset;                /* [G + 1]   */
+  int32_t* send_rdma_head;                  /* [N][G]    */
+  int32_t* rdma_src_idx;                    /* [rdma_capacity] */
+  int32_t* send_nvl_head;                   /* [rdma_capacity][8] */
+  int64_t rdma_capacity;                    /* group rows allocated in rdma_x, rdma_src_idx, send_nvl_head */
+} miep_relay_handle;
+
+/* relay_dispatch -- the normal dispatch through the two-level relay: each
+ * token is written once per destination group into the group rows (rdma_x;
+ * the FP8 cast of MIEP_X_BF16_CAST_FP8 happens once, before this first hop),
+ * then every group row is forwarded to each of the group's ranks that
+ * receive the token.  The receive side (recv_x, recv_x_scales,
+ * recv_topk_*, num_recv_tokens_per_expert and the handle h) is exactly that
+ * of miep_dispatch with the same arguments; rh describes the group rows.
+ *   num_tokens_per_rdma_rank [S][G] from get_dispatch_layout (required)
+ *   rdma_x        [rdma_capacity][H] bf16, or E4M3 codes for the FP8 kinds (16-byte aligned)
+ *   rdma_x_scales [rdma_capacity][H/128] fp32 for the FP8 kinds
+ * Other arguments as in miep_dispatch.  Needs R % 8 == 0 and R > 8.  Group
+ * rows at or past rh->rdma_capacity are neither written nor forwarded;
+ * recv_rdma_offset[G] reports the true total. */
+miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                                int32_t round_scale, const int64_t* topk_idx, const float* topk_weights,
+                                const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_rdma_rank,
+                                const int32_t* num_tokens_per_expert, void* rdma_x, float* rdma_x_scales,
+                                void* recv_x, float* recv_x_scales, int64_t* recv_topk_idx,
+                                float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
+                                const miep_handle* h, const miep_relay_handle* rh, void* stream);
+
+/* relay_combine -- the two-level combine, the reverse of miep_relay_dispatch
+ * ([NvLL] normal mode reduces inside the node first, then once more across
+ * nodes; [Ch4] 4.4: additions only, weights reduced separately).  First
+ * level: each group row sums, in fp32 from its first term, the rows of the
+ * group's ranks j ascending that hold it, rounded to bf16 (the type a
+ * partial travels in) into rdma_y; the received top-k weights likewise in
+ * fp32 into rdma_w.  Second level: each source token sums its groups'
+ * partials g ascending in fp32, then bias_0 and bias_1 as in miep_combine,
+ * rounded once more to bf16.  A token no rank received combines to zero
+ * (or its bias).
+ *   y                     [cap][H] bf16 expert outputs in the receive layout
+ *   recv_topk_weights     [cap][K] fp32, nullable
+ *   bias_0, bias_1        [N][H] bf16, nullable
+ *   rdma_y                [rdma_capacity][H] bf16 scratch (out: the partials)
+ *   rdma_w                [rdma_capacity][K] fp32 scratch, required if recv_topk_weights is given
+ *   combined_x            [N][H] bf16 out
+ *   combined_topk_weights [N][K] fp32 out, nullable (required if recv_topk_weights is given)
+ * Reads h->recv_rank_offset, h->recv_capacity and rh's heads and offsets. */
+miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
+                               const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
+                               const miep_relay_handle* rh, uint16_t* rdma_y, float* rdma_w, uint16_t* combined_x,
+                               float* combined_topk_weights, void* stream);
 
 /* Sizes of one low-latency problem, seen from the receiving rank dest_rank. */
 typedef struct miep_ll_problem {

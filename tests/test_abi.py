@@ -31,6 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
+              "miep_relay_dispatch", "miep_relay_combine",
               "miep_ll_dispatch", "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query"):
         assert f in names
     assert set(names) == set(_lib.EXPORTS)
@@ -128,6 +129,35 @@ def test_combine_validation(lib):
     assert c(8, None, None, None, 16, None) == _lib.MIEP_EUNSUPPORTED     # misaligned y
     assert c(16, None, 8, None, 16, None) == _lib.MIEP_EUNSUPPORTED       # misaligned bias_0
     assert c(16, None, None, 24, 16, None) == _lib.MIEP_EUNSUPPORTED      # misaligned bias_1
+
+
+def test_relay_validation(lib):
+    p = _problem(num_ranks=64)
+    h = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, 100)
+    rh = _lib.RelayHandleC(16, 16, 16, 16, 16, 16, 16, 50)
+
+    def d(prob, handle, relay, rdma_x=16):
+        return lib.miep_relay_dispatch(ctypes.byref(prob), 16, 0, None, 0, 16, 16, 16, 16, 16, rdma_x, None, 16,
+                                       None, 16, 16, None, ctypes.byref(handle), relay, None)
+
+    assert d(_problem(num_ranks=8), h, ctypes.byref(rh)) == _lib.MIEP_EUNSUPPORTED      # one group only
+    assert d(_problem(num_ranks=12), h, ctypes.byref(rh)) == _lib.MIEP_EINVAL          # R > 8 not a multiple of 8
+    assert d(p, h, None) == _lib.MIEP_EINVAL                                          # no relay handle
+    assert d(p, h, ctypes.byref(rh), rdma_x=None) == _lib.MIEP_EINVAL                  # rdma_x NULL
+    assert d(p, h, ctypes.byref(rh), rdma_x=8) == _lib.MIEP_EUNSUPPORTED               # misaligned rdma_x
+    bad = _lib.RelayHandleC(16, 16, 16, 16, 16, 16, 24, 50)                           # misaligned send_nvl_head
+    assert d(p, h, ctypes.byref(bad)) == _lib.MIEP_EUNSUPPORTED
+    neg = _lib.RelayHandleC(16, 16, 16, 16, 16, 16, 16, -1)
+    assert d(p, h, ctypes.byref(neg)) == _lib.MIEP_EINVAL
+
+    def c(relay, y=16, w=None, rdma_y=16, rdma_w=None, out=16, cw=None):
+        return lib.miep_relay_combine(ctypes.byref(p), y, w, None, None, ctypes.byref(h), relay, rdma_y, rdma_w,
+                                      out, cw, None)
+
+    assert c(ctypes.byref(rh), y=None) == _lib.MIEP_EINVAL
+    assert c(ctypes.byref(rh), rdma_y=None) == _lib.MIEP_EINVAL
+    assert c(ctypes.byref(rh), w=16) == _lib.MIEP_EINVAL                               # weights without rdma_w
+    assert c(ctypes.byref(rh), y=8) == _lib.MIEP_EUNSUPPORTED
 
 
 def test_ll_validation(lib):

@@ -1,0 +1,228 @@
+"""GPU parity of the two-level relay: relay dispatch (group rows, relay
+handle, and the receive side) and the two-level combine, through the C ABI,
+against the CPU oracle.  Bar: bit-exact for every output; the identity round
+trip also within calc_diff < 5e-6."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_get_dispatch_histogram_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import combine_get_dispatch_histogram_amd as miep  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def u16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def u8(t):
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def npy(t):
+    return t.detach().cpu().numpy()
+
+
+SHAPES = [
+    # name, S, T, H, E, R, K, C
+    ("r16", 4, 96, 512, 64, 16, 6, 24),
+    ("r24-ragged", 3, 700, 1160, 48, 24, 5, 7),      # 3 groups (scalar send_rdma_head stores), ragged rows
+    ("r64", 4, 128, 256, 256, 64, 8, 5),
+    ("r256", 2, 64, 264, 2048, 256, 9, 3),           # 32 groups
+]
+
+
+def _inputs(S, T, H, E, R, K, C, seed, variant):
+    w = wl.NormalWorkload("relay", S=S, T=T, H=H, E=E, R=R, K=K, C=C)
+    inp = wl.normal_inputs(w, seed)
+    idx = inp["topk_idx"].numpy().copy()
+    if variant == "masked-dup-oob":
+        rng = np.random.default_rng(seed)
+        if K > 1:
+            d = rng.random(w.N) < 0.2
+            idx[d, 1] = idx[d, 0]
+        idx[rng.random(idx.shape) < 0.2] = -1
+        idx[rng.random(idx.shape) < 0.05] = E + 3
+    return w, inp["x"], torch.from_numpy(idx), inp["topk_weights"]
+
+
+def _check_relay_handle(rh, ref):
+    assert np.array_equal(npy(rh.recv_rdma_offset), ref["recv_rdma_offset"])
+    assert np.array_equal(npy(rh.send_rdma_head), ref["send_rdma_head"])
+    assert np.array_equal(npy(rh.rdma_rank_prefix_matrix), ref["rdma_rank_prefix_matrix"])
+    assert np.array_equal(npy(rh.rdma_channel_prefix_matrix), ref["rdma_channel_prefix_matrix"])
+    assert np.array_equal(npy(rh.recv_rdma_channel_prefix_matrix), ref["recv_rdma_channel_prefix_matrix"])
+    n = ref["num_rdma_recv"]
+    assert np.array_equal(npy(rh.rdma_src_idx)[:n], ref["rdma_src_idx"][:n])
+    assert np.array_equal(npy(rh.send_nvl_head)[:n], ref["send_nvl_head"][:n])
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=[c[0] for c in SHAPES])
+@pytest.mark.parametrize("variant", ["plain", "masked-dup-oob"])
+def test_relay_dispatch_combine_small(case, variant):
+    name, S, T, H, E, R, K, C = case
+    say("relay", case, variant)
+    w, x, idx, wts = _inputs(S, T, H, E, R, K, C, 1, variant)
+    idxd = idx.to(DEV)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idxd, E, R, S)
+    out = miep.relay_dispatch(x.to(DEV), idxd, wts.to(DEV), ntpr, ntp_rdma, itr, ntpe, E, C)
+    recv_x, _, rti, rtw, nrte, h, rh, rdma_x, _ = out
+    lay = oracle.layout(idx.numpy(), S, E, R)
+    xb = wl.bf16_bits(x)
+    ref = oracle.relay_dispatch(xb, idx.numpy(), wts.numpy(), lay["is_token_in_rank"], S=S, E=E, R=R, C=C)
+    flat = oracle.dispatch(xb, idx.numpy(), wts.numpy(), lay["is_token_in_rank"], lay["num_tokens_per_expert"],
+                           S=S, E=E, R=R, C=C)
+    torch.cuda.synchronize()
+    _check_relay_handle(rh, ref)
+    n = ref["num_rdma_recv"]
+    assert np.array_equal(u16(rdma_x)[:n], ref["rdma_x"][:n])
+    # the ranks' handle and receive side: the direct dispatch's
+    assert np.array_equal(npy(h.send_head), flat["send_head"])
+    assert np.array_equal(npy(h.rank_prefix_matrix), flat["rank_prefix_matrix"])
+    assert np.array_equal(npy(h.recv_channel_prefix_matrix), flat["recv_channel_prefix_matrix"])
+    assert np.array_equal(npy(h.recv_rank_offset), ref["recv_rank_offset"])
+    assert np.array_equal(u16(recv_x), ref["recv_x"])
+    assert np.array_equal(npy(h.recv_src_idx), ref["recv_src_idx"])
+    assert np.array_equal(npy(rti), ref["recv_topk_idx"])
+    assert np.array_equal(npy(rtw).view(np.uint32), ref["recv_topk_weights"].view(np.uint32))
+    assert np.array_equal(npy(nrte), flat["num_recv_tokens_per_expert"])
+    # two-level combine of random expert outputs, with the weights and a bias
+    g = torch.Generator().manual_seed(5)
+    y = wl.activations(h.recv_capacity, H, g)
+    b = wl.activations(w.N, H, g)
+    cx, cw = miep.relay_combine(y.to(DEV), h, rh, rtw, bias=b.to(DEV))
+    rc = oracle.relay_combine(wl.bf16_bits(y), ref["recv_topk_weights"], ref["recv_rank_offset"],
+                              ref["recv_rdma_offset"], ref["send_nvl_head"], ref["send_rdma_head"], S=S,
+                              bias0=wl.bf16_bits(b))
+    assert np.array_equal(u16(cx), rc["combined_x"])
+    assert np.array_equal(npy(cw).view(np.uint32), rc["combined_topk_weights"].view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["cast", "cast-pow2", "fp8"])
+def test_relay_fp8_kinds_small(kind):
+    S, T, H, E, R, K, C = 3, 200, 1024, 64, 16, 6, 5
+    say("relay fp8", kind)
+    w, x, idx, wts = _inputs(S, T, H, E, R, K, C, 2, "masked-dup-oob")
+    idxd = idx.to(DEV)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idxd, E, R, S)
+    lay = oracle.layout(idx.numpy(), S, E, R)
+    xb = wl.bf16_bits(x)
+    round_scale = kind == "cast-pow2"
+    if kind == "fp8":
+        codes, sci, _ = oracle.fp8_quantize(xb, round_scale=False)
+        xin = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(DEV)
+        xs = torch.from_numpy(sci).to(DEV)
+        out = miep.relay_dispatch(xin, idxd, wts.to(DEV), ntpr, ntp_rdma, itr, ntpe, E, C, x_scales=xs)
+        ref = oracle.relay_dispatch(codes, idx.numpy(), wts.numpy(), lay["is_token_in_rank"], S=S, E=E, R=R,
+                                    C=C, x_kind=oracle.X_FP8, x_scales=sci)
+    else:
+        out = miep.relay_dispatch(x.to(DEV), idxd, wts.to(DEV), ntpr, ntp_rdma, itr, ntpe, E, C, cast_to_fp8=True,
+                                  round_scale=round_scale)
+        ref = oracle.relay_dispatch(xb, idx.numpy(), wts.numpy(), lay["is_token_in_rank"], S=S, E=E, R=R, C=C,
+                                    x_kind=oracle.X_BF16_CAST_FP8, round_scale=round_scale)
+    recv_x, recv_s, rti, rtw, _, h, rh, rdma_x, rdma_s = out
+    torch.cuda.synchronize()
+    _check_relay_handle(rh, ref)
+    n = ref["num_rdma_recv"]
+    assert np.array_equal(u8(rdma_x)[:n], ref["rdma_x"][:n])
+    assert np.array_equal(npy(rdma_s)[:n].view(np.uint32), ref["rdma_x_scales"][:n].view(np.uint32))
+    assert np.array_equal(u8(recv_x), ref["recv_x"])
+    assert np.array_equal(npy(recv_s).view(np.uint32), ref["recv_x_scales"].view(np.uint32))
+    assert np.array_equal(npy(rti), ref["recv_topk_idx"])
+
+
+def test_relay_large_workload_bf16_and_identity_round_trip():
+    """The 64-rank workload (8 groups) through the relay with bf16 rows: every output against the oracle,
+    then identity experts through the two-level combine: bit-exact, and calc_diff < 5e-6 after dividing by
+    the number of receiving ranks."""
+    w = wl.LARGE
+    say("relay large bf16", w.name)
+    inp = wl.normal_inputs(w, 0)
+    x, idx, wts = inp["x"], inp["topk_idx"], inp["topk_weights"]
+    idxd = idx.to(DEV)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    recv_x, _, rti, rtw, _, h, rh, rdma_x, _ = miep.relay_dispatch(x.to(DEV), idxd, wts.to(DEV), ntpr, ntp_rdma,
+                                                                     itr, ntpe, w.E, w.C)
+    lay = oracle.layout(idx.numpy(), w.S, w.E, w.R)
+    xb = wl.bf16_bits(x)
+    ref = oracle.relay_dispatch(xb, idx.numpy(), wts.numpy(), lay["is_token_in_rank"], S=w.S, E=w.E, R=w.R, C=w.C)
+    torch.cuda.synchronize()
+    _check_relay_handle(rh, ref)
+    n = ref["num_rdma_recv"]
+    assert np.array_equal(u16(rdma_x)[:n], ref["rdma_x"][:n])
+    assert np.array_equal(u16(recv_x), ref["recv_x"])
+    assert np.array_equal(npy(rti), ref["recv_topk_idx"])
+    cx, cw = miep.relay_combine(recv_x, h, rh, rtw)
+    rc = oracle.relay_combine(ref["recv_x"], ref["recv_topk_weights"], ref["recv_rank_offset"],
+                              ref["recv_rdma_offset"], ref["send_nvl_head"], ref["send_rdma_head"], S=w.S)
+    assert np.array_equal(u16(cx), rc["combined_x"])
+    cnt = lay["is_token_in_rank"].sum(axis=1).astype(np.float64)
+    got = cx.float().cpu().numpy().astype(np.float64)
+    ok = cnt > 0
+    assert oracle.calc_diff(got[ok] / cnt[ok, None], x.float().numpy().astype(np.float64)[ok]) < 5e-6
+    valid = (idx.numpy() >= 0) & ok[:, None]
+    assert np.array_equal(npy(cw)[valid], wts.numpy()[valid])
+
+
+def test_relay_large_workload_fp8_cast_sampled():
+    """The 64-rank workload with the FP8 cast before the first hop: the handles in full; group rows and
+    forwarded rows of 256 sampled tokens against the oracle's quantiser; the receive side equals the
+    direct FP8-cast dispatch on the GPU."""
+    w = wl.LARGE
+    say("relay large fp8", w.name)
+    inp = wl.normal_inputs(w, 0)
+    x, idx, wts = inp["x"], inp["topk_idx"], inp["topk_weights"]
+    xd, idxd, wd = x.to(DEV), idx.to(DEV), wts.to(DEV)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
+    recv_x, recv_s, rti, rtw, _, h, rh, rdma_x, rdma_s = miep.relay_dispatch(
+        xd, idxd, wd, ntpr, ntp_rdma, itr, ntpe, w.E, w.C, cast_to_fp8=True)
+    direct = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True)
+    torch.cuda.synchronize()
+    assert torch.equal(recv_x.view(torch.uint8), direct[0].view(torch.uint8))
+    assert torch.equal(recv_s, direct[1])
+    assert torch.equal(rti, direct[2])
+    assert torch.equal(h.send_head, direct[5].send_head)
+    # group rows of sampled tokens against the oracle's quantiser
+    rng = np.random.default_rng(0)
+    sample = rng.choice(w.N, 256, replace=False)
+    q_codes, q_sci, _ = oracle.fp8_quantize(wl.bf16_bits(x[torch.from_numpy(sample)]), round_scale=False)
+    srh = npy(rh.send_rdma_head)
+    roff = npy(rh.recv_rdma_offset)
+    codes, scales = u8(rdma_x), npy(rdma_s)
+    checked = 0
+    for j, n in enumerate(sample):
+        for g in range(w.R // 8):
+            if srh[n, g] >= 0:
+                row = roff[g] + srh[n, g]
+                assert np.array_equal(codes[row], q_codes[j])
+                assert np.array_equal(scales[row].view(np.uint32), q_sci[j].view(np.uint32))
+                checked += 1
+    assert checked > 256
+
+
+def test_relay_no_sources():
+    say("relay empty")
+    R, E, H, K = 16, 32, 256, 4
+    idx = torch.empty((0, K), dtype=torch.int64, device=DEV)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idx, E, R, 2)
+    recv_x, _, _, rtw, _, h, rh, _, _ = miep.relay_dispatch(x, idx, None, ntpr, ntp_rdma, itr, ntpe, E, 4)
+    cx, _ = miep.relay_combine(torch.empty((0, H), dtype=torch.bfloat16, device=DEV), h, rh)
+    torch.cuda.synchronize()
+    assert int(h.recv_rank_offset[-1]) == 0 and int(rh.recv_rdma_offset[-1]) == 0
+    assert cx.shape == (0, H)
