@@ -71,6 +71,31 @@ def bytes_ll_combine(msgs, N, H, K, weighted):
     return msgs * (2 * H + 4) + N * (2 * H + K * (8 + (4 if weighted else 0)))
 
 
+def bytes_relay_dispatch(N, H, K, R, S, C, E, rows, grows, kind="cast"):
+    """Relay dispatch: the ranks' notify and the groups' notify, the first hop
+    (x read once, one row per (token, group)), the bookkeeping (8 heads per
+    group row) and the second hop (each group row read once and written to
+    its ranks with the top-k metadata of its source token)."""
+    G = R // 8
+    row_in = 2 * H if kind in ("bf16", "cast") else H
+    row_out = 2 * H if kind == "bf16" else H + 4 * (H // 128)
+    notify = bytes_notify(N, R, S, C, E) + N * R + N * G * 4 + S * G * 4 + 2 * S * G * C * 4 + (G + 1) * 4
+    meta = N * G * 4 + grows * (32 + 32 + 4)   # per group row: 8 send_head entries in, 8 heads + source id out
+    hop1 = N * row_in + N * G * 4 + grows * row_out
+    hop2 = grows * (row_out + 32 + 4 + K * 12) + rows * (row_out + 4 + 12 * K)
+    return notify + meta + hop1 + hop2
+
+
+def bytes_relay_combine(N, H, K, R, rows, grows, weights=True):
+    """Two-level combine: every received row read once into its group row's
+    partial (written once), every partial read once into its token's row."""
+    G = R // 8
+    b = grows * 32 + rows * 2 * H + grows * 2 * H + N * G * 4 + grows * 2 * H + N * 2 * H
+    if weights:
+        b += rows * 4 * K + 2 * grows * 4 * K + N * 4 * K
+    return b
+
+
 # --------------------------------------------------------------------------- helpers
 def src_hash(*names):
     h = hashlib.sha256()
@@ -304,6 +329,53 @@ def run_normal_variant(torch, miep, wl, w, iters, cast_fp8):
                                           1))
 
 
+def run_relay(torch, miep, wl, iters):
+    """The 64-rank workload (8 groups of 8 ranks) with the FP8 cast: relay
+    dispatch and two-level combine against the direct dispatch and combine on
+    the same routing (the relay's extra hop is its cost on one GPU)."""
+    w = wl.LARGE
+    dev = torch.device("cuda:0")
+    inp = wl.normal_inputs(w, 0)
+    x = inp["x"].to(dev)
+    idx = inp["topk_idx"].to(dev)
+    wts = inp["topk_weights"].to(dev)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idx, w.E, w.R, w.S)
+    recv_x, recv_s, rti, rtw, nrte, h, rh, rdma_x, rdma_s = miep.relay_dispatch(
+        x, idx, wts, ntpr, ntp_rdma, itr, ntpe, w.E, w.C, cast_to_fp8=True)
+    rows, grows = h.recv_capacity, rh.rdma_capacity
+    y = (recv_x.float() * recv_s.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+    rdma_y = torch.empty((grows, w.H), dtype=torch.bfloat16, device=dev)
+    rdma_w = torch.empty((grows, w.K), dtype=torch.float32, device=dev)
+    cx = torch.empty((w.N, w.H), dtype=torch.bfloat16, device=dev)
+    cw = torch.empty((w.N, w.K), dtype=torch.float32, device=dev)
+
+    def rd():
+        miep.relay_dispatch_into(x, idx, wts, ntpr, ntp_rdma, ntpe, h, rh, rdma_x, recv_x, rdma_s, recv_s, rti, rtw,
+                                 nrte, cast_to_fp8=True)
+
+    def rc():
+        miep.relay_combine_into(y, h, rh, rdma_y, cx, rtw, rdma_w, cw)
+
+    def dd():
+        miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, recv_s, rti, rtw, nrte, cast_to_fp8=True)
+
+    def dc():
+        miep.combine_into(y, h, cx, rtw, cw)
+
+    t = {k: time_batched(torch, f, iters, batch=4) for k, f in
+         (("relay_dispatch", rd), ("relay_combine", rc), ("direct_dispatch", dd), ("direct_combine", dc))}
+    bd = bytes_relay_dispatch(w.N, w.H, w.K, w.R, w.S, w.C, w.E, rows, grows)
+    bc = bytes_relay_combine(w.N, w.H, w.K, w.R, rows, grows)
+    return dict(rows=rows, group_rows=grows, groups_per_token=round(grows / w.N, 4),
+                relay_dispatch_us=round(t["relay_dispatch"] * 1e3, 1),
+                relay_combine_us=round(t["relay_combine"] * 1e3, 1),
+                direct_dispatch_us=round(t["direct_dispatch"] * 1e3, 1),
+                direct_combine_us=round(t["direct_combine"] * 1e3, 1),
+                relay_tokens_per_s=round(w.N / ((t["relay_dispatch"] + t["relay_combine"]) / 1e3), 1),
+                relay_dispatch_gbs=round(bd / (t["relay_dispatch"] / 1e3) / 1e9, 1),
+                relay_combine_gbs=round(bc / (t["relay_combine"] / 1e3) / 1e9, 1))
+
+
 # --------------------------------------------------------------------------- CPU oracle leg
 def cpu_baseline(wl, budget_s):
     import numpy as np  # noqa: F401
@@ -436,6 +508,8 @@ def main():
     ap.add_argument("--stats-title", default="normal workload step", help="workload named in that summary's title")
     ap.add_argument("--ll-only", action="store_true",
                     help="run only the low-latency dispatch and combine measurement (for a kernel profile)")
+    ap.add_argument("--relay-only", action="store_true",
+                    help="run only the two-level relay measurement on the 64-rank workload (for a kernel profile)")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, os.path.join(PROFILES, args.stats_name + ".md"),
@@ -457,6 +531,9 @@ def main():
 
     if args.ll_only:
         print(json.dumps({"ll": run_ll(torch, miep, wl, 20)}), flush=True)
+        return
+    if args.relay_only:
+        print(json.dumps({"large_fp8_relay": run_relay(torch, miep, wl, 5)}), flush=True)
         return
 
     if args.copy_probe_mib:
@@ -519,7 +596,8 @@ def main():
     if not args.no_secondary:
         sec = {"ll": run_ll(torch, miep, wl, 20),
                "skewed": run_normal_variant(torch, miep, wl, wl.SKEWED, 20, False),
-               "large_fp8": run_normal_variant(torch, miep, wl, wl.LARGE, 10, True)}
+               "large_fp8": run_normal_variant(torch, miep, wl, wl.LARGE, 10, True),
+               "large_fp8_relay": run_relay(torch, miep, wl, 5)}
         line["secondary"] = sec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
