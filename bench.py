@@ -167,6 +167,11 @@ def time_batched(torch, fn, iters, batch=16, warm=5):
     return med(t.ms()) / batch
 
 
+def pct(xs, q):
+    s = sorted(xs)
+    return s[min(len(s) - 1, int(q * (len(s) - 1) + 0.5))] if s else float("nan")
+
+
 def med(xs):
     s = sorted(xs)
     return s[len(s) // 2] if s else float("nan")
@@ -239,8 +244,23 @@ def run_normal(torch, miep, wl, steps, warmup):
     it = max(3, min(steps, 10))
     combine_launch_ms = time_batched(torch, lambda: miep.combine_into(y, h, cx, rtw, cw), it)
     pack_launch_ms = time_batched(torch, lambda: miep.cached_dispatch_into(x, h, recv_x), it)
+    # (5) cold cache: 1 GiB written before each timed call (outside its events)
+    # evicts L2 and the 256 MB last-level cache
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = {}
+    for name, fn in (("dispatch", lambda: miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, None, rti, rtw, nrte)),
+                     ("combine", lambda: miep.combine_into(y, h, cx, rtw, cw))):
+        t = Timer(torch, it)
+        for _ in range(it):
+            flush.fill_(1)
+            with t:
+                fn()
+        torch.cuda.synchronize()
+        cold[name] = t.ms()
+    del flush
     return dict(w=w, rows=rows, wall=wall, layout_ms=tl.ms(), dispatch_ms=td.ms(), combine_ms=tc.ms(),
-                cached_ms=tcd.ms(), combine_launch_ms=combine_launch_ms, pack_launch_ms=pack_launch_ms)
+                cached_ms=tcd.ms(), combine_launch_ms=combine_launch_ms, pack_launch_ms=pack_launch_ms,
+                cold_dispatch_ms=cold["dispatch"], cold_combine_ms=cold["combine"])
 
 
 def run_ll(torch, miep, wl, iters):
@@ -586,6 +606,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": d_bytes, "avg_launch_us": round(d_ms * 1e3, 2)},
+        "stages_p10_p50_p90_us": {k: [round(pct(r[k + "_ms"], q) * 1e3, 2) for q in (0.1, 0.5, 0.9)]
+                                  for k in ("layout", "dispatch", "combine")},
+        "cold_cache_us": {"dispatch": round(med(r["cold_dispatch_ms"]) * 1e3, 2),
+                          "combine": round(med(r["cold_combine_ms"]) * 1e3, 2)},
         "stages_us": {"layout": round(lay_ms * 1e3, 2), "dispatch": round(dis_ms * 1e3, 2),
                       "combine": round(com_ms * 1e3, 2), "cached_dispatch": round(cd_ms * 1e3, 2)},
         "stages_gbs": {"layout": round(b_lay / (lay_ms / 1e3) / 1e9, 1),

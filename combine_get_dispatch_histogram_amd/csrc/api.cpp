@@ -345,8 +345,8 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
   if (num_recv_tokens_per_expert && !num_tokens_per_expert)
     return fail(MIEP_EINVAL, "num_recv_tokens_per_expert needs num_tokens_per_expert");
   if (!aligned16(h->send_head)) return fail(MIEP_EUNSUPPORTED, "send_head must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(h->is_token_in_rank) & 3u) != 0)
-    return fail(MIEP_EUNSUPPORTED, "is_token_in_rank must be 4-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(h->is_token_in_rank) & 7u) != 0)
+    return fail(MIEP_EUNSUPPORTED, "is_token_in_rank must be 8-byte aligned for the relay");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p->num_src == 0) {
     hipError_t e = miep::launch_fill_zero(h->recv_rank_offset, p->num_ranks + 1, s);

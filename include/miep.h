@@ -168,8 +168,8 @@ miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* 
  *   send_nvl_head[row][j]                    row of the group row inside rank 8g+j's receive block, or -1
  * A token goes to group g when it goes to any of the group's ranks; group
  * g's rows are [recv_rdma_offset[g], recv_rdma_offset[g+1]), in (source,
- * token) order.  send_head, send_nvl_head and rdma_src_idx must be 16-byte
- * aligned. */
+ * token) order.  send_head, send_rdma_head and send_nvl_head must be
+ * 16-byte aligned, is_token_in_rank 8-byte aligned. */
 typedef struct miep_relay_handle {
   int32_t* rdma_rank_prefix_matrix;         /* [S][G]    */
   int32_t* rdma_channel_prefix_matrix;      /* [S][G][C] */
