@@ -244,6 +244,25 @@ def run_normal(torch, miep, wl, steps, warmup):
     it = max(3, min(steps, 10))
     combine_launch_ms = time_batched(torch, lambda: miep.combine_into(y, h, cx, rtw, cw), it)
     pack_launch_ms = time_batched(torch, lambda: miep.cached_dispatch_into(x, h, recv_x), it)
+    # (6) the same step captured once in a HIP graph and replayed `steps` times
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_wall = time.perf_counter() - t0
+    del graph
     # (5) cold cache: 1 GiB written before each timed call (outside its events)
     # evicts L2 and the 256 MB last-level cache
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -260,7 +279,7 @@ def run_normal(torch, miep, wl, steps, warmup):
     del flush
     return dict(w=w, rows=rows, wall=wall, layout_ms=tl.ms(), dispatch_ms=td.ms(), combine_ms=tc.ms(),
                 cached_ms=tcd.ms(), combine_launch_ms=combine_launch_ms, pack_launch_ms=pack_launch_ms,
-                cold_dispatch_ms=cold["dispatch"], cold_combine_ms=cold["combine"])
+                cold_dispatch_ms=cold["dispatch"], cold_combine_ms=cold["combine"], graph_wall=graph_wall)
 
 
 def run_ll(torch, miep, wl, iters):
@@ -608,6 +627,7 @@ def main():
                      "algorithmic_bytes_per_launch": d_bytes, "avg_launch_us": round(d_ms * 1e3, 2)},
         "stages_p10_p50_p90_us": {k: [round(pct(r[k + "_ms"], q) * 1e3, 2) for q in (0.1, 0.5, 0.9)]
                                   for k in ("layout", "dispatch", "combine")},
+        "graph_replay_ms_per_step": round(r["graph_wall"] * 1e3 / args.steps, 4),
         "cold_cache_us": {"dispatch": round(med(r["cold_dispatch_ms"]) * 1e3, 2),
                           "combine": round(med(r["cold_combine_ms"]) * 1e3, 2)},
         "stages_us": {"layout": round(lay_ms * 1e3, 2), "dispatch": round(dis_ms * 1e3, 2),
