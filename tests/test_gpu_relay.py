@@ -226,3 +226,56 @@ def test_relay_no_sources():
     torch.cuda.synchronize()
     assert int(h.recv_rank_offset[-1]) == 0 and int(rh.recv_rdma_offset[-1]) == 0
     assert cx.shape == (0, H)
+
+
+@pytest.mark.parametrize("mode", ["worst-case", "overflow"])
+def test_relay_capacities(mode):
+    """Fixed capacities: larger than needed (rows past the totals hold in-range poison that must never be
+    read or overwritten), or smaller (rows past a capacity are neither written nor forwarded) -- against the
+    oracle run with the same capacities."""
+    S, T, H, E, R, K, C = 3, 120, 256, 64, 16, 6, 5
+    say("relay capacities", mode)
+    w, x, idx, wts = _inputs(S, T, H, E, R, K, C, 4, "plain")
+    idxd = idx.to(DEV)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idxd, E, R, S)
+    total, gtotal = int(ntpr.sum()), int(ntp_rdma.sum())
+    cap, rcap = (total + 37, gtotal + 53) if mode == "worst-case" else (total - 41, gtotal - 29)
+    h = miep.Handle.allocate(itr, S, K, E, C, cap)
+    rh = miep.RelayHandle.allocate(w.N, S, R, C, rcap, DEV)
+    rh.send_nvl_head.fill_(0)            # in-range poison: a stray read would misplace rows, not fault
+    rh.rdma_src_idx.fill_(0)
+    recv_x = torch.full((cap, H), 3.0, dtype=torch.bfloat16, device=DEV)
+    rdma_x = torch.full((rcap, H), 5.0, dtype=torch.bfloat16, device=DEV)
+    rti = torch.full((cap, K), -9, dtype=torch.int64, device=DEV)
+    rtw = torch.full((cap, K), 9.0, dtype=torch.float32, device=DEV)
+    miep.relay_dispatch_into(x.to(DEV), idxd, wts.to(DEV), ntpr, ntp_rdma, ntpe, h, rh, rdma_x, recv_x,
+                             recv_topk_idx=rti, recv_topk_weights=rtw)
+    lay = oracle.layout(idx.numpy(), S, E, R)
+    ref = oracle.relay_dispatch(wl.bf16_bits(x), idx.numpy(), wts.numpy(), lay["is_token_in_rank"], S=S, E=E, R=R,
+                                C=C, rdma_capacity=rcap, capacity=cap)
+    torch.cuda.synchronize()
+    assert int(rh.recv_rdma_offset[-1]) == gtotal and int(h.recv_rank_offset[-1]) == total
+    ng, nr = min(gtotal, rcap), min(total, cap)
+    assert np.array_equal(npy(rh.send_nvl_head)[:ng], ref["send_nvl_head"][:ng])
+    assert np.array_equal(u16(rdma_x)[:ng], ref["rdma_x"][:ng])
+    # the oracle leaves unwritten receive rows at zero: compare the rows it wrote
+    written = np.zeros(cap, bool)
+    off = ref["recv_rank_offset"]
+    for r in range(R):
+        for q in range(ref["recv_rank_offset"][r + 1] - off[r]):
+            row = off[r] + q
+            if row < cap:
+                written[row] = (ref["recv_src_idx"][row] >= 0)
+    assert np.array_equal(u16(recv_x)[written], ref["recv_x"][written])
+    assert np.array_equal(npy(rti)[written], ref["recv_topk_idx"][written])
+    # nothing else was touched
+    assert np.all(u16(recv_x)[~written] == np.uint16(0x4040))       # bf16 3.0
+    if mode == "worst-case":
+        assert np.all(u16(rdma_x)[gtotal:] == np.uint16(0x40A0))    # bf16 5.0
+        assert np.all(npy(rti)[total:] == -9)
+    # the two-level combine on the same capacities
+    y = wl.expert_outputs(cap, H, seed=6)
+    cx, _ = miep.relay_combine(y.to(DEV), h, rh)
+    rc = oracle.relay_combine(wl.bf16_bits(y), None, ref["recv_rank_offset"], ref["recv_rdma_offset"],
+                              ref["send_nvl_head"], ref["send_rdma_head"], S=S)
+    assert np.array_equal(u16(cx), rc["combined_x"])
