@@ -475,6 +475,31 @@ def summarize_stats(stats_dir, out_md, command, title="normal workload step"):
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_counters(dirs, out_md, commands, title):
+    """Any number of rocprofv3 --pmc runs -> per-kernel mean of every counter
+    (per dispatch), one markdown table per run."""
+    import csv
+    import glob
+    from collections import defaultdict
+    lines = ["# Hardware counters: %s (rocprofv3 --pmc, mean per dispatch)" % title, "",
+             "Commands (from the repo root on the GPU box; `R` = repo root):", "", "```"] + list(commands) + \
+            ["```", ""]
+    for d in dirs:
+        agg = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(glob.glob(os.path.join(d, "*_counter_collection.csv"))[0])):
+            k = _kernel_key(r["Kernel_Name"])
+            if k is not None:
+                agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        names = sorted({c for v in agg.values() for c in v})
+        lines += ["| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+        for k in sorted(agg):
+            lines.append("| %s | " % k + " | ".join("%.0f" % (sum(agg[k][c]) / len(agg[k][c])) if agg[k][c] else "-"
+                                                 for c in names) + " |")
+        lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_pmc(fetch_dir, write_dir, out_json, out_md, commands, copy_mib):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each miep kernel, scaled by
     what the same counters read for the runtime's plain copy kernel of known size."""
@@ -541,6 +566,8 @@ def main():
     ap.add_argument("--summarize-stats", metavar="DIR", help="write profiles/ summary of a rocprofv3 --stats run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/<stats-name>.md: per-kernel means of any rocprofv3 --pmc runs")
     ap.add_argument("--command", action="append", default=[], help="command line(s) recorded in a summary")
     ap.add_argument("--stats-name", default="normal_step_kernels",
                     help="file name (without .md) of the --summarize-stats output under profiles/")
@@ -553,6 +580,10 @@ def main():
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, os.path.join(PROFILES, args.stats_name + ".md"),
                         "\n".join(args.command), args.stats_title)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, os.path.join(PROFILES, args.stats_name + ".md"), args.command,
+                           args.stats_title)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], os.path.join(PROFILES, "normal_hbm_traffic.json"),
