@@ -52,6 +52,8 @@ miep_status check_problem(const miep_problem* p) {
   if (p->num_topk > 64) return fail(MIEP_EUNSUPPORTED, "num_topk > 64");
   if (static_cast<int64_t>(p->num_src) * p->num_tokens > (1ll << 31) - 1)
     return fail(MIEP_EUNSUPPORTED, "more than 2^31-1 tokens");
+  if (p->num_src > (1 << 20)) return fail(MIEP_EUNSUPPORTED, "num_src > 2^20");
+  if (p->num_channels > 1024) return fail(MIEP_EUNSUPPORTED, "num_channels > 1024");
   return ok();
 }
 

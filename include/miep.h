@@ -55,13 +55,13 @@ typedef enum miep_xkind {
 
 /* Sizes of one normal-mode problem.  N = num_src * num_tokens tokens. */
 typedef struct miep_problem {
-  int32_t num_src;          /* S: source partitions (the sending ranks)                  */
+  int32_t num_src;          /* S: source partitions (the sending ranks), <= 2^20         */
   int32_t num_tokens;       /* T: tokens per source partition                             */
   int32_t hidden;           /* H: channels per token                                      */
   int32_t num_topk;         /* K: experts per token                                       */
   int32_t num_experts;      /* E: experts; expert e lives on rank e / (E / R)              */
   int32_t num_ranks;        /* R: receiving ranks, 1..256; R > 8 needs R % 8 == 0          */
-  int32_t num_channels;     /* C: channels splitting each source's tokens (ceil(T/C) each) */
+  int32_t num_channels;     /* C: channels splitting each source's tokens (ceil(T/C) each), <= 1024 */
   int32_t expert_alignment; /* a >= 1: per-expert receive counts rounded up to a multiple  */
 } miep_problem;
 

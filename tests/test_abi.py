@@ -118,6 +118,17 @@ def test_dispatch_validation(lib):
     assert rc == _lib.MIEP_EINVAL
 
 
+def test_problem_bounds(lib):
+    h = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, 0)
+    for bad, code in ((dict(num_src=(1 << 20) + 1, num_tokens=0), _lib.MIEP_EUNSUPPORTED),
+                      (dict(num_channels=1025), _lib.MIEP_EUNSUPPORTED),
+                      (dict(num_topk=65), _lib.MIEP_EUNSUPPORTED),
+                      (dict(num_ranks=512, num_experts=512), _lib.MIEP_EUNSUPPORTED),
+                      (dict(num_src=70000, num_tokens=40000), _lib.MIEP_EUNSUPPORTED)):
+        p = _problem(**bad)
+        assert lib.miep_combine(ctypes.byref(p), 16, None, None, None, ctypes.byref(h), 16, None, None) == code, bad
+
+
 def test_combine_validation(lib):
     p = _problem()
     h = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, 100)
