@@ -33,7 +33,8 @@ from ._lib import MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # noqa: F401
 __all__ = ["Handle", "MiepError", "get_dispatch_layout", "get_dispatch_layout_into", "dispatch", "dispatch_into", "cached_dispatch",
            "cached_dispatch_into", "combine", "combine_into", "low_latency_dispatch", "low_latency_dispatch_into",
            "low_latency_combine", "low_latency_combine_into", "update_mask_buffer", "clean_mask_buffer",
-           "RelayHandle", "relay_dispatch", "relay_dispatch_into", "relay_combine", "relay_combine_into",
+           "RelayHandle", "relay_dispatch", "relay_dispatch_into", "relay_cached_dispatch",
+           "relay_cached_dispatch_into", "relay_combine", "relay_combine_into",
            "query_mask_buffer", "ll_msg_bytes", "version"]
 
 
@@ -612,6 +613,39 @@ def relay_dispatch(x: torch.Tensor, topk_idx: Optional[torch.Tensor], topk_weigh
                         num_tokens_per_expert, handle, relay, rdma_x, recv_x, rdma_x_scales, recv_x_scales,
                         recv_topk_idx, recv_topk_weights, nrte, x_scales, cast_to_fp8, round_scale, expert_alignment)
     return recv_x, recv_x_scales, recv_topk_idx, recv_topk_weights, nrte, handle, relay, rdma_x, rdma_x_scales
+
+
+def relay_cached_dispatch_into(x, handle: Handle, relay: RelayHandle, rdma_x, recv_x, rdma_x_scales=None,
+                               recv_x_scales=None, x_scales=None, cast_to_fp8: bool = False,
+                               round_scale: bool = False) -> None:
+    """Cached dispatch through the relay into preallocated buffers (allocates nothing)."""
+    kind = _x_kind(x, cast_to_fp8)
+    _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
+    H = x.shape[1]
+    rc = relay.rdma_capacity
+    if rdma_x.dim() != 2 or rdma_x.shape[0] < rc or rdma_x.shape[1] != H:
+        raise ValueError("rdma_x must be [>= %d, %d]" % (rc, H))
+    if kind != X_BF16 and (rdma_x_scales is None or rdma_x_scales.shape[0] < rc):
+        raise ValueError("rdma_x_scales must be [>= %d, %d]" % (rc, H // 128))
+    p = handle.problem(H)
+    h = handle.c()
+    rh = relay.c()
+    _lib.check(_lib.load().miep_relay_cached_dispatch(ctypes.byref(p), _ptr(x), kind, _ptr(x_scales),
+                                                      int(round_scale), ctypes.byref(h), ctypes.byref(rh),
+                                                      _ptr(rdma_x), _ptr(rdma_x_scales), _ptr(recv_x),
+                                                      _ptr(recv_x_scales), _stream(x)))
+
+
+def relay_cached_dispatch(x: torch.Tensor, handle: Handle, relay: RelayHandle, x_scales: Optional[torch.Tensor] = None,
+                          cast_to_fp8: bool = False, round_scale: bool = False):
+    """Dispatch a new x along the handles of an earlier relay dispatch (no top-k inputs).
+    Returns (recv_x, recv_x_scales)."""
+    kind = _x_kind(x, cast_to_fp8)
+    recv_x, recv_x_scales = _recv_buffers(x, kind, handle.recv_capacity, x.device)
+    rdma_x, rdma_x_scales = _recv_buffers(x, kind, relay.rdma_capacity, x.device)
+    relay_cached_dispatch_into(x, handle, relay, rdma_x, recv_x, rdma_x_scales, recv_x_scales, x_scales, cast_to_fp8,
+                               round_scale)
+    return recv_x, recv_x_scales
 
 
 def relay_combine_into(y, handle: Handle, relay: RelayHandle, rdma_y, combined_x, recv_topk_weights=None,

@@ -418,6 +418,43 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
   return hip_status(miep::launch_pack(a2, s), "relay forward launch");
 }
 
+miep_status miep_relay_cached_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                                       int32_t round_scale, const miep_handle* h, const miep_relay_handle* rh,
+                                       void* rdma_x, float* rdma_x_scales, void* recv_x, float* recv_x_scales,
+                                       void* stream) {
+  miep_status st = check_problem(p);
+  if (st != MIEP_OK) return st;
+  if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
+  if ((st = check_handle(p, h, false)) != MIEP_OK) return st;
+  if ((st = check_relay(p, rh)) != MIEP_OK) return st;
+  const int G = p->num_ranks / 8;
+  if (h->recv_capacity > 0 && !recv_x) return fail(MIEP_EINVAL, "recv_x is NULL");
+  if (rh->rdma_capacity > 0 && !rdma_x) return fail(MIEP_EINVAL, "rdma_x is NULL");
+  if (!aligned16(recv_x) || !aligned16(rdma_x)) return fail(MIEP_EUNSUPPORTED, "recv_x and rdma_x must be 16-byte aligned");
+  if (x_kind != MIEP_X_BF16 && ((h->recv_capacity > 0 && !recv_x_scales) || (rh->rdma_capacity > 0 && !rdma_x_scales)))
+    return fail(MIEP_EINVAL, "recv_x_scales / rdma_x_scales is NULL for an FP8 dispatch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  miep::PackArgs a1 = pack_args(p, x, x_kind, x_scales, round_scale, h, rdma_x, rdma_x_scales);
+  a1.R = G;
+  a1.send_head = rh->send_rdma_head;
+  a1.off = rh->recv_rdma_offset;
+  a1.capacity = rh->rdma_capacity;
+  a1.meta = 0;
+  hipError_t e = miep::launch_pack(a1, s);
+  if (e != hipSuccess) return hip_status(e, "relay pack launch");
+  const int fwd_kind = x_kind == MIEP_X_BF16 ? MIEP_X_BF16 : MIEP_X_FP8;
+  miep::PackArgs a2 = pack_args(p, rdma_x, fwd_kind, rdma_x_scales, 0, h, recv_x, recv_x_scales);
+  a2.N = rh->rdma_capacity;
+  a2.R = 8;
+  a2.send_head = rh->send_nvl_head;
+  a2.meta = 0;
+  a2.count = rh->recv_rdma_offset + G;
+  a2.group_off = rh->recv_rdma_offset;
+  a2.groups = G;
+  a2.group_w = 8;
+  return hip_status(miep::launch_pack(a2, s), "relay forward launch");
+}
+
 miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
                                const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
                                const miep_relay_handle* rh, uint16_t* rdma_y, float* rdma_w, uint16_t* combined_x,

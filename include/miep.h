@@ -202,6 +202,17 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
                                 float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
                                 const miep_handle* h, const miep_relay_handle* rh, void* stream);
 
+/* relay_cached_dispatch -- [Ch4] 4.1 cached branch through the relay: with
+ * the handles of an earlier miep_relay_dispatch of the same routing, move
+ * only x (and its scales) through the group rows to the ranks' rows; no
+ * top-k arguments.  Reads h->send_head's placement only through rh
+ * (send_rdma_head, recv_rdma_offset, send_nvl_head) and h->recv_rank_offset;
+ * arguments as in miep_relay_dispatch. */
+miep_status miep_relay_cached_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
+                                       int32_t round_scale, const miep_handle* h, const miep_relay_handle* rh,
+                                       void* rdma_x, float* rdma_x_scales, void* recv_x, float* recv_x_scales,
+                                       void* stream);
+
 /* relay_combine -- the two-level combine, the reverse of miep_relay_dispatch
  * ([NvLL] normal mode reduces inside the node first, then once more across
  * nodes; [Ch4] 4.4: additions only, weights reduced separately).  First

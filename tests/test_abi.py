@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
-              "miep_relay_dispatch", "miep_relay_combine",
+              "miep_relay_dispatch", "miep_relay_cached_dispatch", "miep_relay_combine",
               "miep_ll_dispatch", "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query"):
         assert f in names
     assert set(names) == set(_lib.EXPORTS)

@@ -279,3 +279,29 @@ def test_relay_capacities(mode):
     rc = oracle.relay_combine(wl.bf16_bits(y), None, ref["recv_rank_offset"], ref["recv_rdma_offset"],
                               ref["send_nvl_head"], ref["send_rdma_head"], S=S)
     assert np.array_equal(u16(cx), rc["combined_x"])
+
+
+@pytest.mark.parametrize("cast", [False, True], ids=["bf16", "fp8-cast"])
+def test_relay_cached_dispatch(cast):
+    """A new x through the handles of an earlier relay dispatch equals a fresh relay dispatch of it."""
+    S, T, H, E, R, K, C = 4, 150, 512, 64, 32, 6, 5
+    say("relay cached", cast)
+    w, x, idx, wts = _inputs(S, T, H, E, R, K, C, 8, "masked-dup-oob")
+    idxd = idx.to(DEV)
+    ntpr, ntp_rdma, ntpe, itr = miep.get_dispatch_layout(idxd, E, R, S)
+    out = miep.relay_dispatch(x.to(DEV), idxd, wts.to(DEV), ntpr, ntp_rdma, itr, ntpe, E, C, cast_to_fp8=cast)
+    h, rh = out[5], out[6]
+    x2 = wl.activations(w.N, H, torch.Generator().manual_seed(77))
+    recv2, recv2_s = miep.relay_cached_dispatch(x2.to(DEV), h, rh, cast_to_fp8=cast)
+    fresh = miep.relay_dispatch(x2.to(DEV), idxd, wts.to(DEV), ntpr, ntp_rdma, itr, ntpe, E, C, cast_to_fp8=cast)
+    lay = oracle.layout(idx.numpy(), S, E, R)
+    ref = oracle.relay_dispatch(wl.bf16_bits(x2), idx.numpy(), wts.numpy(), lay["is_token_in_rank"], S=S, E=E, R=R,
+                                C=C, x_kind=oracle.X_BF16_CAST_FP8 if cast else oracle.X_BF16)
+    torch.cuda.synchronize()
+    if cast:
+        assert np.array_equal(u8(recv2), ref["recv_x"])
+        assert np.array_equal(npy(recv2_s).view(np.uint32), ref["recv_x_scales"].view(np.uint32))
+        assert torch.equal(recv2.view(torch.uint8), fresh[0].view(torch.uint8))
+    else:
+        assert np.array_equal(u16(recv2), ref["recv_x"])
+        assert torch.equal(recv2, fresh[0])
