@@ -116,6 +116,14 @@ __device__ __forceinline__ float group16_max(float v) {
   return v;
 }
 
+// Max over the 8 lanes that hold one 128-channel group (16 channels each).
+__device__ __forceinline__ float group8_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 8));
+  v = fmaxf(v, __shfl_xor(v, 2, 8));
+  v = fmaxf(v, __shfl_xor(v, 4, 8));
+  return v;
+}
+
 // 8 bf16 channels (one 16-byte vector) -> amax of their magnitudes.
 __device__ __forceinline__ float absmax8(const v4u& v) {
   float m = fabsf(bf16_lo(v.x));
@@ -147,6 +155,13 @@ __device__ __forceinline__ v2u cast8(const v4u& v, float scale) {
   r.x = e4m3x4(bf16_lo(v.x) * scale, bf16_hi(v.x) * scale, bf16_lo(v.y) * scale, bf16_hi(v.y) * scale);
   r.y = e4m3x4(bf16_lo(v.z) * scale, bf16_hi(v.z) * scale, bf16_lo(v.w) * scale, bf16_hi(v.w) * scale);
   return r;
+}
+
+// 16 bf16 channels (two adjacent 16-byte vectors) -> 16 E4M3 codes, one
+// 16-byte store.
+__device__ __forceinline__ v4u cast16(const v4u& a, const v4u& b, float scale) {
+  const v2u lo = cast8(a, scale), hi = cast8(b, scale);
+  return v4u{lo.x, lo.y, hi.x, hi.y};
 }
 
 // Rank set of one token (up to 64*MW ranks) held in registers; selects

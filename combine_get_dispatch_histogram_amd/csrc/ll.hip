@@ -80,40 +80,53 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   if (tid == 0 && blockIdx.y == 0) a.msg_count[l * a.R + s] = n;
 
   // messages: one wavefront per (message, row slice); the slice's 16-byte
-  // loads are all issued before any of its stores
-  const int nv = a.H / 8;              // 16-byte vectors of 8 bf16
+  // loads are all issued before any of its stores.  A lane's unit is one
+  // 16-byte vector of 8 bf16, or with FP8 a pair of them (16 channels -> 16
+  // codes in one 16-byte store; a 128-channel group is 8 lanes).
+  const int nv = a.H / 8;
+  const int units = a.use_fp8 ? nv / 2 : nv;
   const int span = kWave * VPL;
-  const int nsl = (nv + span - 1) / span;
+  const int nsl = (units + span - 1) / span;
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x) + static_cast<int64_t>(s) * a.T * 2 * a.H;
   for (int task = blockIdx.y * (kLLThreads / kWave) + w; task < n * nsl; task += gridDim.y * (kLLThreads / kWave)) {
     const int j = task / nsl;
-    const int v0 = (task - j * nsl) * span;
+    const int u0 = (task - j * nsl) * span;
     const int t = slot_tok[j];
     uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
-    if (v0 == 0 && lane == 0) *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
-    const uint8_t* xrow = reinterpret_cast<const uint8_t*>(a.x) + (static_cast<int64_t>(s) * a.T + t) * 2 * a.H;
-    v4u d[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int v = v0 + i * kWave + lane;
-      if (v < nv) d[i] = ld16<false>(xrow + static_cast<int64_t>(v) * 16);
-    }
+    if (u0 == 0 && lane == 0) *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
+    const uint8_t* xrow = xsrc + static_cast<int64_t>(t) * 2 * a.H;
     if (a.use_fp8) {
+      v4u d[VPL][2];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int p = u0 + i * kWave + lane;
+        if (p < units) {
+          d[i][0] = ld16<false>(xrow + static_cast<int64_t>(p) * 32);
+          d[i][1] = ld16<false>(xrow + static_cast<int64_t>(p) * 32 + 16);
+        }
+      }
       float* scales = reinterpret_cast<float*>(msg + 16 + a.H);
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
-        const int v = v0 + i * kWave + lane;
-        const float amax = group16_max(v < nv ? absmax8(d[i]) : 0.0f);
+        const int p = u0 + i * kWave + lane;
+        const float amax = group8_max(p < units ? fmaxf(absmax8(d[i][0]), absmax8(d[i][1])) : 0.0f);
         float sci;
         const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
-        if (v < nv) {
-          st8<false>(msg + 16 + static_cast<int64_t>(v) * 8, cast8(d[i], sc));
-          if ((lane & 15) == 0) scales[v / 16] = sci;
+        if (p < units) {
+          st16<false>(msg + 16 + static_cast<int64_t>(p) * 16, cast16(d[i][0], d[i][1], sc));
+          if ((lane & 7) == 0) scales[p / 8] = sci;
         }
       }
     } else {
+      v4u d[VPL];
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
-        const int v = v0 + i * kWave + lane;
+        const int v = u0 + i * kWave + lane;
+        if (v < nv) d[i] = ld16<false>(xrow + static_cast<int64_t>(v) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int v = u0 + i * kWave + lane;
         if (v < nv) st16<false>(msg + 16 + static_cast<int64_t>(v) * 16, d[i]);
       }
     }
@@ -195,9 +208,16 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
   if (blocks == 0) return hipSuccess;
   const Tuning& tu = tuning();
   const int split = tu.ll_split > 0 ? tu.ll_split : kLLSplit;
-  // two 16-byte vectors per lane per task when a bf16 row is a multiple of
-  // 128 vectors (measured best with 8 workgroups per (l, s) block)
-  const int vpl = tu.ll_vpl > 0 ? tu.ll_vpl : ((a.H / 8) % (2 * kWave) == 0 ? 2 : 8);
+  // bf16: two 16-byte vectors per lane per task when a row is a multiple of
+  // 128 vectors (measured best with 8 workgroups per (l, s) block); FP8: one
+  // pair of vectors (16 channels) per lane when a row is 64 pairs' multiple
+  int vpl;
+  if (tu.ll_vpl > 0)
+    vpl = tu.ll_vpl;
+  else if (a.use_fp8)
+    vpl = (a.H / 16) % kWave == 0 ? 1 : 8;
+  else
+    vpl = (a.H / 8) % (2 * kWave) == 0 ? 2 : 8;
   switch (vpl) {
     case 1: return launch_ll_vpl<1>(a, blocks, split, st);
     case 2: return launch_ll_vpl<2>(a, blocks, split, st);

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   // Every independent global load is issued before the first wait: the
   // first token tile's membership rows and up to kB rank / expert counts per
   // thread.
-  constexpr int kB = 8;
+  constexpr int kB = MW == 1 ? 16 : 8;
   const int nt = blockDim.x;
   const bool do_e = a.nrte != nullptr && a.ntpe != nullptr;
   RankMask<MW> first;
@@ -160,33 +160,49 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       run[r] = acc;
     }
     __syncthreads();
-    // pass 2: exclusive rank within source s -> send_head, channel prefixes
+    // pass 2: exclusive rank within source s -> send_head, channel prefixes.
+    // Lane j holds rank r0 + j's wavefront base and rank base (two LDS reads
+    // per 64 ranks, no dependent LDS chain); per-rank values come by readlane.
     const bool last_in_channel = valid && ((t % tc) == tc - 1 || t == T - 1);
-    const int c = t / tc;
-    for (int r0 = 0; r0 < R; r0 += 4) {
-      int v[4];
+    const uint64_t clast = ballot(last_in_channel);
+    for (int r0 = 0; r0 < R; r0 += kWave) {
+      const int rend = R - r0 < kWave ? R - r0 : kWave;
+      const int wt_l = lane < rend ? wt[w][r0 + lane] : 0;
+      const int base_l = lane < rend ? base[r0 + lane] : 0;
+      uint64_t myb = 0;                                // lane j: this wavefront's ballot for rank r0 + j
+      for (int j0 = 0; j0 < rend; j0 += 4) {
+        int v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = r0 + j;
-        v[j] = -1;
-        if (r < R) {
-          const bool bit = m.get(r) != 0;
-          const uint64_t b = ballot(bit);
-          const int pre = wt[w][r] + __popcll(b & lanemask_lt());
-          if (bit) v[j] = base[r] + pre;
-          if (last_in_channel) {
-            const int inc = pre + (bit ? 1 : 0);
-            a.cpm[(static_cast<int64_t>(s) * R + r) * C + c] = inc;
-            a.rcpm[(static_cast<int64_t>(r) * S + s) * C + c] = base[r] + inc;
+        for (int q = 0; q < 4; ++q) {
+          const int j = j0 + q;
+          v[q] = -1;
+          if (j < rend) {
+            const bool bit = m.get(r0 + j) != 0;
+            const uint64_t b = ballot(bit);
+            myb = lane == j ? b : myb;
+            if (bit) v[q] = readlane(base_l, j) + readlane(wt_l, j) + __popcll(b & lanemask_lt());
+          }
+        }
+        if (valid) {
+          int32_t* dst = a.send_head + n * R + r0 + j0;
+          if ((R & 3) == 0) {
+            *reinterpret_cast<int4*>(dst) = make_int4(v[0], v[1], v[2], v[3]);
+          } else {
+            for (int q = 0; q < 4 && j0 + q < rend; ++q) dst[q] = v[q];
           }
         }
       }
-      if (valid) {
-        int32_t* dst = a.send_head + n * R + r0;
-        if ((R & 3) == 0) {
-          *reinterpret_cast<int4*>(dst) = make_int4(v[0], v[1], v[2], v[3]);
-        } else {
-          for (int j = 0; j < 4 && r0 + j < R; ++j) dst[j] = v[j];
+      // channel prefixes: one wavefront-wide store per channel that ends on
+      // a token of this wavefront (lane j writes rank r0 + j)
+      for (uint64_t cl = clast; cl != 0; cl &= cl - 1) {
+        const int L = __builtin_ctzll(cl);
+        const int cc = readlane(t, L) / tc;
+        const uint64_t upto = L == kWave - 1 ? ~0ull : ((2ull << L) - 1);   // lanes 0..L
+        if (lane < rend) {
+          const int inc = wt_l + __popcll(myb & upto);
+          const int r = r0 + lane;
+          a.cpm[(static_cast<int64_t>(s) * R + r) * C + cc] = inc;
+          a.rcpm[(static_cast<int64_t>(r) * S + s) * C + cc] = base_l + inc;
         }
       }
     }

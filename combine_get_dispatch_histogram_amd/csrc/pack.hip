@@ -99,6 +99,52 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   const uint8_t* xrow = static_cast<const uint8_t*>(a.x) + n * in_row_bytes;
   uint8_t* recv = static_cast<uint8_t*>(a.recv_x);
   const int span = kWave * VPL;
+  if constexpr (KIND == kPackCastFp8) {
+    // Fused cast: lane holds pairs of adjacent 16-byte vectors (16
+    // channels), so a 128-channel group is 8 lanes and every code store is
+    // one 16-byte vector per lane (1 KiB per wavefront).  nv is a multiple
+    // of 16, so a group is either entirely in range or entirely out.
+    const int np = nv / 2;
+    for (int p0 = slice * span; p0 < np; p0 += nslices * span) {
+      v4u d[VPL][2];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int pi = p0 + j * kWave + lane;
+        if (pi < np) {
+          d[j][0] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32);
+          d[j][1] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32 + 16);
+        }
+      }
+      v4u q[VPL];
+      float sci[VPL];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int pi = p0 + j * kWave + lane;
+        const float amax = group8_max(pi < np ? fmaxf(absmax8(d[j][0]), absmax8(d[j][1])) : 0.0f);
+        const float sc = fp8_scales(amax, a.round_scale != 0, &sci[j]);
+        if (pi < np) q[j] = cast16(d[j][0], d[j][1], sc);
+      }
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        uint64_t m = dmask[i];
+        while (m) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          const int64_t row = readlane(dst[i], b);
+          uint8_t* orow = recv + row * out_row_bytes;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int pi = p0 + j * kWave + lane;
+            if (pi < np) {
+              st16<(NT & 2) != 0>(orow + static_cast<int64_t>(pi) * 16, q[j]);
+              if ((lane & 7) == 0) a.recv_x_scales[row * G + pi / 8] = sci[j];
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
   for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
     v4u d[VPL];
 #pragma unroll
@@ -106,50 +152,18 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
       const int v = v0 + j * kWave + lane;
       if (v < nv) d[j] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(v) * 16);
     }
-    if constexpr (KIND == kPackCastFp8) {
-      // 16 lanes hold one 128-channel group; nv is a multiple of 16, so a
-      // group is either entirely in range or entirely out.
-      v2u q[VPL];
-      float sci[VPL];
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        const int v = v0 + j * kWave + lane;
-        const float amax = group16_max(v < nv ? absmax8(d[j]) : 0.0f);
-        const float sc = fp8_scales(amax, a.round_scale != 0, &sci[j]);
-        if (v < nv) q[j] = cast8(d[j], sc);
-      }
+    for (int i = 0; i < MW; ++i) {
+      uint64_t m = dmask[i];
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        const int64_t row = readlane(dst[i], b);
+        uint8_t* orow = recv + row * out_row_bytes;
 #pragma unroll
-      for (int i = 0; i < MW; ++i) {
-        uint64_t m = dmask[i];
-        while (m) {
-          const int b = __builtin_ctzll(m);
-          m &= m - 1;
-          const int64_t row = readlane(dst[i], b);
-          uint8_t* orow = recv + row * out_row_bytes;
-#pragma unroll
-          for (int j = 0; j < VPL; ++j) {
-            const int v = v0 + j * kWave + lane;
-            if (v < nv) {
-              st8<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 8, q[j]);
-              if ((lane & 15) == 0) a.recv_x_scales[row * G + v / 16] = sci[j];
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < MW; ++i) {
-        uint64_t m = dmask[i];
-        while (m) {
-          const int b = __builtin_ctzll(m);
-          m &= m - 1;
-          const int64_t row = readlane(dst[i], b);
-          uint8_t* orow = recv + row * out_row_bytes;
-#pragma unroll
-          for (int j = 0; j < VPL; ++j) {
-            const int v = v0 + j * kWave + lane;
-            if (v < nv) st16<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 16, d[j]);
-          }
+        for (int j = 0; j < VPL; ++j) {
+          const int v = v0 + j * kWave + lane;
+          if (v < nv) st16<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 16, d[j]);
         }
       }
     }
@@ -209,26 +223,31 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
       }
     }
   }
-  const int nv = a.H / 8;
+  // lane holds VPL pairs of adjacent 16-byte vectors (16 channels each), so
+  // a 128-channel group is 8 lanes and each code store is 16 bytes per lane
+  const int np = a.H / 16;
   const uint8_t* xrow = static_cast<const uint8_t*>(a.x) + n * 2 * static_cast<int64_t>(a.H);
   uint8_t* recv = static_cast<uint8_t*>(a.recv_x);
-  const int v0 = slice * kWave * VPL;
-  v4u d[VPL];
+  const int p0 = slice * kWave * VPL;
+  v4u d[VPL][2];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
-    const int v = v0 + j * kWave + lane;
-    if (v < nv) d[j] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(v) * 16);
+    const int pi = p0 + j * kWave + lane;
+    if (pi < np) {
+      d[j][0] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32);
+      d[j][1] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32 + 16);
+    }
   }
-  v2u q[VPL];
+  v4u q[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
-    const int v = v0 + j * kWave + lane;
-    const float amax = group16_max(v < nv ? absmax8(d[j]) : 0.0f);
+    const int pi = p0 + j * kWave + lane;
+    const float amax = group8_max(pi < np ? fmaxf(absmax8(d[j][0]), absmax8(d[j][1])) : 0.0f);
     float sci;
     const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
-    if (v < nv) {
-      q[j] = cast8(d[j], sc);
-      if ((lane & 15) == 0) row_scales[v / 16] = sci;
+    if (pi < np) {
+      q[j] = cast16(d[j][0], d[j][1], sc);
+      if ((lane & 7) == 0) row_scales[pi / 8] = sci;
     }
   }
 #pragma unroll
@@ -240,8 +259,8 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
       uint8_t* orow = recv + static_cast<int64_t>(readlane(dst[i], b)) * a.H;
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
-        const int v = v0 + j * kWave + lane;
-        if (v < nv) st8<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 8, q[j]);
+        const int pi = p0 + j * kWave + lane;
+        if (pi < np) st16<(NT & 2) != 0>(orow + static_cast<int64_t>(pi) * 16, q[j]);
       }
     }
   }
@@ -262,8 +281,8 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
 
 template <int VPL, int NT>
 static hipError_t launch_pack_cast_vpl(const PackArgs& a, hipStream_t st) {
-  const int nv = a.H / 8;
-  const int waves = (nv + kWave * VPL - 1) / (kWave * VPL);
+  const int np = a.H / 16;   // pairs of 16-byte input vectors
+  const int waves = (np + kWave * VPL - 1) / (kWave * VPL);
   if (a.R <= 64)
     hipLaunchKernelGGL((pack_cast_kernel<VPL, 1, NT>), dim3(static_cast<unsigned>(a.N)), dim3(waves * kWave), 0, st,
                        a);
@@ -273,14 +292,14 @@ static hipError_t launch_pack_cast_vpl(const PackArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Smallest vectors-per-lane (at least `vpl_hint`) that fits the row in 16
-// wavefronts.
+// Smallest vector pairs per lane (at least `ppl_hint`) that fits the row in
+// 16 wavefronts.
 template <int NT>
-static hipError_t launch_pack_cast(const PackArgs& a, int vpl_hint, hipStream_t st) {
-  const int nv = a.H / 8;
-  if (vpl_hint <= 1 && nv <= 16 * kWave) return launch_pack_cast_vpl<1, NT>(a, st);
-  if (vpl_hint <= 2 && nv <= 32 * kWave) return launch_pack_cast_vpl<2, NT>(a, st);
-  if (vpl_hint <= 4 && nv <= 64 * kWave) return launch_pack_cast_vpl<4, NT>(a, st);
+static hipError_t launch_pack_cast(const PackArgs& a, int ppl_hint, hipStream_t st) {
+  const int np = a.H / 16;
+  if (ppl_hint <= 1 && np <= 16 * kWave) return launch_pack_cast_vpl<1, NT>(a, st);
+  if (ppl_hint <= 2 && np <= 32 * kWave) return launch_pack_cast_vpl<2, NT>(a, st);
+  if (ppl_hint <= 4 && np <= 64 * kWave) return launch_pack_cast_vpl<4, NT>(a, st);
   return launch_pack_cast_vpl<8, NT>(a, st);
 }
 
@@ -321,12 +340,14 @@ static hipError_t launch_pack_nt(const PackArgs& a, int vpl, int nslices, int nt
 hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
   const Tuning& tu = tuning();
-  const int nv = a.kind == kPackFp8 ? a.H / 16 : a.H / 8;
-  // default geometry: one 16-byte vector per lane, i.e. every wavefront moves
-  // one 1 KiB piece of a row to each destination (hidden 7168 bf16 -> 14
+  // per-lane unit: a 16-byte input vector, or for the fused cast a pair of
+  // them (16 channels -> one 16-byte vector of codes)
+  const int nv = a.kind == kPackFp8 ? a.H / 16 : (a.kind == kPackCastFp8 ? a.H / 16 : a.H / 8);
+  // default geometry: one unit per lane, i.e. every wavefront writes one
+  // 1 KiB piece of a row to each destination (hidden 7168 bf16 -> 14
   // wavefronts per token).  Measured on MI355X, writes spread as many small
   // per-wavefront pieces reach ~6.7 TB/s while 4-16 KiB per wavefront drop to
-  // 5.4-5.9 TB/s.  Rows that are not a multiple of 64 vectors keep 8.
+  // 5.4-5.9 TB/s.  Rows that are not a multiple of 64 units keep 8.
   int vpl = tu.pack_vpl > 0 ? tu.pack_vpl : (nv % kWave == 0 ? 1 : 8);
   int span = vpl * kWave;
   int nslices = tu.pack_slices > 0 ? tu.pack_slices : (nv + span - 1) / span;
@@ -340,7 +361,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
       // The token-per-workgroup kernel has no forwarding mode.
       if ((tu.cast_tpb > 0 || (tu.cast_tpb < 0 && a.meta)) && a.group_off == nullptr && a.count == nullptr &&
           a.src_tok == nullptr) {
-        const int hint = tu.pack_vpl > 0 ? tu.pack_vpl : 2;
+        const int hint = tu.pack_vpl > 0 ? tu.pack_vpl : 1;   // 1 pair = 2 vectors per lane
         switch (tu.pack_nt) {
           case 0: return launch_pack_cast<0>(a, hint, st);
           case 1: return launch_pack_cast<1>(a, hint, st);
