@@ -48,7 +48,6 @@ struct alignas(16) v4u { uint32_t x, y, z, w; };
 struct alignas(8) v2u { uint32_t x, y; };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <bool NT>
 __device__ __forceinline__ v4u ld16(const void* p) {
@@ -67,16 +66,6 @@ __device__ __forceinline__ void st16(void* p, const v4u& v) {
     __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
   } else {
     *reinterpret_cast<v4u*>(p) = v;
-  }
-}
-
-template <bool NT>
-__device__ __forceinline__ void st8(void* p, const v2u& v) {
-  if constexpr (NT) {
-    const u32x2 t = {v.x, v.y};
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
-  } else {
-    *reinterpret_cast<v2u*>(p) = v;
   }
 }
 
@@ -105,15 +94,6 @@ __device__ __forceinline__ float fp8_scales(float amax, bool round_scale, float*
   }
   *scale_inv = amax / 448.0f;
   return 448.0f / amax;
-}
-
-// Max over the 16 lanes that hold one 128-channel group (8 channels each).
-__device__ __forceinline__ float group16_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 16));
-  v = fmaxf(v, __shfl_xor(v, 2, 16));
-  v = fmaxf(v, __shfl_xor(v, 4, 16));
-  v = fmaxf(v, __shfl_xor(v, 8, 16));
-  return v;
 }
 
 // Max over the 8 lanes that hold one 128-channel group (16 channels each).

@@ -18,7 +18,7 @@
 // deterministic.  Two kernels, both kLLSplit workgroups per (l, s) block that
 // share its messages (the slot scan is repeated by each; it is tiny):
 //   send: scan source s's top-k for the expert (LDS scan), then cast and
-//         write its messages (16-byte loads, 8/16-byte stores);
+//         write its messages (16-byte loads and stores);
 //   recv: exclusive scan of the counts over s gives the packed range, then
 //         a 16-byte copy of payloads and scales.
 #include "device.h"

@@ -171,10 +171,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
 }
 
 // Fused FP8 cast, one token per workgroup: wavefront w casts row slice w
-// (64 lanes x VPL 16-byte vectors) and stores its codes to every
-// destination; the row's H/128 scales are gathered in LDS and leave as one
-// contiguous store per destination (scattered 16-byte scale pieces written
-// by separate wavefronts cost a quarter of the kernel's time).
+// (64 lanes x VPL pairs of 16-byte vectors) and stores its codes to every
+// destination, 16 bytes per lane; the row's H/128 scales are gathered in LDS
+// and leave as one contiguous store per destination (scattered 16-byte scale
+// pieces written by separate wavefronts cost a quarter of the kernel's time).
 constexpr int kCastMaxGroups = 512;  // H <= 65536
 
 template <int VPL, int MW, int NT>
