@@ -24,9 +24,11 @@
  *     enqueues work on it and returns; the caller orders and synchronises.
  *   - Integer matrices are row-major int32 unless noted; booleans are one
  *     byte, 0 or 1.  bf16 data is passed as its 16-bit patterns.
- *   - Every call returns miep_status; on failure nothing was enqueued and
- *     miep_last_error() describes the reason (thread-local, host memory
- *     owned by the library).  No call aborts, traps or prints.
+ *   - Every call returns miep_status and miep_last_error() describes a
+ *     failure (thread-local, host memory owned by the library).  Argument
+ *     errors (EINVAL, EUNSUPPORTED) are found before anything is enqueued;
+ *     an EHIP from a call that launches several kernels may leave its
+ *     earlier kernels enqueued.  No call aborts, traps or prints.
  *   - Device-side bounds: rows at or past `recv_capacity` are never
  *     written; top-k entries outside [0, num_experts) are treated as masked.
  */
