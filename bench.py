@@ -60,9 +60,12 @@ def bytes_combine(N, H, K, R, rows, weights=True):
 
 
 def bytes_ll(msgs, distinct_tokens, H, use_fp8, R, L):
+    """Low-latency dispatch: each distinct token's row read, every message
+    written once, and its packed row (payload, scales, source index) written
+    once; plus the per-block counts and layout ranges."""
     mb = 16 + (H + 4 * (H // 128) if use_fp8 else 2 * H)
     pb = mb - 16
-    return distinct_tokens * 2 * H + 2 * msgs * mb + msgs * (pb + 4) + L * R * (4 + 8)
+    return distinct_tokens * 2 * H + msgs * mb + msgs * (pb + 4) + L * R * (4 + 8)
 
 
 def bytes_ll_combine(msgs, N, H, K, weighted):
@@ -451,7 +454,7 @@ KERNEL_SRC = {"combine": ("combine.hip", "device.h"), "pack": ("pack.hip", "devi
 
 def _kernel_key(name):
     for k in ("ll_combine_kernel", "combine_kernel", "pack_kernel", "notify_kernel", "layout_kernel", "ll_send_kernel",
-              "ll_recv_kernel"):
+              "ll_count_kernel", "relay_meta_kernel"):
         if "miep::" + k in name:
             return k.replace("_kernel", "")
     return None

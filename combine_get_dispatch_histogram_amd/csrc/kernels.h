@@ -107,7 +107,7 @@ struct RelayMetaArgs {
 };
 hipError_t launch_relay_meta(const RelayMetaArgs& a, hipStream_t st);
 
-// ---- low-latency: expert-major send, then receive-side unpack
+// ---- low-latency: per-block message counts, then messages and packed rows in one pass
 struct LLArgs {
   int R, T, M, H, K, E, L, d;
   int use_fp8, round_scale, use_ue8m0;

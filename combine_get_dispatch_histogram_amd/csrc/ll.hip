@@ -15,12 +15,13 @@
 // Where the transport fills slots in atomic arrival order, these kernels
 // fix the order: slot j of (l, s) is the j-th top-k entry of source s that
 // names expert d*L + l, in (token, k) order, so the output is
-// deterministic.  Two kernels, both kLLSplit workgroups per (l, s) block that
-// share its messages (the slot scan is repeated by each; it is tiny):
-//   send: scan source s's top-k for the expert (LDS scan), then cast and
-//         write its messages (16-byte loads and stores);
-//   recv: exclusive scan of the counts over s gives the packed range, then
-//         a 16-byte copy of payloads and scales.
+// deterministic.  Two kernels:
+//   count: one workgroup per (l, s) block scans source s's top-k for the
+//          expert and writes the block's message count;
+//   send:  kLLSplit workgroups per block repeat the (tiny) scan, take the
+//          block's packed range from the counts of the earlier sources, and
+//          cast and write each message and its packed row in one pass
+//          (16-byte loads and stores), so nothing is read back.
 #include "device.h"
 #include "kernels.h"
 
@@ -30,19 +31,20 @@ constexpr int kLLThreads = 256;
 constexpr int kLLSplit = 8;  // default workgroups sharing one (l, s) block's messages
 constexpr int kLLMaxSlots = 4096;
 
-template <int VPL>
-__global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
-  __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
-  __shared__ int32_t wsum[kLLThreads / kWave];
-  __shared__ int32_t carry_s;
-  const int l = blockIdx.x / a.R;
-  const int s = blockIdx.x % a.R;
+// The slot scan of block (l, s): every top-k entry of source s that names
+// expert d*L + l, in (token, k) order, takes the next slot.  Thread t of the
+// workgroup handles token t (8 entries loaded at a time); a wavefront scan
+// plus an LDS carry across wavefronts and 256-token chunks gives each entry
+// its slot.  With `slot_tok`, slot j < M records its token.  Returns the
+// number of matching entries (uncapped), the same in every thread.
+__device__ __forceinline__ int ll_slot_scan(const LLArgs& a, int l, int s, int32_t* slot_tok, int32_t* wsum,
+                                            int32_t* carry_s) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int64_t target = static_cast<int64_t>(a.d) * a.L + l;
   const int64_t* idx = a.topk_idx + static_cast<int64_t>(s) * a.T * a.K;
   // a masked destination is not sent to, a masked source is not received from
   const bool masked = a.mask != nullptr && (a.mask[a.d] != 0 || a.mask[s] != 0);
-  if (tid == 0) carry_s = 0;
+  if (tid == 0) *carry_s = 0;
   __syncthreads();
   for (int t0 = 0; t0 < a.T; t0 += kLLThreads) {
     const int t = t0 + tid;
@@ -61,39 +63,90 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
     const int inc = wave_inclusive_scan(cnt);
     if (lane == kWave - 1) wsum[w] = inc;
     __syncthreads();
-    int before = carry_s;
-    for (int q = 0; q < w; ++q) before += wsum[q];
-    int j = before + inc - cnt;
-    for (uint64_t km = kmask; km != 0; km &= km - 1) {   // one slot per matching entry, k ascending
-      if (j < a.M) slot_tok[j] = t;
-      ++j;
+    if (slot_tok != nullptr) {
+      int j = *carry_s + inc - cnt;
+      for (int q = 0; q < w; ++q) j += wsum[q];
+      for (uint64_t km = kmask; km != 0; km &= km - 1) {   // one slot per matching entry, k ascending
+        if (j < a.M) slot_tok[j] = t;
+        ++j;
+      }
     }
     __syncthreads();
     if (tid == 0) {
-      int tot = carry_s;
+      int tot = *carry_s;
       for (int q = 0; q < kLLThreads / kWave; ++q) tot += wsum[q];
-      carry_s = tot;
+      *carry_s = tot;
     }
     __syncthreads();
   }
-  const int n = carry_s < a.M ? carry_s : a.M;
-  if (tid == 0 && blockIdx.y == 0) a.msg_count[l * a.R + s] = n;
+  return *carry_s;
+}
 
-  // messages: one wavefront per (message, row slice); the slice's 16-byte
-  // loads are all issued before any of its stores.  A lane's unit is one
-  // 16-byte vector of 8 bf16, or with FP8 a pair of them (16 channels -> 16
-  // codes in one 16-byte store; a 128-channel group is 8 lanes).
+// Per-(l, s) message counts, capped at M (one workgroup per block).
+__global__ __launch_bounds__(kLLThreads) void ll_count_kernel(LLArgs a) {
+  __shared__ int32_t wsum[kLLThreads / kWave];
+  __shared__ int32_t carry_s;
+  const int l = blockIdx.x / a.R;
+  const int s = blockIdx.x % a.R;
+  const int n = ll_slot_scan(a, l, s, nullptr, wsum, &carry_s);
+  if (threadIdx.x == 0) a.msg_count[l * a.R + s] = n < a.M ? n : a.M;
+}
+
+// Messages and their packed receive rows.  Workgroup (l, s, y) repeats the
+// slot scan, takes block (l, s)'s first packed row from the counts of the
+// earlier sources, and serves every kLLSplit-th (message, slice) task: the
+// slice is loaded once (16-byte loads), cast, and written both to the
+// message (the transport buffer) and to the packed row, so the receive side
+// never reads the messages back.
+template <int VPL>
+__global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
+  __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
+  __shared__ int32_t wsum[kLLThreads / kWave];
+  __shared__ int32_t carry_s;
+  __shared__ int32_t begin_s;
+  const int l = blockIdx.x / a.R;
+  const int s = blockIdx.x % a.R;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  // first packed row of the block: messages of the earlier sources for expert l
+  if (w == 0) {
+    int part = 0;
+    for (int q = lane; q < s; q += kWave) part += a.msg_count[l * a.R + q];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
+    if (lane == 0) begin_s = part;
+  }
+  const int cnt = ll_slot_scan(a, l, s, slot_tok, wsum, &carry_s);   // synchronises the workgroup
+  const int n = cnt < a.M ? cnt : a.M;
+  const int begin = begin_s;
+  if (tid == 0 && blockIdx.y == 0) {             // once per (l, s), not per split workgroup
+    a.layout_range[l * a.R + s] = (static_cast<int64_t>(begin) << 32) | static_cast<int64_t>(static_cast<uint32_t>(n));
+    if (s == a.R - 1) {
+      a.count[l] = begin + n;
+      if (a.cumulative) a.cumulative[l] += begin + n;
+    }
+  }
+
+  // one wavefront per (message, row slice).  A lane's unit is one 16-byte
+  // vector of 8 bf16, or with FP8 a pair of them (16 channels -> 16 codes in
+  // one 16-byte store; a 128-channel group is 8 lanes).
   const int nv = a.H / 8;
   const int units = a.use_fp8 ? nv / 2 : nv;
   const int span = kWave * VPL;
   const int nsl = (units + span - 1) / span;
+  const int G = a.H / kFp8Group;
+  const int64_t pb = a.use_fp8 ? a.H : 2 * static_cast<int64_t>(a.H);   // packed row bytes
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x) + static_cast<int64_t>(s) * a.T * 2 * a.H;
   for (int task = blockIdx.y * (kLLThreads / kWave) + w; task < n * nsl; task += gridDim.y * (kLLThreads / kWave)) {
     const int j = task / nsl;
     const int u0 = (task - j * nsl) * span;
     const int t = slot_tok[j];
     uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
-    if (u0 == 0 && lane == 0) *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
+    const int64_t row = static_cast<int64_t>(l) * a.R * a.M + begin + j;
+    uint8_t* prow = static_cast<uint8_t*>(a.prx) + row * pb;
+    if (u0 == 0 && lane == 0) {
+      *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
+      a.src_info[row] = t;
+    }
     const uint8_t* xrow = xsrc + static_cast<int64_t>(t) * 2 * a.H;
     if (a.use_fp8) {
       v4u d[VPL][2];
@@ -113,8 +166,14 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
         float sci;
         const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
         if (p < units) {
-          st16<false>(msg + 16 + static_cast<int64_t>(p) * 16, cast16(d[i][0], d[i][1], sc));
-          if ((lane & 7) == 0) scales[p / 8] = sci;
+          const v4u q = cast16(d[i][0], d[i][1], sc);
+          st16<false>(msg + 16 + static_cast<int64_t>(p) * 16, q);
+          st16<false>(prow + static_cast<int64_t>(p) * 16, q);
+          if ((lane & 7) == 0) {
+            scales[p / 8] = sci;
+            a.prs[row * G + p / 8] = sci;
+            if (a.prue) a.prue[row * G + p / 8] = static_cast<uint8_t>((__float_as_uint(sci) >> 23) & 0xFFu);
+          }
         }
       }
     } else {
@@ -127,67 +186,9 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int v = u0 + i * kWave + lane;
-        if (v < nv) st16<false>(msg + 16 + static_cast<int64_t>(v) * 16, d[i]);
-      }
-    }
-  }
-}
-
-template <int VPL>
-__global__ __launch_bounds__(kLLThreads) void ll_recv_kernel(LLArgs a) {
-  __shared__ int32_t begin_s;
-  const int l = blockIdx.x / a.R;
-  const int s = blockIdx.x % a.R;
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  if (w == 0) {
-    int part = 0;
-    for (int q = lane; q < s; q += kWave) part += a.msg_count[l * a.R + q];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) part += __shfl_xor(part, d, kWave);
-    if (lane == 0) begin_s = part;
-  }
-  __syncthreads();
-  const int begin = begin_s;
-  const int n = a.msg_count[l * a.R + s];
-  if (tid == 0 && blockIdx.y == 0) {          // once per (l, s), not per split workgroup
-    a.layout_range[l * a.R + s] = (static_cast<int64_t>(begin) << 32) | static_cast<int64_t>(static_cast<uint32_t>(n));
-    if (s == a.R - 1) {
-      a.count[l] = begin + n;
-      if (a.cumulative) a.cumulative[l] += begin + n;
-    }
-  }
-  const int64_t pb = a.use_fp8 ? a.H : 2 * static_cast<int64_t>(a.H);  // payload bytes
-  const int nv = static_cast<int>(pb / 16);
-  const int G = a.H / kFp8Group;
-  const int64_t rows_per_expert = static_cast<int64_t>(a.R) * a.M;
-  const int span = kWave * VPL;
-  const int nsl = (nv + span - 1) / span;
-  for (int task = blockIdx.y * (kLLThreads / kWave) + w; task < n * nsl; task += gridDim.y * (kLLThreads / kWave)) {
-    const int j = task / nsl;
-    const int sl = task - j * nsl;
-    const int v0 = sl * span;
-    const uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
-    const int64_t row = l * rows_per_expert + begin + j;
-    v4u d[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int v = v0 + i * kWave + lane;
-      if (v < nv) d[i] = ld16<false>(msg + 16 + static_cast<int64_t>(v) * 16);
-    }
-    uint8_t* out = static_cast<uint8_t*>(a.prx) + row * pb;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int v = v0 + i * kWave + lane;
-      if (v < nv) st16<false>(out + static_cast<int64_t>(v) * 16, d[i]);
-    }
-    if (sl == 0) {
-      if (lane == 0) a.src_info[row] = *reinterpret_cast<const int32_t*>(msg);
-      if (a.use_fp8) {
-        const uint32_t* sc = reinterpret_cast<const uint32_t*>(msg + 16 + a.H);
-        for (int g = lane; g < G; g += kWave) {
-          const uint32_t bits = sc[g];
-          reinterpret_cast<uint32_t*>(a.prs)[row * G + g] = bits;
-          if (a.prue) a.prue[row * G + g] = static_cast<uint8_t>((bits >> 23) & 0xFFu);
+        if (v < nv) {
+          st16<false>(msg + 16 + static_cast<int64_t>(v) * 16, d[i]);
+          st16<false>(prow + static_cast<int64_t>(v) * 16, d[i]);
         }
       }
     }
@@ -196,10 +197,10 @@ __global__ __launch_bounds__(kLLThreads) void ll_recv_kernel(LLArgs a) {
 
 template <int VPL>
 static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, int split, hipStream_t st) {
-  hipLaunchKernelGGL(ll_send_kernel<VPL>, dim3(blocks, split), dim3(kLLThreads), 0, st, a);
+  hipLaunchKernelGGL(ll_count_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ll_recv_kernel<VPL>, dim3(blocks, split), dim3(kLLThreads), 0, st, a);
+  hipLaunchKernelGGL(ll_send_kernel<VPL>, dim3(blocks, split), dim3(kLLThreads), 0, st, a);
   return hipGetLastError();
 }
 
