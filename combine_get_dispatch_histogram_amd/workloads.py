@@ -149,6 +149,16 @@ def ll_inputs(w: LLWorkload, seed: int = 0) -> dict:
     return dict(x=x, topk_idx=idx)
 
 
+def structured_x(S: int, T: int, H: int) -> torch.Tensor:
+    """x whose row (s, t) names its own source token in exact bf16 integers:
+    channel h holds s, t % 256 or t // 256 for h % 3 = 0, 1, 2 (all < 256,
+    so exactly representable), for checking placements by eye."""
+    s = torch.arange(S).repeat_interleave(T)
+    t = torch.arange(T).repeat(S)
+    cols = torch.stack([s, t % 256, t // 256], dim=1).to(torch.float32)   # [N, 3]
+    return cols[:, torch.arange(H) % 3].to(torch.bfloat16).contiguous()
+
+
 def expert_outputs(rows: int, H: int, seed: int = 1) -> torch.Tensor:
     """Synthetic expert outputs in the receive layout: bf16 N(0,1)."""
     return activations(rows, H, _gen(seed))
