@@ -348,7 +348,11 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   // wavefronts per token).  Measured on MI355X, writes spread as many small
   // per-wavefront pieces reach ~6.7 TB/s while 4-16 KiB per wavefront drop to
   // 5.4-5.9 TB/s.  Rows that are not a multiple of 64 units keep 8.
-  int vpl = tu.pack_vpl > 0 ? tu.pack_vpl : (nv % kWave == 0 ? 1 : 8);
+  // Forwarding from group rows has a longer per-wavefront prologue (row
+  // count, group lookup, source token), so it moves 2 units per lane
+  // (measured on the 64-rank FP8 relay: 514 -> 477 us per relay dispatch).
+  const int base_vpl = a.group_off != nullptr ? 2 : 1;
+  int vpl = tu.pack_vpl > 0 ? tu.pack_vpl : (nv % kWave == 0 ? base_vpl : 8);
   int span = vpl * kWave;
   int nslices = tu.pack_slices > 0 ? tu.pack_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
