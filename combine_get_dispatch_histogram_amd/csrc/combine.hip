@@ -199,7 +199,11 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int nv = a.H / 8;
   // default: one 16-byte vector per lane per row and 8 rows' loads in flight
   // (hidden 7168 -> 14 waves per token); ragged rows keep 8 vectors x 2 rows
-  int vpl = tu.combine_vpl > 0 ? tu.combine_vpl : (nv % kWave == 0 ? 1 : 8);
+  // the group-level reduction of the relay (longer per-wavefront prologue:
+  // row count and group lookup) moves 4 vectors per lane (measured on the
+  // 64-rank relay: two-level combine 909 -> 805 us)
+  const int base_vpl = a.group_off != nullptr ? 4 : 1;
+  int vpl = tu.combine_vpl > 0 ? tu.combine_vpl : (nv % kWave == 0 ? base_vpl : 8);
   int maxr = tu.combine_maxr > 0 ? tu.combine_maxr : (vpl <= 2 ? 8 : 2);
   const int span = vpl * kWave;
   int nslices = tu.combine_slices > 0 ? tu.combine_slices : (nv + span - 1) / span;
