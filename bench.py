@@ -350,16 +350,13 @@ def run_normal_variant(torch, miep, wl, w, iters, cast_fp8):
     for _ in range(3):
         miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, recv_s, rti, rtw, nrte, cast_to_fp8=cast_fp8)
         miep.combine_into(y, h, cx, rtw, cw)
-    td, tc, tcd = Timer(torch, iters), Timer(torch, iters), Timer(torch, iters)
-    for _ in range(iters):
-        with td:
-            miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, recv_s, rti, rtw, nrte, cast_to_fp8=cast_fp8)
-        with tc:
-            miep.combine_into(y, h, cx, rtw, cw)
-        with tcd:
-            miep.cached_dispatch_into(x, h, recv_x, recv_s, cast_to_fp8=cast_fp8)
-    torch.cuda.synchronize()
-    d_ms, c_ms, cd_ms = med(td.ms()), med(tc.ms()), med(tcd.ms())
+    # each call timed on its own, a few launches back to back (so the
+    # write-back of one call's output does not land in another call's time)
+    d_ms = time_batched(torch, lambda: miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, recv_s, rti, rtw, nrte,
+                                                          cast_to_fp8=cast_fp8), iters, batch=4)
+    c_ms = time_batched(torch, lambda: miep.combine_into(y, h, cx, rtw, cw), iters, batch=4)
+    cd_ms = time_batched(torch, lambda: miep.cached_dispatch_into(x, h, recv_x, recv_s, cast_to_fp8=cast_fp8), iters,
+                         batch=4)
     kind = "cast" if cast_fp8 else "bf16"
     db = bytes_notify(w.N, w.R, w.S, w.C, w.E) + bytes_pack(w.N, w.H, w.K, w.R, rows, kind)
     cb = bytes_combine(w.N, w.H, w.K, w.R, rows)
