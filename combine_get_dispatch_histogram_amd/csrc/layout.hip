@@ -10,9 +10,10 @@
 //
 // One workgroup owns one source partition, so every count is produced by a
 // single workgroup: no global atomics, no zero-fill launch.  Each thread
-// reads one token's K indices, builds the rank bitmask in registers, writes
-// the membership row with 4-byte stores, and counts experts, ranks and
-// RDMA groups in LDS (integer adds, order-independent).
+// reads one token's K indices (16-byte loads), builds the rank bitmask in
+// registers, writes the membership row with 4-byte stores and counts its
+// experts in LDS; rank and RDMA-group counts are wavefront ballots, one LDS
+// add per rank per wavefront (integer adds, order-independent).
 #include "device.h"
 #include "kernels.h"
 
@@ -29,53 +30,70 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
   for (int i = threadIdx.x; i < a.E + a.R + G; i += blockDim.x) lds[i] = 0;
   __syncthreads();
 
-  for (int t = threadIdx.x; t < a.T; t += blockDim.x) {
+  const int lane = lane_id();
+  const bool vec = (a.K & 1) == 0 && (reinterpret_cast<uintptr_t>(a.topk_idx) & 15u) == 0;   // 16-byte rows pairs
+  // whole wavefronts walk the tokens (the rank counts below are wavefront
+  // ballots, so every lane of a wavefront takes part in each iteration)
+  const int tpad = (a.T + kWave - 1) / kWave * kWave;
+  for (int t = threadIdx.x; t < tpad; t += blockDim.x) {
+    const bool valid = t < a.T;
     const int64_t n = static_cast<int64_t>(s) * a.T + t;
     const int64_t* row = a.topk_idx + n * a.K;
     RankMask<MW> m;
     m.clear();
-    for (int k0 = 0; k0 < a.K; k0 += 8) {         // 8 independent loads in flight
-      int64_t e8[8];
+    if (valid) {
+      for (int k0 = 0; k0 < a.K; k0 += 8) {         // 8 entries in flight (16-byte loads when aligned)
+        int64_t e8[8];
+        if (k0 + 8 <= a.K && vec) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e8[j] = k0 + j < a.K ? row[k0 + j] : -1;
+          for (int j = 0; j < 4; ++j) {
+            const v4u v = ld16<false>(row + k0 + 2 * j);
+            e8[2 * j] = static_cast<int64_t>((static_cast<uint64_t>(v.y) << 32) | v.x);
+            e8[2 * j + 1] = static_cast<int64_t>((static_cast<uint64_t>(v.w) << 32) | v.z);
+          }
+        } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t e = e8[j];
-        if (e < 0 || e >= a.E) continue;            // masked (or out of range)
-        atomicAdd(&hist[e], 1);
-        m.set(static_cast<int>(e) / a.L);
-      }
-    }
-    uint8_t* out = a.in_rank + n * a.R;
-    if ((a.R & 3) == 0) {
-      for (int r0 = 0; r0 < a.R; r0 += 4) {
-        const uint32_t b = m.get(r0) | (m.get(r0 + 1) << 8) | (m.get(r0 + 2) << 16) | (m.get(r0 + 3) << 24);
-        *reinterpret_cast<uint32_t*>(out + r0) = b;
-      }
-    } else {
-      for (int r = 0; r < a.R; ++r) out[r] = static_cast<uint8_t>(m.get(r));
-    }
+          for (int j = 0; j < 8; ++j) e8[j] = k0 + j < a.K ? row[k0 + j] : -1;
+        }
 #pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      uint64_t bits = m.w[i];
-      // RDMA groups: byte j of word i is ranks 64i+8j .. 64i+8j+7
-      uint64_t g = bits;
-      g |= g >> 4;
-      g |= g >> 2;
-      g |= g >> 1;
-      g &= 0x0101010101010101ull;
-      while (bits) {
-        const int b = __builtin_ctzll(bits);
-        bits &= bits - 1;
-        atomicAdd(&rcnt[64 * i + b], 1);
-      }
-      if (G) {
-        while (g) {
-          const int b = __builtin_ctzll(g);
-          g &= g - 1;
-          atomicAdd(&gcnt[8 * i + (b >> 3)], 1);
+        for (int j = 0; j < 8; ++j) {
+          const int64_t e = e8[j];
+          if (e < 0 || e >= a.E) continue;            // masked (or out of range)
+          atomicAdd(&hist[e], 1);
+          m.set(static_cast<int>(e) / a.L);
         }
       }
+      uint8_t* out = a.in_rank + n * a.R;
+      if ((a.R & 3) == 0) {
+        for (int r0 = 0; r0 < a.R; r0 += 4) {
+          const uint32_t b = m.get(r0) | (m.get(r0 + 1) << 8) | (m.get(r0 + 2) << 16) | (m.get(r0 + 3) << 24);
+          *reinterpret_cast<uint32_t*>(out + r0) = b;
+        }
+      } else {
+        for (int r = 0; r < a.R; ++r) out[r] = static_cast<uint8_t>(m.get(r));
+      }
+    }
+    // rank and RDMA-group counts: one ballot per rank over the wavefront;
+    // lane j of each 64-rank chunk adds the chunk's count for rank r0 + j
+    for (int r0 = 0; r0 < a.R; r0 += kWave) {
+      const int rend = a.R - r0 < kWave ? a.R - r0 : kWave;
+      int mine = 0;
+      for (int j = 0; j < rend; ++j) {
+        const int c = __popcll(ballot(m.get(r0 + j) != 0));
+        mine = lane == j ? c : mine;
+      }
+      if (lane < rend && mine) atomicAdd(&rcnt[r0 + lane], mine);
+    }
+    if (G) {
+      int mine = 0;
+      for (int g = 0; g < G; ++g) {
+        bool hit = false;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hit |= m.get(8 * g + j) != 0;
+        const int c = __popcll(ballot(hit));
+        mine = lane == (g & (kWave - 1)) ? mine + c : mine;
+      }
+      if (lane < G && mine) atomicAdd(&gcnt[lane], mine);
     }
   }
   __syncthreads();
