@@ -416,8 +416,47 @@ def run_relay(torch, miep, wl, iters):
 
 
 # --------------------------------------------------------------------------- CPU oracle leg
-def cpu_baseline(wl, budget_s):
-    import numpy as np  # noqa: F401
+def _oracle_pass(oracle, w, x, idx, wts, y):
+    """One pass of the oracle over the normal workload: layout, dispatch, combine."""
+    lay = oracle.layout(idx, w.S, w.E, w.R)
+    d = oracle.dispatch(x, idx, wts, lay["is_token_in_rank"], lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R,
+                        C=w.C)
+    oracle.combine(y, d["recv_topk_weights"], d["send_head"], d["recv_rank_offset"], S=w.S)
+    return d
+
+
+# A worker of the all-cores oracle timing: loads the saved inputs, then runs
+# _oracle_pass until its budget is spent and prints
+# how many passes it finished and how long they took.  Started as a plain
+# child process; it imports neither torch nor the HIP library.
+_CPU_WORKER = r"""
+import json, os, sys, time, types
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+import bench
+import oracle
+d, start, budget = sys.argv[2], float(sys.argv[3]), float(sys.argv[4])
+w = types.SimpleNamespace(**dict(zip("SERC", (int(v) for v in sys.argv[5:9]))))
+a = {k: np.load(os.path.join(d, k + ".npy"), mmap_mode="r") for k in ("x", "idx", "wts", "y")}
+while time.time() < start:
+    time.sleep(0.001)
+runs, t0 = 0, time.perf_counter()
+while runs < 1 or time.perf_counter() - t0 < budget:
+    bench._oracle_pass(oracle, w, a["x"], a["idx"], a["wts"], a["y"])
+    runs += 1
+print(json.dumps({"runs": runs, "seconds": time.perf_counter() - t0}), flush=True)
+"""
+
+
+def cpu_baseline(wl, budget_s, procs=None):
+    """The oracle timed on the host: single-threaded first, then one independent
+    oracle process per host core (capped at 16) on the same inputs at the same
+    time; the reported value is the all-cores aggregate."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    import numpy as np
 
     import oracle
     w = wl.NORMAL
@@ -425,23 +464,45 @@ def cpu_baseline(wl, budget_s):
     x = wl.bf16_bits(inp["x"])
     idx = inp["topk_idx"].numpy()
     wts = inp["topk_weights"].numpy()
-    y = None
+    lay = oracle.layout(idx, w.S, w.E, w.R)
+    d = oracle.dispatch(x, idx, wts, lay["is_token_in_rank"], lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R,
+                        C=w.C)
+    y = wl.bf16_bits(wl.expert_outputs(d["num_recv"], w.H, seed=1))   # input generation is not oracle work
     runs, t_total = 0, 0.0
-    while runs < 1 or (t_total < budget_s and runs < 20):
+    while runs < 1 or (t_total < budget_s / 2 and runs < 20):
         t0 = time.perf_counter()
-        lay = oracle.layout(idx, w.S, w.E, w.R)
-        d = oracle.dispatch(x, idx, wts, lay["is_token_in_rank"], lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R,
-                            C=w.C)
-        if y is None:
-            t_gen = time.perf_counter()
-            y = wl.bf16_bits(wl.expert_outputs(d["num_recv"], w.H, seed=1))
-            t0 += time.perf_counter() - t_gen          # input generation is not oracle work
-        oracle.combine(y, d["recv_topk_weights"], d["send_head"], d["recv_rank_offset"], S=w.S)
+        _oracle_pass(oracle, w, x, idx, wts, y)
         t_total += time.perf_counter() - t0
         runs += 1
-    return dict(value=round(w.N * runs / t_total, 1), unit="tokens/s", cores=1, kind="oracle",
-                sample="the full normal workload (4096 tokens, layout + dispatch + combine), %d run(s), %.1f s, "
-                       "single-threaded C oracle (gcc -O2), host has %d cores" % (runs, t_total, os.cpu_count()))
+    single = w.N * runs / t_total
+    ncpu = os.cpu_count() or 1
+    procs = procs or max(1, min(ncpu, 16))
+    tmp = tempfile.mkdtemp(prefix="miep_cpu_")
+    try:
+        for k, v in (("x", x), ("idx", idx), ("wts", wts), ("y", y)):
+            np.save(os.path.join(tmp, k + ".npy"), np.ascontiguousarray(v))
+        root = os.path.dirname(os.path.abspath(__file__))
+        start = time.time() + 3.0                    # every worker has loaded its inputs by then
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        argv = [sys.executable, "-c", _CPU_WORKER, root, tmp, repr(start), repr(budget_s / 2)] + \
+            [str(v) for v in (w.S, w.E, w.R, w.C)]
+        ps = [subprocess.Popen(argv, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env)
+              for _ in range(procs)]
+        outs = [p.communicate(timeout=120 + 4 * budget_s) for p in ps]
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    rates = []
+    for p, (out, err) in zip(ps, outs):
+        if p.returncode != 0:
+            raise RuntimeError("oracle worker failed: %s" % err[-2000:])
+        r = json.loads(out.strip().splitlines()[-1])
+        rates.append(w.N * r["runs"] / r["seconds"])
+    return dict(value=round(sum(rates), 1), unit="tokens/s", cores=procs, kind="oracle",
+                single_thread_value=round(single, 1),
+                sample="the full normal workload (4096 tokens, layout + dispatch + combine) through the plain C "
+                       "oracle (gcc -O2, single-threaded code): %d independent processes, one per core, each "
+                       "repeating it for ~%.0f s at the same time (value = sum of their rates); single-threaded "
+                       "alone: %d run(s) in %.1f s; host has %d cores" % (procs, budget_s / 2, runs, t_total, ncpu))
 
 
 # --------------------------------------------------------------------------- profile summaries
