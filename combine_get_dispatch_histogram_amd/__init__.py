@@ -38,18 +38,41 @@ __all__ = ["Handle", "MiepError", "get_dispatch_layout", "get_dispatch_layout_in
            "query_mask_buffer", "ll_msg_bytes", "version"]
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    if t is None:
-        return None
-    if not t.is_cuda:
-        raise ValueError("miep expects device tensors")
-    if not t.is_contiguous():
-        raise ValueError("miep expects contiguous tensors")
-    return ctypes.c_void_p(t.data_ptr())
+class _Args:
+    """Pointer marshalling for one library call: every tensor it passes must be
+    a contiguous device tensor on one and the same GPU, and the call runs with
+    that GPU current and on its current stream."""
+
+    def __init__(self):
+        self.dev = None
+
+    def _see(self, t: torch.Tensor) -> None:
+        if not t.is_cuda:
+            raise ValueError("miep expects device tensors")
+        if self.dev is None:
+            self.dev = t.device
+        elif t.device != self.dev:
+            raise ValueError("miep expects every tensor of a call on one device (%s and %s)" % (self.dev, t.device))
+
+    def p(self, t: Optional[torch.Tensor]):
+        if t is None:
+            return None
+        self._see(t)
+        if not t.is_contiguous():
+            raise ValueError("miep expects contiguous tensors")
+        return ctypes.c_void_p(t.data_ptr())
+
+    def handle(self, h) -> None:
+        for t in h.tensors():
+            self.p(t)
 
 
-def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+def _run(a: _Args, name: str, *args) -> None:
+    if a.dev is None:
+        raise ValueError("miep call without device tensors")
+    with torch.cuda.device(a.dev):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(a.dev).cuda_stream)
+        _lib.check(getattr(_lib.load(), name)(*args, stream))
 
 
 def _want(t: Optional[torch.Tensor], name: str, dtype, shape=None):
@@ -108,6 +131,10 @@ class Handle:
                       torch.empty((R, S, num_channels), **i32), torch.empty((R + 1,), **i32),
                       torch.empty((capacity,), **i32), is_token_in_rank, torch.empty((N, R), **i32), S,
                       N // S if S else 0, num_topk, num_experts, R, num_channels)
+
+    def tensors(self):
+        return (self.rank_prefix_matrix, self.channel_prefix_matrix, self.recv_channel_prefix_matrix,
+                self.recv_rank_offset, self.recv_src_idx, self.is_token_in_rank, self.send_head)
 
     def c(self) -> _lib.HandleC:
         return _lib.HandleC(self.rank_prefix_matrix.data_ptr(), self.channel_prefix_matrix.data_ptr(),
@@ -168,9 +195,9 @@ def get_dispatch_layout_into(topk_idx, num_experts: int, num_ranks: int, num_src
     if R > 8:
         _want(num_tokens_per_rdma_rank, "num_tokens_per_rdma_rank", torch.int32, (S, R // 8))
     p = _lib.Problem(S, N // S, 8, K, num_experts, R, 1, 1)
-    _lib.check(_lib.load().miep_get_dispatch_layout(ctypes.byref(p), _ptr(topk_idx), _ptr(num_tokens_per_rank),
-                                                    _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert),
-                                                    _ptr(is_token_in_rank), _stream(topk_idx)))
+    a = _Args()
+    _run(a, "miep_get_dispatch_layout", ctypes.byref(p), a.p(topk_idx), a.p(num_tokens_per_rank),
+         a.p(num_tokens_per_rdma_rank), a.p(num_tokens_per_expert), a.p(is_token_in_rank))
 
 
 # --------------------------------------------------------------------------- dispatch
@@ -194,11 +221,11 @@ def dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per
             raise ValueError("%s must be [>= %d, %d]" % (name, handle.recv_capacity, K))
     p = handle.problem(x.shape[1], expert_alignment)
     h = handle.c()
-    _lib.check(_lib.load().miep_dispatch(ctypes.byref(p), _ptr(x), kind, _ptr(x_scales), int(round_scale),
-                                         _ptr(topk_idx), _ptr(topk_weights), _ptr(num_tokens_per_rank),
-                                         _ptr(num_tokens_per_expert), _ptr(recv_x), _ptr(recv_x_scales),
-                                         _ptr(recv_topk_idx), _ptr(recv_topk_weights),
-                                         _ptr(num_recv_tokens_per_expert), ctypes.byref(h), _stream(x)))
+    a = _Args()
+    a.handle(handle)
+    _run(a, "miep_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), a.p(topk_idx),
+         a.p(topk_weights), a.p(num_tokens_per_rank), a.p(num_tokens_per_expert), a.p(recv_x), a.p(recv_x_scales),
+         a.p(recv_topk_idx), a.p(recv_topk_weights), a.p(num_recv_tokens_per_expert), ctypes.byref(h))
 
 
 def _check_payload_shapes(x, kind, x_scales, handle: Handle, recv_x, recv_x_scales):
@@ -272,8 +299,10 @@ def cached_dispatch_into(x, handle: Handle, recv_x, recv_x_scales=None, x_scales
     _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
     p = handle.problem(x.shape[1])
     h = handle.c()
-    _lib.check(_lib.load().miep_cached_dispatch(ctypes.byref(p), _ptr(x), kind, _ptr(x_scales), int(round_scale),
-                                                ctypes.byref(h), _ptr(recv_x), _ptr(recv_x_scales), _stream(x)))
+    a = _Args()
+    a.handle(handle)
+    _run(a, "miep_cached_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), ctypes.byref(h),
+         a.p(recv_x), a.p(recv_x_scales))
 
 
 def cached_dispatch(x: torch.Tensor, handle: Handle, x_scales: Optional[torch.Tensor] = None,
@@ -314,8 +343,10 @@ def combine_into(y, handle: Handle, combined_x, recv_topk_weights=None, combined
     _want(b1, "bias_1", torch.bfloat16, (N, H))
     p = handle.problem(y.shape[1])
     h = handle.c()
-    _lib.check(_lib.load().miep_combine(ctypes.byref(p), _ptr(y), _ptr(recv_topk_weights), _ptr(b0), _ptr(b1),
-                                        ctypes.byref(h), _ptr(combined_x), _ptr(combined_topk_weights), _stream(y)))
+    a = _Args()
+    a.handle(handle)
+    _run(a, "miep_combine", ctypes.byref(p), a.p(y), a.p(recv_topk_weights), a.p(b0), a.p(b1), ctypes.byref(h),
+         a.p(combined_x), a.p(combined_topk_weights))
 
 
 def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None, bias=None):
@@ -368,11 +399,11 @@ def low_latency_dispatch_into(x, topk_idx, num_ranks: int, max_tokens: int, num_
     _want(cumulative_local_expert_recv_stats, "cumulative_local_expert_recv_stats", torch.int32, (L,))
     _want(mask_buffer, "mask_buffer", torch.int32, (R,))
     q = _lib.LLProblem(num_ranks, N // num_ranks, max_tokens, H, K, num_experts, dest_rank)
-    _lib.check(_lib.load().miep_ll_dispatch(
-        ctypes.byref(q), _ptr(x), _ptr(topk_idx), int(use_fp8), int(round_scale), int(use_ue8m0), _ptr(msg_buf),
-        _ptr(msg_count), _ptr(packed_recv_x), _ptr(packed_recv_x_scales), _ptr(packed_recv_x_scales_ue8m0),
-        _ptr(packed_recv_src_info), _ptr(packed_recv_layout_range), _ptr(packed_recv_count),
-        _ptr(cumulative_local_expert_recv_stats), _ptr(mask_buffer), _stream(x)))
+    a = _Args()
+    _run(a, "miep_ll_dispatch", ctypes.byref(q), a.p(x), a.p(topk_idx), int(use_fp8), int(round_scale),
+         int(use_ue8m0), a.p(msg_buf), a.p(msg_count), a.p(packed_recv_x), a.p(packed_recv_x_scales),
+         a.p(packed_recv_x_scales_ue8m0), a.p(packed_recv_src_info), a.p(packed_recv_layout_range),
+         a.p(packed_recv_count), a.p(cumulative_local_expert_recv_stats), a.p(mask_buffer))
 
 
 def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispatch_tokens_per_rank: int,
@@ -433,9 +464,9 @@ def low_latency_combine_into(y, topk_idx, topk_weights, packed_recv_src_info, pa
     _want(packed_recv_layout_range, "packed_recv_layout_range", torch.int64, (L, R))
     _want(combined_x, "combined_x", torch.bfloat16, (N, H))
     q = _lib.LLProblem(R, N // R, M, H, K, num_experts, dest_rank)
-    _lib.check(_lib.load().miep_ll_combine(ctypes.byref(q), _ptr(y), _ptr(packed_recv_src_info),
-                                           _ptr(packed_recv_layout_range), _ptr(topk_idx), _ptr(topk_weights),
-                                           _ptr(combined_x), _stream(y)))
+    a = _Args()
+    _run(a, "miep_ll_combine", ctypes.byref(q), a.p(y), a.p(packed_recv_src_info), a.p(packed_recv_layout_range),
+         a.p(topk_idx), a.p(topk_weights), a.p(combined_x))
 
 
 def low_latency_combine(y: torch.Tensor, topk_idx: torch.Tensor, topk_weights: Optional[torch.Tensor],
@@ -468,14 +499,15 @@ def _mask_check(mask_buffer):
 def update_mask_buffer(mask_buffer: torch.Tensor, rank: int, mask: bool) -> None:
     """Set (mask=True) or clear rank ``rank``'s entry of the [R] int32 mask."""
     _mask_check(mask_buffer)
-    _lib.check(_lib.load().miep_mask_update(_ptr(mask_buffer), mask_buffer.shape[0], int(rank), int(bool(mask)),
-                                            _stream(mask_buffer)))
+    a = _Args()
+    _run(a, "miep_mask_update", a.p(mask_buffer), mask_buffer.shape[0], int(rank), int(bool(mask)))
 
 
 def clean_mask_buffer(mask_buffer: torch.Tensor) -> None:
     """Clear every entry of the [R] int32 mask."""
     _mask_check(mask_buffer)
-    _lib.check(_lib.load().miep_mask_clean(_ptr(mask_buffer), mask_buffer.shape[0], _stream(mask_buffer)))
+    a = _Args()
+    _run(a, "miep_mask_clean", a.p(mask_buffer), mask_buffer.shape[0])
 
 
 def query_mask_buffer(mask_buffer: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -484,8 +516,8 @@ def query_mask_buffer(mask_buffer: torch.Tensor, out: Optional[torch.Tensor] = N
     if out is None:
         out = torch.empty_like(mask_buffer)
     _want(out, "out", torch.int32, tuple(mask_buffer.shape))
-    _lib.check(_lib.load().miep_mask_query(_ptr(mask_buffer), mask_buffer.shape[0], _ptr(out),
-                                           _stream(mask_buffer)))
+    a = _Args()
+    _run(a, "miep_mask_query", a.p(mask_buffer), mask_buffer.shape[0], a.p(out))
     return out
 
 
@@ -521,6 +553,10 @@ class RelayHandle:
                            torch.empty((G, num_src, num_channels), **i32), torch.empty((G + 1,), **i32),
                            torch.empty((num_tokens, G), **i32), torch.empty((rdma_capacity,), **i32),
                            torch.empty((rdma_capacity, 8), **i32))
+
+    def tensors(self):
+        return (self.rdma_rank_prefix_matrix, self.rdma_channel_prefix_matrix, self.recv_rdma_channel_prefix_matrix,
+                self.recv_rdma_offset, self.send_rdma_head, self.rdma_src_idx, self.send_nvl_head)
 
     def c(self) -> _lib.RelayHandleC:
         return _lib.RelayHandleC(self.rdma_rank_prefix_matrix.data_ptr(), self.rdma_channel_prefix_matrix.data_ptr(),
@@ -570,11 +606,13 @@ def relay_dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_toke
     p = handle.problem(H, expert_alignment)
     h = handle.c()
     rh = relay.c()
-    _lib.check(_lib.load().miep_relay_dispatch(
-        ctypes.byref(p), _ptr(x), kind, _ptr(x_scales), int(round_scale), _ptr(topk_idx), _ptr(topk_weights),
-        _ptr(num_tokens_per_rank), _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert), _ptr(rdma_x),
-        _ptr(rdma_x_scales), _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_topk_idx), _ptr(recv_topk_weights),
-        _ptr(num_recv_tokens_per_expert), ctypes.byref(h), ctypes.byref(rh), _stream(x)))
+    a = _Args()
+    a.handle(handle)
+    a.handle(relay)
+    _run(a, "miep_relay_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), a.p(topk_idx),
+         a.p(topk_weights), a.p(num_tokens_per_rank), a.p(num_tokens_per_rdma_rank), a.p(num_tokens_per_expert),
+         a.p(rdma_x), a.p(rdma_x_scales), a.p(recv_x), a.p(recv_x_scales), a.p(recv_topk_idx), a.p(recv_topk_weights),
+         a.p(num_recv_tokens_per_expert), ctypes.byref(h), ctypes.byref(rh))
 
 
 def relay_dispatch(x: torch.Tensor, topk_idx: Optional[torch.Tensor], topk_weights: Optional[torch.Tensor],
@@ -630,10 +668,11 @@ def relay_cached_dispatch_into(x, handle: Handle, relay: RelayHandle, rdma_x, re
     p = handle.problem(H)
     h = handle.c()
     rh = relay.c()
-    _lib.check(_lib.load().miep_relay_cached_dispatch(ctypes.byref(p), _ptr(x), kind, _ptr(x_scales),
-                                                      int(round_scale), ctypes.byref(h), ctypes.byref(rh),
-                                                      _ptr(rdma_x), _ptr(rdma_x_scales), _ptr(recv_x),
-                                                      _ptr(recv_x_scales), _stream(x)))
+    a = _Args()
+    a.handle(handle)
+    a.handle(relay)
+    _run(a, "miep_relay_cached_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale),
+         ctypes.byref(h), ctypes.byref(rh), a.p(rdma_x), a.p(rdma_x_scales), a.p(recv_x), a.p(recv_x_scales))
 
 
 def relay_cached_dispatch(x: torch.Tensor, handle: Handle, relay: RelayHandle, x_scales: Optional[torch.Tensor] = None,
@@ -673,9 +712,11 @@ def relay_combine_into(y, handle: Handle, relay: RelayHandle, rdma_y, combined_x
     p = handle.problem(H)
     h = handle.c()
     rh = relay.c()
-    _lib.check(_lib.load().miep_relay_combine(ctypes.byref(p), _ptr(y), _ptr(recv_topk_weights), _ptr(b0), _ptr(b1),
-                                              ctypes.byref(h), ctypes.byref(rh), _ptr(rdma_y), _ptr(rdma_w),
-                                              _ptr(combined_x), _ptr(combined_topk_weights), _stream(y)))
+    a = _Args()
+    a.handle(handle)
+    a.handle(relay)
+    _run(a, "miep_relay_combine", ctypes.byref(p), a.p(y), a.p(recv_topk_weights), a.p(b0), a.p(b1), ctypes.byref(h),
+         ctypes.byref(rh), a.p(rdma_y), a.p(rdma_w), a.p(combined_x), a.p(combined_topk_weights))
 
 
 def relay_combine(y: torch.Tensor, handle: Handle, relay: RelayHandle, topk_weights: Optional[torch.Tensor] = None,

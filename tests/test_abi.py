@@ -218,3 +218,21 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_binding_rejects_host_and_mixed_device_tensors():
+    """The binding refuses host tensors before anything reaches the library,
+    and refuses a call whose tensors sit on two different GPUs."""
+    import types
+
+    import torch
+
+    import combine_get_dispatch_histogram_amd as miep
+    idx = torch.zeros((8, 2), dtype=torch.int64)
+    with pytest.raises(ValueError, match="device tensors"):
+        miep.get_dispatch_layout(idx, 8, 4, 4)
+    a = miep._Args()
+    a._see(types.SimpleNamespace(is_cuda=True, device="cuda:0"))
+    a._see(types.SimpleNamespace(is_cuda=True, device="cuda:0"))
+    with pytest.raises(ValueError, match="one device"):
+        a._see(types.SimpleNamespace(is_cuda=True, device="cuda:1"))
