@@ -54,6 +54,7 @@ miep_status check_problem(const miep_problem* p) {
     return fail(MIEP_EUNSUPPORTED, "more than 2^31-1 tokens");
   if (p->num_src > (1 << 20)) return fail(MIEP_EUNSUPPORTED, "num_src > 2^20");
   if (p->num_channels > 1024) return fail(MIEP_EUNSUPPORTED, "num_channels > 1024");
+  if (p->hidden > (1 << 24)) return fail(MIEP_EUNSUPPORTED, "hidden > 2^24");
   return ok();
 }
 
@@ -175,7 +176,7 @@ const Tuning& tuning() {
   static const Tuning t = {env_int("MIEP_PACK_VPL", 0),     env_int("MIEP_PACK_SLICES", 0),
                            env_int("MIEP_COMBINE_VPL", 0),  env_int("MIEP_COMBINE_SLICES", 0),
                            env_int("MIEP_COMBINE_MAXR", 0),
-                           env_int("MIEP_PACK_NT", 2) & 3, env_int("MIEP_COMBINE_NT", 1) & 3,
+                           env_int("MIEP_PACK_NT", 6) & 7, env_int("MIEP_COMBINE_NT", 5) & 7,
                            env_int("MIEP_LL_SPLIT", 0),     env_int("MIEP_LL_VPL", 0),
                            env_int("MIEP_CAST_TPB", -1),    env_int("MIEP_LLC_VPL", 0),
                            env_int("MIEP_LLC_SLICES", 0)};

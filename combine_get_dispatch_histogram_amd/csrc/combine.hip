@@ -10,7 +10,10 @@
 // the token's receiving ranks hold (send_head names them), adds them in
 // ascending rank order in fp32 registers, and writes the bf16 row once.
 // Every HBM byte is touched once: rho row reads + 1 row write per token.
-// No atomics: a token's sum lives in one wavefront's registers.
+// No atomics: a token's sum lives in one wavefront's registers.  Row
+// traffic uses buffer instructions on the wave-uniform row base; by default
+// the expert outputs stream in non-temporal and the combined rows are
+// written at device scope.
 #include "device.h"
 #include "kernels.h"
 
@@ -19,7 +22,7 @@ namespace miep {
 template <int VPL, int MAXR, int MW, int NT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices) {
   const int lane = lane_id();
-  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t gw = wave_index();
   const int64_t n = gw / nslices;
   const int slice = static_cast<int>(gw - n * nslices);
   if (n >= a.N) return;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
               const int v = v0 + j * kWave + lane;
-              if (v < nv) d[q][j] = ld16<(NT & 1) != 0>(yrow + static_cast<int64_t>(v) * 16);
+              if (v < nv) d[q][j] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(v) * 16);
             }
           }
         }
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
         } else {
           o = v4u{0u, 0u, 0u, 0u};
         }
-        st16<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 16, o);
+        stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, o);
       }
     }
   }
@@ -210,9 +213,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   if (nslices < 1) nslices = 1;
   switch (tu.combine_nt) {
     case 0: return launch_combine_nt<0>(a, vpl, maxr, nslices, st);
+    case 1: return launch_combine_nt<1>(a, vpl, maxr, nslices, st);
     case 2: return launch_combine_nt<2>(a, vpl, maxr, nslices, st);
     case 3: return launch_combine_nt<3>(a, vpl, maxr, nslices, st);
-    default: return launch_combine_nt<1>(a, vpl, maxr, nslices, st);
+    case 4: return launch_combine_nt<4>(a, vpl, maxr, nslices, st);
+    case 6: return launch_combine_nt<6>(a, vpl, maxr, nslices, st);
+    case 7: return launch_combine_nt<7>(a, vpl, maxr, nslices, st);
+    default: return launch_combine_nt<5>(a, vpl, maxr, nslices, st);
   }
 }
 

@@ -69,6 +69,46 @@ __device__ __forceinline__ void st16(void* p, const v4u& v) {
   }
 }
 
+// Row traffic of the pack and combine kernels goes through buffer
+// instructions on a wave-uniform row base (the resource lives in scalar
+// registers, the lane's byte offset in one VGPR), which also carries the
+// cache-policy field of gfx950 vector memory instructions: sc0 and sc1 pick
+// the coherence scope, nt marks data that streams through.  Offsets are 32
+// bits, so a row holds at most 2^31 bytes.
+constexpr int kCpolSc0 = 1, kCpolNt = 2, kCpolSc1 = 16;
+
+// Policy codes of the pack / combine kernels: bit 0 = non-temporal loads,
+// bit 1 = non-temporal stores, bit 2 = device-scope (sc1) stores.
+__host__ __device__ constexpr int load_cpol(int code) { return (code & 1) ? kCpolNt : 0; }
+__host__ __device__ constexpr int store_cpol(int code) {
+  return ((code & 2) ? kCpolNt : 0) | ((code & 4) ? kCpolSc1 : 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base) {
+  // raw (untyped) access: stride 0, 2^31 - 1 bytes in range, dword 3 as
+  // every gfx9-family raw buffer access takes it
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+template <int CPOL>
+__device__ __forceinline__ v4u ldb16(const void* base, uint32_t off) {
+  const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(base), off, 0, CPOL);
+  return v4u{t.x, t.y, t.z, t.w};
+}
+
+template <int CPOL>
+__device__ __forceinline__ void stb16(void* base, uint32_t off, const v4u& v) {
+  const u32x4 t = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(t, row_rsrc(base), off, 0, CPOL);
+}
+
+// Wavefront index of the calling lane over the grid, computed from
+// wave-uniform values only (so the compiler keeps it in scalar registers).
+__device__ __forceinline__ int64_t wave_index() {
+  return static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) +
+         __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+}
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

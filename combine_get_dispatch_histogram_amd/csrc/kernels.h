@@ -150,9 +150,13 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // MIEP_LL_VPL, MIEP_CAST_TPB, MIEP_LLC_VPL, MIEP_LLC_SLICES): used by
 // geometry sweeps, never required.
 // combine_maxr: source rows whose loads are issued together.
-// pack_nt: bit 0 = non-temporal payload loads, bit 1 = non-temporal stores;
-// combine_nt: bit 0 = non-temporal loads of the expert outputs, bit 1 =
-// non-temporal stores of the combined rows.  ll_split: workgroups per
+// pack_nt / combine_nt: cache policy of the row traffic, bit 0 =
+// non-temporal loads, bit 1 = non-temporal stores, bit 2 = device-scope
+// (sc1) stores.  Defaults, measured on MI355X over the whole normal step
+// (layout, dispatch, combine back to back): pack 6 (plain loads of x,
+// non-temporal device-scope stores), combine 5 (non-temporal loads of the
+// expert outputs, device-scope stores); setting both or neither of the
+// non-temporal bits costs ~20% in either kernel.  ll_split: workgroups per
 // low-latency (expert, source) block.  cast_tpb: fused FP8 cast with one
 // token per workgroup (1), 1 KiB slices (0), or chosen per call (-1).
 // llc_vpl / llc_slices: low-latency combine vectors per lane and slices per

@@ -14,7 +14,9 @@
 // r holds rank r's row, a ballot gives the destination set, and the wave
 // walks it with scalar find-first-set + readlane, so every store is a fully
 // coalesced 1 KiB wavefront store.  No atomics anywhere: placement was
-// fixed by the notify scan.
+// fixed by the notify scan.  Row traffic uses buffer instructions on the
+// wave-uniform row base; by default x is read with the ordinary cache policy
+// and the receive rows are written non-temporal at device scope.
 #include "device.h"
 #include "kernels.h"
 
@@ -34,7 +36,7 @@ __device__ __forceinline__ int group_rank_base(const int32_t* group_off, int gro
 template <int KIND, int VPL, int MW, int NT>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   const int lane = lane_id();
-  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t gw = wave_index();
   const int64_t n = gw / nslices;
   const int slice = static_cast<int>(gw - n * nslices);
   if (n >= a.N) return;
@@ -111,8 +113,8 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
       for (int j = 0; j < VPL; ++j) {
         const int pi = p0 + j * kWave + lane;
         if (pi < np) {
-          d[j][0] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32);
-          d[j][1] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32 + 16);
+          d[j][0] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(pi) * 32);
+          d[j][1] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(pi) * 32 + 16);
         }
       }
       v4u q[VPL];
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
           for (int j = 0; j < VPL; ++j) {
             const int pi = p0 + j * kWave + lane;
             if (pi < np) {
-              st16<(NT & 2) != 0>(orow + static_cast<int64_t>(pi) * 16, q[j]);
+              stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(pi) * 16, q[j]);
               if ((lane & 7) == 0) a.recv_x_scales[row * G + pi / 8] = sci[j];
             }
           }
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int v = v0 + j * kWave + lane;
-      if (v < nv) d[j] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(v) * 16);
+      if (v < nv) d[j] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(v) * 16);
     }
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
           const int v = v0 + j * kWave + lane;
-          if (v < nv) st16<(NT & 2) != 0>(orow + static_cast<int64_t>(v) * 16, d[j]);
+          if (v < nv) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, d[j]);
         }
       }
     }
@@ -234,8 +236,8 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
   for (int j = 0; j < VPL; ++j) {
     const int pi = p0 + j * kWave + lane;
     if (pi < np) {
-      d[j][0] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32);
-      d[j][1] = ld16<(NT & 1) != 0>(xrow + static_cast<int64_t>(pi) * 32 + 16);
+      d[j][0] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(pi) * 32);
+      d[j][1] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(pi) * 32 + 16);
     }
   }
   v4u q[VPL];
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         const int pi = p0 + j * kWave + lane;
-        if (pi < np) st16<(NT & 2) != 0>(orow + static_cast<int64_t>(pi) * 16, q[j]);
+        if (pi < np) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(pi) * 16, q[j]);
       }
     }
   }
@@ -333,7 +335,11 @@ static hipError_t launch_pack_nt(const PackArgs& a, int vpl, int nslices, int nt
     case 0: return launch_pack_kind<KIND, 0>(a, vpl, nslices, st);
     case 1: return launch_pack_kind<KIND, 1>(a, vpl, nslices, st);
     case 2: return launch_pack_kind<KIND, 2>(a, vpl, nslices, st);
-    default: return launch_pack_kind<KIND, 3>(a, vpl, nslices, st);
+    case 3: return launch_pack_kind<KIND, 3>(a, vpl, nslices, st);
+    case 4: return launch_pack_kind<KIND, 4>(a, vpl, nslices, st);
+    case 5: return launch_pack_kind<KIND, 5>(a, vpl, nslices, st);
+    case 7: return launch_pack_kind<KIND, 7>(a, vpl, nslices, st);
+    default: return launch_pack_kind<KIND, 6>(a, vpl, nslices, st);
   }
 }
 
@@ -369,8 +375,12 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
         switch (tu.pack_nt) {
           case 0: return launch_pack_cast<0>(a, hint, st);
           case 1: return launch_pack_cast<1>(a, hint, st);
+          case 2: return launch_pack_cast<2>(a, hint, st);
           case 3: return launch_pack_cast<3>(a, hint, st);
-          default: return launch_pack_cast<2>(a, hint, st);
+          case 4: return launch_pack_cast<4>(a, hint, st);
+          case 5: return launch_pack_cast<5>(a, hint, st);
+          case 7: return launch_pack_cast<7>(a, hint, st);
+          default: return launch_pack_cast<6>(a, hint, st);
         }
       }
       return launch_pack_nt<kPackCastFp8>(a, vpl, nslices, tu.pack_nt, st);

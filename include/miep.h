@@ -59,7 +59,7 @@ typedef enum miep_xkind {
 typedef struct miep_problem {
   int32_t num_src;          /* S: source partitions (the sending ranks), <= 2^20         */
   int32_t num_tokens;       /* T: tokens per source partition                             */
-  int32_t hidden;           /* H: channels per token                                      */
+  int32_t hidden;           /* H: channels per token, <= 2^24                             */
   int32_t num_topk;         /* K: experts per token                                       */
   int32_t num_experts;      /* E: experts; expert e lives on rank e / (E / R)              */
   int32_t num_ranks;        /* R: receiving ranks, 1..256; R > 8 needs R % 8 == 0          */
