@@ -211,7 +211,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   const int span = vpl * kWave;
   int nslices = tu.combine_slices > 0 ? tu.combine_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
-  switch (tu.combine_nt) {
+  const int nt = tu.combine_nt >= 0 ? tu.combine_nt & 7 : (a.cpol >= 0 ? a.cpol & 7 : 5);
+  switch (nt) {
     case 0: return launch_combine_nt<0>(a, vpl, maxr, nslices, st);
     case 1: return launch_combine_nt<1>(a, vpl, maxr, nslices, st);
     case 2: return launch_combine_nt<2>(a, vpl, maxr, nslices, st);

@@ -70,6 +70,7 @@ struct PackArgs {
   const int32_t* group_off;  // [groups+1] first row of each group; lane j of row n's group g is rank g*group_w + j
   int groups, group_w;
   const int32_t* src_tok;    // [N] source token of row n (top-k metadata, recv_src_idx)
+  int cpol = -1;             // cache-policy code of this launch (-1: the default)
 };
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 
@@ -91,6 +92,7 @@ struct CombineArgs {
   const int32_t* count;
   const int32_t* group_off;  // [groups+1]
   int groups, group_w;
+  int cpol = -1;             // cache-policy code of this launch (-1: the default)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
@@ -152,11 +154,13 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // combine_maxr: source rows whose loads are issued together.
 // pack_nt / combine_nt: cache policy of the row traffic, bit 0 =
 // non-temporal loads, bit 1 = non-temporal stores, bit 2 = device-scope
-// (sc1) stores.  Defaults, measured on MI355X over the whole normal step
-// (layout, dispatch, combine back to back): pack 6 (plain loads of x,
-// non-temporal device-scope stores), combine 5 (non-temporal loads of the
-// expert outputs, device-scope stores); setting both or neither of the
-// non-temporal bits costs ~20% in either kernel.  ll_split: workgroups per
+// (sc1) stores; -1 (unset) leaves it to the launch.  Defaults, measured on
+// MI355X: over the whole normal step (layout, dispatch, combine back to
+// back) pack 6 (plain loads of x, non-temporal device-scope stores) and
+// combine 5 (non-temporal loads of the expert outputs, device-scope
+// stores); setting both or neither of the non-temporal bits costs ~20% in
+// either kernel.  The relay's launches take 7 (its group rows are written
+// once and read once more right after).  ll_split: workgroups per
 // low-latency (expert, source) block.  cast_tpb: fused FP8 cast with one
 // token per workgroup (1), 1 KiB slices (0), or chosen per call (-1).
 // llc_vpl / llc_slices: low-latency combine vectors per lane and slices per

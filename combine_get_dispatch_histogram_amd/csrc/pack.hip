@@ -346,6 +346,7 @@ static hipError_t launch_pack_nt(const PackArgs& a, int vpl, int nslices, int nt
 hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
   const Tuning& tu = tuning();
+  const int nt = tu.pack_nt >= 0 ? tu.pack_nt & 7 : (a.cpol >= 0 ? a.cpol & 7 : 6);
   // per-lane unit: a 16-byte input vector, or for the fused cast a pair of
   // them (16 channels -> one 16-byte vector of codes)
   const int nv = a.kind == kPackFp8 ? a.H / 16 : (a.kind == kPackCastFp8 ? a.H / 16 : a.H / 8);
@@ -363,7 +364,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   int nslices = tu.pack_slices > 0 ? tu.pack_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
   switch (a.kind) {
-    case kPackFp8: return launch_pack_nt<kPackFp8>(a, vpl, nslices, tu.pack_nt, st);
+    case kPackFp8: return launch_pack_nt<kPackFp8>(a, vpl, nslices, nt, st);
     case kPackCastFp8:
       // Measured on the 16384-token workload: with the top-k metadata (fresh
       // dispatch) one token per workgroup at 2 vectors per lane is fastest
@@ -372,7 +373,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
       if ((tu.cast_tpb > 0 || (tu.cast_tpb < 0 && a.meta)) && a.group_off == nullptr && a.count == nullptr &&
           a.src_tok == nullptr) {
         const int hint = tu.pack_vpl > 0 ? tu.pack_vpl : 1;   // 1 pair = 2 vectors per lane
-        switch (tu.pack_nt) {
+        switch (nt) {
           case 0: return launch_pack_cast<0>(a, hint, st);
           case 1: return launch_pack_cast<1>(a, hint, st);
           case 2: return launch_pack_cast<2>(a, hint, st);
@@ -383,8 +384,8 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
           default: return launch_pack_cast<6>(a, hint, st);
         }
       }
-      return launch_pack_nt<kPackCastFp8>(a, vpl, nslices, tu.pack_nt, st);
-    default: return launch_pack_nt<kPackBf16>(a, vpl, nslices, tu.pack_nt, st);
+      return launch_pack_nt<kPackCastFp8>(a, vpl, nslices, nt, st);
+    default: return launch_pack_nt<kPackBf16>(a, vpl, nslices, nt, st);
   }
 }
 
