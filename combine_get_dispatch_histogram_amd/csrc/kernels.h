@@ -149,8 +149,9 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // Optional launch-geometry overrides read once from the environment
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
 // MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT, MIEP_LL_SPLIT,
-// MIEP_LL_VPL, MIEP_CAST_TPB, MIEP_LLC_VPL, MIEP_LLC_SLICES): used by
-// geometry sweeps, never required.
+// MIEP_LL_VPL, MIEP_CAST_TPB, MIEP_LLC_VPL, MIEP_LLC_SLICES, MIEP_LLC_NT,
+// MIEP_LL_NT):
+// used by geometry sweeps, never required.
 // combine_maxr: source rows whose loads are issued together.
 // pack_nt / combine_nt: cache policy of the row traffic, bit 0 =
 // non-temporal loads, bit 1 = non-temporal stores, bit 2 = device-scope
@@ -163,11 +164,12 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // once and read once more right after).  ll_split: workgroups per
 // low-latency (expert, source) block.  cast_tpb: fused FP8 cast with one
 // token per workgroup (1), 1 KiB slices (0), or chosen per call (-1).
-// llc_vpl / llc_slices: low-latency combine vectors per lane and slices per
-// token.
+// llc_vpl / llc_slices / llc_nt: low-latency combine vectors per lane,
+// slices per token and cache-policy code (as pack_nt); ll_nt: the
+// low-latency send's cache-policy code.
 struct Tuning {
   int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl,
-      cast_tpb, llc_vpl, llc_slices;
+      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt;
 };
 const Tuning& tuning();
 

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kLLThreads) void ll_count_kernel(LLArgs a) {
 // slice is loaded once (16-byte loads), cast, and written both to the
 // message (the transport buffer) and to the packed row, so the receive side
 // never reads the messages back.
-template <int VPL>
+template <int VPL, int NT>
 __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
   __shared__ int32_t wsum[kLLThreads / kWave];
@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   __shared__ int32_t begin_s;
   const int l = blockIdx.x / a.R;
   const int s = blockIdx.x % a.R;
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: row bases stay scalar
   // first packed row of the block: messages of the earlier sources for expert l
   if (w == 0) {
     int part = 0;
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
       for (int i = 0; i < VPL; ++i) {
         const int p = u0 + i * kWave + lane;
         if (p < units) {
-          d[i][0] = ld16<false>(xrow + static_cast<int64_t>(p) * 32);
-          d[i][1] = ld16<false>(xrow + static_cast<int64_t>(p) * 32 + 16);
+          d[i][0] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(p) * 32);
+          d[i][1] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(p) * 32 + 16);
         }
       }
       float* scales = reinterpret_cast<float*>(msg + 16 + a.H);
@@ -167,8 +168,8 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
         const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
         if (p < units) {
           const v4u q = cast16(d[i][0], d[i][1], sc);
-          st16<false>(msg + 16 + static_cast<int64_t>(p) * 16, q);
-          st16<false>(prow + static_cast<int64_t>(p) * 16, q);
+          stb16<store_cpol(NT)>(msg, 16 + static_cast<uint32_t>(p) * 16, q);
+          stb16<store_cpol(NT)>(prow, static_cast<uint32_t>(p) * 16, q);
           if ((lane & 7) == 0) {
             scales[p / 8] = sci;
             a.prs[row * G + p / 8] = sci;
@@ -181,27 +182,44 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int v = u0 + i * kWave + lane;
-        if (v < nv) d[i] = ld16<false>(xrow + static_cast<int64_t>(v) * 16);
+        if (v < nv) d[i] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(v) * 16);
       }
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int v = u0 + i * kWave + lane;
         if (v < nv) {
-          st16<false>(msg + 16 + static_cast<int64_t>(v) * 16, d[i]);
-          st16<false>(prow + static_cast<int64_t>(v) * 16, d[i]);
+          stb16<store_cpol(NT)>(msg, 16 + static_cast<uint32_t>(v) * 16, d[i]);
+          stb16<store_cpol(NT)>(prow, static_cast<uint32_t>(v) * 16, d[i]);
         }
       }
     }
   }
 }
 
-template <int VPL>
-static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, int split, hipStream_t st) {
+template <int VPL, int NT>
+static hipError_t launch_ll_cfg(const LLArgs& a, int blocks, int split, hipStream_t st) {
   hipLaunchKernelGGL(ll_count_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ll_send_kernel<VPL>, dim3(blocks, split), dim3(kLLThreads), 0, st, a);
+  hipLaunchKernelGGL((ll_send_kernel<VPL, NT>), dim3(blocks, split), dim3(kLLThreads), 0, st, a);
   return hipGetLastError();
+}
+
+template <int VPL>
+static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, int split, hipStream_t st) {
+  // cache policy: plain loads of x, non-temporal stores of the messages and
+  // packed rows (measured on the low-latency workload: 12.95 us against
+  // 13.5 us with the plain policy)
+  switch (tuning().ll_nt >= 0 ? tuning().ll_nt & 7 : 2) {
+    case 1: return launch_ll_cfg<VPL, 1>(a, blocks, split, st);
+    case 2: return launch_ll_cfg<VPL, 2>(a, blocks, split, st);
+    case 3: return launch_ll_cfg<VPL, 3>(a, blocks, split, st);
+    case 4: return launch_ll_cfg<VPL, 4>(a, blocks, split, st);
+    case 5: return launch_ll_cfg<VPL, 5>(a, blocks, split, st);
+    case 6: return launch_ll_cfg<VPL, 6>(a, blocks, split, st);
+    case 7: return launch_ll_cfg<VPL, 7>(a, blocks, split, st);
+    default: return launch_ll_cfg<VPL, 0>(a, blocks, split, st);
+  }
 }
 
 hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
@@ -247,7 +265,7 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
 // (token, k) order, MAXR rows' loads in flight, and each token's sum is
 // stored when the walk moves past it.
 // bf16 (round to nearest even) of one token's fp32 sums for the slice at v0
-template <int VPL>
+template <int VPL, int SP>
 __device__ __forceinline__ void store_sum(uint8_t* orow, const float (&acc)[VPL][8], int v0, int nv, int lane) {
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
@@ -258,15 +276,15 @@ __device__ __forceinline__ void store_sum(uint8_t* orow, const float (&acc)[VPL]
       o.y = pack_bf16x2(acc[j][2], acc[j][3]);
       o.z = pack_bf16x2(acc[j][4], acc[j][5]);
       o.w = pack_bf16x2(acc[j][6], acc[j][7]);
-      st16<false>(orow + static_cast<int64_t>(v) * 16, o);
+      stb16<SP>(orow, static_cast<uint32_t>(v) * 16, o);
     }
   }
 }
 
-template <int VPL, int MAXR>
+template <int VPL, int MAXR, int NT>
 __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int nslices) {
   const int lane = lane_id();
-  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int64_t gw = wave_index();
   const int K = a.K;
   const int P = kWave / K;                                 // tokens per group
   const int64_t N = static_cast<int64_t>(a.R) * a.T;
@@ -309,7 +327,7 @@ __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int ns
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         const int v = v0 + j * kWave + lane;
-        if (v < nv) st16<false>(orow + static_cast<int64_t>(v) * 16, v4u{0u, 0u, 0u, 0u});
+        if (v < nv) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, v4u{0u, 0u, 0u, 0u});
       }
     }
   if (tok_local == 0) return;
@@ -353,7 +371,7 @@ __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int ns
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
           const int v = v0 + j * kWave + lane;
-          if (v < nv) st16<false>(orow + static_cast<int64_t>(v) * 16, v4u{0u, 0u, 0u, 0u});
+          if (v < nv) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, v4u{0u, 0u, 0u, 0u});
         }
       }
     }
@@ -387,7 +405,7 @@ __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int ns
 #pragma unroll
           for (int j = 0; j < VPL; ++j) {
             const int v = v0 + j * kWave + lane;
-            if (v < nv) dv[q][j] = ld16<false>(yrow + static_cast<int64_t>(v) * 16);
+            if (v < nv) dv[q][j] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(v) * 16);
           }
         }
       }
@@ -395,7 +413,7 @@ __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int ns
       for (int q = 0; q < MAXR; ++q) {
         if (q < nb) {
           const bool first = tq[q] != cur;
-          if (first && cur >= 0) store_sum<VPL>(out + (n0 + cur) * row_bytes, acc, v0, nv, lane);
+          if (first && cur >= 0) store_sum<VPL, store_cpol(NT)>(out + (n0 + cur) * row_bytes, acc, v0, nv, lane);
           cur = tq[q];
 #pragma unroll
           for (int j = 0; j < VPL; ++j) {
@@ -411,18 +429,27 @@ __global__ __launch_bounds__(256) void ll_combine_kernel(LLCombineArgs a, int ns
         }
       }
     }
-    if (cur >= 0) store_sum<VPL>(out + (n0 + cur) * row_bytes, acc, v0, nv, lane);
+    if (cur >= 0) store_sum<VPL, store_cpol(NT)>(out + (n0 + cur) * row_bytes, acc, v0, nv, lane);
   }
 }
 
-template <int VPL, int MAXR>
+template <int VPL, int MAXR, int NT>
 static hipError_t launch_ll_combine_cfg(const LLCombineArgs& a, int nslices, hipStream_t st) {
   const int P = kWave / a.K;
   const int64_t groups = (static_cast<int64_t>(a.R) * a.T + P - 1) / P;
   const int64_t blocks = (groups * nslices + 3) / 4;
-  hipLaunchKernelGGL((ll_combine_kernel<VPL, MAXR>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((ll_combine_kernel<VPL, MAXR, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                      nslices);
   return hipGetLastError();
+}
+
+template <int NT>
+static hipError_t launch_ll_combine_nt(const LLCombineArgs& a, int vpl, int nslices, hipStream_t st) {
+  switch (vpl) {
+    case 2: return launch_ll_combine_cfg<2, 8, NT>(a, nslices, st);
+    case 4: return launch_ll_combine_cfg<4, 4, NT>(a, nslices, st);
+    default: return launch_ll_combine_cfg<1, 8, NT>(a, nslices, st);
+  }
 }
 
 hipError_t launch_ll_combine(const LLCombineArgs& a, hipStream_t st) {
@@ -436,10 +463,17 @@ hipError_t launch_ll_combine(const LLCombineArgs& a, hipStream_t st) {
   const int span = vpl * kWave;
   int nslices = tu.llc_slices > 0 ? tu.llc_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;
-  switch (vpl) {
-    case 2: return launch_ll_combine_cfg<2, 8>(a, nslices, st);
-    case 4: return launch_ll_combine_cfg<4, 4>(a, nslices, st);
-    default: return launch_ll_combine_cfg<1, 8>(a, nslices, st);
+  // cache policy: plain loads, device-scope stores (measured on the
+  // low-latency workload: 13.3 us against 14.3 us with the plain policy)
+  switch (tu.llc_nt >= 0 ? tu.llc_nt & 7 : 4) {
+    case 1: return launch_ll_combine_nt<1>(a, vpl, nslices, st);
+    case 2: return launch_ll_combine_nt<2>(a, vpl, nslices, st);
+    case 3: return launch_ll_combine_nt<3>(a, vpl, nslices, st);
+    case 4: return launch_ll_combine_nt<4>(a, vpl, nslices, st);
+    case 5: return launch_ll_combine_nt<5>(a, vpl, nslices, st);
+    case 6: return launch_ll_combine_nt<6>(a, vpl, nslices, st);
+    case 7: return launch_ll_combine_nt<7>(a, vpl, nslices, st);
+    default: return launch_ll_combine_nt<0>(a, vpl, nslices, st);
   }
 }
 
