@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
         for (int b = 0; b < 2; ++b) {
           const uint16_t* bias = b == 0 ? a.bias0 : a.bias1;
           if (bias == nullptr) continue;
-          const v4u t = ld16<false>(reinterpret_cast<const uint8_t*>(bias) + n * row_bytes + static_cast<int64_t>(v) * 16);
+          const v4u t = ld16(reinterpret_cast<const uint8_t*>(bias) + n * row_bytes + static_cast<int64_t>(v) * 16);
           const float f[8] = {bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y),
                               bf16_lo(t.z), bf16_hi(t.z), bf16_lo(t.w), bf16_hi(t.w)};
 #pragma unroll

@@ -42,34 +42,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 // ---------------------------------------------------------------- memory
-// 16-byte vector types.  Loads of data read once use the non-temporal hint
-// (streamed through, not kept in L2); stores of receive buffers likewise.
+// 16-byte vector types and a plain 16-byte load (bias rows, top-k rows).
 struct alignas(16) v4u { uint32_t x, y, z, w; };
 struct alignas(8) v2u { uint32_t x, y; };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool NT>
-__device__ __forceinline__ v4u ld16(const void* p) {
-  if constexpr (NT) {
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return v4u{t.x, t.y, t.z, t.w};
-  } else {
-    return *reinterpret_cast<const v4u*>(p);
-  }
-}
+__device__ __forceinline__ v4u ld16(const void* p) { return *reinterpret_cast<const v4u*>(p); }
 
-template <bool NT>
-__device__ __forceinline__ void st16(void* p, const v4u& v) {
-  if constexpr (NT) {
-    const u32x4 t = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
-  } else {
-    *reinterpret_cast<v4u*>(p) = v;
-  }
-}
-
-// Row traffic of the pack and combine kernels goes through buffer
+// Row traffic of the pack, combine and low-latency kernels goes through buffer
 // instructions on a wave-uniform row base (the resource lives in scalar
 // registers, the lane's byte offset in one VGPR), which also carries the
 // cache-policy field of gfx950 vector memory instructions: sc0 and sc1 pick

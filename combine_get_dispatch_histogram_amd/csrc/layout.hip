@@ -47,7 +47,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
         if (k0 + 8 <= a.K && vec) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const v4u v = ld16<false>(row + k0 + 2 * j);
+            const v4u v = ld16(row + k0 + 2 * j);
             e8[2 * j] = static_cast<int64_t>((static_cast<uint64_t>(v.y) << 32) | v.x);
             e8[2 * j + 1] = static_cast<int64_t>((static_cast<uint64_t>(v.w) << 32) | v.z);
           }
