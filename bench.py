@@ -524,7 +524,7 @@ def summarize_stats(stats_dir, out_md, command, title="normal workload step"):
     import glob
     path = glob.glob(os.path.join(stats_dir, "*_kernel_stats.csv"))[0]
     lines = ["# Kernel durations: %s (rocprofv3 --kernel-trace --stats)" % title, "",
-             "Command (from the repo root on the GPU box; `R` = repo root):", "", "```", command, "```", "",
+             "Command (run from the repo root on the MI355X host; `R` = repo root):", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for r in csv.DictReader(open(path)):
         if "miep::" not in r["Name"]:
@@ -543,7 +543,7 @@ def summarize_counters(dirs, out_md, commands, title):
     import glob
     from collections import defaultdict
     lines = ["# Hardware counters: %s (rocprofv3 --pmc, mean per dispatch)" % title, "",
-             "Commands (from the repo root on the GPU box; `R` = repo root):", "", "```"] + list(commands) + \
+             "Commands (run from the repo root on the MI355X host; `R` = repo root):", "", "```"] + list(commands) + \
             ["```", ""]
     for d in dirs:
         agg = defaultdict(lambda: defaultdict(list))
