@@ -62,36 +62,20 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   }
 
   const int G = a.H / kFp8Group;
-  // top-k entries, source index and pre-quantised scales: once per token
-  if (slice == 0 && (a.meta || KIND == kPackFp8)) {
-    const int64_t tok = a.src_tok != nullptr ? a.src_tok[n] : n;   // the source token the row carries
-    int64_t e = -1;
-    float wk = 0.0f;
+  // top-k entries, source index and pre-quantised scales, once per token (by
+  // slice 0): loaded here, written after the payload so that their latency
+  // hides behind the row traffic
+  const bool head = slice == 0 && (a.meta || KIND == kPackFp8);
+  int64_t tok = n;
+  int64_t e = -1;
+  float wk = 0.0f, sv = 0.0f;
+  if (head) {
+    tok = a.src_tok != nullptr ? a.src_tok[n] : n;   // the source token the row carries
     if (a.meta && lane < a.K) {
       e = a.topk_idx[tok * a.K + lane];
       if (a.topk_weights) wk = a.topk_weights[tok * a.K + lane];
     }
-#pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      uint64_t m = dmask[i];
-      while (m) {
-        const int b = __builtin_ctzll(m);
-        m &= m - 1;
-        const int r = rbase + kWave * i + b;
-        const int64_t row = readlane(dst[i], b);
-        if (a.meta) {
-          if (lane < a.K) {
-            const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;
-            if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
-            if (a.recv_topk_weights) a.recv_topk_weights[row * a.K + lane] = mine ? wk : 0.0f;
-          }
-          if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(tok % a.T);
-        }
-        if constexpr (KIND == kPackFp8) {
-          for (int g = lane; g < G; g += kWave) a.recv_x_scales[row * G + g] = a.x_scales[n * G + g];
-        }
-      }
-    }
+    if (KIND == kPackFp8 && G <= kWave && lane < G) sv = a.x_scales[n * G + lane];
   }
 
   // payload: input vectors are 16 bytes (8 bf16 or 16 E4M3 codes)
@@ -145,27 +129,55 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
         }
       }
     }
-    return;
-  }
-  for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
-    v4u d[VPL];
+  } else {
+    for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
+      v4u d[VPL];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-      const int v = v0 + j * kWave + lane;
-      if (v < nv) d[j] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(v) * 16);
+      for (int j = 0; j < VPL; ++j) {
+        const int v = v0 + j * kWave + lane;
+        if (v < nv) d[j] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(v) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        uint64_t m = dmask[i];
+        while (m) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          const int64_t row = readlane(dst[i], b);
+          uint8_t* orow = recv + row * out_row_bytes;
+#pragma unroll
+          for (int j = 0; j < VPL; ++j) {
+            const int v = v0 + j * kWave + lane;
+            if (v < nv) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, d[j]);
+          }
+        }
+      }
     }
+  }
+  // the token's metadata and pre-quantised scales, to every destination row
+  if (head) {
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
       uint64_t m = dmask[i];
       while (m) {
         const int b = __builtin_ctzll(m);
         m &= m - 1;
+        const int r = rbase + kWave * i + b;
         const int64_t row = readlane(dst[i], b);
-        uint8_t* orow = recv + row * out_row_bytes;
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-          const int v = v0 + j * kWave + lane;
-          if (v < nv) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, d[j]);
+        if (a.meta) {
+          if (lane < a.K) {
+            const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;
+            if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
+            if (a.recv_topk_weights) a.recv_topk_weights[row * a.K + lane] = mine ? wk : 0.0f;
+          }
+          if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(tok % a.T);
+        }
+        if constexpr (KIND == kPackFp8) {
+          if (G <= kWave) {
+            if (lane < G) a.recv_x_scales[row * G + lane] = sv;
+          } else {
+            for (int g = lane; g < G; g += kWave) a.recv_x_scales[row * G + g] = a.x_scales[n * G + g];
+          }
         }
       }
     }
@@ -201,29 +213,14 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
     dmask[i] = ballot(row >= 0 && row < a.capacity);
   }
   const int G = a.H / kFp8Group;
-  if (slice == 0 && a.meta) {
-    int64_t e = -1;
-    float wk = 0.0f;
-    if (lane < a.K) {
-      e = a.topk_idx[n * a.K + lane];
-      if (a.topk_weights) wk = a.topk_weights[n * a.K + lane];
-    }
-#pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      uint64_t m = dmask[i];
-      while (m) {
-        const int b = __builtin_ctzll(m);
-        m &= m - 1;
-        const int r = kWave * i + b;
-        const int64_t row = readlane(dst[i], b);
-        if (lane < a.K) {
-          const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;
-          if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
-          if (a.recv_topk_weights) a.recv_topk_weights[row * a.K + lane] = mine ? wk : 0.0f;
-        }
-        if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(n % a.T);
-      }
-    }
+  // the token's top-k entries: loaded now, written with the scales after the
+  // payload, so their latency hides behind the row traffic instead of
+  // holding up slice 0 (and through the barrier, the whole token)
+  int64_t e = -1;
+  float wk = 0.0f;
+  if (slice == 0 && a.meta && lane < a.K) {
+    e = a.topk_idx[n * a.K + lane];
+    if (a.topk_weights) wk = a.topk_weights[n * a.K + lane];
   }
   // lane holds VPL pairs of adjacent 16-byte vectors (16 channels each), so
   // a 128-channel group is 8 lanes and each code store is 16 bytes per lane
@@ -274,8 +271,18 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
       while (m) {
         const int b = __builtin_ctzll(m);
         m &= m - 1;
-        float* srow = a.recv_x_scales + static_cast<int64_t>(readlane(dst[i], b)) * G;
+        const int r = kWave * i + b;
+        const int64_t row = readlane(dst[i], b);
+        float* srow = a.recv_x_scales + row * G;
         for (int g = lane; g < G; g += kWave) srow[g] = row_scales[g];
+        if (a.meta) {
+          if (lane < a.K) {
+            const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;
+            if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
+            if (a.recv_topk_weights) a.recv_topk_weights[row * a.K + lane] = mine ? wk : 0.0f;
+          }
+          if (lane == 0) a.recv_src_idx[row] = static_cast<int32_t>(n % a.T);
+        }
       }
     }
   }

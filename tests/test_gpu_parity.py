@@ -87,6 +87,7 @@ SMALL = [
     ("r128", 2, 100, 256, 1024, 128, 8, 5, 1),        # 2-word rank masks
     ("r256", 2, 64, 264, 2048, 256, 9, 3, 1),
     ("r1", 2, 40, 128, 8, 1, 2, 4, 1),
+    ("k20", 2, 50, 128, 64, 8, 20, 4, 1),            # top-20: the pack writes the receive metadata
 ]
 
 
