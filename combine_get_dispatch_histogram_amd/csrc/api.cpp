@@ -146,6 +146,7 @@ miep::NotifyArgs notify_args(const miep_problem* p, const miep_handle* h, const 
   na.E = p->num_experts;
   na.L = p->num_experts / p->num_ranks;
   na.align = p->expert_alignment;
+  na.tcdiv = miep::make_fastdiv(p->num_tokens > 0 ? (p->num_tokens + p->num_channels - 1) / p->num_channels : 1);
   na.in_rank = h->is_token_in_rank;
   na.ntpr = ntpr;
   na.ntpe = ntpe;
@@ -224,6 +225,7 @@ miep_status miep_get_dispatch_layout(const miep_problem* p, const int64_t* topk_
   a.E = p->num_experts;
   a.R = p->num_ranks;
   a.L = p->num_experts / p->num_ranks;
+  a.Ldiv = miep::make_fastdiv(a.L);
   a.topk_idx = topk_idx;
   a.ntpr = num_tokens_per_rank;
   a.ntp_rdma = num_tokens_per_rdma_rank;

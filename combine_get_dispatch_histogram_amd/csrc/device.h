@@ -30,6 +30,11 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // Uniform broadcast of lane `src` (src must be wave-uniform).
 __device__ __forceinline__ int readlane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
+// floor(n / f.d) for 0 <= n with n * f.d < 2^40 (see FastDiv).
+__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+  return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(n)) * f.m) >> 40);
+}
+
 // Inclusive scan across the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int l = lane_id();

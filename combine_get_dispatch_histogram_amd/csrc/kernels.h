@@ -13,9 +13,28 @@ constexpr int kFp8Group = 128;     // channels per FP8 scale
 constexpr int kMaxRanks = 256;     // logical ranks supported by one call
 constexpr int kMaxExperts = 8192;  // experts (LDS histogram bound)
 
+// Division by a launch constant without the ~30-instruction integer divide:
+// floor(n / d) = (n * m) >> 40 with m = ceil(2^40 / d).  Writing m = (2^40 +
+// e) / d with 0 <= e < d, the product overshoots n/d by n*e / (d * 2^40) <
+// n / 2^40, which stays below the 1/d gap to the next integer whenever
+// n * d < 2^40.  Uses: expert / experts-per-rank (both <= 8192, always
+// exact) and token / tokens-per-channel (exact for T <= 2^20, which the
+// kernels check before taking it).
+struct FastDiv {
+  uint64_t m;
+  int d;
+};
+inline FastDiv make_fastdiv(int d) {
+  FastDiv f;
+  f.d = d > 0 ? d : 1;
+  f.m = ((1ull << 40) + static_cast<uint64_t>(f.d) - 1) / static_cast<uint64_t>(f.d);
+  return f;
+}
+
 // ---- layout histogram (one workgroup per source partition)
 struct LayoutArgs {
   int S, T, K, E, R, L;
+  FastDiv Ldiv;             // experts per rank
   const int64_t* topk_idx;  // [S*T][K]
   int32_t* ntpr;            // [S][R]
   int32_t* ntp_rdma;        // [S][R/8] or null
@@ -31,6 +50,7 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t st);
 struct NotifyArgs {
   int S, T, R, C, E, L, align;
   int group_w;
+  FastDiv tcdiv;            // tokens per channel, ceil(T / C)
   const uint8_t* in_rank;   // [S*T][R] (or [S*T][R*group_w])
   const int32_t* ntpr;      // [S][R]
   const int32_t* ntpe;      // [S][E] or null

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
           const int64_t e = e8[j];
           if (e < 0 || e >= a.E) continue;            // masked (or out of range)
           atomicAdd(&hist[e], 1);
-          m.set(static_cast<int>(e) / a.L);
+          m.set(fdiv(static_cast<int>(e), a.Ldiv));
         }
       }
       uint8_t* out = a.in_rank + n * a.R;

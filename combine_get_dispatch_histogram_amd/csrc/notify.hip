@@ -25,6 +25,45 @@
 namespace miep {
 
 constexpr int kNotifyMaxWaves = 16;
+constexpr int kNotifySrcBatch = 8;   // sources whose count rows a wavefront loads at once
+
+// Nonzero bytes of a 32-bit word -> 4 bits (byte j -> bit j): fold each byte
+// onto its low bit, then one multiply moves bits 0, 8, 16, 24 to 28..31 (the
+// other partial products land on distinct lower bits, so nothing carries in).
+__device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t v) {
+  v |= v >> 4;
+  v |= v >> 2;
+  v |= v >> 1;
+  return ((v & 0x01010101u) * 0x10204080u) >> 28;
+}
+
+// Membership row of R <= 64 ranks (R % 4 == 0) kept as raw words between
+// the loads and the decode, so that independent loads issued in between are
+// in flight together.  R == 8 rows (8-byte aligned) take one 8-byte load.
+struct RowWords {
+  uint32_t v[16];
+};
+__device__ __forceinline__ void issue_row_words(const uint8_t* row, int R, bool one8, RowWords& rw) {
+  if (one8) {
+    const uint64_t q = *reinterpret_cast<const uint64_t*>(row);
+    rw.v[0] = static_cast<uint32_t>(q);
+    rw.v[1] = static_cast<uint32_t>(q >> 32);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) rw.v[i] = 0u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rw.v[i] = 4 * i < R ? *reinterpret_cast<const uint32_t*>(row + 4 * i) : 0u;
+  }
+}
+__device__ __forceinline__ RankMask<1> decode_row_words(const RowWords& rw, int R) {
+  uint64_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (4 * i < R) w |= static_cast<uint64_t>(nonzero_bytes4(rw.v[i])) << (4 * i);
+  RankMask<1> m;
+  m.w[0] = w;
+  return m;
+}
 
 // Destination set of token n: its rank row, or (GROUPED, group_w == 8) one
 // bit per group of 8 ranks, set when any of the group's 8 bytes is set (one
@@ -43,12 +82,19 @@ __device__ __forceinline__ RankMask<MW> load_member(const NotifyArgs& a, int64_t
   }
 }
 
+// The kernel is latency-bound (8 workgroups for the normal workload), and a
+// wavefront issues about one instruction per 4 cycles, so its time is the
+// length of its instruction chain plus its global round trips: no integer
+// divides (wavefronts walk whole count rows; channel indices use FastDiv),
+// one round trip for all the loads of the first token tile, and no serial
+// scan across wavefronts (each wavefront sums the earlier ones' counts from
+// LDS with independent reads).
 template <int MW, bool GROUPED>
 __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   __shared__ int32_t base[kMaxRanks];                 // rows of rank r from sources < s
   __shared__ int32_t total[kMaxRanks];                // rows of rank r from all sources
-  __shared__ int32_t run[kMaxRanks];                  // tokens of s already scanned that go to r
-  __shared__ int32_t wt[kNotifyMaxWaves][kMaxRanks];  // per-wavefront counts -> exclusive bases
+  __shared__ int32_t run[kMaxRanks];                  // tokens of s in earlier tiles that go to r
+  __shared__ int32_t wt[kNotifyMaxWaves][kMaxRanks];  // per-wavefront counts of the current tile
 
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -59,22 +105,18 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
 
   extern __shared__ int32_t eacc[];                   // per-expert sums of the experts this workgroup owns
   const int ne = a.E > s ? (a.E - s + S - 1) / S : 0; // experts e = s + k*S
-  // Every independent global load is issued before the first wait: the
-  // first token tile's membership rows and up to kB rank / expert counts per
-  // thread.
-  constexpr int kB = MW == 1 ? 16 : 8;
-  const int nt = blockDim.x;
   const bool do_e = a.nrte != nullptr && a.ntpe != nullptr;
+
+  // (1) the first token tile's membership row: loads issued, decoded later
+  constexpr bool kLazy = MW == 1 && !GROUPED;
+  const bool lazy = kLazy && (R & 3) == 0;
+  const bool one8 = R == 8 && (reinterpret_cast<uintptr_t>(a.in_rank) & 7u) == 0;
+  RowWords rw;
   RankMask<MW> first;
   first.clear();
-  if (tid < T) first = load_member<MW, GROUPED>(a, static_cast<int64_t>(s) * T + tid);
-  int vr[kB], ve[kB];
-#pragma unroll
-  for (int q = 0; q < kB; ++q) {
-    const int i = q * nt + tid;
-    vr[q] = i < S * R ? a.ntpr[i] : 0;
-    const int k = i / S, src = i - k * S;
-    ve[q] = do_e && i < ne * S ? a.ntpe[static_cast<int64_t>(src) * a.E + s + k * S] : 0;
+  if (tid < T) {
+    if (lazy) issue_row_words(a.in_rank + (static_cast<int64_t>(s) * T + tid) * R, R, one8, rw);
+    else first = load_member<MW, GROUPED>(a, static_cast<int64_t>(s) * T + tid);
   }
   for (int r = tid; r < R; r += blockDim.x) {
     base[r] = 0;
@@ -82,28 +124,58 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     run[r] = 0;
   }
   for (int k = tid; k < ne; k += blockDim.x) eacc[k] = 0;
-  __syncthreads();
-  // rank totals and bases, per-expert counts: sums with LDS integer atomics
-  // (order-free), so no thread walks a dependent chain of S loads
-  for (int i0 = 0; i0 < S * R || (do_e && i0 < ne * S); i0 += kB * nt) {
-    if (i0 > 0) {                                    // further batches (large S*R or E)
+
+  // (2) rank totals / bases and the sums of the owned experts' counts:
+  // wavefront w walks sources w, w + nw, ...; lane j of a 64-wide chunk
+  // takes rank 64*i + j (and owned expert j), so the loads are whole rows
+  int tot[MW], bas[MW];
 #pragma unroll
-      for (int q = 0; q < kB; ++q) {
-        const int i = i0 + q * nt + tid;
-        vr[q] = i < S * R ? a.ntpr[i] : 0;
-        const int k = i / S, src = i - k * S;
-        ve[q] = do_e && i < ne * S ? a.ntpe[static_cast<int64_t>(src) * a.E + s + k * S] : 0;
+  for (int i = 0; i < MW; ++i) tot[i] = bas[i] = 0;
+  int eac = 0;
+  const bool e_lane = do_e && lane < ne;
+  for (int src0 = w; src0 < S; src0 += kNotifySrcBatch * nw) {
+    int vr[kNotifySrcBatch][MW], ve[kNotifySrcBatch];
+#pragma unroll
+    for (int u = 0; u < kNotifySrcBatch; ++u) {
+      const int src = src0 + u * nw;
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        const int r = kWave * i + lane;
+        vr[u][i] = src < S && r < R ? a.ntpr[src * R + r] : 0;
       }
+      ve[u] = e_lane && src < S ? a.ntpe[static_cast<int64_t>(src) * a.E + s + lane * S] : 0;
     }
 #pragma unroll
-    for (int q = 0; q < kB; ++q) {
-      const int i = i0 + q * nt + tid;
-      if (i < S * R) {
-        const int src = i / R, r = i - src * R;
-        atomicAdd(&total[r], vr[q]);
-        if (src < s) atomicAdd(&base[r], vr[q]);
+    for (int u = 0; u < kNotifySrcBatch; ++u) {
+      const bool before = src0 + u * nw < s;
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        tot[i] += vr[u][i];
+        bas[i] += before ? vr[u][i] : 0;
       }
-      if (do_e && i < ne * S) atomicAdd(&eacc[i / S], ve[q]);
+      eac += ve[u];
+    }
+  }
+  if constexpr (kLazy) {
+    if (lazy && tid < T) first = decode_row_words(rw, R);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    const int r = kWave * i + lane;
+    if (r < R) {
+      if (tot[i]) atomicAdd(&total[r], tot[i]);
+      if (bas[i]) atomicAdd(&base[r], bas[i]);
+    }
+  }
+  if (e_lane && eac) atomicAdd(&eacc[lane], eac);
+  if (do_e) {                                         // owned experts past the first 64 (few sources)
+    for (int k0 = kWave; k0 < ne; k0 += kWave) {
+      const int k = k0 + lane;
+      int acc = 0;
+      if (k < ne)
+        for (int src = w; src < S; src += nw) acc += a.ntpe[static_cast<int64_t>(src) * a.E + s + k * S];
+      if (k < ne && acc) atomicAdd(&eacc[k], acc);
     }
   }
   __syncthreads();
@@ -129,7 +201,8 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     }
   }
 
-  const int tc = T > 0 ? (T + C - 1) / C : 1;
+  const int tc = a.tcdiv.d;
+  const bool fast_tc = T <= (1 << 20);                // FastDiv is exact there
   for (int t0 = 0; t0 < T; t0 += blockDim.x) {
     const int t = t0 + tid;
     const bool valid = t < T;
@@ -150,25 +223,38 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       if (lane < rend) wt[w][r0 + lane] = mine;
     }
     __syncthreads();
-    for (int r = tid; r < R; r += blockDim.x) {
-      int acc = run[r];
-      for (int q = 0; q < nw; ++q) {
-        const int v = wt[q][r];
-        wt[q][r] = acc;
-        acc += v;
+    // this wavefront's exclusive base per rank within source s: earlier
+    // tiles (run) plus the earlier wavefronts of this tile; all reads independent
+    int pre[MW], tile[MW];
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int r = kWave * i + lane;
+      int acc = 0, all = 0;
+      if (r < R) {
+        acc = run[r];
+        for (int q = 0; q < nw; ++q) {
+          const int v = wt[q][r];
+          acc += q < w ? v : 0;
+          all += v;
+        }
       }
-      run[r] = acc;
+      pre[i] = acc;
+      tile[i] = all;
     }
-    __syncthreads();
     // pass 2: exclusive rank within source s -> send_head, channel prefixes.
-    // Lane j holds rank r0 + j's wavefront base and rank base (two LDS reads
-    // per 64 ranks, no dependent LDS chain); per-rank values come by readlane.
-    const bool last_in_channel = valid && ((t % tc) == tc - 1 || t == T - 1);
+    // Lane j holds rank r0 + j's bases in registers; per-rank values come by
+    // readlane, so no lane walks a dependent LDS chain.
+    const int ch = fast_tc ? fdiv(t, a.tcdiv) : t / tc;   // channel of token t
+    const bool last_in_channel = valid && (t - ch * tc == tc - 1 || t == T - 1);
     const uint64_t clast = ballot(last_in_channel);
-    for (int r0 = 0; r0 < R; r0 += kWave) {
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int r0 = kWave * i;
+      if (r0 >= R) break;
       const int rend = R - r0 < kWave ? R - r0 : kWave;
-      const int wt_l = lane < rend ? wt[w][r0 + lane] : 0;
+      const int wt_l = pre[i];
       const int base_l = lane < rend ? base[r0 + lane] : 0;
+      const int pos_l = base_l + wt_l;
       uint64_t myb = 0;                                // lane j: this wavefront's ballot for rank r0 + j
       for (int j0 = 0; j0 < rend; j0 += 4) {
         int v[4];
@@ -180,7 +266,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
             const bool bit = m.get(r0 + j) != 0;
             const uint64_t b = ballot(bit);
             myb = lane == j ? b : myb;
-            if (bit) v[q] = readlane(base_l, j) + readlane(wt_l, j) + __popcll(b & lanemask_lt());
+            if (bit) v[q] = readlane(pos_l, j) + __popcll(b & lanemask_lt());
           }
         }
         if (valid) {
@@ -196,7 +282,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       // a token of this wavefront (lane j writes rank r0 + j)
       for (uint64_t cl = clast; cl != 0; cl &= cl - 1) {
         const int L = __builtin_ctzll(cl);
-        const int cc = readlane(t, L) / tc;
+        const int cc = readlane(ch, L);
         const uint64_t upto = L == kWave - 1 ? ~0ull : ((2ull << L) - 1);   // lanes 0..L
         if (lane < rend) {
           const int inc = wt_l + __popcll(myb & upto);
@@ -207,7 +293,16 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       }
     }
     __syncthreads();
+    // carry into the next tile (wavefront 0's base is the carry itself)
+    if (w == 0) {
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        const int r = kWave * i + lane;
+        if (r < R) run[r] = pre[i] + tile[i];
+      }
+    }
   }
+  __syncthreads();
 
   // rank prefix row of this source; channels past the last token hold the total
   const int nonempty = T > 0 ? (T + tc - 1) / tc : 0;

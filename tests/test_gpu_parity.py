@@ -88,6 +88,7 @@ SMALL = [
     ("r256", 2, 64, 264, 2048, 256, 9, 3, 1),
     ("r1", 2, 40, 128, 8, 1, 2, 4, 1),
     ("k20", 2, 50, 128, 64, 8, 20, 4, 1),            # top-20: the pack writes the receive metadata
+    ("r8-tiles", 2, 1300, 64, 32, 8, 4, 24, 2),      # 8-byte membership rows, 2 token tiles in the notify
 ]
 
 
