@@ -147,6 +147,7 @@ miep::NotifyArgs notify_args(const miep_problem* p, const miep_handle* h, const 
   na.L = p->num_experts / p->num_ranks;
   na.align = p->expert_alignment;
   na.tcdiv = miep::make_fastdiv(p->num_tokens > 0 ? (p->num_tokens + p->num_channels - 1) / p->num_channels : 1);
+  na.nonempty = p->num_tokens > 0 ? (p->num_tokens + na.tcdiv.d - 1) / na.tcdiv.d : 0;
   na.in_rank = h->is_token_in_rank;
   na.ntpr = ntpr;
   na.ntpe = ntpe;

@@ -51,6 +51,7 @@ struct NotifyArgs {
   int S, T, R, C, E, L, align;
   int group_w;
   FastDiv tcdiv;            // tokens per channel, ceil(T / C)
+  int nonempty;             // channels holding tokens, ceil(T / tcdiv.d)
   const uint8_t* in_rank;   // [S*T][R] (or [S*T][R*group_w])
   const int32_t* ntpr;      // [S][R]
   const int32_t* ntpe;      // [S][E] or null

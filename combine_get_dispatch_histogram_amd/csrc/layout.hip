@@ -19,6 +19,19 @@
 
 namespace miep {
 
+// Membership row of one token: R bytes, 1 where the rank is in the mask.
+template <int MW>
+__device__ __forceinline__ void store_member_row(uint8_t* out, int R, const RankMask<MW>& m) {
+  if ((R & 3) == 0) {
+    for (int r0 = 0; r0 < R; r0 += 4) {
+      const uint32_t b = m.get(r0) | (m.get(r0 + 1) << 8) | (m.get(r0 + 2) << 16) | (m.get(r0 + 3) << 24);
+      *reinterpret_cast<uint32_t*>(out + r0) = b;
+    }
+  } else {
+    for (int r = 0; r < R; ++r) out[r] = static_cast<uint8_t>(m.get(r));
+  }
+}
+
 template <int MW>
 __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
   extern __shared__ int32_t lds[];
@@ -27,15 +40,32 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
   int32_t* rcnt = hist + a.E;     // [R]
   int32_t* gcnt = rcnt + a.R;     // [G]
   const int s = blockIdx.x;
+  const int lane = lane_id();
+  const bool vec = (a.K & 1) == 0 && (reinterpret_cast<uintptr_t>(a.topk_idx) & 15u) == 0;   // 16-byte rows pairs
+  // the first 8 top-k entries of this thread's first token: loaded before
+  // the LDS clear and its barrier, so that their latency covers both
+  const bool pre_ok = vec && a.K >= 8 && static_cast<int>(threadIdx.x) < a.T;
+  int64_t pre8[8];
+  if (pre_ok) {
+    const int64_t* row = a.topk_idx + (static_cast<int64_t>(s) * a.T + threadIdx.x) * a.K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4u v = ld16(row + 2 * j);
+      pre8[2 * j] = static_cast<int64_t>((static_cast<uint64_t>(v.y) << 32) | v.x);
+      pre8[2 * j + 1] = static_cast<int64_t>((static_cast<uint64_t>(v.w) << 32) | v.z);
+    }
+  }
   for (int i = threadIdx.x; i < a.E + a.R + G; i += blockDim.x) lds[i] = 0;
   __syncthreads();
 
-  const int lane = lane_id();
-  const bool vec = (a.K & 1) == 0 && (reinterpret_cast<uintptr_t>(a.topk_idx) & 15u) == 0;   // 16-byte rows pairs
   // whole wavefronts walk the tokens (the rank counts below are wavefront
   // ballots, so every lane of a wavefront takes part in each iteration)
   const int tpad = (a.T + kWave - 1) / kWave * kWave;
+  RankMask<MW> m_last;                 // this thread's token of the last tile
+  m_last.clear();
+  int t_last = -1;
   for (int t = threadIdx.x; t < tpad; t += blockDim.x) {
+    t_last = t;
     const bool valid = t < a.T;
     const int64_t n = static_cast<int64_t>(s) * a.T + t;
     const int64_t* row = a.topk_idx + n * a.K;
@@ -44,7 +74,10 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
     if (valid) {
       for (int k0 = 0; k0 < a.K; k0 += 8) {         // 8 entries in flight (16-byte loads when aligned)
         int64_t e8[8];
-        if (k0 + 8 <= a.K && vec) {
+        if (k0 == 0 && pre_ok && t == static_cast<int>(threadIdx.x)) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e8[j] = pre8[j];
+        } else if (k0 + 8 <= a.K && vec) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const v4u v = ld16(row + k0 + 2 * j);
@@ -63,16 +96,11 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
           m.set(fdiv(static_cast<int>(e), a.Ldiv));
         }
       }
-      uint8_t* out = a.in_rank + n * a.R;
-      if ((a.R & 3) == 0) {
-        for (int r0 = 0; r0 < a.R; r0 += 4) {
-          const uint32_t b = m.get(r0) | (m.get(r0 + 1) << 8) | (m.get(r0 + 2) << 16) | (m.get(r0 + 3) << 24);
-          *reinterpret_cast<uint32_t*>(out + r0) = b;
-        }
-      } else {
-        for (int r = 0; r < a.R; ++r) out[r] = static_cast<uint8_t>(m.get(r));
-      }
+      // the last tile's rows are written after the final barrier, which
+      // would otherwise wait for these stores to land
+      if (t + static_cast<int>(blockDim.x) < tpad) store_member_row(a.in_rank + n * a.R, a.R, m);
     }
+    m_last = m;
     // rank and RDMA-group counts: one ballot per rank over the wavefront;
     // lane j of each 64-rank chunk adds the chunk's count for rank r0 + j
     for (int r0 = 0; r0 < a.R; r0 += kWave) {
@@ -97,6 +125,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
     }
   }
   __syncthreads();
+  if (t_last >= 0 && t_last < a.T) store_member_row(a.in_rank + (static_cast<int64_t>(s) * a.T + t_last) * a.R, a.R, m_last);
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.ntpe[static_cast<int64_t>(s) * a.E + e] = hist[e];
   for (int r = threadIdx.x; r < a.R; r += blockDim.x) a.ntpr[static_cast<int64_t>(s) * a.R + r] = rcnt[r];
   if (a.ntp_rdma)

@@ -37,28 +37,31 @@ __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t v) {
   return ((v & 0x01010101u) * 0x10204080u) >> 28;
 }
 
-// Membership row of R <= 64 ranks (R % 4 == 0) kept as raw words between
+// Membership row of R <= 4*NW ranks (R % 4 == 0) kept as raw words between
 // the loads and the decode, so that independent loads issued in between are
 // in flight together.  R == 8 rows (8-byte aligned) take one 8-byte load.
+template <int NW>
 struct RowWords {
-  uint32_t v[16];
+  uint32_t v[NW];
 };
-__device__ __forceinline__ void issue_row_words(const uint8_t* row, int R, bool one8, RowWords& rw) {
-  if (one8) {
+template <int NW>
+__device__ __forceinline__ void issue_row_words(const uint8_t* row, int R, bool one8, RowWords<NW>& rw) {
+  if (NW >= 2 && one8) {
     const uint64_t q = *reinterpret_cast<const uint64_t*>(row);
     rw.v[0] = static_cast<uint32_t>(q);
     rw.v[1] = static_cast<uint32_t>(q >> 32);
 #pragma unroll
-    for (int i = 2; i < 16; ++i) rw.v[i] = 0u;
+    for (int i = 2; i < NW; ++i) rw.v[i] = 0u;
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rw.v[i] = 4 * i < R ? *reinterpret_cast<const uint32_t*>(row + 4 * i) : 0u;
+    for (int i = 0; i < NW; ++i) rw.v[i] = 4 * i < R ? *reinterpret_cast<const uint32_t*>(row + 4 * i) : 0u;
   }
 }
-__device__ __forceinline__ RankMask<1> decode_row_words(const RowWords& rw, int R) {
+template <int NW>
+__device__ __forceinline__ RankMask<1> decode_row_words(const RowWords<NW>& rw, int R) {
   uint64_t w = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < NW; ++i)
     if (4 * i < R) w |= static_cast<uint64_t>(nonzero_bytes4(rw.v[i])) << (4 * i);
   RankMask<1> m;
   m.w[0] = w;
@@ -67,10 +70,14 @@ __device__ __forceinline__ RankMask<1> decode_row_words(const RowWords& rw, int 
 
 // Destination set of token n: its rank row, or (GROUPED, group_w == 8) one
 // bit per group of 8 ranks, set when any of the group's 8 bytes is set (one
-// 8-byte load per group).
-template <int MW, bool GROUPED>
+// 8-byte load per group).  RB <= 8: rows of 4 or 8 bytes.
+template <int MW, bool GROUPED, int RB>
 __device__ __forceinline__ RankMask<MW> load_member(const NotifyArgs& a, int64_t n) {
-  if constexpr (!GROUPED) {
+  if constexpr (RB <= 8 && MW == 1 && !GROUPED) {
+    RowWords<2> rw;
+    issue_row_words<2>(a.in_rank + n * a.R, a.R, a.R == 8 && (reinterpret_cast<uintptr_t>(a.in_rank) & 7u) == 0, rw);
+    return decode_row_words<2>(rw, a.R);
+  } else if constexpr (!GROUPED) {
     return load_rank_row<MW>(a.in_rank + n * a.R, a.R);
   } else {
     const uint64_t* row = reinterpret_cast<const uint64_t*>(a.in_rank + n * a.R * 8);
@@ -88,8 +95,9 @@ __device__ __forceinline__ RankMask<MW> load_member(const NotifyArgs& a, int64_t
 // divides (wavefronts walk whole count rows; channel indices use FastDiv),
 // one round trip for all the loads of the first token tile, and no serial
 // scan across wavefronts (each wavefront sums the earlier ones' counts from
-// LDS with independent reads).
-template <int MW, bool GROUPED>
+// LDS with independent reads).  RB bounds the ranks per row at compile time
+// (8: rows of at most 8 ranks with unrolled rank loops; else 64*MW).
+template <int MW, bool GROUPED, int RB>
 __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   __shared__ int32_t base[kMaxRanks];                 // rows of rank r from sources < s
   __shared__ int32_t total[kMaxRanks];                // rows of rank r from all sources
@@ -109,14 +117,15 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
 
   // (1) the first token tile's membership row: loads issued, decoded later
   constexpr bool kLazy = MW == 1 && !GROUPED;
+  constexpr int kNW = RB <= 8 ? 2 : 16;               // row words
   const bool lazy = kLazy && (R & 3) == 0;
   const bool one8 = R == 8 && (reinterpret_cast<uintptr_t>(a.in_rank) & 7u) == 0;
-  RowWords rw;
+  RowWords<kNW> rw;
   RankMask<MW> first;
   first.clear();
   if (tid < T) {
-    if (lazy) issue_row_words(a.in_rank + (static_cast<int64_t>(s) * T + tid) * R, R, one8, rw);
-    else first = load_member<MW, GROUPED>(a, static_cast<int64_t>(s) * T + tid);
+    if (lazy) issue_row_words<kNW>(a.in_rank + (static_cast<int64_t>(s) * T + tid) * R, R, one8, rw);
+    else first = load_member<MW, GROUPED, RB>(a, static_cast<int64_t>(s) * T + tid);
   }
   for (int r = tid; r < R; r += blockDim.x) {
     base[r] = 0;
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     }
   }
   if constexpr (kLazy) {
-    if (lazy && tid < T) first = decode_row_words(rw, R);
+    if (lazy && tid < T) first = decode_row_words<kNW>(rw, R);
   }
   __syncthreads();
 #pragma unroll
@@ -180,29 +189,11 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   }
   __syncthreads();
 
-  // receive offsets: exclusive scan of the per-rank totals (workgroup 0)
-  if (s == 0 && w == 0) {
-    int carry = 0;
-    for (int r0 = 0; r0 < R; r0 += kWave) {
-      const int r = r0 + lane;
-      const int v = r < R ? total[r] : 0;
-      const int inc = wave_inclusive_scan(v);
-      if (r < R) a.off[r] = carry + inc - v;
-      carry += readlane(inc, kWave - 1);
-    }
-    if (lane == 0) a.off[R] = carry;
-  }
-
-  // per-expert receive counts, rounded up to the expert alignment
-  if (do_e) {
-    for (int k = tid; k < ne; k += blockDim.x) {
-      const int64_t sum = eacc[k];
-      a.nrte[s + k * S] = static_cast<int32_t>((sum + a.align - 1) / a.align * a.align);
-    }
-  }
-
   const int tc = a.tcdiv.d;
   const bool fast_tc = T <= (1 << 20);                // FastDiv is exact there
+  int fin[MW];                                        // tokens of s per rank (wavefront 0, after the loop)
+#pragma unroll
+  for (int i = 0; i < MW; ++i) fin[i] = 0;
   for (int t0 = 0; t0 < T; t0 += blockDim.x) {
     const int t = t0 + tid;
     const bool valid = t < T;
@@ -210,13 +201,15 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     RankMask<MW> m = first;
     if (t0 > 0) {
       m.clear();
-      if (valid) m = load_member<MW, GROUPED>(a, n);
+      if (valid) m = load_member<MW, GROUPED, RB>(a, n);
     }
     // pass 1: per-wavefront counts, lane j of the wave keeps rank r0 + j
     for (int r0 = 0; r0 < R; r0 += kWave) {
       const int rend = R - r0 < kWave ? R - r0 : kWave;
       int mine = 0;
-      for (int j = 0; j < rend; ++j) {
+#pragma unroll(RB <= 8 ? RB : 1)
+      for (int j = 0; j < (RB < kWave ? RB : kWave); ++j) {
+        if (j >= rend) break;
         const int c = __popcll(ballot(m.get(r0 + j) != 0));
         mine = lane == j ? c : mine;
       }
@@ -256,7 +249,9 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       const int base_l = lane < rend ? base[r0 + lane] : 0;
       const int pos_l = base_l + wt_l;
       uint64_t myb = 0;                                // lane j: this wavefront's ballot for rank r0 + j
-      for (int j0 = 0; j0 < rend; j0 += 4) {
+#pragma unroll(RB <= 8 ? RB / 4 : 1)
+      for (int j0 = 0; j0 < (RB < kWave ? RB : kWave); j0 += 4) {
+        if (j0 >= rend) break;
         int v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -292,25 +287,60 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
         }
       }
     }
-    __syncthreads();
-    // carry into the next tile (wavefront 0's base is the carry itself)
-    if (w == 0) {
+    // carry into the next tile (wavefront 0's base is the carry itself);
+    // after the last tile wavefront 0 keeps the source's totals in registers
 #pragma unroll
-      for (int i = 0; i < MW; ++i) {
-        const int r = kWave * i + lane;
-        if (r < R) run[r] = pre[i] + tile[i];
+    for (int i = 0; i < MW; ++i) fin[i] = pre[i] + tile[i];
+    if (t0 + static_cast<int>(blockDim.x) < T) {
+      __syncthreads();
+      if (w == 0) {
+#pragma unroll
+        for (int i = 0; i < MW; ++i) {
+          const int r = kWave * i + lane;
+          if (r < R) run[r] = fin[i];
+        }
       }
     }
   }
-  __syncthreads();
 
-  // rank prefix row of this source; channels past the last token hold the total
-  const int nonempty = T > 0 ? (T + tc - 1) / tc : 0;
-  for (int r = tid; r < R; r += blockDim.x) {
-    a.rpm[static_cast<int64_t>(s) * R + r] = base[r] + run[r];
-    for (int c = nonempty; c < C; ++c) {
-      a.cpm[(static_cast<int64_t>(s) * R + r) * C + c] = run[r];
-      a.rcpm[(static_cast<int64_t>(r) * S + s) * C + c] = base[r] + run[r];
+  // Everything below only stores, after the last barrier (a barrier's
+  // fence waits for the wavefront's outstanding global stores).
+  // Rank prefix row of this source; channels past the last token hold the total.
+  if (w == 0) {
+    const int nonempty = a.nonempty;
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+      const int r = kWave * i + lane;
+      if (r < R) {
+        const int b = base[r];
+        a.rpm[static_cast<int64_t>(s) * R + r] = b + fin[i];
+        for (int c = nonempty; c < C; ++c) {
+          a.cpm[(static_cast<int64_t>(s) * R + r) * C + c] = fin[i];
+          a.rcpm[(static_cast<int64_t>(r) * S + s) * C + c] = b + fin[i];
+        }
+      }
+    }
+  }
+  // receive offsets: exclusive scan of the per-rank totals (workgroup 0)
+  if (s == 0 && w == 0) {
+    int carry = 0;
+    for (int r0 = 0; r0 < R; r0 += kWave) {
+      const int r = r0 + lane;
+      const int v = r < R ? total[r] : 0;
+      const int inc = wave_inclusive_scan(v);
+      if (r < R) a.off[r] = carry + inc - v;
+      carry += readlane(inc, kWave - 1);
+    }
+    if (lane == 0) a.off[R] = carry;
+  }
+
+  // per-expert receive counts, rounded up to the expert alignment (the sum
+  // is at most S*T < 2^31, so sum + align - 1 fits 32 unsigned bits)
+  if (do_e) {
+    const uint32_t al = static_cast<uint32_t>(a.align);
+    for (int k = tid; k < ne; k += blockDim.x) {
+      const uint32_t sum = static_cast<uint32_t>(eacc[k]);
+      a.nrte[s + k * S] = static_cast<int32_t>(al == 1u ? sum : (sum + al - 1u) / al * al);
     }
   }
 }
@@ -333,11 +363,13 @@ hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
   const int ne_max = (a.E + a.S - 1) / a.S;  // experts owned by workgroup 0 (the most)
   const size_t lds = sizeof(int32_t) * static_cast<size_t>(ne_max > 0 ? ne_max : 1);
   if (a.group_w != 0)      // groups: R <= 32 destinations
-    hipLaunchKernelGGL((notify_kernel<1, true>), dim3(a.S), dim3(threads), lds, st, a);
+    hipLaunchKernelGGL((notify_kernel<1, true, 64>), dim3(a.S), dim3(threads), lds, st, a);
+  else if (a.R <= 8 && (a.R & 3) == 0)
+    hipLaunchKernelGGL((notify_kernel<1, false, 8>), dim3(a.S), dim3(threads), lds, st, a);
   else if (a.R <= 64)
-    hipLaunchKernelGGL((notify_kernel<1, false>), dim3(a.S), dim3(threads), lds, st, a);
+    hipLaunchKernelGGL((notify_kernel<1, false, 64>), dim3(a.S), dim3(threads), lds, st, a);
   else
-    hipLaunchKernelGGL((notify_kernel<4, false>), dim3(a.S), dim3(threads), lds, st, a);
+    hipLaunchKernelGGL((notify_kernel<4, false, 256>), dim3(a.S), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 
