@@ -25,7 +25,6 @@
 namespace miep {
 
 constexpr int kNotifyMaxWaves = 16;
-constexpr int kNotifySrcBatch = 8;   // sources whose count rows a wavefront loads at once
 
 // Nonzero bytes of a 32-bit word -> 4 bits (byte j -> bit j): fold each byte
 // onto its low bit, then one multiply moves bits 0, 8, 16, 24 to 28..31 (the
@@ -53,8 +52,11 @@ __device__ __forceinline__ void issue_row_words(const uint8_t* row, int R, bool 
 #pragma unroll
     for (int i = 2; i < NW; ++i) rw.v[i] = 0u;
   } else {
+    // unconditional loads from clamped offsets (words past the row are
+    // skipped by the decode): a load whose result is selected right away
+    // gets its own wait from the compiler
 #pragma unroll
-    for (int i = 0; i < NW; ++i) rw.v[i] = 4 * i < R ? *reinterpret_cast<const uint32_t*>(row + 4 * i) : 0u;
+    for (int i = 0; i < NW; ++i) rw.v[i] = *reinterpret_cast<const uint32_t*>(row + (4 * i < R ? 4 * i : R - 4));
   }
 }
 template <int NW>
@@ -74,6 +76,7 @@ __device__ __forceinline__ RankMask<1> decode_row_words(const RowWords<NW>& rw, 
 template <int MW, bool GROUPED, int RB>
 __device__ __forceinline__ RankMask<MW> load_member(const NotifyArgs& a, int64_t n) {
   if constexpr (RB <= 8 && MW == 1 && !GROUPED) {
+    if ((a.R & 3) != 0) return load_rank_row<1>(a.in_rank + n * a.R, a.R);   // byte rows
     RowWords<2> rw;
     issue_row_words<2>(a.in_rank + n * a.R, a.R, a.R == 8 && (reinterpret_cast<uintptr_t>(a.in_rank) & 7u) == 0, rw);
     return decode_row_words<2>(rw, a.R);
@@ -95,8 +98,13 @@ __device__ __forceinline__ RankMask<MW> load_member(const NotifyArgs& a, int64_t
 // divides (wavefronts walk whole count rows; channel indices use FastDiv),
 // one round trip for all the loads of the first token tile, and no serial
 // scan across wavefronts (each wavefront sums the earlier ones' counts from
-// LDS with independent reads).  RB bounds the ranks per row at compile time
-// (8: rows of at most 8 ranks with unrolled rank loops; else 64*MW).
+// LDS with independent reads).  RB bounds the ranks per row at compile time:
+// 8 = rows of at most 8 ranks, one ballot per rank (unrolled); 64 = rows of
+// up to 64 ranks (or groups), where the wavefront's membership masks go
+// through LDS and lane r assembles rank r's 64-token bit column, which gives
+// the rank's count and every in-wavefront prefix by popcount, and send_head
+// leaves one token row at a time with the ranks side by side (contiguous
+// stores); 256 = rows of up to 256 ranks, one ballot per rank.
 template <int MW, bool GROUPED, int RB>
 __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   __shared__ int32_t base[kMaxRanks];                 // rows of rank r from sources < s
@@ -107,15 +115,71 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int w = tid / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: source loops stay scalar
   const int nw = blockDim.x / kWave;
   const int R = a.R, T = a.T, C = a.C, S = a.S;
 
-  extern __shared__ int32_t eacc[];                   // per-expert sums of the experts this workgroup owns
+  constexpr bool kWide = MW == 1 && RB == 64;
+  constexpr int kRankUnroll = RB <= 8 ? RB : 1;        // ballot loops: unrolled for rows of <= 8 ranks
+  constexpr int kQuadUnroll = RB <= 8 ? RB / 4 : 1;
+  extern __shared__ uint64_t dyn[];
+  uint64_t* mk = dyn;                                  // [nw][64] membership masks (wide rows)
+  // wide rows: [nw][64] masks (later the rank columns), then [nw][64] rank bases
+  int32_t* eacc = reinterpret_cast<int32_t*>(dyn + (kWide ? nw * kWave : 0)) + (kWide ? nw * kWave : 0);
   const int ne = a.E > s ? (a.E - s + S - 1) / S : 0; // experts e = s + k*S
   const bool do_e = a.nrte != nullptr && a.ntpe != nullptr;
 
-  // (1) the first token tile's membership row: loads issued, decoded later
+  // (1) rank totals / bases and the sums of the owned experts' counts:
+  // wavefront w walks sources w, w + nw, ...; lane j of a 64-wide chunk
+  // takes rank 64*i + j (and owned expert j), so the loads are whole rows.
+  // The first batch is issued before the membership loads, so that a wait
+  // the compiler places on those cannot hold the count loads back.
+  int tot[MW], bas[MW];
+#pragma unroll
+  for (int i = 0; i < MW; ++i) tot[i] = bas[i] = 0;
+  int eac = 0;
+  const bool e_lane = do_e && lane < ne;
+  // every load is unconditional, from a clamped (always valid) index, and
+  // masked afterwards; a batch of B sources is chosen by a uniform branch
+  const int32_t* ep = do_e ? a.ntpe : a.ntpr;
+  const int kc = e_lane ? lane : 0;
+  int vr[16][MW], ve[16];
+  auto issue_counts = [&](int src0, int B) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (u < B) {
+        const int src = src0 + u * nw;
+        const int sc = src < S ? src : S - 1;
+#pragma unroll
+        for (int i = 0; i < MW; ++i) {
+          const int r = kWave * i + lane;
+          vr[u][i] = a.ntpr[sc * R + (r < R ? r : R - 1)];
+        }
+        ve[u] = ep[do_e ? static_cast<int64_t>(sc) * a.E + s + kc * S : 0];
+      }
+    }
+  };
+  auto add_counts = [&](int src0, int B) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (u < B) {
+        const int src = src0 + u * nw;
+        const bool before = src < s;                  // (s < S, so also src < S)
+#pragma unroll
+        for (int i = 0; i < MW; ++i) {
+          const int v = src < S && kWave * i + lane < R ? vr[u][i] : 0;
+          tot[i] += v;
+          bas[i] += before ? v : 0;
+        }
+        eac += e_lane && src < S ? ve[u] : 0;
+      }
+    }
+  };
+  const int need = w < S ? (S - w + nw - 1) / nw : 0;   // sources this wavefront walks
+  const int b0 = need <= 1 ? 1 : (need <= 4 ? 4 : 16);
+  if (need > 0) issue_counts(w, b0);
+
+  // (2) the first token tile's membership row: loads issued, decoded later
   constexpr bool kLazy = MW == 1 && !GROUPED;
   constexpr int kNW = RB <= 8 ? 2 : 16;               // row words
   const bool lazy = kLazy && (R & 3) == 0;
@@ -133,37 +197,10 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     run[r] = 0;
   }
   for (int k = tid; k < ne; k += blockDim.x) eacc[k] = 0;
-
-  // (2) rank totals / bases and the sums of the owned experts' counts:
-  // wavefront w walks sources w, w + nw, ...; lane j of a 64-wide chunk
-  // takes rank 64*i + j (and owned expert j), so the loads are whole rows
-  int tot[MW], bas[MW];
-#pragma unroll
-  for (int i = 0; i < MW; ++i) tot[i] = bas[i] = 0;
-  int eac = 0;
-  const bool e_lane = do_e && lane < ne;
-  for (int src0 = w; src0 < S; src0 += kNotifySrcBatch * nw) {
-    int vr[kNotifySrcBatch][MW], ve[kNotifySrcBatch];
-#pragma unroll
-    for (int u = 0; u < kNotifySrcBatch; ++u) {
-      const int src = src0 + u * nw;
-#pragma unroll
-      for (int i = 0; i < MW; ++i) {
-        const int r = kWave * i + lane;
-        vr[u][i] = src < S && r < R ? a.ntpr[src * R + r] : 0;
-      }
-      ve[u] = e_lane && src < S ? a.ntpe[static_cast<int64_t>(src) * a.E + s + lane * S] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kNotifySrcBatch; ++u) {
-      const bool before = src0 + u * nw < s;
-#pragma unroll
-      for (int i = 0; i < MW; ++i) {
-        tot[i] += vr[u][i];
-        bas[i] += before ? vr[u][i] : 0;
-      }
-      eac += ve[u];
-    }
+  if (need > 0) add_counts(w, b0);
+  for (int src0 = w + 16 * nw; src0 < S; src0 += 16 * nw) {   // more than 16 sources per wavefront
+    issue_counts(src0, 16);
+    add_counts(src0, 16);
   }
   if constexpr (kLazy) {
     if (lazy && tid < T) first = decode_row_words<kNW>(rw, R);
@@ -204,16 +241,32 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       if (valid) m = load_member<MW, GROUPED, RB>(a, n);
     }
     // pass 1: per-wavefront counts, lane j of the wave keeps rank r0 + j
-    for (int r0 = 0; r0 < R; r0 += kWave) {
-      const int rend = R - r0 < kWave ? R - r0 : kWave;
-      int mine = 0;
-#pragma unroll(RB <= 8 ? RB : 1)
-      for (int j = 0; j < (RB < kWave ? RB : kWave); ++j) {
-        if (j >= rend) break;
-        const int c = __popcll(ballot(m.get(r0 + j) != 0));
-        mine = lane == j ? c : mine;
+    uint64_t col = 0;                                 // wide rows: bit q = token q of this wavefront goes to rank `lane`
+    if constexpr (kWide) {
+      mk[w * kWave + lane] = m.w[0];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the wavefront reads back its own masks
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const ulonglong2* mw = reinterpret_cast<const ulonglong2*>(mk + w * kWave);
+#pragma unroll 8
+      for (int q = 0; q < kWave / 2; ++q) {           // broadcast reads, two masks each
+        const ulonglong2 p = mw[q];
+        col |= ((p.x >> lane) & 1ull) << (2 * q);
+        col |= ((p.y >> lane) & 1ull) << (2 * q + 1);
       }
-      if (lane < rend) wt[w][r0 + lane] = mine;
+      if (lane < R) wt[w][lane] = __popcll(col);
+    } else {
+      for (int r0 = 0; r0 < R; r0 += kWave) {
+        const int rend = R - r0 < kWave ? R - r0 : kWave;
+        int mine = 0;
+#pragma unroll kRankUnroll
+        for (int j = 0; j < (RB < kWave ? RB : kWave); ++j) {
+          if (j >= rend) break;
+          const int c = __popcll(ballot(m.get(r0 + j) != 0));
+          mine = lane == j ? c : mine;
+        }
+        if (lane < rend) wt[w][r0 + lane] = mine;
+      }
     }
     __syncthreads();
     // this wavefront's exclusive base per rank within source s: earlier
@@ -240,8 +293,66 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
     const int ch = fast_tc ? fdiv(t, a.tcdiv) : t / tc;   // channel of token t
     const bool last_in_channel = valid && (t - ch * tc == tc - 1 || t == T - 1);
     const uint64_t clast = ballot(last_in_channel);
+    if constexpr (kWide) {
+      const int wt_l = pre[0];
+      const int base_l = lane < R ? base[lane] : 0;
+      const int pos_l = base_l + wt_l;
+      const int tw0 = t0 + w * kWave;                 // first token of this wavefront
+      const int nq = T - tw0 < kWave ? T - tw0 : kWave;
+      int32_t* row0 = a.send_head + (static_cast<int64_t>(s) * T + tw0) * R;
+      if ((R & 3) == 0) {
+        // rows leave as 16-byte pieces: lane (tq, j) writes ranks 4j..4j+3 of
+        // token q0 + tq, so one store instruction covers 64 / QP token rows
+        // (QP = R/4 rounded up to a power of two); the rank lanes' columns and
+        // bases go through this wavefront's LDS slot first
+        uint64_t* cb = mk + w * kWave;
+        int32_t* pb = reinterpret_cast<int32_t*>(mk + nw * kWave) + w * kWave;
+        cb[lane] = col;
+        pb[lane] = pos_l;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int ql = R >> 2;                        // lanes per token row
+        const int lg = ql <= 1 ? 0 : 32 - __builtin_clz(static_cast<unsigned>(ql - 1));
+        const int tq = lane >> lg, j = lane & ((1 << lg) - 1);
+        const bool act = j < ql;
+        uint64_t c4[4];
+        int p4[4];
 #pragma unroll
-    for (int i = 0; i < MW; ++i) {
+        for (int k = 0; k < 4; ++k) {
+          c4[k] = act ? cb[4 * j + k] : 0ull;
+          p4[k] = act ? pb[4 * j + k] : 0;
+        }
+        for (int q0 = 0; q0 < nq; q0 += kWave >> lg) {
+          const int q = q0 + tq;
+          if (act && q < nq) {
+            const uint64_t below = (1ull << q) - 1ull;
+            int v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              v[k] = ((c4[k] >> q) & 1ull) ? p4[k] + __popcll(c4[k] & below) : -1;
+            *reinterpret_cast<int4*>(row0 + static_cast<int64_t>(q) * R + 4 * j) = make_int4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      } else {
+        for (int q = 0; q < nq; ++q) {                // token q's row: lane r writes rank r
+          const bool bit = ((col >> q) & 1ull) != 0;
+          const int v = bit ? pos_l + __popcll(col & ((1ull << q) - 1ull)) : -1;
+          if (lane < R) row0[static_cast<int64_t>(q) * R + lane] = v;
+        }
+      }
+      for (uint64_t cl = clast; cl != 0; cl &= cl - 1) {
+        const int L = __builtin_ctzll(cl);
+        const int cc = readlane(ch, L);
+        const uint64_t upto = L == kWave - 1 ? ~0ull : ((2ull << L) - 1);   // tokens 0..L
+        if (lane < R) {
+          const int inc = wt_l + __popcll(col & upto);
+          a.cpm[(static_cast<int64_t>(s) * R + lane) * C + cc] = inc;
+          a.rcpm[(static_cast<int64_t>(lane) * S + s) * C + cc] = base_l + inc;
+        }
+      }
+    }
+    for (int i = 0; i < (kWide ? 0 : MW); ++i) {
       const int r0 = kWave * i;
       if (r0 >= R) break;
       const int rend = R - r0 < kWave ? R - r0 : kWave;
@@ -249,7 +360,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       const int base_l = lane < rend ? base[r0 + lane] : 0;
       const int pos_l = base_l + wt_l;
       uint64_t myb = 0;                                // lane j: this wavefront's ballot for rank r0 + j
-#pragma unroll(RB <= 8 ? RB / 4 : 1)
+#pragma unroll kQuadUnroll
       for (int j0 = 0; j0 < (RB < kWave ? RB : kWave); j0 += 4) {
         if (j0 >= rend) break;
         int v[4];
@@ -361,10 +472,18 @@ hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
   int threads = ((a.T + kWave - 1) / kWave) * kWave;
   threads = threads < kWave ? kWave : (threads > kNotifyMaxWaves * kWave ? kNotifyMaxWaves * kWave : threads);
   const int ne_max = (a.E + a.S - 1) / a.S;  // experts owned by workgroup 0 (the most)
-  const size_t lds = sizeof(int32_t) * static_cast<size_t>(ne_max > 0 ? ne_max : 1);
-  if (a.group_w != 0)      // groups: R <= 32 destinations
+  const bool wide = a.R > 8 && a.R <= 64;   // the notify_kernel<1, *, 64> instantiations
+  const size_t lds = sizeof(int32_t) * static_cast<size_t>(ne_max > 0 ? ne_max : 1) +
+                     (wide ? (sizeof(uint64_t) + sizeof(int32_t)) * static_cast<size_t>(threads) : 0);
+  // rows of <= 8 ranks (or groups): one unrolled ballot per rank; wider
+  // rows: the LDS bit transpose (measured on the 64-rank workload: 64-rank
+  // notify 18.0 -> 15.3 us with it, while 8 groups took 7.3 us with ballots
+  // against 11.1 us transposed)
+  if (a.group_w != 0 && a.R <= 8)   // groups: R <= 32 destinations
+    hipLaunchKernelGGL((notify_kernel<1, true, 8>), dim3(a.S), dim3(threads), lds, st, a);
+  else if (a.group_w != 0)
     hipLaunchKernelGGL((notify_kernel<1, true, 64>), dim3(a.S), dim3(threads), lds, st, a);
-  else if (a.R <= 8 && (a.R & 3) == 0)
+  else if (a.R <= 8)
     hipLaunchKernelGGL((notify_kernel<1, false, 8>), dim3(a.S), dim3(threads), lds, st, a);
   else if (a.R <= 64)
     hipLaunchKernelGGL((notify_kernel<1, false, 64>), dim3(a.S), dim3(threads), lds, st, a);
