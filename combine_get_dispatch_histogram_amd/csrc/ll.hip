@@ -44,8 +44,9 @@ __device__ __forceinline__ int ll_slot_scan(const LLArgs& a, int l, int s, int32
   const int64_t* idx = a.topk_idx + static_cast<int64_t>(s) * a.T * a.K;
   // a masked destination is not sent to, a masked source is not received from
   const bool masked = a.mask != nullptr && (a.mask[a.d] != 0 || a.mask[s] != 0);
+  // the carry is first read after the first barrier of the loop, so its
+  // reset needs no barrier of its own (the top-k loads go out at once)
   if (tid == 0) *carry_s = 0;
-  __syncthreads();
   for (int t0 = 0; t0 < a.T; t0 += kLLThreads) {
     const int t = t0 + tid;
     uint64_t kmask = 0;                           // entries k of token t that name the expert
@@ -79,7 +80,7 @@ __device__ __forceinline__ int ll_slot_scan(const LLArgs& a, int l, int s, int32
     }
     __syncthreads();
   }
-  return *carry_s;
+  return a.T > 0 ? *carry_s : 0;
 }
 
 // Per-(l, s) message counts, capped at M (one workgroup per block).
@@ -103,22 +104,22 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
   __shared__ int32_t wsum[kLLThreads / kWave];
   __shared__ int32_t carry_s;
-  __shared__ int32_t begin_s;
   const int l = blockIdx.x / a.R;
   const int s = blockIdx.x % a.R;
   const int tid = threadIdx.x, lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: row bases stay scalar
-  // first packed row of the block: messages of the earlier sources for expert l
-  if (w == 0) {
-    int part = 0;
-    for (int q = lane; q < s; q += kWave) part += a.msg_count[l * a.R + q];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
-    if (lane == 0) begin_s = part;
-  }
+  // first packed row of the block: messages of the earlier sources for
+  // expert l, summed by every wavefront; the first 64 counts are loaded
+  // unconditionally (clamped index) so that they are in flight with the
+  // scan's top-k loads, and masked only after the scan
+  const int p_raw = a.msg_count[l * a.R + (lane < a.R ? lane : a.R - 1)];
   const int cnt = ll_slot_scan(a, l, s, slot_tok, wsum, &carry_s);   // synchronises the workgroup
   const int n = cnt < a.M ? cnt : a.M;
-  const int begin = begin_s;
+  int part = lane < s ? p_raw : 0;
+  for (int q = lane + kWave; q < s; q += kWave) part += a.msg_count[l * a.R + q];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
+  const int begin = part;
   if (tid == 0 && blockIdx.y == 0) {             // once per (l, s), not per split workgroup
     a.layout_range[l * a.R + s] = (static_cast<int64_t>(begin) << 32) | static_cast<int64_t>(static_cast<uint32_t>(n));
     if (s == a.R - 1) {
