@@ -31,7 +31,7 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ int readlane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 // floor(n / f.d) for 0 <= n with n * f.d < 2^40 (see FastDiv).
-__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+__host__ __device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
   return static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(n)) * f.m) >> 40);
 }
 

@@ -89,6 +89,9 @@ SMALL = [
     ("r1", 2, 40, 128, 8, 1, 2, 4, 1),
     ("k20", 2, 50, 128, 64, 8, 20, 4, 1),            # top-20: the pack writes the receive metadata
     ("r8-tiles", 2, 1300, 64, 32, 8, 4, 24, 2),      # 8-byte membership rows, 2 token tiles in the notify
+    ("r40", 2, 300, 64, 80, 40, 6, 9, 1),            # bit-transpose notify: 10 of 16 lanes per token row
+    ("r24-tiles", 2, 1100, 64, 96, 24, 6, 7, 1),     # bit-transpose notify over 2 token tiles
+    ("r64-tiles", 1, 1100, 64, 128, 64, 4, 24, 1),   # 64 ranks, 2 token tiles, one source
 ]
 
 
