@@ -141,7 +141,8 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   const bool e_lane = do_e && lane < ne;
   // every load is unconditional, from a clamped (always valid) index, and
   // masked afterwards; a batch of B sources is chosen by a uniform branch
-  const int32_t* ep = do_e ? a.ntpe : a.ntpr;
+  const bool e_any = do_e && ne > 0;                  // expert s exists (E > s)
+  const int32_t* ep = e_any ? a.ntpe : a.ntpr;
   const int kc = e_lane ? lane : 0;
   int vr[16][MW], ve[16];
   auto issue_counts = [&](int src0, int B) {
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
           const int r = kWave * i + lane;
           vr[u][i] = a.ntpr[sc * R + (r < R ? r : R - 1)];
         }
-        ve[u] = ep[do_e ? static_cast<int64_t>(sc) * a.E + s + kc * S : 0];
+        ve[u] = ep[e_any ? static_cast<int64_t>(sc) * a.E + s + kc * S : 0];
       }
     }
   };
