@@ -447,6 +447,7 @@ LL_SMALL = [
     # name, R, T, M, H, E, K, d
     ("ll-tiny", 4, 6, 8, 512, 16, 3, 1),
     ("ll-ragged", 6, 300, 320, 1536, 24, 4, 5),
+    ("ll-r72", 72, 20, 24, 512, 144, 4, 70),        # > 64 earlier sources summed for the packed range
 ]
 
 
