@@ -92,6 +92,8 @@ SMALL = [
     ("r40", 2, 300, 64, 80, 40, 6, 9, 1),            # bit-transpose notify: 10 of 16 lanes per token row
     ("r24-tiles", 2, 1100, 64, 96, 24, 6, 7, 1),     # bit-transpose notify over 2 token tiles
     ("r64-tiles", 1, 1100, 64, 128, 64, 4, 24, 1),   # 64 ranks, 2 token tiles, one source
+    ("many-src", 40, 32, 64, 16, 4, 4, 5, 1),        # notify: > 16 sources per wavefront (batched count rows)
+    ("many-src-r16", 33, 16, 64, 32, 16, 4, 3, 1),   # the same on the bit-transpose path
 ]
 
 
