@@ -94,6 +94,7 @@ SMALL = [
     ("r64-tiles", 1, 1100, 64, 128, 64, 4, 24, 1),   # 64 ranks, 2 token tiles, one source
     ("many-src", 40, 32, 64, 16, 4, 4, 5, 1),        # notify: > 16 sources per wavefront (batched count rows)
     ("many-src-r16", 33, 16, 64, 32, 16, 4, 3, 1),   # the same on the bit-transpose path
+    ("huge-T", 1, (1 << 20) + 7, 8, 2, 2, 1, 3, 1),  # > 2^20 tokens per source: channel index by plain division
 ]
 
 
