@@ -457,10 +457,12 @@ hipError_t launch_ll_combine(const LLCombineArgs& a, hipStream_t st) {
   if (static_cast<int64_t>(a.R) * a.T == 0) return hipSuccess;
   const Tuning& tu = tuning();
   const int nv = a.H / 8;
-  // default: two 16-byte vectors per lane per token (2 KiB row pieces) when
-  // a row is a multiple of 128 vectors (measured: 14.3 us against 15.1 us
-  // with one vector per lane on the low-latency workload), else one
-  const int vpl = tu.llc_vpl > 0 ? tu.llc_vpl : (nv % (2 * kWave) == 0 ? 2 : 1);
+  // default: four 16-byte vectors per lane per token (4 KiB row pieces; the
+  // last slice of a row may be partial) for rows of at least 256 vectors
+  // (measured on the low-latency workload: 12.6-12.7 us against 13.3 us with
+  // two, 14.5 us with one), else two when a row is a multiple of 128
+  // vectors, else one
+  const int vpl = tu.llc_vpl > 0 ? tu.llc_vpl : (nv >= 4 * kWave ? 4 : (nv % (2 * kWave) == 0 ? 2 : 1));
   const int span = vpl * kWave;
   int nslices = tu.llc_slices > 0 ? tu.llc_slices : (nv + span - 1) / span;
   if (nslices < 1) nslices = 1;

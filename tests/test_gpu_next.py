@@ -179,6 +179,7 @@ LL_COMBINE_CASES = [
     ("ll-masked", 6, 300, 320, 1536, 24, 4, 5, (0, 3)),
     ("ll-wide", 1, 200, 200, 7168, 12, 9, 0, ()),     # one rank, K = 9 local entries: two load batches
     ("ll-odd-row", 5, 64, 64, 1000, 10, 2, 4, ()),    # row of 125 vectors: a ragged slice
+    ("ll-odd-wide", 4, 50, 64, 2120, 16, 4, 2, ()),   # row of 265 vectors: 4-vector slices, the last one partial
     ("ll-k1", 2, 100, 100, 256, 4, 1, 1, ()),         # 64 tokens per wavefront group
     ("ll-k64", 2, 16, 16, 256, 128, 64, 0, ()),       # one token per group
 ]
