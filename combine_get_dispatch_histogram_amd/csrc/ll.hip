@@ -18,7 +18,8 @@
 // deterministic.  Two kernels:
 //   count: one workgroup per (l, s) block scans source s's top-k for the
 //          expert and writes the block's message count;
-//   send:  kLLSplit workgroups per block repeat the (tiny) scan, take the
+//   send:  a few workgroups per block (kLLSplit; 6 for wide FP8 rows)
+//          repeat the (tiny) scan, take the
 //          block's packed range from the counts of the earlier sources, and
 //          cast and write each message and its packed row in one pass
 //          (16-byte loads and stores), so nothing is read back.
@@ -227,15 +228,20 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
   const int blocks = a.L * a.R;
   if (blocks == 0) return hipSuccess;
   const Tuning& tu = tuning();
-  const int split = tu.ll_split > 0 ? tu.ll_split : kLLSplit;
   // bf16: two 16-byte vectors per lane per task when a row is a multiple of
-  // 128 vectors (measured best with 8 workgroups per (l, s) block); FP8: one
-  // pair of vectors (16 channels) per lane when a row is 64 pairs' multiple
+  // 128 vectors, 8 workgroups per (l, s) block (measured best).  FP8: rows of
+  // at least 128 pairs of vectors take two pairs (32 channels) per lane with
+  // 6 workgroups per block (the last slice of a row may be partial; measured
+  // on the low-latency workload: 12.6 us against 13.0 us with one pair and 8
+  // workgroups, which fill every wavefront slot of the chip exactly), shorter
+  // rows one pair when a row is 64 pairs' multiple
+  const bool fp8_wide = a.use_fp8 && a.H / 16 >= 2 * kWave;
+  const int split = tu.ll_split > 0 ? tu.ll_split : (fp8_wide ? 6 : kLLSplit);
   int vpl;
   if (tu.ll_vpl > 0)
     vpl = tu.ll_vpl;
   else if (a.use_fp8)
-    vpl = (a.H / 16) % kWave == 0 ? 1 : 8;
+    vpl = fp8_wide ? 2 : ((a.H / 16) % kWave == 0 ? 1 : 8);
   else
     vpl = (a.H / 8) % (2 * kWave) == 0 ? 2 : 8;
   switch (vpl) {

@@ -451,6 +451,7 @@ LL_SMALL = [
     ("ll-tiny", 4, 6, 8, 512, 16, 3, 1),
     ("ll-ragged", 6, 300, 320, 1536, 24, 4, 5),
     ("ll-r72", 72, 20, 24, 512, 144, 4, 70),        # > 64 earlier sources summed for the packed range
+    ("ll-fp8-wide", 4, 40, 48, 2560, 16, 4, 1),     # FP8 rows of 160 pairs: two pairs per lane, partial last slice
 ]
 
 
