@@ -11,9 +11,10 @@
 // One workgroup owns one source partition, so every count is produced by a
 // single workgroup: no global atomics, no zero-fill launch.  Each thread
 // reads one token's K indices (16-byte loads), builds the rank bitmask in
-// registers, writes the membership row with 4-byte stores and counts its
-// experts in LDS; rank and RDMA-group counts are wavefront ballots, one LDS
-// add per rank per wavefront (integer adds, order-independent).
+// registers (expert -> rank by multiply-shift), writes the membership row
+// with 4-byte stores and counts its experts in LDS; rank and RDMA-group
+// counts are wavefront ballots, one LDS add per rank per wavefront (integer
+// adds, order-independent).
 #include "device.h"
 #include "kernels.h"
 

@@ -13,12 +13,14 @@
 //
 // One workgroup per source partition s.  Its rank bases (rows of rank r
 // before source s) come from the layout's num_tokens_per_rank, so the
-// workgroups never wait on each other.  The token scan is a 64-lane ballot
-// + popcount per rank and wavefront, then an LDS scan across the
-// workgroup's wavefronts; send_head rows leave as 16-byte stores.  (Splitting
-// a source over several workgroups, each counting the earlier tokens of its
-// source itself, measured slower: 14.2 us with 64-token tiles against 8.7 us
-// for the normal workload.)
+// workgroups never wait on each other.  Within a wavefront of 64 tokens the
+// per-rank counts and prefixes come from one ballot per rank (rows of <= 8
+// ranks) or from a bit transpose of the tokens' rank masks through LDS
+// (wider rows); each wavefront adds the earlier wavefronts' counts from LDS
+// with independent reads; send_head rows leave as 16-byte stores.
+// (Splitting a source over several workgroups, each counting the earlier
+// tokens of its source itself, measured slower: 14.2 us with 64-token tiles
+// against 8.7 us for the normal workload.)
 #include "device.h"
 #include "kernels.h"
 
