@@ -65,9 +65,9 @@ _I64 = ctypes.c_int64
 def _declare(lib):
     lib.oracle_layout.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
     lib.oracle_layout.restype = _I
-    lib.oracle_dispatch.argtypes = [_I] * 8 + [_I, _P, _P, _I, _P, _P, _P, _P, _I64] + [_P] * 11
+    lib.oracle_dispatch.argtypes = [_I] * 8 + [_I, _P, _P, _I, _P, _P, _P, _P, _I64] + [_P] * 12
     lib.oracle_dispatch.restype = _I
-    lib.oracle_cached_dispatch.argtypes = [_I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I64, _P, _P]
+    lib.oracle_cached_dispatch.argtypes = [_I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _I64, _P, _P, _P]
     lib.oracle_cached_dispatch.restype = _I
     lib.oracle_combine.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P]
     lib.oracle_combine.restype = _I
@@ -83,8 +83,8 @@ def _declare(lib):
     # rdma_capacity + 9 pointers, capacity + 6 pointers
     lib.oracle_relay_dispatch.argtypes = [_I] * 7 + [_I, _P, _P, _I, _P, _P, _P, _I64] + [_P] * 9 + [_I64] + [_P] * 6
     lib.oracle_relay_dispatch.restype = _I
-    # S T H K R, y w bias0 bias1, capacity off, rdma_capacity roff nvl_head rdma_head, 5 outputs
-    lib.oracle_relay_combine.argtypes = [_I] * 5 + [_P] * 4 + [_I64, _P, _I64, _P, _P, _P] + [_P] * 5
+    # S T H K R, y w bias0 bias1, capacity off, rdma_capacity roff nvl_head rdma_head, partial_f32, 6 outputs
+    lib.oracle_relay_combine.argtypes = [_I] * 5 + [_P] * 4 + [_I64, _P, _I64, _P, _P, _P, _I] + [_P] * 6
     lib.oracle_relay_combine.restype = _I
     lib.oracle_e4m3_encode_n.argtypes = [_I64, _P, _P]
     lib.oracle_e4m3_decode_n.argtypes = [_I64, _P, _P]
@@ -134,15 +134,32 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
     return (_c(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def fp8_quantize(x_bf16: np.ndarray, round_scale: bool):
-    """x_bf16: uint16 [rows][H] -> (codes u8 [rows][H], scale_inv f32 [rows][H/128], ue8m0 u8 or None)."""
+def fp8_quantize(x_bf16: np.ndarray, round_scale: bool, threads: int = 1):
+    """x_bf16: uint16 [rows][H] -> (codes u8 [rows][H], scale_inv f32 [rows][H/128], ue8m0 u8 or None).
+
+    Rows are quantised independently, so ``threads`` > 1 only splits the rows
+    into contiguous chunks, each handed to the same C function on its own
+    thread (ctypes releases the GIL during the call)."""
     x = _c(x_bf16, np.uint16)
     rows, H = x.shape
     codes = np.empty((rows, H), np.uint8)
     sci = np.empty((rows, H // FP8_GROUP), np.float32)
     ue = np.empty((rows, H // FP8_GROUP), np.uint8) if round_scale else None
-    _check(_load().oracle_fp8_quantize(rows, H, _ptr(x), int(round_scale), _ptr(codes), _ptr(sci), _ptr(ue)),
-           "fp8_quantize")
+    lib = _load()
+
+    def run(a, b):
+        _check(lib.oracle_fp8_quantize(b - a, H, _ptr(x[a:b]), int(round_scale), _ptr(codes[a:b]), _ptr(sci[a:b]),
+                                       _ptr(ue[a:b]) if ue is not None else None), "fp8_quantize")
+
+    threads = max(1, min(int(threads), rows))
+    if threads == 1:
+        run(0, rows)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        cuts = [rows * i // threads for i in range(threads + 1)]
+        with ThreadPoolExecutor(threads) as ex:
+            for f in [ex.submit(run, cuts[i], cuts[i + 1]) for i in range(threads)]:
+                f.result()
     return codes, sci, ue
 
 
@@ -166,8 +183,10 @@ def layout(topk_idx: np.ndarray, S: int, E: int, R: int) -> dict:
 # --------------------------------------------------------------------------- O2 + O3
 def dispatch(x: np.ndarray, topk_idx, topk_weights, is_token_in_rank: np.ndarray, num_tokens_per_expert,
              S: int, E: int, R: int, C: int, expert_alignment: int = 1, x_kind: int = X_BF16,
-             x_scales=None, round_scale: bool = False, capacity: int | None = None) -> dict:
-    """Normal-mode dispatch.  x: uint16 bf16 bits [N][H] (kinds 0, 2) or uint8 codes [N][H] (kind 1)."""
+             x_scales=None, round_scale: bool = False, capacity: int | None = None,
+             use_ue8m0: bool = False) -> dict:
+    """Normal-mode dispatch.  x: uint16 bf16 bits [N][H] (kinds 0, 2) or uint8 codes [N][H] (kind 1).
+    ``use_ue8m0`` (cast kind with round_scale) adds recv_x_scales_ue8m0, the scales' exponent bytes."""
     in_rank = _c(is_token_in_rank, np.uint8)
     N, R_ = in_rank.shape
     assert R_ == R and N % S == 0
@@ -189,6 +208,7 @@ def dispatch(x: np.ndarray, topk_idx, topk_weights, is_token_in_rank: np.ndarray
     else:
         recv_x = np.zeros((cap, H), np.uint8)
         recv_sc = np.zeros((cap, G), np.float32)
+    recv_ue = np.zeros((cap, G), np.uint8) if use_ue8m0 else None
     recv_src = np.full((cap,), -1, np.int32)
     recv_idx = np.full((cap, K), -1, np.int64) if idx is not None else None
     recv_w = np.zeros((cap, K), np.float32) if (idx is not None and w is not None) else None
@@ -200,10 +220,12 @@ def dispatch(x: np.ndarray, topk_idx, topk_weights, is_token_in_rank: np.ndarray
     send_head = np.empty((N, R), np.int32)
     _check(_load().oracle_dispatch(S, T, H, K, E, R, C, expert_alignment, x_kind, _ptr(x), _ptr(xs),
                                    int(round_scale), _ptr(idx), _ptr(w), _ptr(in_rank), _ptr(ntpe), cap,
-                                   _ptr(recv_x), _ptr(recv_sc), _ptr(recv_src), _ptr(recv_idx), _ptr(recv_w),
-                                   _ptr(nrte), _ptr(rpm), _ptr(cpm), _ptr(rcpm), _ptr(off), _ptr(send_head)),
+                                   _ptr(recv_x), _ptr(recv_sc), _ptr(recv_ue), _ptr(recv_src), _ptr(recv_idx),
+                                   _ptr(recv_w), _ptr(nrte), _ptr(rpm), _ptr(cpm), _ptr(rcpm), _ptr(off),
+                                   _ptr(send_head)),
            "dispatch")
-    return dict(recv_x=recv_x, recv_x_scales=recv_sc, recv_src_idx=recv_src, recv_topk_idx=recv_idx,
+    return dict(recv_x=recv_x, recv_x_scales=recv_sc, recv_x_scales_ue8m0=recv_ue, recv_src_idx=recv_src,
+                recv_topk_idx=recv_idx,
                 recv_topk_weights=recv_w, num_recv_tokens_per_expert=nrte, rank_prefix_matrix=rpm,
                 channel_prefix_matrix=cpm, recv_channel_prefix_matrix=rcpm, recv_rank_offset=off,
                 send_head=send_head, num_recv=int(off[R]))
@@ -211,7 +233,7 @@ def dispatch(x: np.ndarray, topk_idx, topk_weights, is_token_in_rank: np.ndarray
 
 # --------------------------------------------------------------------------- O5
 def cached_dispatch(x: np.ndarray, send_head: np.ndarray, recv_rank_offset: np.ndarray, S: int, capacity: int,
-                    x_kind: int = X_BF16, x_scales=None, round_scale: bool = False) -> dict:
+                    x_kind: int = X_BF16, x_scales=None, round_scale: bool = False, use_ue8m0: bool = False) -> dict:
     sh = _c(send_head, np.int32)
     off = _c(recv_rank_offset, np.int32)
     N, R = sh.shape
@@ -226,9 +248,11 @@ def cached_dispatch(x: np.ndarray, send_head: np.ndarray, recv_rank_offset: np.n
     else:
         recv_x = np.zeros((capacity, H), np.uint8)
         recv_sc = np.zeros((capacity, G), np.float32)
+    recv_ue = np.zeros((capacity, G), np.uint8) if use_ue8m0 else None
     _check(_load().oracle_cached_dispatch(S, T, H, R, x_kind, _ptr(x), _ptr(xs), int(round_scale), _ptr(sh),
-                                          _ptr(off), capacity, _ptr(recv_x), _ptr(recv_sc)), "cached_dispatch")
-    return dict(recv_x=recv_x, recv_x_scales=recv_sc)
+                                          _ptr(off), capacity, _ptr(recv_x), _ptr(recv_sc), _ptr(recv_ue)),
+           "cached_dispatch")
+    return dict(recv_x=recv_x, recv_x_scales=recv_sc, recv_x_scales_ue8m0=recv_ue)
 
 
 # --------------------------------------------------------------------------- O4
@@ -366,8 +390,10 @@ def relay_dispatch(x: np.ndarray, topk_idx, topk_weights, is_token_in_rank: np.n
 
 
 def relay_combine(y: np.ndarray, recv_topk_weights, recv_rank_offset, recv_rdma_offset, send_nvl_head, send_rdma_head,
-                  S: int, K: int = 0, bias0=None, bias1=None, want_f64: bool = False) -> dict:
-    """Two-level combine: y uint16 bf16 bits [capacity][H] -> partials per RDMA row, then per source token."""
+                  S: int, K: int = 0, bias0=None, bias1=None, want_f64: bool = False, want_f32: bool = False,
+                  partial_f32: bool = False) -> dict:
+    """Two-level combine: y uint16 bf16 bits [capacity][H] -> partials per RDMA row (bf16, or fp32 with
+    ``partial_f32``), then per source token."""
     y = _c(y, np.uint16)
     cap, H = y.shape
     off = _c(recv_rank_offset, np.int32)
@@ -383,15 +409,18 @@ def relay_combine(y: np.ndarray, recv_topk_weights, recv_rank_offset, recv_rdma_
         K = w.shape[1]
     b0 = _c(bias0, np.uint16) if bias0 is not None else None
     b1 = _c(bias1, np.uint16) if bias1 is not None else None
-    rdma_y = np.zeros((rcap, H), np.uint16)
+    rdma_y = np.zeros((rcap, H), np.float32 if partial_f32 else np.uint16)
     rdma_w = np.zeros((rcap, K), np.float32) if w is not None else None
     out = np.empty((N, H), np.uint16)
     out_w = np.zeros((N, K), np.float32) if w is not None else None
+    out32 = np.empty((N, H), np.float32) if want_f32 else None
     out64 = np.empty((N, H), np.float64) if want_f64 else None
     _check(_load().oracle_relay_combine(S, T, H, K, R, _ptr(y), _ptr(w), _ptr(b0), _ptr(b1), cap, _ptr(off), rcap,
-                                        _ptr(roff), _ptr(snh), _ptr(srh), _ptr(rdma_y), _ptr(rdma_w), _ptr(out),
-                                        _ptr(out_w), _ptr(out64)), "relay_combine")
-    return dict(rdma_y=rdma_y, rdma_w=rdma_w, combined_x=out, combined_topk_weights=out_w, combined_f64=out64)
+                                        _ptr(roff), _ptr(snh), _ptr(srh), int(partial_f32), _ptr(rdma_y),
+                                        _ptr(rdma_w), _ptr(out), _ptr(out_w), _ptr(out32), _ptr(out64)),
+           "relay_combine")
+    return dict(rdma_y=rdma_y, rdma_w=rdma_w, combined_x=out, combined_topk_weights=out_w, combined_f32=out32,
+                combined_f64=out64)
 
 
 def calc_diff(x: np.ndarray, y: np.ndarray) -> float:

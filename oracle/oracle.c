@@ -238,8 +238,10 @@ int oracle_layout(int S, int T, int K, int E, int R, const int64_t* topk_idx,
 
 static int64_t orc_row_bytes(int kind, int H) { return kind == ORC_X_BF16 ? 2LL * H : (int64_t)H; }
 
+/* dst_ue8m0 (nullable, cast kind with round_scale only) receives the
+ * exponent byte e + 127 of every power-of-two scale 2^e of the row.        */
 static void orc_write_payload(int kind, int H, const void* x, const float* x_scales, int round_scale,
-                              int64_t src_row, uint8_t* dst_row, float* dst_scales) {
+                              int64_t src_row, uint8_t* dst_row, float* dst_scales, uint8_t* dst_ue8m0) {
     const int G = H / ORC_FP8_GROUP;
     if (kind == ORC_X_BF16) {
         memcpy(dst_row, (const uint8_t*)x + src_row * 2LL * H, 2ULL * H);
@@ -248,8 +250,11 @@ static void orc_write_payload(int kind, int H, const void* x, const float* x_sca
         if (dst_scales) memcpy(dst_scales, x_scales + src_row * G, sizeof(float) * G);
     } else {
         float tmp_scales[1024];
-        oracle_fp8_quantize(1, H, (const uint16_t*)x + src_row * H, round_scale, dst_row, tmp_scales, NULL);
+        uint8_t tmp_ue[1024];
+        oracle_fp8_quantize(1, H, (const uint16_t*)x + src_row * H, round_scale, dst_row, tmp_scales,
+                            round_scale ? tmp_ue : NULL);
         if (dst_scales) memcpy(dst_scales, tmp_scales, sizeof(float) * G);
+        if (dst_ue8m0 && round_scale) memcpy(dst_ue8m0, tmp_ue, (size_t)G);
     }
 }
 
@@ -275,19 +280,23 @@ static void orc_write_payload(int kind, int H, const void* x, const float* x_sca
  *   recv_topk_idx[row][k] = e - r*L if expert e lives on r, else -1;
  *   recv_topk_weights[row][k] = w if so, else 0;
  *   num_recv_tokens_per_expert[r][l] = ceil(sum_s ntpe[s][r*L+l] / a) * a.
+ * With the cast kind and round_scale, recv_x_scales_ue8m0 (nullable)
+ * receives each scale's exponent byte e + 127 ([Ch4] 4.3 use_ue8m0: the
+ * power-of-two scale kept as its exponent).
  * Rows at or beyond `capacity` are not written (the call reports the
  * total in off[R] so that the caller can detect the overflow).            */
 int oracle_dispatch(int S, int T, int H, int K, int E, int R, int C, int align,
                     int x_kind, const void* x, const float* x_scales, int round_scale,
                     const int64_t* topk_idx, const float* topk_weights,
                     const uint8_t* in_rank, const int32_t* ntpe, int64_t capacity,
-                    void* recv_x, float* recv_x_scales, int32_t* recv_src_idx,
+                    void* recv_x, float* recv_x_scales, uint8_t* recv_x_scales_ue8m0, int32_t* recv_src_idx,
                     int64_t* recv_topk_idx, float* recv_topk_weights,
                     int32_t* num_recv_tokens_per_expert,
                     int32_t* rpm, int32_t* cpm, int32_t* rcpm, int32_t* recv_rank_offset,
                     int32_t* send_head) {
     if (S < 0 || T < 0 || H <= 0 || E <= 0 || R <= 0 || C <= 0 || E % R != 0 || align <= 0) return ORC_EINVAL;
     if (x_kind != ORC_X_BF16 && (H % ORC_FP8_GROUP != 0 || H / ORC_FP8_GROUP > 1024)) return ORC_EINVAL;
+    if (recv_x_scales_ue8m0 && !(x_kind == ORC_X_BF16_CAST_FP8 && round_scale)) return ORC_EINVAL;
     const int L = E / R;
     const int tc = (T + C - 1) / C;                   /* tokens per channel */
     const int G = H / ORC_FP8_GROUP;
@@ -340,7 +349,8 @@ int oracle_dispatch(int S, int T, int H, int K, int E, int R, int C, int align,
                 if (g >= capacity) continue;
                 orc_write_payload(x_kind, H, x, x_scales, round_scale, n,
                                   (uint8_t*)recv_x + g * rb,
-                                  recv_x_scales && x_kind != ORC_X_BF16 ? recv_x_scales + g * G : NULL);
+                                  recv_x_scales && x_kind != ORC_X_BF16 ? recv_x_scales + g * G : NULL,
+                                  recv_x_scales_ue8m0 ? recv_x_scales_ue8m0 + g * G : NULL);
                 recv_src_idx[g] = t;
                 if (topk_idx && recv_topk_idx) {
                     for (int k = 0; k < K; ++k) {
@@ -360,9 +370,10 @@ int oracle_dispatch(int S, int T, int H, int K, int E, int R, int C, int align,
  * (and its scales) move; the placement is the handle's send_head.         */
 int oracle_cached_dispatch(int S, int T, int H, int R, int x_kind, const void* x, const float* x_scales,
                            int round_scale, const int32_t* send_head, const int32_t* recv_rank_offset,
-                           int64_t capacity, void* recv_x, float* recv_x_scales) {
+                           int64_t capacity, void* recv_x, float* recv_x_scales, uint8_t* recv_x_scales_ue8m0) {
     if (S < 0 || T < 0 || H <= 0 || R <= 0) return ORC_EINVAL;
     if (x_kind != ORC_X_BF16 && (H % ORC_FP8_GROUP != 0 || H / ORC_FP8_GROUP > 1024)) return ORC_EINVAL;
+    if (recv_x_scales_ue8m0 && !(x_kind == ORC_X_BF16_CAST_FP8 && round_scale)) return ORC_EINVAL;
     const int G = H / ORC_FP8_GROUP;
     const int64_t rb = orc_row_bytes(x_kind, H);
     for (int64_t n = 0; n < (int64_t)S * T; ++n)
@@ -372,7 +383,8 @@ int oracle_cached_dispatch(int S, int T, int H, int R, int x_kind, const void* x
             int64_t g = (int64_t)recv_rank_offset[r] + j;
             if (g >= capacity) continue;
             orc_write_payload(x_kind, H, x, x_scales, round_scale, n, (uint8_t*)recv_x + g * rb,
-                              recv_x_scales && x_kind != ORC_X_BF16 ? recv_x_scales + g * G : NULL);
+                              recv_x_scales && x_kind != ORC_X_BF16 ? recv_x_scales + g * G : NULL,
+                              recv_x_scales_ue8m0 ? recv_x_scales_ue8m0 + g * G : NULL);
         }
     return ORC_OK;
 }
@@ -700,7 +712,7 @@ int oracle_relay_dispatch(int S, int T, int H, int K, int E, int R, int C,
                 row++;
                 if (i >= rdma_capacity) continue;
                 orc_write_payload(x_kind, H, x, x_scales, round_scale, n, (uint8_t*)rdma_x + i * rb,
-                                  fp8 ? rdma_x_scales + i * G : NULL);
+                                  fp8 ? rdma_x_scales + i * G : NULL, NULL);
                 rdma_src_idx[i] = (int32_t)n;
             }
     }
@@ -755,20 +767,28 @@ int oracle_relay_dispatch(int S, int T, int H, int K, int E, int R, int C,
  *     send_nvl_head[row][j] >= 0, and is rounded to bf16 -- the type a
  *     partial travels in; the top-k weights are summed the same way in fp32;
  *     a row no rank holds is +0.0;
+ *   - with partial_f32 the partial rows stay fp32 (no rounding between the
+ *     levels): twice the partial bytes, and the result is then one fp32
+ *     sum rounded once, like O4's;
  *   - second level: every source token sums, in fp32 from its first term,
  *     its groups' partial rows g ascending (send_rdma_head >= 0), then the
  *     bias rows as in O4, and is rounded once more to bf16; weights as fp32.
  *   y [capacity][H] bf16, w [capacity][K] (nullable) -> rdma_y
- *   [rdma_capacity][H] bf16 partials, rdma_w (nullable), out [S*T][H] bf16,
- *   out_w [S*T][K] (nullable), out_f64: every contribution and bias summed
- *   in fp64 without the intermediate rounding (accuracy reference).        */
+ *   [rdma_capacity][H] partials (bf16, or fp32 with partial_f32), rdma_w
+ *   (nullable), out [S*T][H] bf16, out_w [S*T][K] (nullable), out_f32
+ *   (nullable): the second level's fp32 sums before the last rounding;
+ *   out_f64 (nullable): every contribution and bias summed in fp64 without
+ *   any intermediate rounding (accuracy reference).                        */
 int oracle_relay_combine(int S, int T, int H, int K, int R,
                          const uint16_t* y, const float* w, const uint16_t* bias0, const uint16_t* bias1,
                          int64_t capacity, const int32_t* recv_rank_offset,
                          int64_t rdma_capacity, const int32_t* recv_rdma_offset, const int32_t* send_nvl_head,
-                         const int32_t* send_rdma_head,
-                         uint16_t* rdma_y, float* rdma_w, uint16_t* out, float* out_w, double* out_f64) {
+                         const int32_t* send_rdma_head, int partial_f32,
+                         void* rdma_y, float* rdma_w, uint16_t* out, float* out_w, float* out_f32,
+                         double* out_f64) {
     if (S < 0 || T < 0 || H <= 0 || R <= 0 || R % 8 != 0 || K < 0) return ORC_EINVAL;
+    uint16_t* py16 = partial_f32 ? NULL : (uint16_t*)rdma_y;
+    float* py32 = partial_f32 ? (float*)rdma_y : NULL;
     const int NG = R / 8;
     float* acc = (float*)malloc(sizeof(float) * (size_t)H);
     double* acc64 = (double*)malloc(sizeof(double) * (size_t)H);
@@ -792,7 +812,10 @@ int oracle_relay_combine(int S, int T, int H, int K, int R,
                 if (w) for (int k = 0; k < K; ++k) wacc[k] = have ? wacc[k] + w[row * K + k] : w[row * K + k];
                 have = 1;
             }
-            for (int c = 0; c < H; ++c) rdma_y[i * H + c] = have ? oracle_bf16_round(acc[c]) : 0;
+            for (int c = 0; c < H; ++c) {
+                if (py32) py32[i * H + c] = have ? acc[c] : 0.0f;
+                else py16[i * H + c] = have ? oracle_bf16_round(acc[c]) : 0;
+            }
             if (w && rdma_w) for (int k = 0; k < K; ++k) rdma_w[i * K + k] = have ? wacc[k] : 0.0f;
         }
 
@@ -806,7 +829,7 @@ int oracle_relay_combine(int S, int T, int H, int K, int R,
             int64_t i = (int64_t)recv_rdma_offset[g] + h;
             if (i >= rdma_capacity) continue;
             for (int c = 0; c < H; ++c) {
-                float v = oracle_bf16_to_f32(rdma_y[i * H + c]);
+                float v = py32 ? py32[i * H + c] : oracle_bf16_to_f32(py16[i * H + c]);
                 acc[c] = have ? acc[c] + v : v;
             }
             if (w && rdma_w) for (int k = 0; k < K; ++k) wacc[k] = have ? wacc[k] + rdma_w[i * K + k] : rdma_w[i * K + k];
@@ -829,6 +852,7 @@ int oracle_relay_combine(int S, int T, int H, int K, int R,
                 if (bias1) { acc[c] += oracle_bf16_to_f32(bias1[n * H + c]); acc64[c] += oracle_bf16_to_f32(bias1[n * H + c]); }
             }
             out[n * H + c] = (have || biased) ? oracle_bf16_round(acc[c]) : 0;
+            if (out_f32) out_f32[n * H + c] = (have || biased) ? acc[c] : 0.0f;
             if (out_f64) out_f64[n * H + c] = acc64[c];
         }
         if (out_w) for (int k = 0; k < K; ++k) out_w[n * K + k] = (have && w && rdma_w) ? wacc[k] : 0.0f;

@@ -219,9 +219,9 @@ def relay_plan(in_rank, S: int):
     return rows, send_rdma_head, nvl
 
 
-def relay_combine(y_bits, recv_rank_offset, rows, send_rdma_head, nvl, S: int):
-    """Two-level sum: per group row, fp32 over the group's ranks then one bf16 rounding (torch's cast);
-    per token, fp32 over its groups' rounded partials, then bf16 again."""
+def relay_combine(y_bits, recv_rank_offset, rows, send_rdma_head, nvl, S: int, partial_f32: bool = False):
+    """Two-level sum: per group row, fp32 over the group's ranks then one bf16 rounding (torch's cast), or
+    no rounding with ``partial_f32``; per token, fp32 over its groups' partials, then bf16."""
     N, G = send_rdma_head.shape
     H = y_bits.shape[1]
     partial = {}
@@ -233,7 +233,10 @@ def relay_combine(y_bits, recv_rank_offset, rows, send_rdma_head, nvl, S: int):
                     continue
                 v = (y_bits[int(recv_rank_offset[8 * g + j]) + h].astype(np.uint32) << 16).view(np.float32)
                 acc = v.copy() if acc is None else (acc + v).astype(np.float32)
-            partial[(g, i)] = np.zeros(H, np.uint16) if acc is None else bf16_round_lib(acc)
+            if partial_f32:
+                partial[(g, i)] = np.zeros(H, np.float32) if acc is None else acc
+            else:
+                partial[(g, i)] = np.zeros(H, np.uint16) if acc is None else bf16_round_lib(acc)
     out = np.zeros((N, H), np.uint16)
     for n in range(N):
         acc = None
@@ -241,7 +244,8 @@ def relay_combine(y_bits, recv_rank_offset, rows, send_rdma_head, nvl, S: int):
             i = int(send_rdma_head[n, g])
             if i < 0:
                 continue
-            v = (partial[(g, i)].astype(np.uint32) << 16).view(np.float32)
+            p = partial[(g, i)]
+            v = p if partial_f32 else (p.astype(np.uint32) << 16).view(np.float32)
             acc = v.copy() if acc is None else (acc + v).astype(np.float32)
         if acc is not None:
             out[n] = bf16_round_lib(acc)

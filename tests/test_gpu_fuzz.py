@@ -122,7 +122,9 @@ def test_fuzz_normal(case):
     y = wl.activations(h.recv_capacity, H, g)
     b = wl.activations(N, H, g) if c["bias"] else None
     cx, cw = miep.combine(y.to(DEV), h, rtw, bias=None if b is None else b.to(DEV))
-    rc = oracle.combine(wl.bf16_bits(y), npy(rtw), ref["send_head"], ref["recv_rank_offset"], S=S,
+    assert np.array_equal(npy(rtw)[:n].view(np.uint32), ref["recv_topk_weights"][:n].view(np.uint32))
+    assert ref["recv_topk_weights"].shape[0] == h.recv_capacity
+    rc = oracle.combine(wl.bf16_bits(y), ref["recv_topk_weights"], ref["send_head"], ref["recv_rank_offset"], S=S,
                         bias0=None if b is None else wl.bf16_bits(b))
     assert np.array_equal(u16(cx), rc["combined_x"])
     assert np.array_equal(npy(cw).view(np.uint32), rc["combined_topk_weights"].view(np.uint32))

@@ -48,10 +48,19 @@ BIAS_CASES = [
 
 
 def _dispatch(w, x, idx, wts):
+    """The GPU dispatch and, for the expected values, the oracle's own one of
+    the same routing (its handle and received weights)."""
     idxd = idx.to(DEV)
     ntpr, _, ntpe, itr = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
     recv_x, _, rti, rtw, _, h = miep.dispatch(x.to(DEV), idxd, wts.to(DEV), ntpr, itr, ntpe, w.E, w.C)
-    return recv_x, rtw, h
+    lay = oracle.layout(idx.numpy(), w.S, w.E, w.R)
+    ref = oracle.dispatch(np.zeros((w.N, 8), np.uint16), idx.numpy(), wts.numpy(), lay["is_token_in_rank"], None,
+                          S=w.S, E=w.E, R=w.R, C=w.C)
+    torch.cuda.synchronize()
+    assert np.array_equal(npy(h.send_head), ref["send_head"])
+    assert np.array_equal(npy(h.recv_rank_offset), ref["recv_rank_offset"])
+    assert np.array_equal(npy(rtw).view(np.uint32), ref["recv_topk_weights"].view(np.uint32))
+    return recv_x, rtw, h, ref
 
 
 @pytest.mark.parametrize("case", BIAS_CASES, ids=[c[0] for c in BIAS_CASES])
@@ -63,14 +72,14 @@ def test_combine_bias_small(case, which):
     inp = wl.normal_inputs(w, 4)
     idx = inp["topk_idx"].clone()
     idx[::9] = -1                                     # tokens no rank receives: bias only
-    _, rtw, h = _dispatch(w, inp["x"], idx, inp["topk_weights"])
+    _, rtw, h, ref = _dispatch(w, inp["x"], idx, inp["topk_weights"])
     g = torch.Generator().manual_seed(21)
     y = wl.activations(h.recv_capacity, H, g)
     b0 = wl.activations(w.N, H, g) if which in ("b0", "both") else None
     b1 = wl.activations(w.N, H, g) if which in ("b1", "both") else None
     cx, cw = miep.combine(y.to(DEV), h, rtw, bias=(None if b0 is None else b0.to(DEV),
                                                    None if b1 is None else b1.to(DEV)))
-    rc = oracle.combine(wl.bf16_bits(y), npy(rtw), npy(h.send_head), npy(h.recv_rank_offset), S=S,
+    rc = oracle.combine(wl.bf16_bits(y), ref["recv_topk_weights"], ref["send_head"], ref["recv_rank_offset"], S=S,
                         bias0=None if b0 is None else wl.bf16_bits(b0),
                         bias1=None if b1 is None else wl.bf16_bits(b1))
     assert np.array_equal(u16(cx), rc["combined_x"])
@@ -87,16 +96,16 @@ def test_combine_bias_normal_single_tensor():
     w = wl.NORMAL
     say("combine bias normal", w.name)
     inp = wl.normal_inputs(w, 0)
-    recv_x, rtw, h = _dispatch(w, inp["x"], inp["topk_idx"], inp["topk_weights"])
+    recv_x, rtw, h, ref = _dispatch(w, inp["x"], inp["topk_idx"], inp["topk_weights"])
     y = wl.expert_outputs(h.recv_capacity, w.H, seed=7)
     b = wl.activations(w.N, w.H, torch.Generator().manual_seed(8))
     cx, _ = miep.combine(y.to(DEV), h, None, bias=b.to(DEV))
-    rc = oracle.combine(wl.bf16_bits(y), None, npy(h.send_head), npy(h.recv_rank_offset), S=w.S,
+    rc = oracle.combine(wl.bf16_bits(y), None, ref["send_head"], ref["recv_rank_offset"], S=w.S,
                         bias0=wl.bf16_bits(b))
     assert np.array_equal(u16(cx), rc["combined_x"])
     # unbiased call on the same buffers is unchanged by the bias path
     cx2, _ = miep.combine(y.to(DEV), h)
-    rc2 = oracle.combine(wl.bf16_bits(y), None, npy(h.send_head), npy(h.recv_rank_offset), S=w.S)
+    rc2 = oracle.combine(wl.bf16_bits(y), None, ref["send_head"], ref["recv_rank_offset"], S=w.S)
     assert np.array_equal(u16(cx2), rc2["combined_x"])
 
 
@@ -235,10 +244,18 @@ def test_ll_combine_full_workload(weighted):
     wts = wl.gate_weights(w.N, w.K, g)
     idxd = inp["topk_idx"].to(DEV)
     out = miep.low_latency_dispatch(inp["x"].to(DEV), idxd, w.M, w.E, w.dest_rank, w.R, True)
+    # the oracle's own receive layout of the same routing (the payload does not enter it)
+    ref = oracle.ll_dispatch(np.zeros((w.N, 8), np.uint16), inp["topk_idx"].numpy(), S=w.S, M=w.M, E=w.E, R=w.R,
+                             dest_rank=w.dest_rank, use_fp8=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(npy(out["packed_recv_layout_range"]), ref["packed_recv_layout_range"])
+    n = ref["packed_recv_count"]
+    for l in range(w.L):
+        assert np.array_equal(npy(out["packed_recv_src_info"])[l, :n[l]], ref["packed_recv_src_info"][l, :n[l]])
     y = wl.expert_outputs(w.L * w.R * w.M, w.H, seed=13).view(w.L, w.R * w.M, w.H)
     cx = miep.low_latency_combine(y.to(DEV), idxd, wts.to(DEV) if weighted else None, out["packed_recv_src_info"],
                                   out["packed_recv_layout_range"], w.M, w.E, w.dest_rank, w.R)
-    rc = oracle.ll_combine(wl.bf16_bits(y), npy(out["packed_recv_src_info"]), npy(out["packed_recv_layout_range"]),
+    rc = oracle.ll_combine(wl.bf16_bits(y), ref["packed_recv_src_info"], ref["packed_recv_layout_range"],
                            inp["topk_idx"].numpy(), S=w.S, M=w.M, E=w.E, R=w.R, dest_rank=w.dest_rank,
                            topk_weights=wts.numpy() if weighted else None, want_f64=True)
     got = u16(cx)

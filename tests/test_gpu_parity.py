@@ -6,8 +6,9 @@ codes and scales, and the low-latency messages and packed outputs.  Combine
 is compared bit-exactly too (same summation order), and additionally held to
 the stated tolerances: max relative error < 1e-2 against the fp32 reference
 and, for identity experts, calc_diff < 5e-6 after dividing by the number of
-receiving ranks.  Full-size workloads compare every output the oracle can
-produce in seconds and sampled rows for the FP8 payloads.
+receiving ranks.  Full-size workloads are compared in full, FP8 payloads
+included.  Every expected value comes from the oracle run on its own
+inputs (its own handle and weights), never from a GPU output.
 """
 import sys
 
@@ -202,8 +203,13 @@ def test_cached_dispatch_normal():
     _, _, _, _, _, h = miep.dispatch(x.to(DEV), idxd, wts.to(DEV), ntpr, itr, ntpe, w.E, w.C)
     x2 = wl.activations(w.N, w.H, torch.Generator().manual_seed(9))
     recv2, _ = miep.cached_dispatch(x2.to(DEV), h)
-    ref = oracle.cached_dispatch(wl.bf16_bits(x2), npy(h.send_head), npy(h.recv_rank_offset), S=w.S,
-                                 capacity=h.recv_capacity)
+    # the oracle's own handle, from its own layout and dispatch of the routing
+    lay = oracle.layout(idx.numpy(), w.S, w.E, w.R)
+    d = oracle.dispatch(np.zeros((w.N, 8), np.uint16), idx.numpy(), None, lay["is_token_in_rank"], None, S=w.S,
+                        E=w.E, R=w.R, C=w.C)
+    ref = oracle.cached_dispatch(wl.bf16_bits(x2), d["send_head"], d["recv_rank_offset"], S=w.S,
+                                 capacity=d["num_recv"])
+    assert h.recv_capacity == d["num_recv"]
     assert np.array_equal(u16(recv2), ref["recv_x"])
 
 
@@ -375,9 +381,16 @@ def test_fp8_dispatch_kinds_small(round_scale):
 @pytest.mark.parametrize("round_scale", [False, True])
 def test_large_two_level_fp8_roundtrip(round_scale):
     """Large workload: 16384 tokens, 64 ranks in 8 RDMA groups, FP8-cast
-    dispatch, bf16 combine of the dequantised identity experts.  The layout
-    and the handle are compared in full; the FP8 rows of 512 sampled source
-    tokens are compared bit-exactly against the oracle's quantiser."""
+    dispatch, bf16 combine of the dequantised identity experts.  Everything is
+    compared in full: layout, handle, every receive row's E4M3 codes and fp32
+    scales, the top-k metadata, and the combine (bit-exact against the
+    oracle, max relative error < 1e-2 against its fp32 sums, calc_diff < 5e-6
+    for the identity round trip).
+
+    The oracle's fused-cast dispatch quantises once per receive row; here it
+    quantises each source row once (threads over row chunks) and dispatches
+    the codes as pre-quantised FP8, which the CPU pins show to be the same
+    result (the cast is a function of the source row alone)."""
     w = wl.LARGE
     say("large fp8", round_scale)
     x, idx, wts = _inputs(w, 0)
@@ -387,38 +400,41 @@ def test_large_two_level_fp8_roundtrip(round_scale):
     ntpr, _, ntpe, itr = lay
     rx, rs, rti, rtw, nrte, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True,
                                               round_scale=round_scale)
-    # handle and metadata: oracle run on a narrow payload (placement does not depend on H)
-    ref = oracle.dispatch(np.zeros((w.N, 8), np.uint16), idx.numpy(), wts.numpy(), ref_lay["is_token_in_rank"],
-                          ref_lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R, C=w.C)
+    xb = wl.bf16_bits(x)
+    codes, sci, _ = oracle.fp8_quantize(xb, round_scale, threads=16)
+    ref = oracle.dispatch(codes, idx.numpy(), wts.numpy(), ref_lay["is_token_in_rank"],
+                          ref_lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R, C=w.C, x_kind=oracle.X_FP8,
+                          x_scales=sci)
     torch.cuda.synchronize()
     _check_handle(h, ref)
+    assert h.recv_capacity == ref["num_recv"]
+    assert np.array_equal(u8(rx), ref["recv_x"])
+    assert np.array_equal(npy(rs).view(np.uint32), ref["recv_x_scales"].view(np.uint32))
     assert np.array_equal(npy(rti), ref["recv_topk_idx"])
+    assert np.array_equal(npy(rtw).view(np.uint32), ref["recv_topk_weights"].view(np.uint32))
     assert np.array_equal(npy(nrte), ref["num_recv_tokens_per_expert"])
-    # sampled payload rows
-    rng = np.random.default_rng(1)
-    sample = rng.choice(w.N, 512, replace=False)
-    xb = wl.bf16_bits(x)
-    codes, sci, _ = oracle.fp8_quantize(xb[sample], round_scale)
-    send_head = ref["send_head"]
-    off = ref["recv_rank_offset"]
-    rows, srcs = [], []
-    for i, n in enumerate(sample):
-        for r in np.nonzero(send_head[n] >= 0)[0]:
-            rows.append(off[r] + send_head[n, r])
-            srcs.append(i)
-    rows = torch.tensor(rows, device=DEV)
-    assert np.array_equal(u8(rx[rows]), codes[srcs])
-    assert np.array_equal(npy(rs[rows]).view(np.uint32), sci[srcs].view(np.uint32))
-    # identity expert on the dequantised rows, bf16 combine
-    y = (rx.float() * rs.repeat_interleave(128, dim=1)).to(torch.bfloat16)
-    cx, cw = miep.combine(y, h, rtw)
+    # identity experts on the oracle's dequantised receive rows, bf16 combine
+    ref_rx = torch.from_numpy(ref["recv_x"]).view(torch.float8_e4m3fn)
+    ref_rs = torch.from_numpy(ref["recv_x_scales"])
+    y = (ref_rx.float() * ref_rs.repeat_interleave(128, dim=1)).to(torch.bfloat16)
+    del ref_rx
+    cx, cw = miep.combine(y.to(DEV), h, rtw)
+    rc = oracle.combine(wl.bf16_bits(y), ref["recv_topk_weights"], ref["send_head"], ref["recv_rank_offset"], S=w.S,
+                        want_f32=True)
+    del y
+    got = u16(cx)
+    assert np.array_equal(got, rc["combined_x"])
+    assert np.array_equal(npy(cw).view(np.uint32), rc["combined_topk_weights"].view(np.uint32))
+    g = oracle.bf16_to_f32(got).reshape(got.shape).astype(np.float64)
+    f = rc["combined_f32"].astype(np.float64)
+    assert (np.abs(g - f) / np.maximum(np.abs(f), 1e-6)).max() < 1e-2
     deq = (torch.from_numpy(codes).view(torch.float8_e4m3fn).float() *
            torch.from_numpy(sci).repeat_interleave(128, dim=1)).to(torch.bfloat16).float().numpy().astype(np.float64)
-    cnt = ref_lay["is_token_in_rank"].sum(axis=1).astype(np.float64)[sample]
-    got = cx[torch.from_numpy(sample).to(DEV)].float().cpu().numpy().astype(np.float64)
+    cnt = ref_lay["is_token_in_rank"].sum(axis=1).astype(np.float64)
     ok = cnt > 0
-    assert oracle.calc_diff(got[ok] / cnt[ok, None], deq[ok]) < 5e-6
-    valid = (idx.numpy() >= 0)
+    assert oracle.calc_diff(g[ok] / cnt[ok, None], deq[ok]) < 5e-6
+    assert np.all(g[~ok] == 0)
+    valid = (idx.numpy() >= 0) & ok[:, None]
     assert np.array_equal(npy(cw)[valid], wts.numpy()[valid])
 
 

@@ -313,6 +313,37 @@ def test_dispatch_fp8_kinds(orc, round_scale):
     assert orc.calc_diff(got[ok] / cnt[ok, None], ref[ok]) < 5e-6
 
 
+def test_dispatch_ue8m0_exponent_bytes(orc):
+    """use_ue8m0 on the normal dispatch ([Ch4] 4.3 flag): each receive row's exponent bytes are e + 127 of
+    the power-of-two scales the brute force finds for its source row, and equal log2 of the fp32 scale;
+    the cached dispatch gives the same bytes; the flag needs the cast kind with round_scale."""
+    w = wl.NormalWorkload("t", S=3, T=12, H=384, E=24, R=6, K=3, C=4)
+    inp, idx, lay = _normal_case(orc, w)
+    x = wl.bf16_bits(inp["x"])
+    x[2, :128] = 0                                  # an all-zero group: the amax floor's exponent
+    x[5] = brute.bf16_round_lib(orc.bf16_to_f32(x[5]) * np.float32(2.0 ** -40))   # small magnitudes
+    d = orc.dispatch(x, idx, None, lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R, C=w.C,
+                     x_kind=orc.X_BF16_CAST_FP8, round_scale=True, use_ue8m0=True)
+    ue, sc = d["recv_x_scales_ue8m0"], d["recv_x_scales"]
+    for r in range(w.R):
+        for j in range(d["recv_rank_offset"][r + 1] - d["recv_rank_offset"][r]):
+            row = d["recv_rank_offset"][r] + j
+            s = next(s for s in range(w.S) if d["rank_prefix_matrix"][s, r] > j)
+            n = s * w.T + d["recv_src_idx"][row]
+            _, _, exps = brute.fp8_quantize_row(x[n], True)
+            assert ue[row].tolist() == [e + 127 for e in exps]
+    m, e = np.frexp(sc.astype(np.float64))
+    assert np.all(m == 0.5) and np.array_equal(ue.astype(np.int64), e.astype(np.int64) - 1 + 127)
+    c = orc.cached_dispatch(x, d["send_head"], d["recv_rank_offset"], S=w.S, capacity=d["num_recv"],
+                            x_kind=orc.X_BF16_CAST_FP8, round_scale=True, use_ue8m0=True)
+    assert np.array_equal(c["recv_x_scales_ue8m0"], ue)
+    with pytest.raises(ValueError):
+        orc.dispatch(x, idx, None, lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R, C=w.C,
+                     x_kind=orc.X_BF16_CAST_FP8, round_scale=False, use_ue8m0=True)
+    with pytest.raises(ValueError):
+        orc.dispatch(x, idx, None, lay["is_token_in_rank"], None, S=w.S, E=w.E, R=w.R, C=w.C, use_ue8m0=True)
+
+
 def test_calc_diff_definition(orc):
     x = np.array([1.0, -2.0, 3.0])
     assert orc.calc_diff(x, x) == 0.0

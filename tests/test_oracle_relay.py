@@ -93,20 +93,53 @@ def test_relay_fp8_cast_once_before_first_hop(round_scale):
 
 
 @pytest.mark.parametrize("shape", SHAPES[:3], ids=[s[0] for s in SHAPES[:3]])
-def test_relay_combine_matches_brute(shape):
+@pytest.mark.parametrize("partial_f32", [False, True], ids=["bf16-partials", "fp32-partials"])
+def test_relay_combine_matches_brute(shape, partial_f32):
     name, S, T, H, E, R, K, C = shape
     w, x, idx, wts = _inputs(S, T, H, E, R, K, C, 7, masked=True)
     itr = oracle.layout(idx, S, E, R)["is_token_in_rank"]
     r = oracle.relay_dispatch(x, idx, wts, itr, S=S, E=E, R=R, C=C)
     y = wl.bf16_bits(wl.expert_outputs(r["num_recv"], H, seed=9))
     c = oracle.relay_combine(y, r["recv_topk_weights"], r["recv_rank_offset"], r["recv_rdma_offset"],
-                             r["send_nvl_head"], r["send_rdma_head"], S=S)
+                             r["send_nvl_head"], r["send_rdma_head"], S=S, partial_f32=partial_f32, want_f32=True)
     rows, srh, nvl = brute.relay_plan(itr, S)
-    out, partial = brute.relay_combine(y, r["recv_rank_offset"], rows, srh, nvl, S)
+    out, partial = brute.relay_combine(y, r["recv_rank_offset"], rows, srh, nvl, S, partial_f32=partial_f32)
     assert np.array_equal(c["combined_x"], out)
     roff = r["recv_rdma_offset"]
     for (g, i), p in partial.items():
-        assert np.array_equal(c["rdma_y"][roff[g] + i], p)
+        got = c["rdma_y"][roff[g] + i]
+        assert np.array_equal(got.view(np.uint32) if partial_f32 else got, p.view(np.uint32) if partial_f32 else p)
+    # the reported fp32 sums are the values the output rounds (torch's cast)
+    assert np.array_equal(brute.bf16_round_lib(c["combined_f32"]).reshape(out.shape), out)
+
+
+def test_relay_combine_fp32_partials_error_bound():
+    """With fp32 partials the two-level result is one fp32 sum rounded once: against the fp64 sum, the
+    error is at most the bf16 half-ulp plus the fp32 summation bound (n - 1) * 2^-24 * sum|y|; and
+    against the fp32 sums it reports, the relative error is the bf16 rounding alone (< 2^-8)."""
+    S, T, H, E, R, K, C = 4, 64, 512, 64, 16, 8, 4
+    w, x, idx, wts = _inputs(S, T, H, E, R, K, C, 17)
+    itr = oracle.layout(idx, S, E, R)["is_token_in_rank"]
+    r = oracle.relay_dispatch(x, idx, wts, itr, S=S, E=E, R=R, C=C)
+    y = wl.bf16_bits(wl.expert_outputs(r["num_recv"], H, seed=3))
+    c = oracle.relay_combine(y, None, r["recv_rank_offset"], r["recv_rdma_offset"], r["send_nvl_head"],
+                             r["send_rdma_head"], S=S, partial_f32=True, want_f32=True, want_f64=True)
+    got = oracle.bf16_to_f32(c["combined_x"]).reshape(S * T, H).astype(np.float64)
+    f32 = c["combined_f32"].astype(np.float64)
+    f64 = c["combined_f64"]
+    assert (np.abs(got - f32) / np.maximum(np.abs(f32), 1e-30)).max() <= 2.0 ** -8
+    # sum of |y| per token, built from the dispatch's own rows
+    absy = np.zeros((S * T, H))
+    yf = np.abs(oracle.bf16_to_f32(y).reshape(y.shape).astype(np.float64))
+    d = oracle.dispatch(np.zeros((S * T, 8), np.uint16), idx, None, itr, None, S=S, E=E, R=R, C=C)
+    for n in range(S * T):
+        for rr in range(R):
+            j = d["send_head"][n, rr]
+            if j >= 0:
+                absy[n] += yf[d["recv_rank_offset"][rr] + j]
+    cnt = itr.sum(axis=1)[:, None]
+    bound = 2.0 ** -8 * np.abs(f64) + np.maximum(cnt - 1, 0) * 2.0 ** -24 * absy * 1.001
+    assert np.all(np.abs(got - f64) <= bound)
 
 
 def test_relay_combine_identity_and_weights():
@@ -150,6 +183,9 @@ def test_relay_combine_equals_flat_when_one_rank_per_group():
     d = oracle.dispatch(x, idx, None, itr, lay["num_tokens_per_expert"], S=S, E=E, R=R, C=3)
     f = oracle.combine(y, None, d["send_head"], d["recv_rank_offset"], S=S)
     assert np.array_equal(c["combined_x"], f["combined_x"])
+    c32 = oracle.relay_combine(y, None, r["recv_rank_offset"], r["recv_rdma_offset"], r["send_nvl_head"],
+                               r["send_rdma_head"], S=S, partial_f32=True)
+    assert np.array_equal(c32["combined_x"], f["combined_x"])
 
 
 def test_relay_combine_bias_added_last():
