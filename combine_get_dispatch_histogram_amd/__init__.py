@@ -28,14 +28,14 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # noqa: F401
+from ._lib import MIEP_ECAPACITY, MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # noqa: F401
 
 __all__ = ["Handle", "MiepError", "get_dispatch_layout", "get_dispatch_layout_into", "dispatch", "dispatch_into", "cached_dispatch",
            "cached_dispatch_into", "combine", "combine_into", "low_latency_dispatch", "low_latency_dispatch_into",
            "low_latency_combine", "low_latency_combine_into", "update_mask_buffer", "clean_mask_buffer",
            "RelayHandle", "relay_dispatch", "relay_dispatch_into", "relay_cached_dispatch",
            "relay_cached_dispatch_into", "relay_combine", "relay_combine_into",
-           "query_mask_buffer", "ll_msg_bytes", "version"]
+           "query_mask_buffer", "check_status", "ll_msg_bytes", "version", "MIEP_ECAPACITY"]
 
 
 class _Args:
@@ -86,6 +86,15 @@ def _want(t: Optional[torch.Tensor], name: str, dtype, shape=None):
 
 def version() -> str:
     return _lib.load().miep_version().decode()
+
+
+def check_status(status: torch.Tensor) -> None:
+    """Read a dispatch's device status word (synchronous: waits for the
+    current stream); raises MiepError(MIEP_ECAPACITY) if the receive rows
+    exceeded their fixed capacity."""
+    _want(status, "status", torch.int32, (1,))
+    a = _Args()
+    _run(a, "miep_check_status", a.p(status))
 
 
 def ll_msg_bytes(hidden: int, use_fp8: bool) -> int:
@@ -204,10 +213,15 @@ def get_dispatch_layout_into(topk_idx, num_experts: int, num_ranks: int, num_src
 def dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_expert, handle: Handle, recv_x,
                   recv_x_scales=None, recv_topk_idx=None, recv_topk_weights=None, num_recv_tokens_per_expert=None,
                   x_scales=None, cast_to_fp8: bool = False, round_scale: bool = False,
-                  expert_alignment: int = 1) -> None:
-    """Fresh dispatch into preallocated outputs (allocates nothing)."""
+                  expert_alignment: int = 1, use_ue8m0: bool = False, recv_x_scales_ue8m0=None,
+                  status=None) -> None:
+    """Fresh dispatch into preallocated outputs (allocates nothing).  ``status`` ([1] int32, optional) receives
+    0 or MIEP_ECAPACITY (read it with ``check_status``); ``recv_x_scales_ue8m0`` ([cap, H/128] uint8) receives
+    the scales' exponent bytes when ``use_ue8m0``."""
     kind = _x_kind(x, cast_to_fp8)
     _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
+    _check_ue8m0(x, kind, round_scale, use_ue8m0, handle, recv_x_scales_ue8m0)
+    _want(status, "status", torch.int32, (1,))
     N, S, R, K = x.shape[0], handle.num_src, handle.num_ranks, handle.num_topk
     _want(num_tokens_per_rank, "num_tokens_per_rank", torch.int32, (S, R))
     _want(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, (S, handle.num_experts))
@@ -223,9 +237,21 @@ def dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per
     h = handle.c()
     a = _Args()
     a.handle(handle)
-    _run(a, "miep_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), a.p(topk_idx),
-         a.p(topk_weights), a.p(num_tokens_per_rank), a.p(num_tokens_per_expert), a.p(recv_x), a.p(recv_x_scales),
-         a.p(recv_topk_idx), a.p(recv_topk_weights), a.p(num_recv_tokens_per_expert), ctypes.byref(h))
+    _run(a, "miep_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), int(use_ue8m0),
+         a.p(topk_idx), a.p(topk_weights), a.p(num_tokens_per_rank), a.p(num_tokens_per_expert), a.p(recv_x),
+         a.p(recv_x_scales), a.p(recv_x_scales_ue8m0 if use_ue8m0 else None), a.p(recv_topk_idx),
+         a.p(recv_topk_weights), a.p(num_recv_tokens_per_expert), a.p(status), ctypes.byref(h))
+
+
+def _check_ue8m0(x, kind, round_scale, use_ue8m0, handle: Handle, out):
+    if not use_ue8m0:
+        return
+    if kind != X_BF16_CAST_FP8 or not round_scale:
+        raise ValueError("use_ue8m0 needs the FP8 cast (cast_to_fp8=True) with round_scale=True")
+    H = x.shape[1]
+    if out is None or out.dtype != torch.uint8 or out.dim() != 2 or out.shape[1] != H // 128 or \
+            out.shape[0] < handle.recv_capacity:
+        raise ValueError("recv_x_scales_ue8m0 must be uint8 [>= %d, %d]" % (handle.recv_capacity, H // 128))
 
 
 def _check_payload_shapes(x, kind, x_scales, handle: Handle, recv_x, recv_x_scales):
@@ -263,13 +289,18 @@ def dispatch(x: torch.Tensor, topk_idx: Optional[torch.Tensor], topk_weights: Op
              num_tokens_per_rank: torch.Tensor, is_token_in_rank: torch.Tensor,
              num_tokens_per_expert: Optional[torch.Tensor], num_experts: int, num_channels: int = 24,
              expert_alignment: int = 1, num_worst_tokens: int = 0, x_scales: Optional[torch.Tensor] = None,
-             cast_to_fp8: bool = False, round_scale: bool = False):
+             cast_to_fp8: bool = False, round_scale: bool = False, use_ue8m0: bool = False,
+             check_capacity: bool = True):
     """Normal-mode dispatch (section 4.1, fresh branch).
 
     Receive buffers are sized exactly from num_tokens_per_rank (one host
     read, the CPU-sync mode) unless ``num_worst_tokens`` > 0 gives a fixed
-    capacity.  Returns (recv_x, recv_x_scales, recv_topk_idx,
-    recv_topk_weights, num_recv_tokens_per_expert [R, E/R], handle).
+    capacity; then, with ``check_capacity``, the device status word is read
+    back (synchronously) and an overflow raises MiepError(MIEP_ECAPACITY).
+    Returns (recv_x, recv_x_scales, recv_topk_idx, recv_topk_weights,
+    num_recv_tokens_per_expert [R, E/R], handle), and with ``use_ue8m0``
+    (FP8 cast with round_scale) a seventh item, the scales' exponent bytes
+    [cap, H/128] uint8.
     """
     kind = _x_kind(x, cast_to_fp8)
     N, H = x.shape
@@ -287,31 +318,40 @@ def dispatch(x: torch.Tensor, topk_idx: Optional[torch.Tensor], topk_weights: Op
     recv_topk_weights = torch.empty((cap, K), dtype=torch.float32, device=dev) if topk_weights is not None else None
     nrte = torch.empty((R, num_experts // R), dtype=torch.int32, device=dev) if num_tokens_per_expert is not None \
         else None
+    ue = torch.empty((cap, H // 128), dtype=torch.uint8, device=dev) if use_ue8m0 else None
+    status = torch.empty((1,), dtype=torch.int32, device=dev) if num_worst_tokens > 0 else None
     dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_tokens_per_expert, handle, recv_x,
                   recv_x_scales, recv_topk_idx, recv_topk_weights, nrte, x_scales, cast_to_fp8, round_scale,
-                  expert_alignment)
-    return recv_x, recv_x_scales, recv_topk_idx, recv_topk_weights, nrte, handle
+                  expert_alignment, use_ue8m0, ue, status)
+    if status is not None and check_capacity:
+        check_status(status)
+    out = (recv_x, recv_x_scales, recv_topk_idx, recv_topk_weights, nrte, handle)
+    return out + (ue,) if use_ue8m0 else out
 
 
 def cached_dispatch_into(x, handle: Handle, recv_x, recv_x_scales=None, x_scales=None, cast_to_fp8: bool = False,
-                         round_scale: bool = False) -> None:
+                         round_scale: bool = False, use_ue8m0: bool = False, recv_x_scales_ue8m0=None) -> None:
     kind = _x_kind(x, cast_to_fp8)
     _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
+    _check_ue8m0(x, kind, round_scale, use_ue8m0, handle, recv_x_scales_ue8m0)
     p = handle.problem(x.shape[1])
     h = handle.c()
     a = _Args()
     a.handle(handle)
-    _run(a, "miep_cached_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), ctypes.byref(h),
-         a.p(recv_x), a.p(recv_x_scales))
+    _run(a, "miep_cached_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), int(use_ue8m0),
+         ctypes.byref(h), a.p(recv_x), a.p(recv_x_scales), a.p(recv_x_scales_ue8m0 if use_ue8m0 else None))
 
 
 def cached_dispatch(x: torch.Tensor, handle: Handle, x_scales: Optional[torch.Tensor] = None,
-                    cast_to_fp8: bool = False, round_scale: bool = False):
-    """Dispatch a new x along a handle's routing (section 4.1, cached branch): no top-k inputs."""
+                    cast_to_fp8: bool = False, round_scale: bool = False, use_ue8m0: bool = False):
+    """Dispatch a new x along a handle's routing (section 4.1, cached branch): no top-k inputs.
+    Returns (recv_x, recv_x_scales), plus the exponent bytes with ``use_ue8m0``."""
     kind = _x_kind(x, cast_to_fp8)
     recv_x, recv_x_scales = _recv_buffers(x, kind, handle.recv_capacity, x.device)
-    cached_dispatch_into(x, handle, recv_x, recv_x_scales, x_scales, cast_to_fp8, round_scale)
-    return recv_x, recv_x_scales
+    ue = torch.empty((handle.recv_capacity, x.shape[1] // 128), dtype=torch.uint8, device=x.device) \
+        if use_ue8m0 else None
+    cached_dispatch_into(x, handle, recv_x, recv_x_scales, x_scales, cast_to_fp8, round_scale, use_ue8m0, ue)
+    return (recv_x, recv_x_scales, ue) if use_ue8m0 else (recv_x, recv_x_scales)
 
 
 # --------------------------------------------------------------------------- combine
@@ -569,8 +609,9 @@ def relay_dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_toke
                         num_tokens_per_expert, handle: Handle, relay: RelayHandle, rdma_x, recv_x,
                         rdma_x_scales=None, recv_x_scales=None, recv_topk_idx=None, recv_topk_weights=None,
                         num_recv_tokens_per_expert=None, x_scales=None, cast_to_fp8: bool = False,
-                        round_scale: bool = False, expert_alignment: int = 1) -> None:
-    """Relay dispatch into preallocated outputs (allocates nothing)."""
+                        round_scale: bool = False, expert_alignment: int = 1, status=None) -> None:
+    """Relay dispatch into preallocated outputs (allocates nothing).  ``status`` ([1] int32, optional) receives
+    0 or MIEP_ECAPACITY (group rows or receive rows past their capacity)."""
     kind = _x_kind(x, cast_to_fp8)
     _check_payload_shapes(x, kind, x_scales, handle, recv_x, recv_x_scales)
     N, H = x.shape
@@ -603,6 +644,7 @@ def relay_dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_toke
         _want(rdma_x_scales, "rdma_x_scales", torch.float32)
     if relay.send_rdma_head.shape != (N, G):
         raise ValueError("relay.send_rdma_head must be [%d, %d]" % (N, G))
+    _want(status, "status", torch.int32, (1,))
     p = handle.problem(H, expert_alignment)
     h = handle.c()
     rh = relay.c()
@@ -612,7 +654,7 @@ def relay_dispatch_into(x, topk_idx, topk_weights, num_tokens_per_rank, num_toke
     _run(a, "miep_relay_dispatch", ctypes.byref(p), a.p(x), kind, a.p(x_scales), int(round_scale), a.p(topk_idx),
          a.p(topk_weights), a.p(num_tokens_per_rank), a.p(num_tokens_per_rdma_rank), a.p(num_tokens_per_expert),
          a.p(rdma_x), a.p(rdma_x_scales), a.p(recv_x), a.p(recv_x_scales), a.p(recv_topk_idx), a.p(recv_topk_weights),
-         a.p(num_recv_tokens_per_expert), ctypes.byref(h), ctypes.byref(rh))
+         a.p(num_recv_tokens_per_expert), a.p(status), ctypes.byref(h), ctypes.byref(rh))
 
 
 def relay_dispatch(x: torch.Tensor, topk_idx: Optional[torch.Tensor], topk_weights: Optional[torch.Tensor],
@@ -689,11 +731,15 @@ def relay_cached_dispatch(x: torch.Tensor, handle: Handle, relay: RelayHandle, x
 
 def relay_combine_into(y, handle: Handle, relay: RelayHandle, rdma_y, combined_x, recv_topk_weights=None,
                        rdma_w=None, combined_topk_weights=None, bias=None) -> None:
+    """Two-level combine into preallocated buffers (allocates nothing).  The partials' type follows rdma_y:
+    bfloat16 (rounded between the levels) or float32 (kept unrounded)."""
     N, H, K = handle.send_head.shape[0], y.shape[1], handle.num_topk
     _want(y, "y", torch.bfloat16)
     if y.dim() != 2 or y.shape[0] < handle.recv_capacity:
         raise ValueError("y must be [>= %d, H]" % handle.recv_capacity)
-    _want(rdma_y, "rdma_y", torch.bfloat16)
+    if rdma_y.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("rdma_y must be bfloat16 or float32, got %s" % rdma_y.dtype)
+    partial_f32 = rdma_y.dtype == torch.float32
     if rdma_y.dim() != 2 or rdma_y.shape[0] < relay.rdma_capacity or rdma_y.shape[1] != H:
         raise ValueError("rdma_y must be [>= %d, %d]" % (relay.rdma_capacity, H))
     _want(combined_x, "combined_x", torch.bfloat16, (N, H))
@@ -716,18 +762,19 @@ def relay_combine_into(y, handle: Handle, relay: RelayHandle, rdma_y, combined_x
     a.handle(handle)
     a.handle(relay)
     _run(a, "miep_relay_combine", ctypes.byref(p), a.p(y), a.p(recv_topk_weights), a.p(b0), a.p(b1), ctypes.byref(h),
-         ctypes.byref(rh), a.p(rdma_y), a.p(rdma_w), a.p(combined_x), a.p(combined_topk_weights))
+         ctypes.byref(rh), int(partial_f32), a.p(rdma_y), a.p(rdma_w), a.p(combined_x), a.p(combined_topk_weights))
 
 
 def relay_combine(y: torch.Tensor, handle: Handle, relay: RelayHandle, topk_weights: Optional[torch.Tensor] = None,
-                  bias=None):
-    """Two-level combine: each group row sums its group's ranks (rounded to bf16, the partial's travel type),
-    then each token sums its groups' partials and the bias.  Returns (combined_x [N, H] bf16,
-    combined_topk_weights [N, K] fp32 or None)."""
+                  bias=None, partial_f32: bool = False):
+    """Two-level combine: each group row sums its group's ranks (rounded to bf16, the partial's travel type,
+    or kept fp32 with ``partial_f32``), then each token sums its groups' partials and the bias.  Returns
+    (combined_x [N, H] bf16, combined_topk_weights [N, K] fp32 or None)."""
     _want(y, "y", torch.bfloat16)
     N, H = handle.send_head.shape[0], y.shape[1]
     dev = y.device
-    rdma_y = torch.empty((relay.rdma_capacity, H), dtype=torch.bfloat16, device=dev)
+    rdma_y = torch.empty((relay.rdma_capacity, H), dtype=torch.float32 if partial_f32 else torch.bfloat16,
+                         device=dev)
     combined_x = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     rdma_w = cw = None
     if topk_weights is not None:

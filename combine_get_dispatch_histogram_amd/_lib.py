@@ -11,11 +11,11 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmiep.so")
 
-MIEP_OK, MIEP_EINVAL, MIEP_EUNSUPPORTED, MIEP_EHIP = 0, 1, 2, 3
+MIEP_OK, MIEP_EINVAL, MIEP_EUNSUPPORTED, MIEP_EHIP, MIEP_ECAPACITY = 0, 1, 2, 3, 4
 X_BF16, X_FP8, X_BF16_CAST_FP8 = 0, 1, 2
 
 # Every symbol the header declares (checked by the CPU ABI test).
-EXPORTS = ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
+EXPORTS = ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_check_status", "miep_combine",
            "miep_relay_dispatch", "miep_relay_cached_dispatch", "miep_relay_combine", "miep_ll_dispatch",
            "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query", "miep_ll_msg_bytes",
            "miep_last_error", "miep_version")
@@ -66,24 +66,25 @@ def load() -> ctypes.CDLL:
                               % LIB_PATH)
         lib = ctypes.CDLL(LIB_PATH)
         lib.miep_get_dispatch_layout.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P]
-        lib.miep_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                      ctypes.POINTER(HandleC), _P]
-        lib.miep_cached_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, ctypes.POINTER(HandleC), _P,
-                                             _P, _P]
+        lib.miep_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, _I32] + [_P] * 11 + \
+            [ctypes.POINTER(HandleC), _P]
+        lib.miep_cached_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, _I32, ctypes.POINTER(HandleC),
+                                             _P, _P, _P, _P]
+        lib.miep_check_status.argtypes = [_P, _P]
         lib.miep_combine.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.POINTER(HandleC), _P, _P, _P]
-        lib.miep_relay_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32] + [_P] * 12 + \
+        lib.miep_relay_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32] + [_P] * 13 + \
             [ctypes.POINTER(HandleC), ctypes.POINTER(RelayHandleC), _P]
         lib.miep_relay_cached_dispatch.argtypes = [ctypes.POINTER(Problem), _P, _I32, _P, _I32, ctypes.POINTER(HandleC),
                                                    ctypes.POINTER(RelayHandleC), _P, _P, _P, _P, _P]
         lib.miep_relay_combine.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.POINTER(HandleC),
-                                           ctypes.POINTER(RelayHandleC), _P, _P, _P, _P, _P]
+                                           ctypes.POINTER(RelayHandleC), _I32, _P, _P, _P, _P, _P]
         lib.miep_ll_dispatch.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P]
         lib.miep_ll_combine.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _P, _P, _P, _P, _P]
         lib.miep_mask_update.argtypes = [_P, _I32, _I32, _I32, _P]
         lib.miep_mask_clean.argtypes = [_P, _I32, _P]
         lib.miep_mask_query.argtypes = [_P, _I32, _P, _P]
-        for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_combine",
+        for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_check_status", "miep_combine",
                   "miep_relay_dispatch", "miep_relay_cached_dispatch", "miep_relay_combine",
                   "miep_ll_dispatch", "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query"):
             getattr(lib, f).restype = ctypes.c_int

@@ -64,6 +64,17 @@ miep_status check_problem(const miep_problem* p) {
   return ok();
 }
 
+static_assert(miep::kStatusCapacity == MIEP_ECAPACITY, "device status code must match the header");
+
+// use_ue8m0 needs power-of-two scales from the fused cast, and somewhere to put the bytes
+miep_status check_ue8m0(int32_t x_kind, int32_t round_scale, int32_t use_ue8m0, const uint8_t* out, int64_t cap) {
+  if (!use_ue8m0) return MIEP_OK;
+  if (x_kind != MIEP_X_BF16_CAST_FP8 || !round_scale)
+    return fail(MIEP_EINVAL, "use_ue8m0 needs x_kind MIEP_X_BF16_CAST_FP8 with round_scale");
+  if (cap > 0 && !out) return fail(MIEP_EINVAL, "recv_x_scales_ue8m0 is NULL with use_ue8m0");
+  return MIEP_OK;
+}
+
 miep_status check_payload(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales) {
   if (x_kind != MIEP_X_BF16 && x_kind != MIEP_X_FP8 && x_kind != MIEP_X_BF16_CAST_FP8)
     return fail(MIEP_EINVAL, "unknown x_kind %d", x_kind);
@@ -236,14 +247,16 @@ miep_status miep_get_dispatch_layout(const miep_problem* p, const int64_t* topk_
 }
 
 miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
-                          int32_t round_scale, const int64_t* topk_idx, const float* topk_weights,
+                          int32_t round_scale, int32_t use_ue8m0, const int64_t* topk_idx, const float* topk_weights,
                           const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_expert, void* recv_x,
-                          float* recv_x_scales, int64_t* recv_topk_idx, float* recv_topk_weights,
-                          int32_t* num_recv_tokens_per_expert, const miep_handle* h, void* stream) {
+                          float* recv_x_scales, uint8_t* recv_x_scales_ue8m0, int64_t* recv_topk_idx,
+                          float* recv_topk_weights, int32_t* num_recv_tokens_per_expert, int32_t* status,
+                          const miep_handle* h, void* stream) {
   miep_status st = check_problem(p);
   if (st != MIEP_OK) return st;
   if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
   if ((st = check_handle(p, h, true)) != MIEP_OK) return st;
+  if ((st = check_ue8m0(x_kind, round_scale, use_ue8m0, recv_x_scales_ue8m0, h->recv_capacity)) != MIEP_OK) return st;
   if (p->num_src > 0 && !num_tokens_per_rank) return fail(MIEP_EINVAL, "num_tokens_per_rank is NULL");
   if (h->recv_capacity > 0 && !recv_x) return fail(MIEP_EINVAL, "recv_x is NULL");
   if (!aligned16(recv_x)) return fail(MIEP_EUNSUPPORTED, "recv_x must be 16-byte aligned");
@@ -262,17 +275,21 @@ miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, 
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   miep::NotifyArgs na = notify_args(p, h, num_tokens_per_rank, num_tokens_per_expert, num_recv_tokens_per_expert);
+  na.status = status;
+  na.capacity = h->recv_capacity;
   if (p->num_src == 0) {
-    // no sources: every receive offset is 0 and every expert count is 0
+    // no sources: every receive offset is 0, every expert count is 0, nothing overflows
     hipError_t e = miep::launch_fill_zero(h->recv_rank_offset, p->num_ranks + 1, s);
     if (e == hipSuccess && num_recv_tokens_per_expert)
       e = miep::launch_fill_zero(num_recv_tokens_per_expert, p->num_experts, s);
+    if (e == hipSuccess && status) e = miep::launch_fill_zero(status, 1, s);
     return hip_status(e, "dispatch (no sources)");
   }
   hipError_t e = miep::launch_notify(na, s);
   if (e != hipSuccess) return hip_status(e, "notify launch");
 
   miep::PackArgs a = pack_args(p, x, x_kind, x_scales, round_scale, h, recv_x, recv_x_scales);
+  a.recv_ue = use_ue8m0 ? recv_x_scales_ue8m0 : nullptr;
   a.meta = 1;
   a.topk_idx = topk_idx;
   a.topk_weights = topk_weights;
@@ -284,20 +301,35 @@ miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, 
 }
 
 miep_status miep_cached_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
-                                 int32_t round_scale, const miep_handle* h, void* recv_x, float* recv_x_scales,
-                                 void* stream) {
+                                 int32_t round_scale, int32_t use_ue8m0, const miep_handle* h, void* recv_x,
+                                 float* recv_x_scales, uint8_t* recv_x_scales_ue8m0, void* stream) {
   miep_status st = check_problem(p);
   if (st != MIEP_OK) return st;
   if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
   if ((st = check_handle(p, h, false)) != MIEP_OK) return st;
+  if ((st = check_ue8m0(x_kind, round_scale, use_ue8m0, recv_x_scales_ue8m0, h->recv_capacity)) != MIEP_OK) return st;
   if (h->recv_capacity > 0 && !recv_x) return fail(MIEP_EINVAL, "recv_x is NULL");
   if (!aligned16(recv_x)) return fail(MIEP_EUNSUPPORTED, "recv_x must be 16-byte aligned");
   if (x_kind != MIEP_X_BF16 && h->recv_capacity > 0 && !recv_x_scales)
     return fail(MIEP_EINVAL, "recv_x_scales is NULL for an FP8 dispatch");
   miep::PackArgs a = pack_args(p, x, x_kind, x_scales, round_scale, h, recv_x, recv_x_scales);
+  a.recv_ue = use_ue8m0 ? recv_x_scales_ue8m0 : nullptr;
   a.meta = 0;
   a.K = 0;
   return hip_status(miep::launch_pack(a, static_cast<hipStream_t>(stream)), "cached pack launch");
+}
+
+miep_status miep_check_status(const int32_t* status, void* stream) {
+  if (!status) return fail(MIEP_EINVAL, "status is NULL");
+  int32_t v = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&v, status, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "status read");
+  if (v == MIEP_OK) return ok();
+  if (v == MIEP_ECAPACITY)
+    return fail(MIEP_ECAPACITY, "the receive side needed more rows than its fixed capacity; rows past it were dropped");
+  return fail(MIEP_EINVAL, "status word holds %d, not a status a dispatch writes", v);
 }
 
 miep_status miep_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
@@ -336,7 +368,7 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
                                 const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_rdma_rank,
                                 const int32_t* num_tokens_per_expert, void* rdma_x, float* rdma_x_scales,
                                 void* recv_x, float* recv_x_scales, int64_t* recv_topk_idx,
-                                float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
+                                float* recv_topk_weights, int32_t* num_recv_tokens_per_expert, int32_t* status,
                                 const miep_handle* h, const miep_relay_handle* rh, void* stream) {
   miep_status st = check_problem(p);
   if (st != MIEP_OK) return st;
@@ -366,10 +398,13 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
     if (e == hipSuccess) e = miep::launch_fill_zero(rh->recv_rdma_offset, G + 1, s);
     if (e == hipSuccess && num_recv_tokens_per_expert)
       e = miep::launch_fill_zero(num_recv_tokens_per_expert, p->num_experts, s);
+    if (e == hipSuccess && status) e = miep::launch_fill_zero(status, 1, s);
     return hip_status(e, "relay dispatch (no sources)");
   }
   // the ranks' handle (the receive side is the direct dispatch's)
   miep::NotifyArgs na = notify_args(p, h, num_tokens_per_rank, num_tokens_per_expert, num_recv_tokens_per_expert);
+  na.status = status;
+  na.capacity = h->recv_capacity;
   hipError_t e = miep::launch_notify(na, s);
   if (e != hipSuccess) return hip_status(e, "notify launch");
   // the groups' prefix matrices, offsets and send_rdma_head
@@ -385,6 +420,8 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
   ng.rcpm = rh->recv_rdma_channel_prefix_matrix;
   ng.off = rh->recv_rdma_offset;
   ng.send_head = rh->send_rdma_head;
+  ng.capacity = rh->rdma_capacity;
+  ng.status_or = 1;                  // keeps the first notify's verdict and adds the group rows' one
   e = miep::launch_notify(ng, s);
   if (e != hipSuccess) return hip_status(e, "group notify launch");
   miep::RelayMetaArgs rm{};
@@ -472,8 +509,8 @@ miep_status miep_relay_cached_dispatch(const miep_problem* p, const void* x, int
 
 miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
                                const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
-                               const miep_relay_handle* rh, uint16_t* rdma_y, float* rdma_w, uint16_t* combined_x,
-                               float* combined_topk_weights, void* stream) {
+                               const miep_relay_handle* rh, int32_t partial_f32, void* rdma_y, float* rdma_w,
+                               uint16_t* combined_x, float* combined_topk_weights, void* stream) {
   miep_status st = check_problem(p);
   if (st != MIEP_OK) return st;
   if ((st = check_handle(p, h, false)) != MIEP_OK) return st;
@@ -500,7 +537,8 @@ miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const f
   c1.w = recv_topk_weights;
   c1.send_head = rh->send_nvl_head;
   c1.off = h->recv_rank_offset;
-  c1.out = rdma_y;
+  c1.out = static_cast<uint16_t*>(rdma_y);
+  c1.out_f32 = partial_f32 ? 1 : 0;
   c1.out_w = recv_topk_weights ? rdma_w : nullptr;
   c1.count = rh->recv_rdma_offset + G;
   c1.group_off = rh->recv_rdma_offset;
@@ -516,7 +554,8 @@ miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const f
   c2.K = p->num_topk;
   c2.R = G;
   c2.capacity = rh->rdma_capacity;
-  c2.y = rdma_y;
+  c2.y = static_cast<const uint16_t*>(rdma_y);
+  c2.in_f32 = partial_f32 ? 1 : 0;
   c2.w = recv_topk_weights ? rdma_w : nullptr;
   c2.bias0 = N > 0 ? bias_0 : nullptr;
   c2.bias1 = N > 0 ? bias_1 : nullptr;
@@ -528,12 +567,19 @@ miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const f
   return hip_status(miep::launch_combine(c2, s), "relay combine (token level) launch");
 }
 
-miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,
+}  // extern "C"
+
+namespace {
+
+// Checks and arguments of a low-latency dispatch.  with_msgs: the caller's
+// message buffer and counts (msg_buf, msg_count) are required; otherwise
+// they are null and the caller fills a.msg_count.
+miep_status ll_dispatch_args(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,
                              int32_t round_scale, int32_t use_ue8m0, void* msg_buf, int32_t* msg_count,
                              void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
                              int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
                              int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats,
-                             const int32_t* mask_buffer, void* stream) {
+                             const int32_t* mask_buffer, bool with_msgs, miep::LLArgs* out) {
   miep_status st = check_ll_problem(q);
   if (st != MIEP_OK) return st;
   const int R = q->num_ranks, T = q->num_tokens, M = q->max_tokens, H = q->hidden, K = q->num_topk,
@@ -542,13 +588,14 @@ miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const 
   if (use_ue8m0 && !use_fp8) return fail(MIEP_EINVAL, "use_ue8m0 requires use_fp8");
   if (use_fp8 && H % 512 != 0)
     return fail(MIEP_EUNSUPPORTED, "FP8 low-latency messages need hidden % 512 == 0 (16-byte message stride)");
-  if ((T > 0 && (!x || !topk_idx)) || !msg_buf || !msg_count || !packed_recv_x || !packed_recv_src_info ||
-      !packed_recv_layout_range || !packed_recv_count)
+  if ((T > 0 && (!x || !topk_idx)) || (with_msgs && (!msg_buf || !msg_count)) || !packed_recv_x ||
+      !packed_recv_src_info || !packed_recv_layout_range || !packed_recv_count)
     return fail(MIEP_EINVAL, "a required pointer is NULL");
   if (use_fp8 && !packed_recv_x_scales) return fail(MIEP_EINVAL, "packed_recv_x_scales is NULL with use_fp8");
   if (!aligned16(x) || !aligned16(msg_buf) || !aligned16(packed_recv_x))
     return fail(MIEP_EUNSUPPORTED, "x, msg_buf and packed_recv_x must be 16-byte aligned");
-  miep::LLArgs a{};
+  miep::LLArgs& a = *out;
+  a = miep::LLArgs{};
   a.R = R;
   a.T = T;
   a.M = M;
@@ -573,6 +620,25 @@ miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const 
   a.count = packed_recv_count;
   a.cumulative = cumulative_local_expert_recv_stats;
   a.mask = mask_buffer;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,
+                             int32_t round_scale, int32_t use_ue8m0, void* msg_buf, int32_t* msg_count,
+                             void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
+                             int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
+                             int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats,
+                             const int32_t* mask_buffer, void* stream) {
+  miep::LLArgs a;
+  miep_status st = ll_dispatch_args(q, x, topk_idx, use_fp8, round_scale, use_ue8m0, msg_buf, msg_count,
+                                    packed_recv_x, packed_recv_x_scales, packed_recv_x_scales_ue8m0,
+                                    packed_recv_src_info, packed_recv_layout_range, packed_recv_count,
+                                    cumulative_local_expert_recv_stats, mask_buffer, true, &a);
+  if (st != MIEP_OK) return st;
   return hip_status(miep::launch_ll(a, static_cast<hipStream_t>(stream)), "low-latency launch");
 }
 

@@ -14,13 +14,38 @@
 // traffic uses buffer instructions on the wave-uniform row base; by default
 // the expert outputs stream in non-temporal and the combined rows are
 // written at device scope.
+//
+// Row element types (IO): kBf16 reads bf16 rows and writes bf16 rows;
+// kToF32 writes the fp32 sums unrounded (the two-level combine's first
+// level with fp32 partials); kFromF32 reads fp32 rows (its second level).
+// A lane always owns 8 consecutive channels: one 16-byte vector of bf16 or
+// two of fp32.
 #include "device.h"
 #include "kernels.h"
 
 namespace miep {
 
-template <int VPL, int MAXR, int MW, int NT>
+enum CombineIO { kBf16 = 0, kToF32 = 1, kFromF32 = 2 };
+
+// 8 channels of an expert-output row -> fp32 (one bf16 vector, or two fp32 vectors)
+template <bool IN32>
+__device__ __forceinline__ void widen8(const v4u (&d)[2], float (&f)[8]) {
+  if constexpr (IN32) {
+    f[0] = __uint_as_float(d[0].x); f[1] = __uint_as_float(d[0].y);
+    f[2] = __uint_as_float(d[0].z); f[3] = __uint_as_float(d[0].w);
+    f[4] = __uint_as_float(d[1].x); f[5] = __uint_as_float(d[1].y);
+    f[6] = __uint_as_float(d[1].z); f[7] = __uint_as_float(d[1].w);
+  } else {
+    f[0] = bf16_lo(d[0].x); f[1] = bf16_hi(d[0].x); f[2] = bf16_lo(d[0].y); f[3] = bf16_hi(d[0].y);
+    f[4] = bf16_lo(d[0].z); f[5] = bf16_hi(d[0].z); f[6] = bf16_lo(d[0].w); f[7] = bf16_hi(d[0].w);
+  }
+}
+
+template <int VPL, int MAXR, int MW, int NT, int IO = kBf16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices) {
+  constexpr bool kIn32 = IO == kFromF32;
+  constexpr bool kOut32 = IO == kToF32;
+  constexpr int kInVec = kIn32 ? 2 : 1;          // 16-byte input vectors per 8 channels
   const int lane = lane_id();
   const int64_t gw = wave_index();
   const int64_t n = gw / nslices;
@@ -72,10 +97,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
     if (lane < a.K) a.out_w[n * a.K + lane] = have ? acc : 0.0f;
   }
 
-  const int nv = a.H / 8;  // 16-byte vectors of 8 bf16
+  const int nv = a.H / 8;  // groups of 8 channels
   const uint8_t* y = reinterpret_cast<const uint8_t*>(a.y);
-  const int64_t row_bytes = 2 * static_cast<int64_t>(a.H);
-  uint8_t* orow = reinterpret_cast<uint8_t*>(a.out) + n * row_bytes;
+  const int64_t bf_row_bytes = 2 * static_cast<int64_t>(a.H);
+  const int64_t in_row_bytes = (kIn32 ? 4 : 2) * static_cast<int64_t>(a.H);
+  uint8_t* orow = reinterpret_cast<uint8_t*>(a.out) + n * (kOut32 ? 4 : 2) * static_cast<int64_t>(a.H);
   const int span = kWave * VPL;
   for (int v0 = slice * span; v0 < nv; v0 += nslices * span) {
     float acc[VPL][8];
@@ -98,15 +124,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
             nb = q + 1;
           }
         }
-        v4u d[MAXR][VPL];
+        v4u d[MAXR][VPL][2];
 #pragma unroll
         for (int q = 0; q < MAXR; ++q) {
           if (q < nb) {
-            const uint8_t* yrow = y + rows[q] * row_bytes;
+            const uint8_t* yrow = y + rows[q] * in_row_bytes;
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
               const int v = v0 + j * kWave + lane;
-              if (v < nv) d[q][j] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(v) * 16);
+              if (v < nv) {
+#pragma unroll
+                for (int h = 0; h < kInVec; ++h)
+                  d[q][j][h] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(v) * (16 * kInVec) + 16 * h);
+              }
             }
           }
         }
@@ -115,8 +145,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
           if (q < nb) {
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
-              const float f[8] = {bf16_lo(d[q][j].x), bf16_hi(d[q][j].x), bf16_lo(d[q][j].y), bf16_hi(d[q][j].y),
-                                  bf16_lo(d[q][j].z), bf16_hi(d[q][j].z), bf16_lo(d[q][j].w), bf16_hi(d[q][j].w)};
+              float f[8];
+              widen8<kIn32>(d[q][j], f);
 #pragma unroll
               for (int k = 0; k < 8; ++k) acc[j][k] = have ? acc[j][k] + f[k] : f[k];
             }
@@ -139,7 +169,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
         for (int b = 0; b < 2; ++b) {
           const uint16_t* bias = b == 0 ? a.bias0 : a.bias1;
           if (bias == nullptr) continue;
-          const v4u t = ld16(reinterpret_cast<const uint8_t*>(bias) + n * row_bytes + static_cast<int64_t>(v) * 16);
+          const v4u t = ld16(reinterpret_cast<const uint8_t*>(bias) + n * bf_row_bytes + static_cast<int64_t>(v) * 16);
           const float f[8] = {bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y),
                               bf16_lo(t.z), bf16_hi(t.z), bf16_lo(t.w), bf16_hi(t.w)};
 #pragma unroll
@@ -152,32 +182,55 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
     for (int j = 0; j < VPL; ++j) {
       const int v = v0 + j * kWave + lane;
       if (v < nv) {
-        v4u o;
-        if (have) {
-          o.x = pack_bf16x2(acc[j][0], acc[j][1]);
-          o.y = pack_bf16x2(acc[j][2], acc[j][3]);
-          o.z = pack_bf16x2(acc[j][4], acc[j][5]);
-          o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+        if constexpr (kOut32) {
+          const v4u o0 = have ? v4u{__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]), __float_as_uint(acc[j][2]),
+                                    __float_as_uint(acc[j][3])}
+                              : v4u{0u, 0u, 0u, 0u};
+          const v4u o1 = have ? v4u{__float_as_uint(acc[j][4]), __float_as_uint(acc[j][5]), __float_as_uint(acc[j][6]),
+                                    __float_as_uint(acc[j][7])}
+                              : v4u{0u, 0u, 0u, 0u};
+          stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 32, o0);
+          stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 32 + 16, o1);
         } else {
-          o = v4u{0u, 0u, 0u, 0u};
+          v4u o;
+          if (have) {
+            o.x = pack_bf16x2(acc[j][0], acc[j][1]);
+            o.y = pack_bf16x2(acc[j][2], acc[j][3]);
+            o.z = pack_bf16x2(acc[j][4], acc[j][5]);
+            o.w = pack_bf16x2(acc[j][6], acc[j][7]);
+          } else {
+            o = v4u{0u, 0u, 0u, 0u};
+          }
+          stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, o);
         }
-        stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 16, o);
       }
     }
   }
 }
 
-template <int VPL, int MAXR, int NT>
+template <int VPL, int MAXR, int NT, int IO = kBf16>
 static hipError_t launch_combine_cfg(const CombineArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
   const int64_t blocks = (waves + 3) / 4;
   if (a.R <= 64)
-    hipLaunchKernelGGL((combine_kernel<VPL, MAXR, 1, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
-                       nslices);
+    hipLaunchKernelGGL((combine_kernel<VPL, MAXR, 1, NT, IO>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       a, nslices);
   else
-    hipLaunchKernelGGL((combine_kernel<VPL, MAXR, 4, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
-                       nslices);
+    hipLaunchKernelGGL((combine_kernel<VPL, MAXR, 4, NT, IO>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       a, nslices);
   return hipGetLastError();
+}
+
+// The two-level combine with fp32 partials: one geometry, the relay's
+// cache-policy code (non-temporal loads and stores at device scope), and 4
+// channel groups per lane as the bf16 group level (8 for ragged rows).
+template <int IO>
+static hipError_t launch_combine_f32(const CombineArgs& a, hipStream_t st) {
+  const int nv = a.H / 8;
+  const int vpl = nv % kWave == 0 ? 4 : 8;
+  const int span = vpl * kWave;
+  const int nslices = (nv + span - 1) / span;
+  return vpl == 4 ? launch_combine_cfg<4, 2, 7, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 7, IO>(a, nslices, st);
 }
 
 // (vectors per lane, rows loaded per batch) pairs compiled in; register use
@@ -198,6 +251,8 @@ static hipError_t launch_combine_nt(const CombineArgs& a, int vpl, int maxr, int
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
+  if (a.out_f32) return launch_combine_f32<kToF32>(a, st);
+  if (a.in_f32) return launch_combine_f32<kFromF32>(a, st);
   const Tuning& tu = tuning();
   const int nv = a.H / 8;
   // default: one 16-byte vector per lane per row and 8 rows' loads in flight

@@ -122,6 +122,13 @@ __device__ __forceinline__ float fp8_scales(float amax, bool round_scale, float*
   return 448.0f / amax;
 }
 
+// Exponent byte (UE8M0) of a power-of-two scale 2^e from fp8_scales with
+// round_scale: its biased fp32 exponent field, e + 127 (the sign is 0 and the
+// mantissa 0, and e + 127 stays in [1, 254] for every floored amax).
+__device__ __forceinline__ uint8_t ue8m0_byte(float pow2_scale) {
+  return static_cast<uint8_t>(__float_as_uint(pow2_scale) >> 23);
+}
+
 // Max over the 8 lanes that hold one 128-channel group (16 channels each).
 __device__ __forceinline__ float group8_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 1, 8));

@@ -12,6 +12,7 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kFp8Group = 128;     // channels per FP8 scale
 constexpr int kMaxRanks = 256;     // logical ranks supported by one call
 constexpr int kMaxExperts = 8192;  // experts (LDS histogram bound)
+constexpr int kStatusCapacity = 4; // device status word value of MIEP_ECAPACITY
 
 // Division by a launch constant without the ~30-instruction integer divide:
 // floor(n / d) = (n * m) >> 40 with m = ceil(2^40 / d).  Writing m = (2^40 +
@@ -61,6 +62,12 @@ struct NotifyArgs {
   int32_t* off;             // [R+1]
   int32_t* send_head;       // [S*T][R]
   int32_t* nrte;            // [R][L] or null
+  // Device status word (null: none): workgroup 0 writes kStatusCapacity when
+  // the receive rows exceed `capacity`, else 0 -- or, with status_or, writes
+  // only on an overflow (a second notify of the same call keeps the first's).
+  int32_t* status = nullptr;
+  int64_t capacity = 0;
+  int status_or = 0;
 };
 hipError_t launch_notify(const NotifyArgs& a, hipStream_t st);
 // Zero-fill of an int32 array by a kernel (no memset node in captured graphs).
@@ -83,6 +90,7 @@ struct PackArgs {
   const int32_t* off;
   void* recv_x;
   float* recv_x_scales;
+  uint8_t* recv_ue = nullptr;  // [cap][H/128] exponent bytes of power-of-two scales (fused cast), or null
   int64_t* recv_topk_idx;
   float* recv_topk_weights;
   int32_t* recv_src_idx;
@@ -114,6 +122,9 @@ struct CombineArgs {
   const int32_t* group_off;  // [groups+1]
   int groups, group_w;
   int cpol = -1;             // cache-policy code of this launch (-1: the default)
+  // Row element types (the two-level combine's fp32 partials): y is fp32
+  // [cap][H] when in_f32, out is fp32 [N][H] when out_f32 (no rounding).
+  int in_f32 = 0, out_f32 = 0;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 

@@ -445,7 +445,15 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
       if (r < R) a.off[r] = carry + inc - v;
       carry += readlane(inc, kWave - 1);
     }
-    if (lane == 0) a.off[R] = carry;
+    if (lane == 0) {
+      a.off[R] = carry;
+      // capacity overflow (fixed-capacity receive side): rows past it are skipped by every writer
+      if (a.status != nullptr) {
+        const bool over = carry > a.capacity;
+        if (!a.status_or) *a.status = over ? kStatusCapacity : 0;
+        else if (over) *a.status = kStatusCapacity;
+      }
+    }
   }
 
   // per-expert receive counts, rounded up to the expert alignment (the sum

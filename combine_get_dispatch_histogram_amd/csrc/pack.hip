@@ -123,7 +123,10 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
             const int pi = p0 + j * kWave + lane;
             if (pi < np) {
               stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(pi) * 16, q[j]);
-              if ((lane & 7) == 0) a.recv_x_scales[row * G + pi / 8] = sci[j];
+              if ((lane & 7) == 0) {
+                a.recv_x_scales[row * G + pi / 8] = sci[j];
+                if (a.recv_ue) a.recv_ue[row * G + pi / 8] = ue8m0_byte(sci[j]);
+              }
             }
           }
         }
@@ -275,6 +278,10 @@ __global__ __launch_bounds__(1024) void pack_cast_kernel(PackArgs a) {
         const int64_t row = readlane(dst[i], b);
         float* srow = a.recv_x_scales + row * G;
         for (int g = lane; g < G; g += kWave) srow[g] = row_scales[g];
+        if (a.recv_ue) {
+          uint8_t* urow = a.recv_ue + row * G;
+          for (int g = lane; g < G; g += kWave) urow[g] = ue8m0_byte(row_scales[g]);
+        }
         if (a.meta) {
           if (lane < a.K) {
             const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;

@@ -31,6 +31,10 @@
  *     earlier kernels enqueued.  No call aborts, traps or prints.
  *   - Device-side bounds: rows at or past `recv_capacity` are never
  *     written; top-k entries outside [0, num_experts) are treated as masked.
+ *   - Errors the host cannot see at call time (a receive side larger than
+ *     its fixed capacity) are reported through a caller-owned device status
+ *     word: the call writes 0 or the miep_status code, and
+ *     miep_check_status() reads it back synchronously.
  */
 #ifndef MIEP_H
 #define MIEP_H
@@ -45,7 +49,8 @@ typedef enum miep_status {
   MIEP_OK = 0,
   MIEP_EINVAL = 1,       /* a bad argument: null pointer, size or flag */
   MIEP_EUNSUPPORTED = 2, /* valid, but outside what the kernels handle (e.g. R > 256, misaligned x) */
-  MIEP_EHIP = 3          /* the HIP runtime refused a launch */
+  MIEP_EHIP = 3,         /* the HIP runtime refused a launch */
+  MIEP_ECAPACITY = 4     /* device status: the receive rows exceeded a fixed capacity (rows past it were dropped) */
 } miep_status;
 
 /* Payload kinds of a normal-mode dispatch. */
@@ -110,37 +115,57 @@ miep_status miep_get_dispatch_layout(const miep_problem* p, const int64_t* topk_
  *   x                  [N][H] per x_kind (16-byte aligned; H % 8 == 0, FP8 kinds H % 128 == 0)
  *   x_scales           [N][H/128] fp32 for MIEP_X_FP8, else ignored
  *   round_scale        for MIEP_X_BF16_CAST_FP8: power-of-two scales
+ *   use_ue8m0          ([Ch4] 4.3 flag) also emit each power-of-two scale 2^e as
+ *                      its exponent byte e + 127; needs MIEP_X_BF16_CAST_FP8 with
+ *                      round_scale (else EINVAL).  The fp32 scales are written too.
  *   topk_idx           [N][K] int64, nullable (then no recv_topk_* output)
  *   topk_weights       [N][K] fp32, nullable
  *   num_tokens_per_rank   [S][R] from get_dispatch_layout (source of the rank prefixes)
  *   num_tokens_per_expert [S][E] from get_dispatch_layout, nullable
  *   recv_x             [cap][H] bf16, or [cap][H] E4M3 codes for the FP8 kinds
  *   recv_x_scales      [cap][H/128] fp32 for the FP8 kinds
+ *   recv_x_scales_ue8m0 [cap][H/128] uint8, required with use_ue8m0, else ignored
  *   recv_topk_idx      [cap][K] int64: local expert id (e - r*E/R) where expert e is on the row's rank, else -1
  *   recv_topk_weights  [cap][K] fp32: the weight there, else 0
  *   num_recv_tokens_per_expert [R][E/R] out, nullable: per-expert receive count rounded up to expert_alignment
+ *   status             one int32 of device memory, nullable: set to 0, or to
+ *                      MIEP_ECAPACITY when the receive rows exceed recv_capacity
  *   h                  the handle (all members required; cap = h->recv_capacity)
- * Size the receive side exactly with sum(num_tokens_per_rank), or with a
- * worst case (the num_worst_tokens mode): recv_rank_offset[R] reports the
- * true total either way. */
+ * Size the receive side exactly with sum(num_tokens_per_rank) (never
+ * overflows), or with a worst case (the num_worst_tokens mode of [Ch4] 4.1):
+ * recv_rank_offset[R] reports the true total either way, and rows at or past
+ * the capacity are neither written nor, later, combined -- a token whose row
+ * fell past it loses that contribution in miep_combine.  A dispatch whose
+ * status reads MIEP_ECAPACITY must be redone with a larger capacity before
+ * its handle is used. */
 miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
-                          int32_t round_scale, const int64_t* topk_idx, const float* topk_weights,
+                          int32_t round_scale, int32_t use_ue8m0, const int64_t* topk_idx, const float* topk_weights,
                           const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_expert, void* recv_x,
-                          float* recv_x_scales, int64_t* recv_topk_idx, float* recv_topk_weights,
-                          int32_t* num_recv_tokens_per_expert, const miep_handle* h, void* stream);
+                          float* recv_x_scales, uint8_t* recv_x_scales_ue8m0, int64_t* recv_topk_idx,
+                          float* recv_topk_weights, int32_t* num_recv_tokens_per_expert, int32_t* status,
+                          const miep_handle* h, void* stream);
 
 /* cached_dispatch -- [Ch4] 4.1 cached branch: with a handle from an earlier
  * dispatch of the same routing, move only x (and its scales); there are no
- * top-k arguments.  Arguments as in miep_dispatch; only h->send_head,
- * h->recv_rank_offset and h->recv_capacity are read. */
+ * top-k arguments.  Arguments as in miep_dispatch (use_ue8m0 and
+ * recv_x_scales_ue8m0 likewise); only h->send_head, h->recv_rank_offset and
+ * h->recv_capacity are read. */
 miep_status miep_cached_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
-                                 int32_t round_scale, const miep_handle* h, void* recv_x, float* recv_x_scales,
-                                 void* stream);
+                                 int32_t round_scale, int32_t use_ue8m0, const miep_handle* h, void* recv_x,
+                                 float* recv_x_scales, uint8_t* recv_x_scales_ue8m0, void* stream);
+
+/* check_status -- host-side read of a status word written by miep_dispatch
+ * or miep_relay_dispatch: waits for `stream` (synchronous), copies the word
+ * and returns it (MIEP_OK or MIEP_ECAPACITY).  EINVAL for a null pointer,
+ * EHIP if the copy fails. */
+miep_status miep_check_status(const int32_t* status, void* stream);
 
 /* combine -- [Ch4] 4.2 and 4.4: send expert outputs back through the handle
  * and add them per source token in fp32 (no gate weights applied), and
  * separately add the received top-k weights.  Contributions are added in
- * ascending rank order; a token no rank received combines to zero.
+ * ascending rank order; a token no rank received combines to zero.  Only
+ * rows below h->recv_capacity are read (after an overflowed dispatch the
+ * rows past it are missing from the sums).
  * [Ch4] 4.2 also unpacks a bias into two rows for the combine without a
  * formula; here each given bias row is added to its token's fp32 sum after
  * the received contributions, bias_0 first (a token no rank received then
@@ -195,13 +220,15 @@ typedef struct miep_relay_handle {
  *   rdma_x_scales [rdma_capacity][H/128] fp32 for the FP8 kinds
  * Other arguments as in miep_dispatch.  Needs R % 8 == 0 and R > 8.  Group
  * rows at or past rh->rdma_capacity are neither written nor forwarded;
- * recv_rdma_offset[G] reports the true total. */
+ * recv_rdma_offset[G] reports the true total.  `status` (nullable) reads
+ * MIEP_ECAPACITY when either the group rows or the receive rows exceed
+ * their capacity, else 0. */
 miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_kind, const float* x_scales,
                                 int32_t round_scale, const int64_t* topk_idx, const float* topk_weights,
                                 const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_rdma_rank,
                                 const int32_t* num_tokens_per_expert, void* rdma_x, float* rdma_x_scales,
                                 void* recv_x, float* recv_x_scales, int64_t* recv_topk_idx,
-                                float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
+                                float* recv_topk_weights, int32_t* num_recv_tokens_per_expert, int32_t* status,
                                 const miep_handle* h, const miep_relay_handle* rh, void* stream);
 
 /* relay_cached_dispatch -- [Ch4] 4.1 cached branch through the relay: with
@@ -219,24 +246,27 @@ miep_status miep_relay_cached_dispatch(const miep_problem* p, const void* x, int
  * ([NvLL] normal mode reduces inside the node first, then once more across
  * nodes; [Ch4] 4.4: additions only, weights reduced separately).  First
  * level: each group row sums, in fp32 from its first term, the rows of the
- * group's ranks j ascending that hold it, rounded to bf16 (the type a
- * partial travels in) into rdma_y; the received top-k weights likewise in
- * fp32 into rdma_w.  Second level: each source token sums its groups'
- * partials g ascending in fp32, then bias_0 and bias_1 as in miep_combine,
- * rounded once more to bf16.  A token no rank received combines to zero
- * (or its bias).
+ * group's ranks j ascending that hold it, into rdma_y: rounded to bf16 (the
+ * type a partial travels in), or kept fp32 when partial_f32 is set (twice
+ * the partial bytes; the result is then one fp32 sum rounded once, which
+ * stays within bf16 rounding of the fp32 reference even where partials
+ * cancel); the received top-k weights likewise in fp32 into rdma_w.
+ * Second level: each source token sums its groups' partials g ascending in
+ * fp32, then bias_0 and bias_1 as in miep_combine, rounded once more to
+ * bf16.  A token no rank received combines to zero (or its bias).
  *   y                     [cap][H] bf16 expert outputs in the receive layout
  *   recv_topk_weights     [cap][K] fp32, nullable
  *   bias_0, bias_1        [N][H] bf16, nullable
- *   rdma_y                [rdma_capacity][H] bf16 scratch (out: the partials)
+ *   partial_f32           0: bf16 partials, 1: fp32 partials
+ *   rdma_y                [rdma_capacity][H] bf16 (or fp32) scratch (out: the partials), 16-byte aligned
  *   rdma_w                [rdma_capacity][K] fp32 scratch, required if recv_topk_weights is given
  *   combined_x            [N][H] bf16 out
  *   combined_topk_weights [N][K] fp32 out, nullable (required if recv_topk_weights is given)
  * Reads h->recv_rank_offset, h->recv_capacity and rh's heads and offsets. */
 miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const float* recv_topk_weights,
                                const uint16_t* bias_0, const uint16_t* bias_1, const miep_handle* h,
-                               const miep_relay_handle* rh, uint16_t* rdma_y, float* rdma_w, uint16_t* combined_x,
-                               float* combined_topk_weights, void* stream);
+                               const miep_relay_handle* rh, int32_t partial_f32, void* rdma_y, float* rdma_w,
+                               uint16_t* combined_x, float* combined_topk_weights, void* stream);
 
 /* Sizes of one low-latency problem, seen from the receiving rank dest_rank. */
 typedef struct miep_ll_problem {

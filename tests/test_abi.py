@@ -87,35 +87,44 @@ def test_layout_rejects_null_and_rdma_mismatch(lib):
     assert lib.miep_get_dispatch_layout(ctypes.byref(p16), 16, 16, None, 16, 16, None) == _lib.MIEP_EINVAL
 
 
+def _dispatch(lib, p, h, x=16, kind=0, x_scales=None, round_scale=0, use_ue8m0=0, recv_x_scales=None, ue=None,
+              status=None):
+    # p, x, kind, x_scales, round_scale, use_ue8m0, topk_idx, topk_weights, num_tokens_per_rank,
+    # num_tokens_per_expert, recv_x, recv_x_scales, recv_x_scales_ue8m0, recv_topk_idx, recv_topk_weights,
+    # num_recv_tokens_per_expert, status, handle, stream
+    return lib.miep_dispatch(ctypes.byref(p), x, kind, x_scales, round_scale, use_ue8m0, 16, 16, 16, 16, 16,
+                             recv_x_scales, ue, 16, 16, None, status, ctypes.byref(h), None)
+
+
 def test_dispatch_validation(lib):
     p = _problem()
     h = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, 100)
-    # misaligned x
-    rc = lib.miep_dispatch(ctypes.byref(p), 8, 0, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None, ctypes.byref(h),
-                           None)
-    assert rc == _lib.MIEP_EUNSUPPORTED
-    # FP8 payload without scales
-    rc = lib.miep_dispatch(ctypes.byref(p), 16, 1, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None, ctypes.byref(h),
-                           None)
-    assert rc == _lib.MIEP_EINVAL
-    # unknown kind
-    rc = lib.miep_dispatch(ctypes.byref(p), 16, 7, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None, ctypes.byref(h),
-                           None)
-    assert rc == _lib.MIEP_EINVAL
-    # handle missing arrays
+    assert _dispatch(lib, p, h, x=8) == _lib.MIEP_EUNSUPPORTED                  # misaligned x
+    assert _dispatch(lib, p, h, kind=1) == _lib.MIEP_EINVAL                     # FP8 payload without scales
+    assert _dispatch(lib, p, h, kind=7) == _lib.MIEP_EINVAL                     # unknown kind
     hbad = _lib.HandleC(None, 16, 16, 16, 16, 16, 16, 100)
-    rc = lib.miep_dispatch(ctypes.byref(p), 16, 0, None, 0, 16, 16, 16, 16, 16, None, 16, 16, None,
-                           ctypes.byref(hbad), None)
-    assert rc == _lib.MIEP_EINVAL
-    # FP8 cast needs hidden % 128 == 0
+    assert _dispatch(lib, p, hbad) == _lib.MIEP_EINVAL                         # handle missing arrays
     p2 = _problem(hidden=200)
-    rc = lib.miep_dispatch(ctypes.byref(p2), 16, 2, None, 0, 16, 16, 16, 16, 16, 16, 16, 16, None, ctypes.byref(h),
-                           None)
-    assert rc == _lib.MIEP_EINVAL
+    assert _dispatch(lib, p2, h, kind=2, recv_x_scales=16) == _lib.MIEP_EINVAL  # FP8 cast needs hidden % 128 == 0
+    # use_ue8m0: only with the fused cast and power-of-two scales, and with somewhere to put the bytes
+    assert _dispatch(lib, p, h, kind=2, recv_x_scales=16, use_ue8m0=1, ue=16) == _lib.MIEP_EINVAL
+    assert _dispatch(lib, p, h, kind=0, round_scale=1, use_ue8m0=1, ue=16) == _lib.MIEP_EINVAL
+    assert _dispatch(lib, p, h, kind=2, recv_x_scales=16, round_scale=1, use_ue8m0=1) == _lib.MIEP_EINVAL
+    assert "ue8m0" in lib.miep_last_error().decode()
     # negative capacity
     hneg = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, -1)
-    rc = lib.miep_cached_dispatch(ctypes.byref(p), 16, 0, None, 0, ctypes.byref(hneg), 16, None, None)
+    rc = lib.miep_cached_dispatch(ctypes.byref(p), 16, 0, None, 0, 0, ctypes.byref(hneg), 16, None, None, None)
     assert rc == _lib.MIEP_EINVAL
+    rc = lib.miep_cached_dispatch(ctypes.byref(p), 16, 2, None, 0, 1, ctypes.byref(h), 16, 16, 16, None)
+    assert rc == _lib.MIEP_EINVAL                                              # ue8m0 without round_scale
+
+
+def test_status_codes_and_check(lib):
+    """The capacity status code matches the header, and reading a status word validates its pointer."""
+    text = open(HEADER).read()
+    assert re.search(r"MIEP_ECAPACITY\s*=\s*4", text) and _lib.MIEP_ECAPACITY == 4
+    assert lib.miep_check_status(None, None) == _lib.MIEP_EINVAL
+    assert lib.miep_last_error()
 
 
 def test_problem_bounds(lib):
@@ -149,7 +158,7 @@ def test_relay_validation(lib):
 
     def d(prob, handle, relay, rdma_x=16):
         return lib.miep_relay_dispatch(ctypes.byref(prob), 16, 0, None, 0, 16, 16, 16, 16, 16, rdma_x, None, 16,
-                                       None, 16, 16, None, ctypes.byref(handle), relay, None)
+                                       None, 16, 16, None, None, ctypes.byref(handle), relay, None)
 
     assert d(_problem(num_ranks=8), h, ctypes.byref(rh)) == _lib.MIEP_EUNSUPPORTED      # one group only
     assert d(_problem(num_ranks=12), h, ctypes.byref(rh)) == _lib.MIEP_EINVAL          # R > 8 not a multiple of 8
@@ -161,14 +170,15 @@ def test_relay_validation(lib):
     neg = _lib.RelayHandleC(16, 16, 16, 16, 16, 16, 16, -1)
     assert d(p, h, ctypes.byref(neg)) == _lib.MIEP_EINVAL
 
-    def c(relay, y=16, w=None, rdma_y=16, rdma_w=None, out=16, cw=None):
-        return lib.miep_relay_combine(ctypes.byref(p), y, w, None, None, ctypes.byref(h), relay, rdma_y, rdma_w,
+    def c(relay, y=16, w=None, rdma_y=16, rdma_w=None, out=16, cw=None, f32=0):
+        return lib.miep_relay_combine(ctypes.byref(p), y, w, None, None, ctypes.byref(h), relay, f32, rdma_y, rdma_w,
                                       out, cw, None)
 
     assert c(ctypes.byref(rh), y=None) == _lib.MIEP_EINVAL
     assert c(ctypes.byref(rh), rdma_y=None) == _lib.MIEP_EINVAL
     assert c(ctypes.byref(rh), w=16) == _lib.MIEP_EINVAL                               # weights without rdma_w
     assert c(ctypes.byref(rh), y=8) == _lib.MIEP_EUNSUPPORTED
+    assert c(ctypes.byref(rh), rdma_y=8, f32=1) == _lib.MIEP_EUNSUPPORTED              # misaligned fp32 partials
 
 
 def test_ll_validation(lib):

@@ -215,7 +215,8 @@ def test_cached_dispatch_normal():
 
 def test_capacity_guard_and_worst_case_mode():
     """Worst-case capacity: the true total is reported, rows past the
-    capacity are never written (guard rows stay intact)."""
+    capacity are never written (guard rows stay intact), and the device
+    status word reads MIEP_ECAPACITY exactly when the capacity is too small."""
     w = _small_workload("cap", 2, 300, 512, 32, 4, 4, 6, 1)
     say("capacity guard", w)
     x, idx, wts = _inputs(w, 4)
@@ -230,16 +231,40 @@ def test_capacity_guard_and_worst_case_mode():
         recv_x = torch.full((cap + guard, w.H), 7.0, dtype=torch.bfloat16, device=DEV)
         rti = torch.full((cap + guard, w.K), 123, dtype=torch.int64, device=DEV)
         rtw = torch.full((cap + guard, w.K), 5.0, dtype=torch.float32, device=DEV)
-        miep.dispatch_into(xd, idxd, wd, ntpr, ntpe, h, recv_x, None, rti, rtw, None)
+        status = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+        miep.dispatch_into(xd, idxd, wd, ntpr, ntpe, h, recv_x, None, rti, rtw, None, status=status)
         torch.cuda.synchronize()
         n = min(cap, total)
         assert int(h.recv_rank_offset[-1]) == total
+        assert int(status) == (miep.MIEP_ECAPACITY if total > cap else 0)
+        if total > cap:
+            with pytest.raises(miep.MiepError) as err:
+                miep.check_status(status)
+            assert err.value.status == miep.MIEP_ECAPACITY
+        else:
+            miep.check_status(status)
         assert np.array_equal(u16(recv_x[:n]), ref["recv_x"][:n])
         assert np.array_equal(npy(rti[:n]), ref["recv_topk_idx"][:n])
         assert bool((recv_x[cap:] == 7.0).all()) and bool((rti[cap:] == 123).all()) and bool((rtw[cap:] == 5).all())
         if cap > total:
             assert bool((recv_x[total:] == 7.0).all())
         assert np.array_equal(npy(h.send_head), ref["send_head"])
+    # the allocating call raises on an overflow (its synchronous check), and not otherwise
+    with pytest.raises(miep.MiepError) as err:
+        miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, num_worst_tokens=total - 1)
+    assert err.value.status == miep.MIEP_ECAPACITY
+    out = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, num_worst_tokens=total)
+    assert int(out[5].recv_rank_offset[-1]) == total
+    # no sources: the status is cleared
+    st = torch.full((1,), 4, dtype=torch.int32, device=DEV)
+    e = torch.empty((0, w.K), dtype=torch.int64, device=DEV)
+    z = _small_workload("cap0", 2, 0, 512, 32, 4, 4, 6, 1)
+    ntpr0, _, ntpe0, itr0 = miep.get_dispatch_layout(e, z.E, z.R, z.S)
+    h0 = miep.Handle.allocate(itr0, z.S, z.K, z.E, z.C, 4)
+    miep.dispatch_into(torch.empty((0, z.H), dtype=torch.bfloat16, device=DEV), e, None, ntpr0, ntpe0, h0,
+                       torch.empty((4, z.H), dtype=torch.bfloat16, device=DEV), status=st)
+    torch.cuda.synchronize()
+    assert int(st) == 0
 
 
 def test_empty_inputs():
@@ -361,12 +386,20 @@ def test_fp8_dispatch_kinds_small(round_scale):
     ref_lay = oracle.layout(idx.numpy(), w.S, w.E, w.R)
     ref = _ref_dispatch(w, xb, idx.numpy(), wts.numpy(), ref_lay, x_kind=oracle.X_BF16_CAST_FP8,
                         round_scale=round_scale)
-    rx, rs, rti, rtw, _, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True,
-                                           round_scale=round_scale)
+    out = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True, round_scale=round_scale,
+                        use_ue8m0=round_scale)
+    rx, rs, rti, rtw, _, h = out[:6]
     torch.cuda.synchronize()
     _check_handle(h, ref)
     assert np.array_equal(u8(rx), ref["recv_x"])
     assert np.array_equal(npy(rs).view(np.uint32), ref["recv_x_scales"].view(np.uint32))
+    if round_scale:
+        # UE8M0 exponent bytes against the oracle's (fresh and cached dispatch)
+        ref_ue = _ref_dispatch(w, xb, idx.numpy(), wts.numpy(), ref_lay, x_kind=oracle.X_BF16_CAST_FP8,
+                               round_scale=True, use_ue8m0=True)["recv_x_scales_ue8m0"]
+        assert np.array_equal(npy(out[6]), ref_ue)
+        _, _, cue = miep.cached_dispatch(xd, h, cast_to_fp8=True, round_scale=True, use_ue8m0=True)
+        assert np.array_equal(npy(cue), ref_ue)
     # pre-quantised codes + scales travel unchanged
     codes, sci, _ = oracle.fp8_quantize(xb, round_scale)
     cd = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(DEV)
@@ -398,10 +431,11 @@ def test_large_two_level_fp8_roundtrip(round_scale):
     lay = miep.get_dispatch_layout(idxd, w.E, w.R, w.S)
     ref_lay = _check_layout(w, idx, lay)
     ntpr, _, ntpe, itr = lay
-    rx, rs, rti, rtw, nrte, h = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True,
-                                              round_scale=round_scale)
+    out = miep.dispatch(xd, idxd, wd, ntpr, itr, ntpe, w.E, w.C, cast_to_fp8=True, round_scale=round_scale,
+                        use_ue8m0=round_scale)
+    rx, rs, rti, rtw, nrte, h = out[:6]
     xb = wl.bf16_bits(x)
-    codes, sci, _ = oracle.fp8_quantize(xb, round_scale, threads=16)
+    codes, sci, ue = oracle.fp8_quantize(xb, round_scale, threads=16)
     ref = oracle.dispatch(codes, idx.numpy(), wts.numpy(), ref_lay["is_token_in_rank"],
                           ref_lay["num_tokens_per_expert"], S=w.S, E=w.E, R=w.R, C=w.C, x_kind=oracle.X_FP8,
                           x_scales=sci)
@@ -413,6 +447,13 @@ def test_large_two_level_fp8_roundtrip(round_scale):
     assert np.array_equal(npy(rti), ref["recv_topk_idx"])
     assert np.array_equal(npy(rtw).view(np.uint32), ref["recv_topk_weights"].view(np.uint32))
     assert np.array_equal(npy(nrte), ref["num_recv_tokens_per_expert"])
+    if round_scale:
+        # exponent bytes: the oracle's per-source bytes, placed by the oracle's own send_head
+        rows = ref["recv_rank_offset"][:-1][None, :] + ref["send_head"]
+        n_of_row = np.empty(ref["num_recv"], np.int64)
+        sel = ref["send_head"] >= 0
+        n_of_row[rows[sel]] = np.nonzero(sel)[0]
+        assert np.array_equal(npy(out[6]), ue[n_of_row])
     # identity experts on the oracle's dequantised receive rows, bf16 combine
     ref_rx = torch.from_numpy(ref["recv_x"]).view(torch.float8_e4m3fn)
     ref_rs = torch.from_numpy(ref["recv_x_scales"])
