@@ -32,7 +32,8 @@ from ._lib import MIEP_ECAPACITY, MiepError, X_BF16, X_BF16_CAST_FP8, X_FP8  # n
 
 __all__ = ["Handle", "MiepError", "get_dispatch_layout", "get_dispatch_layout_into", "dispatch", "dispatch_into", "cached_dispatch",
            "cached_dispatch_into", "combine", "combine_into", "low_latency_dispatch", "low_latency_dispatch_into",
-           "low_latency_combine", "low_latency_combine_into", "update_mask_buffer", "clean_mask_buffer",
+           "low_latency_dispatch_noalloc", "low_latency_combine", "low_latency_combine_into", "update_mask_buffer",
+           "clean_mask_buffer",
            "RelayHandle", "relay_dispatch", "relay_dispatch_into", "relay_cached_dispatch",
            "relay_cached_dispatch_into", "relay_combine", "relay_combine_into",
            "query_mask_buffer", "check_status", "ll_msg_bytes", "version", "MIEP_ECAPACITY"]
@@ -444,6 +445,40 @@ def low_latency_dispatch_into(x, topk_idx, num_ranks: int, max_tokens: int, num_
          int(use_ue8m0), a.p(msg_buf), a.p(msg_count), a.p(packed_recv_x), a.p(packed_recv_x_scales),
          a.p(packed_recv_x_scales_ue8m0), a.p(packed_recv_src_info), a.p(packed_recv_layout_range),
          a.p(packed_recv_count), a.p(cumulative_local_expert_recv_stats), a.p(mask_buffer))
+
+
+def low_latency_dispatch_noalloc(x, topk_idx, num_ranks: int, max_tokens: int, num_experts: int, dest_rank: int,
+                                 use_fp8: bool, round_scale: bool, use_ue8m0: bool, packed_recv_x,
+                                 packed_recv_x_scales, packed_recv_x_scales_ue8m0, packed_recv_src_info,
+                                 packed_recv_layout_range, packed_recv_count, cumulative_local_expert_recv_stats=None,
+                                 mask_buffer=None) -> None:
+    """low_latency_dispatch_into without the message buffer and counts, for callers that cannot allocate:
+    the library keeps the counts in a device array of its own (at most 65536 = num_experts, shared by every
+    call on the device, so calls on concurrent streams race).  Fills the same packed receive side."""
+    N, H = x.shape
+    R, M, L, K = num_ranks, max_tokens, num_experts // num_ranks, topk_idx.shape[1]
+    if N % R:
+        raise ValueError("x rows must split evenly over the source ranks")
+    _want(x, "x", torch.bfloat16)
+    _want(topk_idx, "topk_idx", torch.int64, (N, K))
+    if use_fp8:
+        if packed_recv_x.dtype not in (torch.float8_e4m3fn, torch.uint8) or tuple(packed_recv_x.shape) != (L, R * M, H):
+            raise ValueError("packed_recv_x must be [%d, %d, %d] E4M3 codes" % (L, R * M, H))
+        _want(packed_recv_x_scales, "packed_recv_x_scales", torch.float32, (L, R * M, H // 128))
+        _want(packed_recv_x_scales_ue8m0, "packed_recv_x_scales_ue8m0", torch.uint8, (L, R * M, H // 128))
+    else:
+        _want(packed_recv_x, "packed_recv_x", torch.bfloat16, (L, R * M, H))
+    _want(packed_recv_src_info, "packed_recv_src_info", torch.int32, (L, R * M))
+    _want(packed_recv_layout_range, "packed_recv_layout_range", torch.int64, (L, R))
+    _want(packed_recv_count, "packed_recv_count", torch.int32, (L,))
+    _want(cumulative_local_expert_recv_stats, "cumulative_local_expert_recv_stats", torch.int32, (L,))
+    _want(mask_buffer, "mask_buffer", torch.int32, (R,))
+    q = _lib.LLProblem(num_ranks, N // num_ranks, max_tokens, H, K, num_experts, dest_rank)
+    a = _Args()
+    _run(a, "miep_ll_dispatch_noalloc", ctypes.byref(q), a.p(x), a.p(topk_idx), int(use_fp8), int(round_scale),
+         int(use_ue8m0), a.p(packed_recv_x), a.p(packed_recv_x_scales), a.p(packed_recv_x_scales_ue8m0),
+         a.p(packed_recv_src_info), a.p(packed_recv_layout_range), a.p(packed_recv_count),
+         a.p(cumulative_local_expert_recv_stats), a.p(mask_buffer))
 
 
 def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispatch_tokens_per_rank: int,

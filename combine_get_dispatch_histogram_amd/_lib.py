@@ -17,7 +17,7 @@ X_BF16, X_FP8, X_BF16_CAST_FP8 = 0, 1, 2
 # Every symbol the header declares (checked by the CPU ABI test).
 EXPORTS = ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_check_status", "miep_combine",
            "miep_relay_dispatch", "miep_relay_cached_dispatch", "miep_relay_combine", "miep_ll_dispatch",
-           "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query", "miep_ll_msg_bytes",
+           "miep_ll_dispatch_noalloc", "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query", "miep_ll_msg_bytes",
            "miep_last_error", "miep_version")
 
 
@@ -80,13 +80,15 @@ def load() -> ctypes.CDLL:
                                            ctypes.POINTER(RelayHandleC), _I32, _P, _P, _P, _P, _P]
         lib.miep_ll_dispatch.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P]
+        lib.miep_ll_dispatch_noalloc.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _I32, _I32, _I32] + [_P] * 9
         lib.miep_ll_combine.argtypes = [ctypes.POINTER(LLProblem), _P, _P, _P, _P, _P, _P, _P]
         lib.miep_mask_update.argtypes = [_P, _I32, _I32, _I32, _P]
         lib.miep_mask_clean.argtypes = [_P, _I32, _P]
         lib.miep_mask_query.argtypes = [_P, _I32, _P, _P]
         for f in ("miep_get_dispatch_layout", "miep_dispatch", "miep_cached_dispatch", "miep_check_status", "miep_combine",
                   "miep_relay_dispatch", "miep_relay_cached_dispatch", "miep_relay_combine",
-                  "miep_ll_dispatch", "miep_ll_combine", "miep_mask_update", "miep_mask_clean", "miep_mask_query"):
+                  "miep_ll_dispatch", "miep_ll_dispatch_noalloc", "miep_ll_combine", "miep_mask_update",
+                  "miep_mask_clean", "miep_mask_query"):
             getattr(lib, f).restype = ctypes.c_int
         lib.miep_ll_msg_bytes.argtypes = [_I32, _I32]
         lib.miep_ll_msg_bytes.restype = ctypes.c_int64

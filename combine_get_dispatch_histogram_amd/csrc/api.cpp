@@ -642,6 +642,30 @@ miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const 
   return hip_status(miep::launch_ll(a, static_cast<hipStream_t>(stream)), "low-latency launch");
 }
 
+miep_status miep_ll_dispatch_noalloc(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx,
+                                     int32_t use_fp8, int32_t round_scale, int32_t use_ue8m0, void* packed_recv_x,
+                                     float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
+                                     int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
+                                     int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats,
+                                     const int32_t* mask_buffer, void* stream) {
+  miep::LLArgs a;
+  miep_status st = ll_dispatch_args(q, x, topk_idx, use_fp8, round_scale, use_ue8m0, nullptr, nullptr,
+                                    packed_recv_x, packed_recv_x_scales, packed_recv_x_scales_ue8m0,
+                                    packed_recv_src_info, packed_recv_layout_range, packed_recv_count,
+                                    cumulative_local_expert_recv_stats, mask_buffer, false, &a);
+  if (st != MIEP_OK) return st;
+  if (static_cast<int64_t>(a.L) * a.R > miep::kLLScratchCounts)
+    return fail(MIEP_EUNSUPPORTED, "the allocation-free low-latency dispatch holds at most %d (local expert, source) "
+                "counts; this problem needs %lld (num_experts)", miep::kLLScratchCounts,
+                static_cast<long long>(a.L) * a.R);
+  int32_t* counts = nullptr;
+  hipError_t e = miep::ll_scratch_counts(&counts);
+  if (e != hipSuccess) return hip_status(e, "scratch address");
+  a.msg = nullptr;
+  a.msg_count = counts;
+  return hip_status(miep::launch_ll(a, static_cast<hipStream_t>(stream)), "low-latency launch");
+}
+
 miep_status miep_ll_combine(const miep_ll_problem* q, const uint16_t* y, const int32_t* packed_recv_src_info,
                             const int64_t* packed_recv_layout_range, const int64_t* topk_idx,
                             const float* topk_weights, uint16_t* combined_x, void* stream) {

@@ -148,7 +148,7 @@ struct LLArgs {
   int64_t msg_bytes;
   const uint16_t* x;
   const int64_t* topk_idx;
-  uint8_t* msg;
+  uint8_t* msg;              // [L][R][M] messages, or null: not materialised
   int32_t* msg_count;        // [L][R]
   void* prx;                 // [L][R*M][H] codes or bf16
   float* prs;                // [L][R*M][H/128]
@@ -160,6 +160,12 @@ struct LLArgs {
   const int32_t* mask;       // [R] nonzero = masked rank, or null
 };
 hipError_t launch_ll(const LLArgs& a, hipStream_t st);
+// The allocation-free variant's count buffer: a file-scope device array of
+// kLLScratchCounts int32 (one copy per device); its device address for the
+// current device, looked up once per device.
+constexpr int kLLScratchCounts = 65536;
+constexpr int kMaxDevices = 64;
+hipError_t ll_scratch_counts(int32_t** out);
 
 // ---- low-latency combine: rank d's expert outputs back to source-token order
 struct LLCombineArgs {

@@ -23,10 +23,39 @@
 //          block's packed range from the counts of the earlier sources, and
 //          cast and write each message and its packed row in one pass
 //          (16-byte loads and stores), so nothing is read back.
+#include <mutex>
+
 #include "device.h"
 #include "kernels.h"
 
 namespace miep {
+
+// Scratch of the allocation-free low-latency dispatch: the per-(local
+// expert, source) message counts that the count kernel hands to the send
+// kernel, for callers that pass no message buffer.  One copy per device,
+// held until the process ends; every call on a device overwrites all L*R
+// counts it uses before reading them, so nothing needs clearing.
+static __device__ __align__(256) int32_t scratch[kLLScratchCounts];
+
+hipError_t ll_scratch_counts(int32_t** out) {
+  // the array's name is a host-side stand-in: its device address comes from
+  // the runtime, once per device, with that device current
+  static std::mutex mu;
+  static int32_t* ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 constexpr int kLLThreads = 256;
 constexpr int kLLSplit = 8;  // default workgroups sharing one (l, s) block's messages
@@ -99,7 +128,8 @@ __global__ __launch_bounds__(kLLThreads) void ll_count_kernel(LLArgs a) {
 // earlier sources, and serves every kLLSplit-th (message, slice) task: the
 // slice is loaded once (16-byte loads), cast, and written both to the
 // message (the transport buffer) and to the packed row, so the receive side
-// never reads the messages back.
+// never reads the messages back.  Without a message buffer (a.msg null)
+// only the packed rows are written.
 template <int VPL, int NT>
 __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
@@ -139,15 +169,16 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   const int G = a.H / kFp8Group;
   const int64_t pb = a.use_fp8 ? a.H : 2 * static_cast<int64_t>(a.H);   // packed row bytes
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x) + static_cast<int64_t>(s) * a.T * 2 * a.H;
+  const bool keep = a.msg != nullptr;                       // messages materialised
   for (int task = blockIdx.y * (kLLThreads / kWave) + w; task < n * nsl; task += gridDim.y * (kLLThreads / kWave)) {
     const int j = task / nsl;
     const int u0 = (task - j * nsl) * span;
     const int t = slot_tok[j];
-    uint8_t* msg = a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes;
+    uint8_t* msg = keep ? a.msg + ((static_cast<int64_t>(l) * a.R + s) * a.M + j) * a.msg_bytes : nullptr;
     const int64_t row = static_cast<int64_t>(l) * a.R * a.M + begin + j;
     uint8_t* prow = static_cast<uint8_t*>(a.prx) + row * pb;
     if (u0 == 0 && lane == 0) {
-      *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
+      if (keep) *reinterpret_cast<int4*>(msg) = make_int4(t, 0, 0, 0);
       a.src_info[row] = t;
     }
     const uint8_t* xrow = xsrc + static_cast<int64_t>(t) * 2 * a.H;
@@ -161,7 +192,7 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
           d[i][1] = ldb16<load_cpol(NT)>(xrow, static_cast<uint32_t>(p) * 32 + 16);
         }
       }
-      float* scales = reinterpret_cast<float*>(msg + 16 + a.H);
+      float* scales = keep ? reinterpret_cast<float*>(msg + 16 + a.H) : nullptr;
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int p = u0 + i * kWave + lane;
@@ -170,10 +201,10 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
         const float sc = fp8_scales(amax, a.round_scale != 0, &sci);
         if (p < units) {
           const v4u q = cast16(d[i][0], d[i][1], sc);
-          stb16<store_cpol(NT)>(msg, 16 + static_cast<uint32_t>(p) * 16, q);
+          if (keep) stb16<store_cpol(NT)>(msg, 16 + static_cast<uint32_t>(p) * 16, q);
           stb16<store_cpol(NT)>(prow, static_cast<uint32_t>(p) * 16, q);
           if ((lane & 7) == 0) {
-            scales[p / 8] = sci;
+            if (keep) scales[p / 8] = sci;
             a.prs[row * G + p / 8] = sci;
             if (a.prue) a.prue[row * G + p / 8] = static_cast<uint8_t>((__float_as_uint(sci) >> 23) & 0xFFu);
           }
@@ -190,7 +221,7 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
       for (int i = 0; i < VPL; ++i) {
         const int v = u0 + i * kWave + lane;
         if (v < nv) {
-          stb16<store_cpol(NT)>(msg, 16 + static_cast<uint32_t>(v) * 16, d[i]);
+          if (keep) stb16<store_cpol(NT)>(msg, 16 + static_cast<uint32_t>(v) * 16, d[i]);
           stb16<store_cpol(NT)>(prow, static_cast<uint32_t>(v) * 16, d[i]);
         }
       }

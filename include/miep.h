@@ -316,6 +316,27 @@ miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const 
                              int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats,
                              const int32_t* mask_buffer, void* stream);
 
+/* low_latency_dispatch_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): miep_ll_dispatch without the message buffer and counts.
+ * Same arguments and the same receive side (packed_recv_*, cumulative stats,
+ * rank mask) as miep_ll_dispatch; the messages, which only stand in for the
+ * transport, are not materialised, and the per-(local expert, source)
+ * message counts that its two kernels share live in a device array of the
+ * library (65536 int32 per device, held until the process ends).
+ * It allocates nothing (no hipMalloc, no hipFree, no allocating library call).
+ * Every call on one device shares that array: calls that overlap on one
+ * device (concurrent streams) race and must be ordered by the caller; each
+ * call overwrites every count it reads, so nothing needs clearing.
+ * Errors: as miep_ll_dispatch; EUNSUPPORTED when num_experts (L * R counts)
+ * exceeds 65536; EHIP if the device address of the array cannot be found. */
+miep_status miep_ll_dispatch_noalloc(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx,
+                                     int32_t use_fp8, int32_t round_scale, int32_t use_ue8m0, void* packed_recv_x,
+                                     float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,
+                                     int32_t* packed_recv_src_info, int64_t* packed_recv_layout_range,
+                                     int32_t* packed_recv_count, int32_t* cumulative_local_expert_recv_stats,
+                                     const int32_t* mask_buffer, void* stream);
+
 /* low_latency_combine -- [Ch4] 4.3 and [NvLL] name it beside the
  * low-latency dispatch without its arithmetic.  Here it is the reverse of
  * miep_ll_dispatch seen from rank d: each source token (s, t) gets back the

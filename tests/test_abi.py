@@ -212,6 +212,29 @@ def test_ll_validation(lib):
     assert lib.miep_ll_combine(ctypes.byref(q()), *bad) == _lib.MIEP_EUNSUPPORTED
 
 
+def test_ll_noalloc_validation(lib):
+    """The allocation-free low-latency dispatch checks its sizes before touching the device: more experts
+    than its count array holds (65536) is EUNSUPPORTED, and the usual argument errors are reported."""
+    def q(**kw):
+        d = dict(num_ranks=32, num_tokens=128, max_tokens=128, hidden=7168, num_topk=8, num_experts=256, dest_rank=0)
+        d.update(kw)
+        return _lib.LLProblem(**d)
+
+    # x, topk_idx, use_fp8, round_scale, use_ue8m0, packed_recv_x, scales, ue8m0, src_info, layout_range, count,
+    # cumulative stats, mask, stream
+    args = [16, 16, 0, 0, 0, 16, None, None, 16, 16, 16, None, None, None]
+    assert lib.miep_ll_dispatch_noalloc(ctypes.byref(q(num_ranks=2, num_tokens=4, max_tokens=8,
+                                                       num_experts=2 * 65536)), *args) == _lib.MIEP_EUNSUPPORTED
+    assert "65536" in lib.miep_last_error().decode()
+    assert lib.miep_ll_dispatch_noalloc(ctypes.byref(q(num_tokens=129)), *args) == _lib.MIEP_EINVAL
+    bad = list(args)
+    bad[5] = None                              # packed_recv_x NULL
+    assert lib.miep_ll_dispatch_noalloc(ctypes.byref(q()), *bad) == _lib.MIEP_EINVAL
+    bad = list(args)
+    bad[2] = 1                                 # FP8 without scales
+    assert lib.miep_ll_dispatch_noalloc(ctypes.byref(q()), *bad) == _lib.MIEP_EINVAL
+
+
 def test_mask_validation(lib):
     assert lib.miep_mask_update(None, 8, 0, 1, None) == _lib.MIEP_EINVAL
     assert lib.miep_mask_update(16, 8, 8, 1, None) == _lib.MIEP_EINVAL
