@@ -266,23 +266,45 @@ def run_normal(torch, miep, wl, steps, warmup):
     torch.cuda.synchronize()
     graph_wall = time.perf_counter() - t0
     del graph
-    # (5) cold cache: 1 GiB written before each timed call (outside its events)
-    # evicts L2 and the 256 MB last-level cache
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cold = {}
-    for name, fn in (("dispatch", lambda: miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, None, rti, rtw, nrte)),
-                     ("combine", lambda: miep.combine_into(y, h, cx, rtw, cw))):
-        t = Timer(torch, it)
-        for _ in range(it):
-            flush.fill_(1)
-            with t:
-                fn()
-        torch.cuda.synchronize()
-        cold[name] = t.ms()
-    del flush
+    # (5) cold caches
+    cold = measure_cold(torch, dev, {
+        "dispatch": lambda: miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, None, rti, rtw, nrte),
+        "combine": lambda: miep.combine_into(y, h, cx, rtw, cw)}, max(20, steps))
     return dict(w=w, rows=rows, wall=wall, layout_ms=tl.ms(), dispatch_ms=td.ms(), combine_ms=tc.ms(),
                 cached_ms=tcd.ms(), combine_launch_ms=combine_launch_ms, pack_launch_ms=pack_launch_ms,
-                cold_dispatch_ms=cold["dispatch"], cold_combine_ms=cold["combine"], graph_wall=graph_wall)
+                cold=cold, graph_wall=graph_wall)
+
+
+FLUSH_BYTES = 1 << 30
+
+
+def measure_cold(torch, dev, calls, iters):
+    """Each call (and the calls back to back, "pair") timed with cold caches:
+    before every timed run, 1 GiB is written and a second 1 GiB is read,
+    then the device synchronises.  The write evicts L2 and the 256 MB
+    last-level cache; the read sweep then replaces the flush's dirty lines by
+    clean ones, so that no write-back of the flush lands in the timed run and
+    every byte of the call comes from HBM.  A short GPU spin ahead of the
+    start event lets the host queue the call first (no launch cost in the
+    interval).  Returns {name: [ms per run]}."""
+    fw = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    fr = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+    names = list(calls) + ["pair"]
+    out = {k: Timer(torch, iters, LEAD_CYCLES) for k in names}
+    for _ in range(iters):
+        for k in names:
+            fw.fill_(1)
+            fr.max()
+            torch.cuda.synchronize()
+            with out[k]:
+                if k == "pair":
+                    for f in calls.values():
+                        f()
+                else:
+                    calls[k]()
+            torch.cuda.synchronize()
+    del fw, fr
+    return {k: t.ms() for k, t in out.items()}
 
 
 def run_ll(torch, miep, wl, iters):
@@ -415,6 +437,26 @@ def run_relay(torch, miep, wl, iters):
                 relay_combine_gbs=round(bc / (t["relay_combine"] / 1e3) / 1e9, 1))
 
 
+def cold_summary(cold, N, nbytes):
+    """Per cold-timed call: p10/p50/p90 in us, and at the median tokens/s,
+    GB/s of algorithmic bytes and the fraction of the HBM peak; plus the sum
+    of the separately timed dispatch and combine medians."""
+    out = {}
+    for k, ms in cold.items():
+        m = med(ms)
+        gbs = nbytes[k] / (m / 1e3) / 1e9
+        out[k] = {"us_p10_p50_p90": [round(pct(ms, q) * 1e3, 2) for q in (0.1, 0.5, 0.9)],
+                  "tokens_per_s": round(N / (m / 1e3), 1), "gbs": round(gbs, 1),
+                  "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    t = med(cold["dispatch"]) + med(cold["combine"])
+    gbs = (nbytes["dispatch"] + nbytes["combine"]) / (t / 1e3) / 1e9
+    out["dispatch_plus_combine"] = {"us": round(t * 1e3, 2), "tokens_per_s": round(N / (t / 1e3), 1),
+                                    "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    out["protocol"] = ("before every run: 1 GiB written, a second 1 GiB read, device synchronised; "
+                       "%d runs per call; pair = dispatch and combine back to back in one timed run" % len(cold["pair"]))
+    return out
+
+
 # --------------------------------------------------------------------------- CPU oracle leg
 def _oracle_pass(oracle, w, x, idx, wts, y):
     """One pass of the oracle over the normal workload: layout, dispatch, combine."""
@@ -425,38 +467,73 @@ def _oracle_pass(oracle, w, x, idx, wts, y):
     return d
 
 
-# A worker of the all-cores oracle timing: loads the saved inputs, then runs
-# _oracle_pass until its budget is spent and prints
-# how many passes it finished and how long they took.  Started as a plain
-# child process; it imports neither torch nor the HIP library.
-_CPU_WORKER = r"""
-import json, os, sys, time, types
-import numpy as np
-sys.path.insert(0, sys.argv[1])
-import bench
-import oracle
-d, start, budget = sys.argv[2], float(sys.argv[3]), float(sys.argv[4])
-w = types.SimpleNamespace(**dict(zip("SERC", (int(v) for v in sys.argv[5:9]))))
-a = {k: np.load(os.path.join(d, k + ".npy"), mmap_mode="r") for k in ("x", "idx", "wts", "y")}
-while time.time() < start:
-    time.sleep(0.001)
-runs, t0 = 0, time.perf_counter()
-while runs < 1 or time.perf_counter() - t0 < budget:
-    bench._oracle_pass(oracle, w, a["x"], a["idx"], a["wts"], a["y"])
-    runs += 1
-print(json.dumps({"runs": runs, "seconds": time.perf_counter() - t0}), flush=True)
-"""
-
-
-def cpu_baseline(wl, budget_s, procs=None):
-    """The oracle timed on the host: single-threaded first, then one independent
-    oracle process per host core (capped at 16) on the same inputs at the same
-    time; the reported value is the all-cores aggregate."""
-    import shutil
-    import subprocess
-    import tempfile
-
+def _oracle_parallel_pass(oracle, w, x, idx, wts, y, pool):
+    """One pass of the same oracle over the normal workload, split over the
+    host cores: every piece is a call of the unchanged oracle functions on an
+    independent part of the problem.
+      layout:   one call per source partition (the counts of a source depend
+                on its own tokens only);
+      dispatch: one call per destination rank r, as a one-rank problem: the
+                column r of is_token_in_rank, the top-k entries of r's experts
+                renumbered to 0..L-1 (all others masked) and r's per-expert
+                counts; its rows are exactly rank r's receive block;
+      combine:  one call per chunk of source tokens (a token's sum reads only
+                its own send_head row and the receive offsets).
+    Returns the pieces the single pass returns, for the equality check."""
     import numpy as np
+    S, E, R, C = w.S, w.E, w.R, w.C
+    N, K = idx.shape
+    T = N // S
+    L = E // R
+    lay = list(pool.map(lambda s: oracle.layout(idx[s * T:(s + 1) * T], 1, E, R), range(S)))
+    in_rank = np.concatenate([d["is_token_in_rank"] for d in lay])
+    ntpr = np.concatenate([d["num_tokens_per_rank"] for d in lay])
+    ntpe = np.concatenate([d["num_tokens_per_expert"] for d in lay])
+
+    def one_rank(r):
+        lo = r * L
+        mine = (idx >= lo) & (idx < lo + L)
+        idx_r = np.where(mine, idx - lo, -1)
+        return oracle.dispatch(x, idx_r, wts, np.ascontiguousarray(in_rank[:, r:r + 1]),
+                               np.ascontiguousarray(ntpe[:, lo:lo + L]), S=S, E=L, R=1, C=C)
+
+    parts = list(pool.map(one_rank, range(R)))
+    off = np.zeros(R + 1, np.int32)
+    off[1:] = np.cumsum([p["num_recv"] for p in parts])
+    send_head = np.concatenate([p["send_head"] for p in parts], axis=1)
+    recv_w = np.concatenate([p["recv_topk_weights"] for p in parts])
+    nchunk = max(1, pool._max_workers)
+    cuts = [N * i // nchunk for i in range(nchunk + 1)]
+
+    def one_chunk(i):
+        a, b = cuts[i], cuts[i + 1]
+        return oracle.combine(y, recv_w, send_head[a:b], off, S=1) if b > a else None
+
+    comb = list(pool.map(one_chunk, range(nchunk)))
+    return dict(num_tokens_per_rank=ntpr, num_tokens_per_expert=ntpe, is_token_in_rank=in_rank, send_head=send_head,
+                recv_rank_offset=off, recv_x=np.concatenate([p["recv_x"] for p in parts]),
+                recv_topk_idx=np.concatenate([p["recv_topk_idx"] for p in parts]), recv_topk_weights=recv_w,
+                combined_x=np.concatenate([c["combined_x"] for c in comb if c is not None]),
+                combined_topk_weights=np.concatenate([c["combined_topk_weights"] for c in comb if c is not None]))
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, budget_s, threads=None):
+    """The oracle timed on the host, on the full normal workload: one
+    single-threaded pass repeated for about half the budget, then the same
+    pass split over the host cores (threads; capped at 16, the host share of
+    one GPU) for the other half.  The reported value is the all-cores pass."""
+    from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     w = wl.NORMAL
@@ -476,33 +553,22 @@ def cpu_baseline(wl, budget_s, procs=None):
         runs += 1
     single = w.N * runs / t_total
     ncpu = os.cpu_count() or 1
-    procs = procs or max(1, min(ncpu, 16))
-    tmp = tempfile.mkdtemp(prefix="miep_cpu_")
-    try:
-        for k, v in (("x", x), ("idx", idx), ("wts", wts), ("y", y)):
-            np.save(os.path.join(tmp, k + ".npy"), np.ascontiguousarray(v))
-        root = os.path.dirname(os.path.abspath(__file__))
-        start = time.time() + 3.0                    # every worker has loaded its inputs by then
-        env = dict(os.environ, OMP_NUM_THREADS="1")
-        argv = [sys.executable, "-c", _CPU_WORKER, root, tmp, repr(start), repr(budget_s / 2)] + \
-            [str(v) for v in (w.S, w.E, w.R, w.C)]
-        ps = [subprocess.Popen(argv, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env)
-              for _ in range(procs)]
-        outs = [p.communicate(timeout=120 + 4 * budget_s) for p in ps]
-    finally:
-        shutil.rmtree(tmp, ignore_errors=True)
-    rates = []
-    for p, (out, err) in zip(ps, outs):
-        if p.returncode != 0:
-            raise RuntimeError("oracle worker failed: %s" % err[-2000:])
-        r = json.loads(out.strip().splitlines()[-1])
-        rates.append(w.N * r["runs"] / r["seconds"])
-    return dict(value=round(sum(rates), 1), unit="tokens/s", cores=procs, kind="oracle",
-                single_thread_value=round(single, 1),
-                sample="the full normal workload (4096 tokens, layout + dispatch + combine) through the plain C "
-                       "oracle (gcc -O2, single-threaded code): %d independent processes, one per core, each "
-                       "repeating it for ~%.0f s at the same time (value = sum of their rates); single-threaded "
-                       "alone: %d run(s) in %.1f s; host has %d cores" % (procs, budget_s / 2, runs, t_total, ncpu))
+    threads = threads or max(1, min(ncpu, 16))
+    with ThreadPoolExecutor(threads) as pool:
+        _oracle_parallel_pass(oracle, w, x, idx, wts, y, pool)      # thread start-up outside the timing
+        pruns, p_total = 0, 0.0
+        while pruns < 1 or (p_total < budget_s / 2 and pruns < 100):
+            t0 = time.perf_counter()
+            _oracle_parallel_pass(oracle, w, x, idx, wts, y, pool)
+            p_total += time.perf_counter() - t0
+            pruns += 1
+    return dict(value=round(w.N * pruns / p_total, 1), unit="tokens/s", cores=threads, kind="oracle",
+                single_thread_value=round(single, 1), cpu_count=ncpu, cpu_model=_cpu_model(),
+                sample="the full normal workload (4096 tokens: layout + dispatch + combine) through the plain C "
+                       "oracle (gcc -O2): one pass split over %d threads (layout per source, dispatch per "
+                       "destination rank, combine per token chunk; ctypes releases the GIL), %d pass(es) in "
+                       "%.1f s; single-threaded: %d pass(es) in %.1f s; the host reports %d cores"
+                       % (threads, pruns, p_total, runs, t_total, ncpu))
 
 
 # --------------------------------------------------------------------------- profile summaries
@@ -720,8 +786,7 @@ def main():
         "stages_p10_p50_p90_us": {k: [round(pct(r[k + "_ms"], q) * 1e3, 2) for q in (0.1, 0.5, 0.9)]
                                   for k in ("layout", "dispatch", "combine")},
         "graph_replay_ms_per_step": round(r["graph_wall"] * 1e3 / args.steps, 4),
-        "cold_cache_us": {"dispatch": round(med(r["cold_dispatch_ms"]) * 1e3, 2),
-                          "combine": round(med(r["cold_combine_ms"]) * 1e3, 2)},
+        "cold": cold_summary(r["cold"], N, {"dispatch": b_dis, "combine": b_com, "pair": b_dis + b_com}),
         "stages_us": {"layout": round(lay_ms * 1e3, 2), "dispatch": round(dis_ms * 1e3, 2),
                       "combine": round(com_ms * 1e3, 2), "cached_dispatch": round(cd_ms * 1e3, 2)},
         "stages_gbs": {"layout": round(b_lay / (lay_ms / 1e3) / 1e9, 1),
