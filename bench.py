@@ -573,12 +573,14 @@ def cpu_baseline(wl, budget_s, threads=None):
 
 # --------------------------------------------------------------------------- profile summaries
 KERNEL_SRC = {"combine": ("combine.hip", "device.h"), "pack": ("pack.hip", "device.h"),
-              "notify": ("notify.hip", "device.h"), "layout": ("layout.hip", "device.h")}
+              "pack_cast": ("pack.hip", "device.h"), "notify": ("notify.hip", "device.h"),
+              "layout": ("layout.hip", "device.h"), "ll_send": ("ll.hip", "device.h"),
+              "ll_count": ("ll.hip", "device.h"), "ll_combine": ("ll.hip", "device.h")}
 
 
 def _kernel_key(name):
-    for k in ("ll_combine_kernel", "combine_kernel", "pack_kernel", "notify_kernel", "layout_kernel", "ll_send_kernel",
-              "ll_count_kernel", "relay_meta_kernel"):
+    for k in ("ll_combine_kernel", "combine_kernel", "pack_cast_kernel", "pack_kernel", "notify_kernel",
+              "layout_kernel", "ll_send_kernel", "ll_count_kernel", "relay_meta_kernel"):
         if "miep::" + k in name:
             return k.replace("_kernel", "")
     return None
@@ -627,7 +629,7 @@ def summarize_counters(dirs, out_md, commands, title):
         f.write("\n".join(lines) + "\n")
 
 
-def summarize_pmc(fetch_dir, write_dir, out_json, out_md, commands, copy_mib):
+def summarize_pmc(fetch_dir, write_dir, out_json, out_md, commands, copy_mib, title="normal workload"):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each miep kernel, scaled by
     what the same counters read for the runtime's plain copy kernel of known size."""
     import csv
@@ -655,7 +657,7 @@ def summarize_pmc(fetch_dir, write_dir, out_json, out_md, commands, copy_mib):
     sf, sw = copy_f / true_kib, copy_w / true_kib
     out = {"copy_probe_mib": copy_mib, "fetch_scale": round(sf, 5), "write_scale": round(sw, 5),
            "commands": commands, "kernels": {}}
-    lines = ["# HBM traffic per launch: normal workload (rocprofv3 --pmc)", "",
+    lines = ["# HBM traffic per launch: %s (rocprofv3 --pmc)" % title, "",
              "Counters are KiB per dispatch.  Scale factors come from the runtime's plain copy kernel "
              "(`__amd_rocclr_copyBuffer`) of %d MiB run in the same process: FETCH_SIZE reads %.5f x its true bytes, "
              "WRITE_SIZE %.5f x." % (copy_mib, sf, sw), "", "Commands:", "", "```"] + commands + ["```", "",
@@ -703,6 +705,9 @@ def main():
                     help="run only the low-latency dispatch and combine measurement (for a kernel profile)")
     ap.add_argument("--relay-only", action="store_true",
                     help="run only the two-level relay measurement on the 64-rank workload (for a kernel profile)")
+    ap.add_argument("--workload-only", choices=("skewed", "large"),
+                    help="run only the dispatch / combine / cached-dispatch measurement of one secondary workload "
+                         "(for a kernel or counter profile)")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, os.path.join(PROFILES, args.stats_name + ".md"),
@@ -713,8 +718,10 @@ def main():
                            args.stats_title)
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], os.path.join(PROFILES, "normal_hbm_traffic.json"),
-                      os.path.join(PROFILES, "normal_hbm_traffic.md"), args.command, args.copy_probe_mib or 512)
+        name = args.stats_name if args.stats_name != "normal_step_kernels" else "normal_hbm_traffic"
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], os.path.join(PROFILES, name + ".json"),
+                      os.path.join(PROFILES, name + ".md"), args.command, args.copy_probe_mib or 512,
+                      args.stats_title if args.stats_title != "normal workload step" else "normal workload")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the logical ranks are partitions of one GPU's HBM and nothing here "
@@ -732,7 +739,6 @@ def main():
     if args.relay_only:
         print(json.dumps({"large_fp8_relay": run_relay(torch, miep, wl, 5)}), flush=True)
         return
-
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -741,6 +747,11 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.workload_only:
+        w = wl.SKEWED if args.workload_only == "skewed" else wl.LARGE
+        print(json.dumps({args.workload_only: run_normal_variant(torch, miep, wl, w, args.steps,
+                                                                 args.workload_only == "large")}), flush=True)
+        return
 
     r = run_normal(torch, miep, wl, args.steps, args.warmup)
     w, rows = r["w"], r["rows"]

@@ -199,7 +199,7 @@ const Tuning& tuning() {
                            env_int("MIEP_LL_SPLIT", 0),     env_int("MIEP_LL_VPL", 0),
                            env_int("MIEP_CAST_TPB", -1),    env_int("MIEP_LLC_VPL", 0),
                            env_int("MIEP_LLC_SLICES", 0),   env_int("MIEP_LLC_NT", -1),
-                           env_int("MIEP_LL_NT", -1)};
+                           env_int("MIEP_LL_NT", -1),       env_int("MIEP_PACK_RECORDS", -1)};
   return t;
 }
 }  // namespace miep
@@ -291,6 +291,9 @@ miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, 
   miep::PackArgs a = pack_args(p, x, x_kind, x_scales, round_scale, h, recv_x, recv_x_scales);
   a.recv_ue = use_ue8m0 ? recv_x_scales_ue8m0 : nullptr;
   a.meta = 1;
+  a.S = p->num_src;
+  a.rpm = h->rank_prefix_matrix;
+  a.in_rank = h->is_token_in_rank;
   a.topk_idx = topk_idx;
   a.topk_weights = topk_weights;
   a.recv_topk_idx = topk_idx ? recv_topk_idx : nullptr;

@@ -100,6 +100,13 @@ struct PackArgs {
   int groups, group_w;
   const int32_t* src_tok;    // [N] source token of row n (top-k metadata, recv_src_idx)
   int cpol = -1;             // cache-policy code of this launch (-1: the default)
+  // Receive records of a fresh direct dispatch in their own wavefronts (one
+  // per (source, rank)): needs the rank prefix matrix and the membership.
+  int S = 0;
+  const int32_t* rpm = nullptr;       // [S][R] inclusive rows per rank from sources 0..s
+  const uint8_t* in_rank = nullptr;   // [S*T][R]
+  int rec_waves = 0, rec_blocks = 0;  // set by launch_pack
+  int rec_last = 0;                   // record workgroups at the end of the grid instead of the front
 };
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);
 
@@ -188,7 +195,7 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
 // MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT, MIEP_LL_SPLIT,
 // MIEP_LL_VPL, MIEP_CAST_TPB, MIEP_LLC_VPL, MIEP_LLC_SLICES, MIEP_LLC_NT,
-// MIEP_LL_NT):
+// MIEP_LL_NT, MIEP_PACK_RECORDS):
 // used by geometry sweeps, never required.
 // combine_maxr: source rows whose loads are issued together.
 // pack_nt / combine_nt: cache policy of the row traffic, bit 0 =
@@ -201,13 +208,15 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // either kernel.  The relay's launches take 7 (its group rows are written
 // once and read once more right after).  ll_split: workgroups per
 // low-latency (expert, source) block.  cast_tpb: fused FP8 cast with one
-// token per workgroup (1), 1 KiB slices (0), or chosen per call (-1).
+// token per workgroup (1), or 1 KiB slices (0 or -1, the default).
 // llc_vpl / llc_slices / llc_nt: low-latency combine vectors per lane,
 // slices per token and cache-policy code (as pack_nt); ll_nt: the
-// low-latency send's cache-policy code.
+// low-latency send's cache-policy code.  pack_records: 0 writes a fresh
+// dispatch's receive records from the payload wavefronts instead of the
+// record wavefronts (-1, the default: record wavefronts where supported).
 struct Tuning {
   int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl,
-      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt;
+      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt, pack_records;
 };
 const Tuning& tuning();
 

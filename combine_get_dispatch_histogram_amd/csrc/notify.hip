@@ -28,6 +28,24 @@ namespace miep {
 
 constexpr int kNotifyMaxWaves = 16;
 
+// send_head rows leave in 16-byte stores.  Large send_head arrays (64 ranks:
+// 4 MB for the 16384-token workload) are written with the streaming
+// (non-temporal) policy: left as ordinary dirty lines they slowed the pack
+// that follows by ~9 us (measured: notify then cached pack 193.6 us, 179.4 us
+// with streaming stores, against 183.5 us for the two apart); small ones
+// keep the default policy (8 ranks: streaming cost the next pack ~2 us).
+template <bool NT>
+__device__ __forceinline__ void store_head4(int32_t* base, int64_t idx, int4 v) {
+  if constexpr (NT) {
+    const u32x4 t = {static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y), static_cast<uint32_t>(v.z),
+                     static_cast<uint32_t>(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(t, row_rsrc(base), static_cast<uint32_t>(idx * 4), 0, kCpolNt);
+  } else {
+    *reinterpret_cast<int4*>(base + idx) = v;
+  }
+}
+constexpr int64_t kHeadStreamBytes = 1 << 20;   // send_head arrays above this size stream
+
 // Nonzero bytes of a 32-bit word -> 4 bits (byte j -> bit j): fold each byte
 // onto its low bit, then one multiply moves bits 0, 8, 16, 24 to 28..31 (the
 // other partial products land on distinct lower bits, so nothing carries in).
@@ -107,7 +125,7 @@ __device__ __forceinline__ RankMask<MW> load_member(const NotifyArgs& a, int64_t
 // the rank's count and every in-wavefront prefix by popcount, and send_head
 // leaves one token row at a time with the ranks side by side (contiguous
 // stores); 256 = rows of up to 256 ranks, one ballot per rank.
-template <int MW, bool GROUPED, int RB>
+template <int MW, bool GROUPED, int RB, bool HNT>
 __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   __shared__ int32_t base[kMaxRanks];                 // rows of rank r from sources < s
   __shared__ int32_t total[kMaxRanks];                // rows of rank r from all sources
@@ -334,7 +352,8 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
               v[k] = ((c4[k] >> q) & 1ull) ? p4[k] + __popcll(c4[k] & below) : -1;
-            *reinterpret_cast<int4*>(row0 + static_cast<int64_t>(q) * R + 4 * j) = make_int4(v[0], v[1], v[2], v[3]);
+            store_head4<HNT>(a.send_head, (static_cast<int64_t>(s) * T + tw0 + q) * R + 4 * j,
+                             make_int4(v[0], v[1], v[2], v[3]));
           }
         }
       } else {
@@ -381,7 +400,7 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
         if (valid) {
           int32_t* dst = a.send_head + n * R + r0 + j0;
           if ((R & 3) == 0) {
-            *reinterpret_cast<int4*>(dst) = make_int4(v[0], v[1], v[2], v[3]);
+            store_head4<HNT>(a.send_head, n * R + r0 + j0, make_int4(v[0], v[1], v[2], v[3]));
           } else {
             for (int q = 0; q < 4 && j0 + q < rend; ++q) dst[q] = v[q];
           }
@@ -478,6 +497,21 @@ hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool HNT>
+static hipError_t launch_notify_cfg(const NotifyArgs& a, int threads, size_t lds, hipStream_t st) {
+  if (a.group_w != 0 && a.R <= 8)   // groups: R <= 32 destinations
+    hipLaunchKernelGGL((notify_kernel<1, true, 8, HNT>), dim3(a.S), dim3(threads), lds, st, a);
+  else if (a.group_w != 0)
+    hipLaunchKernelGGL((notify_kernel<1, true, 64, HNT>), dim3(a.S), dim3(threads), lds, st, a);
+  else if (a.R <= 8)
+    hipLaunchKernelGGL((notify_kernel<1, false, 8, HNT>), dim3(a.S), dim3(threads), lds, st, a);
+  else if (a.R <= 64)
+    hipLaunchKernelGGL((notify_kernel<1, false, 64, HNT>), dim3(a.S), dim3(threads), lds, st, a);
+  else
+    hipLaunchKernelGGL((notify_kernel<4, false, 256, HNT>), dim3(a.S), dim3(threads), lds, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
   if (a.S == 0) return hipSuccess;
   int threads = ((a.T + kWave - 1) / kWave) * kWave;
@@ -490,17 +524,11 @@ hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
   // rows: the LDS bit transpose (measured on the 64-rank workload: 64-rank
   // notify 18.0 -> 15.3 us with it, while 8 groups took 7.3 us with ballots
   // against 11.1 us transposed)
-  if (a.group_w != 0 && a.R <= 8)   // groups: R <= 32 destinations
-    hipLaunchKernelGGL((notify_kernel<1, true, 8>), dim3(a.S), dim3(threads), lds, st, a);
-  else if (a.group_w != 0)
-    hipLaunchKernelGGL((notify_kernel<1, true, 64>), dim3(a.S), dim3(threads), lds, st, a);
-  else if (a.R <= 8)
-    hipLaunchKernelGGL((notify_kernel<1, false, 8>), dim3(a.S), dim3(threads), lds, st, a);
-  else if (a.R <= 64)
-    hipLaunchKernelGGL((notify_kernel<1, false, 64>), dim3(a.S), dim3(threads), lds, st, a);
-  else
-    hipLaunchKernelGGL((notify_kernel<4, false, 256>), dim3(a.S), dim3(threads), lds, st, a);
-  return hipGetLastError();
+  // streaming send_head stores (buffer offsets are 32 bits: arrays below 2 GiB)
+  const int64_t head_bytes = static_cast<int64_t>(a.S) * a.T * a.R * 4;
+  const bool hnt = head_bytes > kHeadStreamBytes && head_bytes < (1ll << 31);
+  if (hnt) return launch_notify_cfg<true>(a, threads, lds, st);
+  return launch_notify_cfg<false>(a, threads, lds, st);
 }
 
 }  // namespace miep

@@ -17,6 +17,14 @@
 // fixed by the notify scan.  Row traffic uses buffer instructions on the
 // wave-uniform row base; by default x is read with the ordinary cache policy
 // and the receive rows are written non-temporal at device scope.
+//
+// The small per-row records of a fresh dispatch (source index, the top-k
+// entries the row's rank owns and their weights) are not written by the
+// payload wavefronts, where each would leave as a scattered partial-line
+// piece per (token, destination): extra wavefronts at the front of the same
+// grid, one per (source, rank) pair, walk the source's tokens in order and
+// write the rank's consecutive receive rows with coalesced stores, while
+// the payload wavefronts run.
 #include "device.h"
 #include "kernels.h"
 
@@ -33,10 +41,99 @@ __device__ __forceinline__ int group_rank_base(const int32_t* group_off, int gro
   return (__popcll(ballot(le)) - 1) * group_w;
 }
 
+constexpr int kRecordMaxTokens = 1024;   // tokens per source for the record wavefronts
+constexpr int kRecordChunks = kRecordMaxTokens / kWave;
+constexpr int kRecordBatch = 8;          // store instructions per batch of gathered records
+
+// Records of rank r's rows from source s (wavefront (s, r) = mw): the rows
+// [off[r] + rpm[s-1][r], off[r] + rpm[s][r]) hold source s's tokens that go
+// to r, in token order.  Every membership byte of the column is loaded at
+// once (one load per lane per 64-token chunk, all in flight), ballots list
+// the members' tokens in this wavefront's LDS slot, and the top-k entries
+// and weights are gathered kRecordBatch store instructions at a time (all
+// loads of a batch issued before its stores): lane (j, k) writes entry k of
+// row j, so each store covers 64 / K whole rows.  The chain is one round
+// trip for the membership plus one per batch of 8 * (64 / K) rows.  The
+// records are written with the streaming (non-temporal) policy: their lines
+// are whole, and as ordinary dirty lines they cost the 64-rank FP8 dispatch
+// ~27 us (measured: 216.6 -> 189.6 us).
+__device__ __forceinline__ void pack_records(const PackArgs& a, int mw, int32_t* lst) {
+  const int lane = lane_id();
+  const int R = a.R, T = a.T, K = a.K;
+  const int s = mw / R;
+  const int r = mw - s * R;
+  const int row0 = a.off[r] + (s > 0 ? a.rpm[(s - 1) * R + r] : 0);   // receive row of the first member
+  const uint8_t* col = a.in_rank + static_cast<int64_t>(s) * T * R + r;
+  const int nch = (T + kWave - 1) / kWave;
+  uint8_t mb[kRecordChunks];
+#pragma unroll
+  for (int c = 0; c < kRecordChunks; ++c) {
+    const int t = c * kWave + lane;
+    mb[c] = (c < nch && t < T) ? col[static_cast<int64_t>(t) * R] : 0;
+  }
+  int nm = 0;                                       // members so far (uniform)
+#pragma unroll
+  for (int c = 0; c < kRecordChunks; ++c) {
+    if (c < nch) {
+      const bool member = mb[c] != 0;
+      const uint64_t m = ballot(member);
+      const int pos = nm + __popcll(m & lanemask_lt());
+      const int t = c * kWave + lane;
+      if (member) {
+        lst[pos] = t;
+        if (row0 + pos < a.capacity) __builtin_nontemporal_store(t, a.recv_src_idx + row0 + pos);
+      }
+      nm += __popcll(m);
+    }
+  }
+  if (K == 0 || a.recv_topk_idx == nullptr || nm == 0) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the wavefront reads back its own list
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int rows_per = kWave / K;                   // whole rows per store instruction
+  const int j_l = lane / K;
+  const int k_l = lane - j_l * K;
+  const bool act = j_l < rows_per;
+  const int64_t lo = static_cast<int64_t>(r) * a.L;
+  const bool wts = a.recv_topk_weights != nullptr;
+  for (int j0 = 0; j0 < nm; j0 += kRecordBatch * rows_per) {
+    int64_t e[kRecordBatch];
+    float wv[kRecordBatch];
+#pragma unroll
+    for (int b = 0; b < kRecordBatch; ++b) {        // every load of the batch in flight together
+      const int j = j0 + b * rows_per + j_l;
+      const bool ok = act && j < nm;
+      const int64_t n = static_cast<int64_t>(s) * T + (ok ? lst[j] : 0);
+      e[b] = ok ? a.topk_idx[n * K + k_l] : -1;
+      wv[b] = ok && wts ? a.topk_weights[n * K + k_l] : 0.0f;
+    }
+#pragma unroll
+    for (int b = 0; b < kRecordBatch; ++b) {
+      const int j = j0 + b * rows_per + j_l;
+      const int64_t g = static_cast<int64_t>(row0) + j;
+      if (act && j < nm && g < a.capacity) {
+        const bool mine = e[b] >= lo && e[b] < lo + a.L && e[b] < a.E;
+        __builtin_nontemporal_store(mine ? e[b] - lo : int64_t(-1), a.recv_topk_idx + g * K + k_l);
+        if (wts) __builtin_nontemporal_store(mine ? wv[b] : 0.0f, a.recv_topk_weights + g * K + k_l);
+      }
+    }
+  }
+}
+
 template <int KIND, int VPL, int MW, int NT>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
+  __shared__ int32_t lst[256 / kWave][kRecordMaxTokens];   // record wavefronts: member tokens of the source
   const int lane = lane_id();
-  const int64_t gw = wave_index();
+  // record workgroups: the first rec_blocks of the grid, or with rec_last the last ones
+  const int rb = a.rec_last ? static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x - a.rec_blocks)
+                            : static_cast<int>(blockIdx.x);
+  if (rb >= 0 && rb < a.rec_blocks) {   // record wavefronts (uniform per workgroup)
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+    const int mw = rb * (256 / kWave) + w;
+    if (mw < a.rec_waves) pack_records(a, mw, lst[w]);
+    return;
+  }
+  const int64_t gw = wave_index() - (a.rec_last ? 0 : static_cast<int64_t>(a.rec_blocks) * (256 / kWave));
   const int64_t n = gw / nslices;
   const int slice = static_cast<int>(gw - n * nslices);
   if (n >= a.N) return;
@@ -65,13 +162,14 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
   // top-k entries, source index and pre-quantised scales, once per token (by
   // slice 0): loaded here, written after the payload so that their latency
   // hides behind the row traffic
-  const bool head = slice == 0 && (a.meta || KIND == kPackFp8);
+  const bool inline_meta = a.meta && a.rec_waves == 0;   // else the record wavefronts write them
+  const bool head = slice == 0 && (inline_meta || KIND == kPackFp8);
   int64_t tok = n;
   int64_t e = -1;
   float wk = 0.0f, sv = 0.0f;
   if (head) {
     tok = a.src_tok != nullptr ? a.src_tok[n] : n;   // the source token the row carries
-    if (a.meta && lane < a.K) {
+    if (inline_meta && lane < a.K) {
       e = a.topk_idx[tok * a.K + lane];
       if (a.topk_weights) wk = a.topk_weights[tok * a.K + lane];
     }
@@ -167,7 +265,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a, int nslices) {
         m &= m - 1;
         const int r = rbase + kWave * i + b;
         const int64_t row = readlane(dst[i], b);
-        if (a.meta) {
+        if (inline_meta) {
           if (lane < a.K) {
             const bool mine = e >= 0 && e < a.E && static_cast<int>(e) / a.L == r;
             if (a.recv_topk_idx) a.recv_topk_idx[row * a.K + lane] = mine ? e - static_cast<int64_t>(r) * a.L : -1;
@@ -322,7 +420,7 @@ static hipError_t launch_pack_cast(const PackArgs& a, int ppl_hint, hipStream_t 
 template <int KIND, int VPL, int NT>
 static hipError_t launch_pack_vpl(const PackArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
-  const int64_t blocks = (waves + 3) / 4;
+  const int64_t blocks = (waves + 3) / 4 + a.rec_blocks;
   if (a.R <= 64)
     hipLaunchKernelGGL((pack_kernel<KIND, VPL, 1, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                        nslices);
@@ -357,9 +455,25 @@ static hipError_t launch_pack_nt(const PackArgs& a, int vpl, int nslices, int nt
   }
 }
 
-hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
-  if (a.N == 0) return hipSuccess;
+hipError_t launch_pack(const PackArgs& a_in, hipStream_t st) {
+  if (a_in.N == 0) return hipSuccess;
   const Tuning& tu = tuning();
+  PackArgs a = a_in;
+  // record wavefronts, one per (source, rank), for a fresh direct dispatch
+  // whose sources hold at most kRecordMaxTokens tokens (a record wavefront
+  // walks its source in 64-token chunks); forwarded group rows, longer
+  // sources and the one-token-per-workgroup cast keep the records in their
+  // payload wavefronts
+  const bool cast_tpb = a.kind == kPackCastFp8 && tu.cast_tpb > 0;
+  if (a.meta && a.group_off == nullptr && a.src_tok == nullptr && a.count == nullptr && a.rpm != nullptr &&
+      a.in_rank != nullptr && !cast_tpb && tu.pack_records != 0 && a.T <= kRecordMaxTokens) {
+    a.rec_waves = a.S * a.R;
+    a.rec_blocks = (a.rec_waves + 3) / 4;
+    a.rec_last = tu.pack_records == 2 ? 1 : 0;
+  } else {
+    a.rec_waves = 0;
+    a.rec_blocks = 0;
+  }
   const int nt = tu.pack_nt >= 0 ? tu.pack_nt & 7 : (a.cpol >= 0 ? a.cpol & 7 : 6);
   // per-lane unit: a 16-byte input vector, or for the fused cast a pair of
   // them (16 channels -> one 16-byte vector of codes)
@@ -380,12 +494,11 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t st) {
   switch (a.kind) {
     case kPackFp8: return launch_pack_nt<kPackFp8>(a, vpl, nslices, nt, st);
     case kPackCastFp8:
-      // Measured on the 16384-token workload: with the top-k metadata (fresh
-      // dispatch) one token per workgroup at 2 vectors per lane is fastest
-      // (229 vs 264 us); without it (cached) the 1 KiB slices are (247 vs 262).
-      // The token-per-workgroup kernel has no forwarding mode.
-      if ((tu.cast_tpb > 0 || (tu.cast_tpb < 0 && a.meta)) && a.group_off == nullptr && a.count == nullptr &&
-          a.src_tok == nullptr) {
+      // One token per workgroup (its H/128 scales gathered in LDS and stored
+      // contiguously, the records written inline) only on request: with the
+      // records in their own wavefronts the 1 KiB slices are faster also for
+      // a fresh dispatch.  The token-per-workgroup kernel has no forwarding mode.
+      if (cast_tpb && a.group_off == nullptr && a.count == nullptr && a.src_tok == nullptr) {
         const int hint = tu.pack_vpl > 0 ? tu.pack_vpl : 1;   // 1 pair = 2 vectors per lane
         switch (nt) {
           case 0: return launch_pack_cast<0>(a, hint, st);
