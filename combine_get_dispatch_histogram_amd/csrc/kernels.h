@@ -195,7 +195,7 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
 // MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT, MIEP_LL_SPLIT,
 // MIEP_LL_VPL, MIEP_CAST_TPB, MIEP_LLC_VPL, MIEP_LLC_SLICES, MIEP_LLC_NT,
-// MIEP_LL_NT, MIEP_PACK_RECORDS):
+// MIEP_LL_NT, MIEP_PACK_RECORDS, MIEP_LL_TPB, MIEP_LL_COUNT_SRC):
 // used by geometry sweeps, never required.
 // combine_maxr: source rows whose loads are issued together.
 // pack_nt / combine_nt: cache policy of the row traffic, bit 0 =
@@ -214,9 +214,12 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // low-latency send's cache-policy code.  pack_records: 0 writes a fresh
 // dispatch's receive records from the payload wavefronts instead of the
 // record wavefronts (-1, the default: record wavefronts where supported).
+// ll_tpb: threads per low-latency send workgroup (256, 512 or 1024; 0 =
+// chosen per call); ll_count_src: 0 counts messages with one workgroup per
+// (l, s) block instead of one per source (-1, the default).
 struct Tuning {
   int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl,
-      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt, pack_records;
+      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt, pack_records, ll_tpb, ll_count_src;
 };
 const Tuning& tuning();
 

@@ -16,12 +16,13 @@
 // fix the order: slot j of (l, s) is the j-th top-k entry of source s that
 // names expert d*L + l, in (token, k) order, so the output is
 // deterministic.  Two kernels:
-//   count: one workgroup per (l, s) block scans source s's top-k for the
-//          expert and writes the block's message count;
-//   send:  a few workgroups per block (kLLSplit; 6 for wide FP8 rows)
-//          repeat the (tiny) scan, take the
-//          block's packed range from the counts of the earlier sources, and
-//          cast and write each message and its packed row in one pass
+//   count: one workgroup per source s counts, for each of d's local
+//          experts, the top-k entries naming it (an LDS histogram), and
+//          writes the (l, s) message counts;
+//   send:  a few workgroups per (l, s) block (kLLSplit of 256 threads; 3 of
+//          512 threads for wide FP8 rows) repeat the (tiny) slot scan, take
+//          the block's packed range from the counts of the earlier sources,
+//          and cast and write each message and its packed row in one pass
 //          (16-byte loads and stores), so nothing is read back.
 #include <mutex>
 
@@ -67,6 +68,7 @@ constexpr int kLLMaxSlots = 4096;
 // plus an LDS carry across wavefronts and 256-token chunks gives each entry
 // its slot.  With `slot_tok`, slot j < M records its token.  Returns the
 // number of matching entries (uncapped), the same in every thread.
+template <int TPB>
 __device__ __forceinline__ int ll_slot_scan(const LLArgs& a, int l, int s, int32_t* slot_tok, int32_t* wsum,
                                             int32_t* carry_s) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -77,7 +79,7 @@ __device__ __forceinline__ int ll_slot_scan(const LLArgs& a, int l, int s, int32
   // the carry is first read after the first barrier of the loop, so its
   // reset needs no barrier of its own (the top-k loads go out at once)
   if (tid == 0) *carry_s = 0;
-  for (int t0 = 0; t0 < a.T; t0 += kLLThreads) {
+  for (int t0 = 0; t0 < a.T; t0 += TPB) {
     const int t = t0 + tid;
     uint64_t kmask = 0;                           // entries k of token t that name the expert
     if (t < a.T && !masked) {
@@ -105,7 +107,7 @@ __device__ __forceinline__ int ll_slot_scan(const LLArgs& a, int l, int s, int32
     __syncthreads();
     if (tid == 0) {
       int tot = *carry_s;
-      for (int q = 0; q < kLLThreads / kWave; ++q) tot += wsum[q];
+      for (int q = 0; q < TPB / kWave; ++q) tot += wsum[q];
       *carry_s = tot;
     }
     __syncthreads();
@@ -119,8 +121,41 @@ __global__ __launch_bounds__(kLLThreads) void ll_count_kernel(LLArgs a) {
   __shared__ int32_t carry_s;
   const int l = blockIdx.x / a.R;
   const int s = blockIdx.x % a.R;
-  const int n = ll_slot_scan(a, l, s, nullptr, wsum, &carry_s);
+  const int n = ll_slot_scan<kLLThreads>(a, l, s, nullptr, wsum, &carry_s);
   if (threadIdx.x == 0) a.msg_count[l * a.R + s] = n < a.M ? n : a.M;
+}
+
+// Per-(l, s) message counts, capped at M, one workgroup per source s: every
+// thread takes tokens t, t + blockDim, ... and counts, in an LDS histogram
+// over d's L local experts, the top-k entries naming each of them (a
+// source's top-k rows are read once instead of once per local expert).
+__global__ __launch_bounds__(kLLThreads) void ll_count_src_kernel(LLArgs a) {
+  extern __shared__ int32_t hist[];               // [L]
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int l = tid; l < a.L; l += blockDim.x) hist[l] = 0;
+  const bool masked = a.mask != nullptr && (a.mask[a.d] != 0 || a.mask[s] != 0);
+  const int64_t lo = static_cast<int64_t>(a.d) * a.L;
+  __syncthreads();
+  if (!masked) {
+    const int64_t* idx = a.topk_idx + static_cast<int64_t>(s) * a.T * a.K;
+    for (int t = tid; t < a.T; t += blockDim.x) {
+      const int64_t* row = idx + static_cast<int64_t>(t) * a.K;
+      for (int k0 = 0; k0 < a.K; k0 += 8) {       // 8 independent loads in flight
+        int64_t e8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e8[j] = k0 + j < a.K ? row[k0 + j] : -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (e8[j] >= lo && e8[j] < lo + a.L) atomicAdd(&hist[e8[j] - lo], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int l = tid; l < a.L; l += blockDim.x) {
+    const int n = hist[l];
+    a.msg_count[l * a.R + s] = n < a.M ? n : a.M;
+  }
 }
 
 // Messages and their packed receive rows.  Workgroup (l, s, y) repeats the
@@ -130,10 +165,10 @@ __global__ __launch_bounds__(kLLThreads) void ll_count_kernel(LLArgs a) {
 // message (the transport buffer) and to the packed row, so the receive side
 // never reads the messages back.  Without a message buffer (a.msg null)
 // only the packed rows are written.
-template <int VPL, int NT>
-__global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
+template <int VPL, int NT, int TPB>
+__global__ __launch_bounds__(TPB) void ll_send_kernel(LLArgs a) {
   __shared__ int32_t slot_tok[kLLMaxSlots];  // message j -> source token
-  __shared__ int32_t wsum[kLLThreads / kWave];
+  __shared__ int32_t wsum[TPB / kWave];
   __shared__ int32_t carry_s;
   const int l = blockIdx.x / a.R;
   const int s = blockIdx.x % a.R;
@@ -144,7 +179,7 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   // unconditionally (clamped index) so that they are in flight with the
   // scan's top-k loads, and masked only after the scan
   const int p_raw = a.msg_count[l * a.R + (lane < a.R ? lane : a.R - 1)];
-  const int cnt = ll_slot_scan(a, l, s, slot_tok, wsum, &carry_s);   // synchronises the workgroup
+  const int cnt = ll_slot_scan<TPB>(a, l, s, slot_tok, wsum, &carry_s);   // synchronises the workgroup
   const int n = cnt < a.M ? cnt : a.M;
   int part = lane < s ? p_raw : 0;
   for (int q = lane + kWave; q < s; q += kWave) part += a.msg_count[l * a.R + q];
@@ -170,7 +205,7 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   const int64_t pb = a.use_fp8 ? a.H : 2 * static_cast<int64_t>(a.H);   // packed row bytes
   const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x) + static_cast<int64_t>(s) * a.T * 2 * a.H;
   const bool keep = a.msg != nullptr;                       // messages materialised
-  for (int task = blockIdx.y * (kLLThreads / kWave) + w; task < n * nsl; task += gridDim.y * (kLLThreads / kWave)) {
+  for (int task = blockIdx.y * (TPB / kWave) + w; task < n * nsl; task += gridDim.y * (TPB / kWave)) {
     const int j = task / nsl;
     const int u0 = (task - j * nsl) * span;
     const int t = slot_tok[j];
@@ -229,29 +264,40 @@ __global__ __launch_bounds__(kLLThreads) void ll_send_kernel(LLArgs a) {
   }
 }
 
+// count: one workgroup per source (an LDS histogram over the L local
+// experts; measured on the low-latency workload 12.55 -> 12.15 us for count +
+// send) when L fits in LDS, else one per (l, s) block.  send: tpb threads
+// per workgroup (512 with 3 workgroups per block for wide FP8 rows: 11.95 us).
 template <int VPL, int NT>
-static hipError_t launch_ll_cfg(const LLArgs& a, int blocks, int split, hipStream_t st) {
-  hipLaunchKernelGGL(ll_count_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
+static hipError_t launch_ll_cfg(const LLArgs& a, int blocks, int split, int tpb, hipStream_t st) {
+  if (tuning().ll_count_src != 0 && a.L <= 16384)
+    hipLaunchKernelGGL(ll_count_src_kernel, dim3(a.R), dim3(kLLThreads), sizeof(int32_t) * a.L, st, a);
+  else
+    hipLaunchKernelGGL(ll_count_kernel, dim3(blocks), dim3(kLLThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ll_send_kernel<VPL, NT>), dim3(blocks, split), dim3(kLLThreads), 0, st, a);
+  switch (tpb) {
+    case 512: hipLaunchKernelGGL((ll_send_kernel<VPL, NT, 512>), dim3(blocks, split), dim3(512), 0, st, a); break;
+    case 1024: hipLaunchKernelGGL((ll_send_kernel<VPL, NT, 1024>), dim3(blocks, split), dim3(1024), 0, st, a); break;
+    default: hipLaunchKernelGGL((ll_send_kernel<VPL, NT, kLLThreads>), dim3(blocks, split), dim3(kLLThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
 template <int VPL>
-static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, int split, hipStream_t st) {
+static hipError_t launch_ll_vpl(const LLArgs& a, int blocks, int split, int tpb, hipStream_t st) {
   // cache policy: plain loads of x, non-temporal stores of the messages and
   // packed rows (measured on the low-latency workload: 12.95 us against
   // 13.5 us with the plain policy)
   switch (tuning().ll_nt >= 0 ? tuning().ll_nt & 7 : 2) {
-    case 1: return launch_ll_cfg<VPL, 1>(a, blocks, split, st);
-    case 2: return launch_ll_cfg<VPL, 2>(a, blocks, split, st);
-    case 3: return launch_ll_cfg<VPL, 3>(a, blocks, split, st);
-    case 4: return launch_ll_cfg<VPL, 4>(a, blocks, split, st);
-    case 5: return launch_ll_cfg<VPL, 5>(a, blocks, split, st);
-    case 6: return launch_ll_cfg<VPL, 6>(a, blocks, split, st);
-    case 7: return launch_ll_cfg<VPL, 7>(a, blocks, split, st);
-    default: return launch_ll_cfg<VPL, 0>(a, blocks, split, st);
+    case 1: return launch_ll_cfg<VPL, 1>(a, blocks, split, tpb, st);
+    case 2: return launch_ll_cfg<VPL, 2>(a, blocks, split, tpb, st);
+    case 3: return launch_ll_cfg<VPL, 3>(a, blocks, split, tpb, st);
+    case 4: return launch_ll_cfg<VPL, 4>(a, blocks, split, tpb, st);
+    case 5: return launch_ll_cfg<VPL, 5>(a, blocks, split, tpb, st);
+    case 6: return launch_ll_cfg<VPL, 6>(a, blocks, split, tpb, st);
+    case 7: return launch_ll_cfg<VPL, 7>(a, blocks, split, tpb, st);
+    default: return launch_ll_cfg<VPL, 0>(a, blocks, split, tpb, st);
   }
 }
 
@@ -267,7 +313,8 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
   // workgroups, which fill every wavefront slot of the chip exactly), shorter
   // rows one pair when a row is 64 pairs' multiple
   const bool fp8_wide = a.use_fp8 && a.H / 16 >= 2 * kWave;
-  const int split = tu.ll_split > 0 ? tu.ll_split : (fp8_wide ? 6 : kLLSplit);
+  const int tpb = tu.ll_tpb > 0 ? tu.ll_tpb : (fp8_wide ? 512 : kLLThreads);
+  const int split = tu.ll_split > 0 ? tu.ll_split : (fp8_wide ? (tpb == 512 ? 3 : 6) : kLLSplit);
   int vpl;
   if (tu.ll_vpl > 0)
     vpl = tu.ll_vpl;
@@ -276,10 +323,10 @@ hipError_t launch_ll(const LLArgs& a, hipStream_t st) {
   else
     vpl = (a.H / 8) % (2 * kWave) == 0 ? 2 : 8;
   switch (vpl) {
-    case 1: return launch_ll_vpl<1>(a, blocks, split, st);
-    case 2: return launch_ll_vpl<2>(a, blocks, split, st);
-    case 4: return launch_ll_vpl<4>(a, blocks, split, st);
-    default: return launch_ll_vpl<8>(a, blocks, split, st);
+    case 1: return launch_ll_vpl<1>(a, blocks, split, tpb, st);
+    case 2: return launch_ll_vpl<2>(a, blocks, split, tpb, st);
+    case 4: return launch_ll_vpl<4>(a, blocks, split, tpb, st);
+    default: return launch_ll_vpl<8>(a, blocks, split, tpb, st);
   }
 }
 
