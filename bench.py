@@ -379,10 +379,12 @@ def run_normal_variant(torch, miep, wl, w, iters, cast_fp8):
     c_ms = time_batched(torch, lambda: miep.combine_into(y, h, cx, rtw, cw), iters, batch=4)
     cd_ms = time_batched(torch, lambda: miep.cached_dispatch_into(x, h, recv_x, recv_s, cast_to_fp8=cast_fp8), iters,
                          batch=4)
+    lay_ms = time_batched(torch, lambda: miep.get_dispatch_layout_into(idx, w.E, w.R, w.S, ntpr, ntp_rdma, ntpe, itr),
+                          iters)
     kind = "cast" if cast_fp8 else "bf16"
     db = bytes_notify(w.N, w.R, w.S, w.C, w.E) + bytes_pack(w.N, w.H, w.K, w.R, rows, kind)
     cb = bytes_combine(w.N, w.H, w.K, w.R, rows)
-    return dict(rows=rows, rho=round(rows / w.N, 4), dispatch_us=round(d_ms * 1e3, 1),
+    return dict(rows=rows, rho=round(rows / w.N, 4), layout_us=round(lay_ms * 1e3, 2), dispatch_us=round(d_ms * 1e3, 1),
                 combine_us=round(c_ms * 1e3, 1), cached_dispatch_us=round(cd_ms * 1e3, 1),
                 tokens_per_s=round(w.N / ((d_ms + c_ms) / 1e3), 1),
                 dispatch_gbs=round(db / (d_ms / 1e3) / 1e9, 1), combine_gbs=round(cb / (c_ms / 1e3) / 1e9, 1),

@@ -20,10 +20,26 @@
 
 namespace miep {
 
-// Membership row of one token: R bytes, 1 where the rank is in the mask.
+// 4 mask bits -> 4 bytes of 0/1 (bit i -> byte i): one multiply places bits
+// 0..3 at bits 0, 8, 16, 24 (the four partial products occupy disjoint bit
+// ranges, so nothing carries).
+__device__ __forceinline__ uint32_t bits4_to_bytes(uint32_t b4) { return (b4 * 0x00204081u) & 0x01010101u; }
+
+// Membership row of one token: R bytes, 1 where the rank is in the mask
+// (16-byte stores when R % 16 == 0 and the rows are 16-byte aligned).
 template <int MW>
-__device__ __forceinline__ void store_member_row(uint8_t* out, int R, const RankMask<MW>& m) {
-  if ((R & 3) == 0) {
+__device__ __forceinline__ void store_member_row(uint8_t* out, int R, const RankMask<MW>& m, bool vec16) {
+  if (vec16) {
+    for (int r0 = 0; r0 < R; r0 += 16) {
+      const int q = r0 >> 6;
+      uint64_t w = m.w[0];
+#pragma unroll
+      for (int i = 1; i < MW; ++i) w = (q == i) ? m.w[i] : w;
+      const uint32_t b16 = static_cast<uint32_t>(w >> (r0 & 63)) & 0xFFFFu;
+      *reinterpret_cast<uint4*>(out + r0) = make_uint4(bits4_to_bytes(b16 & 15u), bits4_to_bytes((b16 >> 4) & 15u),
+                                                       bits4_to_bytes((b16 >> 8) & 15u), bits4_to_bytes(b16 >> 12));
+    }
+  } else if ((R & 3) == 0) {
     for (int r0 = 0; r0 < R; r0 += 4) {
       const uint32_t b = m.get(r0) | (m.get(r0 + 1) << 8) | (m.get(r0 + 2) << 16) | (m.get(r0 + 3) << 24);
       *reinterpret_cast<uint32_t*>(out + r0) = b;
@@ -43,6 +59,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
   const int s = blockIdx.x;
   const int lane = lane_id();
   const bool vec = (a.K & 1) == 0 && (reinterpret_cast<uintptr_t>(a.topk_idx) & 15u) == 0;   // 16-byte rows pairs
+  const bool vec16 = (a.R & 15) == 0 && (reinterpret_cast<uintptr_t>(a.in_rank) & 15u) == 0;
   // the first 8 top-k entries of this thread's first token: loaded before
   // the LDS clear and its barrier, so that their latency covers both
   const bool pre_ok = vec && a.K >= 8 && static_cast<int>(threadIdx.x) < a.T;
@@ -99,11 +116,28 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
       }
       // the last tile's rows are written after the final barrier, which
       // would otherwise wait for these stores to land
-      if (t + static_cast<int>(blockDim.x) < tpad) store_member_row(a.in_rank + n * a.R, a.R, m);
+      if (t + static_cast<int>(blockDim.x) < tpad) store_member_row(a.in_rank + n * a.R, a.R, m, vec16);
     }
     m_last = m;
-    // rank and RDMA-group counts: one ballot per rank over the wavefront;
-    // lane j of each 64-rank chunk adds the chunk's count for rank r0 + j
+    if (a.R > 8) {
+      // rank and RDMA-group counts of wide rows: one LDS add per set bit of
+      // the token's rank mask and of its group mask (about rho adds per
+      // token instead of one ballot per rank per wavefront)
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        for (uint64_t mm = m.w[i]; mm != 0; mm &= mm - 1) atomicAdd(&rcnt[kWave * i + __builtin_ctzll(mm)], 1);
+        // group g (ranks 8g..8g+7) of this word is hit when its byte is nonzero
+        uint64_t f = m.w[i];
+        f |= f >> 4;
+        f |= f >> 2;
+        f |= f >> 1;
+        uint32_t gm = static_cast<uint32_t>(((f & 0x0101010101010101ull) * 0x0102040810204080ull) >> 56);
+        for (; gm != 0; gm &= gm - 1) atomicAdd(&gcnt[8 * i + __builtin_ctz(gm)], 1);
+      }
+      continue;
+    }
+    // rank counts of rows of <= 8 ranks: one ballot per rank over the
+    // wavefront; lane j adds the wavefront's count for rank j
     for (int r0 = 0; r0 < a.R; r0 += kWave) {
       const int rend = a.R - r0 < kWave ? a.R - r0 : kWave;
       int mine = 0;
@@ -126,7 +160,8 @@ __global__ __launch_bounds__(1024) void layout_kernel(LayoutArgs a) {
     }
   }
   __syncthreads();
-  if (t_last >= 0 && t_last < a.T) store_member_row(a.in_rank + (static_cast<int64_t>(s) * a.T + t_last) * a.R, a.R, m_last);
+  if (t_last >= 0 && t_last < a.T)
+    store_member_row(a.in_rank + (static_cast<int64_t>(s) * a.T + t_last) * a.R, a.R, m_last, vec16);
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.ntpe[static_cast<int64_t>(s) * a.E + e] = hist[e];
   for (int r = threadIdx.x; r < a.R; r += blockDim.x) a.ntpr[static_cast<int64_t>(s) * a.R + r] = rcnt[r];
   if (a.ntp_rdma)

@@ -71,6 +71,16 @@ __device__ __forceinline__ void issue_row_words(const uint8_t* row, int R, bool 
     rw.v[1] = static_cast<uint32_t>(q >> 32);
 #pragma unroll
     for (int i = 2; i < NW; ++i) rw.v[i] = 0u;
+  } else if (NW >= 16 && (R & 15) == 0 && (reinterpret_cast<uintptr_t>(row) & 15u) == 0) {
+    // 16-byte pieces (rows of 16, 32, 48 or 64 ranks), clamped like below
+#pragma unroll
+    for (int i = 0; i < NW; i += 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(row + (4 * i < R ? 4 * i : R - 16));
+      rw.v[i] = q.x;
+      rw.v[i + 1] = q.y;
+      rw.v[i + 2] = q.z;
+      rw.v[i + 3] = q.w;
+    }
   } else {
     // unconditional loads from clamped offsets (words past the row are
     // skipped by the decode): a load whose result is selected right away

@@ -96,6 +96,10 @@ SMALL = [
     ("many-src", 40, 32, 64, 16, 4, 4, 5, 1),        # notify: > 16 sources per wavefront (batched count rows)
     ("many-src-r16", 33, 16, 64, 32, 16, 4, 3, 1),   # the same on the bit-transpose path
     ("huge-T", 1, (1 << 20) + 7, 8, 2, 2, 1, 3, 1),  # > 2^20 tokens per source: channel index by plain division
+    ("rec-1024", 2, 1024, 64, 64, 16, 8, 24, 1),     # longest sources written by the record wavefronts
+    ("rec-1025", 2, 1025, 64, 64, 16, 8, 24, 1),     # one token more: the records go back inline
+    ("rec-k64", 3, 130, 64, 256, 8, 64, 5, 1),       # top-64: one record row per store instruction
+    ("rec-k20-r64", 2, 200, 64, 128, 64, 20, 7, 1),  # 3 rows per store, 64 ranks, four 64-token chunks
 ]
 
 
