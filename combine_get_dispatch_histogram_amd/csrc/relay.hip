@@ -34,9 +34,9 @@ __global__ __launch_bounds__(256) void relay_meta_kernel(RelayMetaArgs a) {
   const int4* src = reinterpret_cast<const int4*>(a.send_head + n * a.R + g * 8);
   const int4 lo = src[0], hi = src[1];
   int4* dst = reinterpret_cast<int4*>(a.send_nvl_head + row * 8);
-  dst[0] = lo;
-  dst[1] = hi;
-  a.rdma_src_idx[row] = static_cast<int32_t>(n);
+  __builtin_nontemporal_store(lo, dst);
+  __builtin_nontemporal_store(hi, dst + 1);
+  __builtin_nontemporal_store(static_cast<int32_t>(n), a.rdma_src_idx + row);
 }
 
 hipError_t launch_relay_meta(const RelayMetaArgs& a, hipStream_t st) {
