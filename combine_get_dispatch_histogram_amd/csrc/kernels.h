@@ -44,7 +44,9 @@ struct LayoutArgs {
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t st);
 
-// ---- notify: prefix matrices, receive offsets, send_head (one workgroup per source)
+// ---- notify: prefix matrices, receive offsets, send_head (one workgroup per
+// group of channels of a source, or per source where that kernel's conditions
+// do not hold)
 // group_w == 0: the destinations are the R ranks of in_rank's rows.
 // group_w == 8: the destinations are R groups of 8 ranks (rows of R*8
 // bytes); a token goes to a group when it goes to any of its ranks.
@@ -216,10 +218,13 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // record wavefronts (-1, the default: record wavefronts where supported).
 // ll_tpb: threads per low-latency send workgroup (256, 512 or 1024; 0 =
 // chosen per call); ll_count_src: 0 counts messages with one workgroup per
-// (l, s) block instead of one per source (-1, the default).
+// (l, s) block instead of one per source (-1, the default).  notify_chan: 0
+// runs the per-source notify everywhere, n > 0 caps the channels per
+// workgroup of the channel-group notify (-1, the default: as many whole
+// channels as fit in one wavefront, where supported).
 struct Tuning {
   int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl,
-      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt, pack_records, ll_tpb, ll_count_src;
+      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt, pack_records, ll_tpb, ll_count_src, notify_chan;
 };
 const Tuning& tuning();
 

@@ -404,7 +404,8 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
             const bool bit = m.get(r0 + j) != 0;
             const uint64_t b = ballot(bit);
             myb = lane == j ? b : myb;
-            if (bit) v[q] = readlane(pos_l, j) + __popcll(b & lanemask_lt());
+            const int pj = readlane(pos_l, j);        // with every lane active
+            if (bit) v[q] = pj + __popcll(b & lanemask_lt());
           }
         }
         if (valid) {
@@ -496,6 +497,397 @@ __global__ __launch_bounds__(1024) void notify_kernel(NotifyArgs a) {
   }
 }
 
+// ---- one workgroup per group of channels of one source --------------------
+//
+// Rows of R = 8, 16, 32 or 64 ranks with channels of at most 256 tokens.  The
+// per-source kernel above is bound by the length of one workgroup's chain;
+// here a workgroup handles a run of whole channels of one source (as many as
+// fit in one wavefront of 64 tokens, else one channel: 96 workgroups of two
+// 22-token channels for the normal workload, 320 of five 11-token channels
+// at 64 ranks) and takes everything that other workgroups would produce
+// straight from the inputs, so that no workgroup waits on another:
+//  - rows of rank r from sources before s: the sum of those sources'
+//    num_tokens_per_rank rows;
+//  - rows of rank r from the earlier channels of s: a byte-wise sum of their
+//    tokens' membership rows, which are one contiguous byte range (16-byte
+//    loads; byte b of the range belongs to rank b mod R, so every piece a
+//    lane loads covers the same ranks and byte counters add without carries);
+//  - its own tokens: ballots per rank (R = 8) or the bit transpose through
+//    LDS (wider rows), as in the per-source kernel.
+// Every load is issued before the first wait, and the cross-lane sums run in
+// DPP row operations plus two lane exchanges, so a workgroup's chain is one
+// round trip, a few dozen ALU instructions, one barrier and its stores.  The
+// per-expert receive counts are spread over all workgroups.
+constexpr int kChanMaxTokens = 256;   // tokens per channel (4 wavefronts)
+constexpr int kChanMaxPieces = 127;   // 16-byte pieces per lane in the recount (byte counters, folded for R = 8)
+constexpr int kChanBatch = 16;        // loads of one kind in flight per lane
+constexpr int kChanEarlyE = 4;        // owned experts whose count loads join the first round trip
+
+template <int R>
+struct ChanRow {
+  uint32_t v[R <= 8 ? 2 : R / 4];
+};
+template <int R>
+__device__ __forceinline__ void chan_load_row(const uint8_t* row, ChanRow<R>& cr) {
+  if constexpr (R == 8) {
+    const uint64_t q = *reinterpret_cast<const uint64_t*>(row);
+    cr.v[0] = static_cast<uint32_t>(q);
+    cr.v[1] = static_cast<uint32_t>(q >> 32);
+  } else {
+#pragma unroll
+    for (int i = 0; i < R / 16; ++i) {
+      const uint4 q = reinterpret_cast<const uint4*>(row)[i];
+      cr.v[4 * i] = q.x;
+      cr.v[4 * i + 1] = q.y;
+      cr.v[4 * i + 2] = q.z;
+      cr.v[4 * i + 3] = q.w;
+    }
+  }
+}
+template <int R>
+__device__ __forceinline__ uint64_t chan_row_mask(const ChanRow<R>& cr) {
+  uint64_t m = 0;
+#pragma unroll
+  for (int i = 0; i < (R <= 8 ? 2 : R / 4); ++i) m |= static_cast<uint64_t>(nonzero_bytes4(cr.v[i])) << (4 * i);
+  return m;
+}
+
+// Sum of the lanes that agree modulo P (P = 1, 2, 4, 8 or 16) across the
+// wavefront: DPP within each row of 16 lanes (quad permutes, then row shifts
+// by 4 and 8 that fill with 0), then the four rows through two lane
+// exchanges.  Lane 16 - P + j of every row ends up with class j's sum.
+template <int P>
+__device__ __forceinline__ uint32_t class_sum(uint32_t v) {
+  int x = static_cast<int>(v);
+  if constexpr (P == 1) x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  if constexpr (P <= 2) x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  if constexpr (P <= 4) x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  if constexpr (P <= 8) x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return static_cast<uint32_t>(x);
+}
+
+// Count rows (scalar per lane for R <= 16: lane -> rank tid % R; 16-byte
+// quads for wider rows: lane -> ranks 4q..4q+3, q = tid % (R/4)) and
+// membership pieces, B of each per lane, all loads issued before the first
+// sum; indices past the ends are clamped to 0 (valid: the arrays are never
+// empty here) and their values dropped.
+template <int R, int B>
+__device__ __forceinline__ void chan_sums(const int32_t* ntpr, int nq, const uint4* pc, int np, bool half_tail,
+                                          int i0, int nthr, int tid, int4& acc, uint32_t (&bsum)[4]) {
+  constexpr bool kQuad = R > 16;
+  int4 v[B];
+  uint4 pv[B];
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const int i = i0 + u * nthr + tid;
+    if constexpr (kQuad) v[u] = reinterpret_cast<const int4*>(ntpr)[i < nq ? i : 0];
+    else v[u].x = ntpr[i < nq ? i : 0];
+  }
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const int i = i0 + u * nthr + tid;
+    pv[u] = pc[i < np ? i : 0];
+  }
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    const int i = i0 + u * nthr + tid;
+    const bool okq = i < nq, okp = i < np;
+    const bool cut = half_tail && i == np - 1;
+    acc.x += okq ? v[u].x : 0;
+    if constexpr (kQuad) {
+      acc.y += okq ? v[u].y : 0;
+      acc.z += okq ? v[u].z : 0;
+      acc.w += okq ? v[u].w : 0;
+    }
+    bsum[0] += okp ? pv[u].x : 0u;
+    bsum[1] += okp ? pv[u].y : 0u;
+    bsum[2] += okp && !cut ? pv[u].z : 0u;
+    bsum[3] += okp && !cut ? pv[u].w : 0u;
+  }
+}
+
+template <int R, bool HNT>
+__global__ __launch_bounds__(256) void notify_chan_kernel(NotifyArgs a, int cpw) {
+  constexpr bool kQuad = R > 16;
+  constexpr int kCP = kQuad ? R / 4 : R;          // count classes (lanes that agree mod kCP share a rank set)
+  constexpr int kWin = R < 16 ? 8 : 16;           // ranks one lane's recount bytes cover
+  constexpr int kNWin = R < 16 ? 1 : R / 16;      // recount classes
+  __shared__ int32_t cnt_w[kNotifyMaxWaves][R];   // per wavefront: count rows of the summed sources
+  __shared__ int32_t pre_w[kNotifyMaxWaves][R];   // per wavefront: member bytes of the earlier channels
+  __shared__ int32_t own_w[kNotifyMaxWaves][R];   // per wavefront: its tokens per rank
+  __shared__ uint64_t mk[kNotifyMaxWaves][kWave];    // wide rows: token masks, then rank columns
+  __shared__ int32_t pk[kNotifyMaxWaves][kWave];     // wide rows: per-rank positions
+
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int nw = blockDim.x / kWave;
+  const int nthr = blockDim.x;
+  const int S = a.S, T = a.T, C = a.C;
+  const int tc = a.tcdiv.d;
+  const int c0 = static_cast<int>(blockIdx.x) * cpw;          // first channel of this workgroup
+  const int c1 = c0 + cpw < a.nonempty ? c0 + cpw : a.nonempty;
+  const int t0 = c0 * tc;                         // first token
+  const int tend = c1 * tc < T ? c1 * tc : T;
+  const int n_own = tend - t0;
+  const bool first = s == 0 && blockIdx.x == 0;   // also computes the receive offsets and the status
+  const int limit = first ? S : s;                // count rows summed (workgroup (0, 0): all, for the totals)
+  const int64_t tok0 = static_cast<int64_t>(s) * T;
+
+  // Every load below is unconditional, from a clamped (always valid) index,
+  // and masked where it is summed: a load under a branch gets a wait of its
+  // own from the compiler, which would serialise the round trips.
+  // (1a) this thread's token
+  ChanRow<R> cr;
+  const bool mine = tid < n_own;
+  chan_load_row<R>(a.in_rank + (tok0 + t0 + (mine ? tid : 0)) * R, cr);
+
+  // (1b) owned experts e = b, b + nb, ... (b = workgroup index): lane j
+  // loads source j's count of the first kChanEarlyE of them
+  const bool do_e = a.nrte != nullptr && a.ntpe != nullptr;
+  const int b = s * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
+  const int nb = static_cast<int>(gridDim.x * gridDim.y);
+  int ev[kChanEarlyE];
+  if (do_e) {
+    const int jc = lane < S ? lane : S - 1;
+#pragma unroll
+    for (int k = 0; k < kChanEarlyE; ++k) {
+      const int e = b + k * nb;
+      ev[k] = a.ntpe[static_cast<int64_t>(jc) * a.E + (e < a.E ? e : a.E - 1)];
+    }
+  }
+
+  // (1c) count rows of sources < limit (elements, or 16-byte quads, i = tid,
+  // tid + nthr, ...; nthr is a multiple of kCP, so the class is tid % kCP);
+  // (1d) membership bytes of tokens [0, t0) of s: 16-byte pieces p = tid,
+  // tid + nthr, ... (R = 8 with t0 odd: the last piece's second token is not
+  // an earlier one)
+  const int nq = limit * (kQuad ? R / 4 : R);
+  const int64_t pbytes = static_cast<int64_t>(t0) * R;
+  const int np = static_cast<int>((pbytes + 15) / 16);
+  const bool half_tail = (pbytes & 15) != 0;
+  const uint4* pc = reinterpret_cast<const uint4*>(a.in_rank + tok0 * R);
+  int4 acc = make_int4(0, 0, 0, 0);
+  uint32_t bsum[4] = {0u, 0u, 0u, 0u};
+  const int nuq = (nq + nthr - 1) / nthr, nup = (np + nthr - 1) / nthr;
+  const int nu = nuq > nup ? nuq : nup;           // loads per lane of the longer kind (wave-uniform)
+  if (nu <= 1) {
+    chan_sums<R, 1>(a.ntpr, nq, pc, np, half_tail, 0, nthr, tid, acc, bsum);
+  } else if (nu <= 4) {
+    chan_sums<R, 4>(a.ntpr, nq, pc, np, half_tail, 0, nthr, tid, acc, bsum);
+  } else {
+    for (int u0 = 0; u0 < nu; u0 += kChanBatch)
+      chan_sums<R, kChanBatch>(a.ntpr, nq, pc, np, half_tail, u0 * nthr, nthr, tid, acc, bsum);
+  }
+
+  // (2) own tokens: per-wavefront rank counts (and, wide rows, rank columns)
+  const uint64_t m = mine ? chan_row_mask<R>(cr) : 0ull;
+  uint64_t bal[R <= 8 ? R : 1];                   // R = 8: ballot per rank
+  uint64_t col = 0;                               // bit q: token q of the wavefront goes to rank `lane`
+  if constexpr (R <= 8) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      bal[j] = ballot(((m >> j) & 1ull) != 0);
+      col = lane == j ? bal[j] : col;
+    }
+  } else {
+    mk[w][lane] = m;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const ulonglong2* mw = reinterpret_cast<const ulonglong2*>(&mk[w][0]);
+#pragma unroll 8
+    for (int q = 0; q < kWave / 2; ++q) {          // broadcast reads, two masks each
+      const ulonglong2 pq = mw[q];
+      col |= ((pq.x >> lane) & 1ull) << (2 * q);
+      col |= ((pq.y >> lane) & 1ull) << (2 * q + 1);
+    }
+  }
+  if (lane < R) own_w[w][lane] = __popcll(col);
+
+  // (3) count rows: class sums; lanes 16 - kCP + j hold class j
+  {
+    const uint32_t x = class_sum<kCP>(static_cast<uint32_t>(acc.x));
+    if constexpr (kQuad) {
+      const uint32_t y = class_sum<kCP>(static_cast<uint32_t>(acc.y));
+      const uint32_t z = class_sum<kCP>(static_cast<uint32_t>(acc.z));
+      const uint32_t ww = class_sum<kCP>(static_cast<uint32_t>(acc.w));
+      const int j = lane - (16 - kCP);
+      if (j >= 0 && j < kCP) {
+        cnt_w[w][4 * j] = static_cast<int32_t>(x);
+        cnt_w[w][4 * j + 1] = static_cast<int32_t>(y);
+        cnt_w[w][4 * j + 2] = static_cast<int32_t>(z);
+        cnt_w[w][4 * j + 3] = static_cast<int32_t>(ww);
+      }
+    } else {
+      const int j = lane - (16 - kCP);
+      if (j >= 0 && j < kCP) cnt_w[w][j] = static_cast<int32_t>(x);
+    }
+  }
+
+  // (4) membership bytes: 16-bit counters (even / odd bytes of each word),
+  // class sums over the lanes that share a window
+  constexpr int kWords = kWin / 2;
+  uint32_t u16[kWords];
+  if constexpr (R == 8) {
+    const uint32_t f0 = bsum[0] + bsum[2], f1 = bsum[1] + bsum[3];   // bytes j and j + 8 are the same rank
+    u16[0] = f0 & 0x00FF00FFu;
+    u16[1] = (f0 >> 8) & 0x00FF00FFu;
+    u16[2] = f1 & 0x00FF00FFu;
+    u16[3] = (f1 >> 8) & 0x00FF00FFu;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u16[2 * i] = bsum[i] & 0x00FF00FFu;
+      u16[2 * i + 1] = (bsum[i] >> 8) & 0x00FF00FFu;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) u16[i] = class_sum<kNWin>(u16[i]);
+  {
+    const int j = lane - (16 - kNWin);
+    if (j >= 0 && j < kNWin) {
+#pragma unroll
+      for (int i = 0; i < kWords / 2; ++i) {      // word 2i: ranks 4i, 4i+2; word 2i+1: ranks 4i+1, 4i+3
+        int32_t* d = &pre_w[w][kWin * j + 4 * i];
+        d[0] = static_cast<int32_t>(u16[2 * i] & 0xFFFFu);
+        d[2] = static_cast<int32_t>(u16[2 * i] >> 16);
+        d[1] = static_cast<int32_t>(u16[2 * i + 1] & 0xFFFFu);
+        d[3] = static_cast<int32_t>(u16[2 * i + 1] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+
+  // (5) lane r: rank r's bases
+  int cnt = 0, pre = 0, own = 0, wp = 0;
+  if (lane < R) {
+    for (int q = 0; q < nw; ++q) {
+      cnt += cnt_w[q][lane];
+      pre += pre_w[q][lane];
+      const int o = own_w[q][lane];
+      own += o;
+      wp += q < w ? o : 0;
+    }
+  }
+  const int base_l = first ? 0 : cnt;             // rows of rank `lane` from sources < s
+  const int pos_l = base_l + pre + wp;            // row of this wavefront's first member
+
+  // (6) send_head rows of this wavefront's tokens
+  if constexpr (R <= 8) {
+    // rank j's position read from lane j with every lane active (inside the
+    // branch below, the compiler may compute pos_l only on the active lanes)
+    int posj[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) posj[j] = readlane(pos_l, j);
+    if (mine) {
+      int v[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) v[j] = ((m >> j) & 1ull) ? posj[j] + __popcll(bal[j] & lanemask_lt()) : -1;
+      const int64_t n = tok0 + t0 + tid;
+      store_head4<HNT>(a.send_head, n * R, make_int4(v[0], v[1], v[2], v[3]));
+      store_head4<HNT>(a.send_head, n * R + 4, make_int4(v[4], v[5], v[6], v[7]));
+    }
+  } else {
+    // lane (tq, j) writes ranks 4j..4j+3 of token q0 + tq: one store
+    // instruction covers 64 / (R/4) token rows
+    mk[w][lane] = col;
+    pk[w][lane] = pos_l;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int kQ = R / 4;
+    constexpr int kLg = R == 16 ? 2 : (R == 32 ? 3 : 4);   // log2(R / 4)
+    const int tq = lane >> kLg, j = lane & (kQ - 1);
+    uint64_t c4[4];
+    int p4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c4[k] = mk[w][4 * j + k];
+      p4[k] = pk[w][4 * j + k];
+    }
+    const int tw0 = w * kWave;                    // this wavefront's first token within the workgroup
+    const int nqw = n_own - tw0 < kWave ? n_own - tw0 : kWave;
+    for (int q0 = 0; q0 < nqw; q0 += kWave / kQ) {
+      const int q = q0 + tq;
+      if (q < nqw) {
+        const uint64_t below = (1ull << q) - 1ull;
+        int v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = ((c4[k] >> q) & 1ull) ? p4[k] + __popcll(c4[k] & below) : -1;
+        store_head4<HNT>(a.send_head, (tok0 + t0 + tw0 + q) * R + 4 * j, make_int4(v[0], v[1], v[2], v[3]));
+      }
+    }
+  }
+
+  // (7) channel prefixes (inclusive of the channel): one store per rank for
+  // every channel that ends on a token of this wavefront
+  {
+    const int t = t0 + tid;
+    const int ch = T <= (1 << 20) ? fdiv(t, a.tcdiv) : t / tc;   // FastDiv is exact below 2^20
+    const bool last_in_channel = mine && (t - ch * tc == tc - 1 || t == T - 1);
+    const uint64_t clast = ballot(last_in_channel);
+    for (uint64_t cl = clast; cl != 0; cl &= cl - 1) {
+      const int L = __builtin_ctzll(cl);
+      const int cc = readlane(ch, L);
+      const uint64_t upto = L == kWave - 1 ? ~0ull : ((2ull << L) - 1);   // tokens 0..L of the wavefront
+      if (lane < R) {
+        const int inc = pre + wp + __popcll(col & upto);
+        a.cpm[(static_cast<int64_t>(s) * R + lane) * C + cc] = inc;
+        a.rcpm[(static_cast<int64_t>(lane) * S + s) * C + cc] = base_l + inc;
+      }
+    }
+  }
+  // the source's last workgroup: tail channels and the rank prefix
+  if (w == 0 && lane < R && c1 == a.nonempty) {
+    const int r = lane;
+    const int inc = pre + own;
+    a.rpm[static_cast<int64_t>(s) * R + r] = base_l + inc;
+    for (int cc = c1; cc < C; ++cc) {
+      a.cpm[(static_cast<int64_t>(s) * R + r) * C + cc] = inc;
+      a.rcpm[(static_cast<int64_t>(r) * S + s) * C + cc] = base_l + inc;
+    }
+  }
+  // receive offsets and the capacity status (workgroup (0, 0): cnt = totals)
+  if (first && w == 0) {
+    const int v = lane < R ? cnt : 0;
+    const int incl = wave_inclusive_scan(v);
+    if (lane < R) a.off[lane] = incl - v;
+    const int sum = readlane(incl, kWave - 1);
+    if (lane == 0) {
+      a.off[R] = sum;
+      if (a.status != nullptr) {
+        const bool over = sum > a.capacity;
+        if (!a.status_or) *a.status = over ? kStatusCapacity : 0;
+        else if (over) *a.status = kStatusCapacity;
+      }
+    }
+  }
+  // (8) per-expert receive counts, rounded up to the alignment
+  if (do_e && w == 0) {
+    const uint32_t al = static_cast<uint32_t>(a.align);
+    for (int k = 0; b + k * nb < a.E; ++k) {
+      const int e = b + k * nb;
+      int sum = 0;
+      if (k < kChanEarlyE) {
+#pragma unroll
+        for (int kk = 0; kk < kChanEarlyE; ++kk) sum = kk == k && lane < S ? ev[kk] : sum;
+      } else if (lane < S) {
+        sum = a.ntpe[static_cast<int64_t>(lane) * a.E + e];
+      }
+      for (int src = kWave + lane; src < S; src += kWave) sum += a.ntpe[static_cast<int64_t>(src) * a.E + e];
+      sum = static_cast<int>(class_sum<1>(static_cast<uint32_t>(sum)));
+      if (lane == 15) {
+        const uint32_t t = static_cast<uint32_t>(sum);
+        a.nrte[e] = static_cast<int32_t>(al == 1u ? t : (t + al - 1u) / al * al);
+      }
+    }
+  }
+}
+
 __global__ void fill_zero_kernel(int32_t* p, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -522,8 +914,50 @@ static hipError_t launch_notify_cfg(const NotifyArgs& a, int threads, size_t lds
   return hipGetLastError();
 }
 
+// Geometry of the per-channel-group kernel: threads per workgroup and
+// channels per workgroup, or {0, 0} where its conditions do not hold (then
+// the per-source kernel runs).
+struct ChanGeom {
+  int threads, cpw;
+};
+static ChanGeom chan_geom(const NotifyArgs& a) {
+  const ChanGeom none{0, 0};
+  if (tuning().notify_chan == 0 || a.group_w != 0) return none;
+  if (a.R != 8 && a.R != 16 && a.R != 32 && a.R != 64) return none;
+  if (a.T <= 0 || a.S <= 0 || a.S > 65535 || (static_cast<int64_t>(a.T) * a.R) % 16 != 0) return none;
+  const int tc = a.tcdiv.d;
+  if (tc <= 0 || tc > kChanMaxTokens || a.nonempty <= 0) return none;
+  if (((reinterpret_cast<uintptr_t>(a.in_rank) | reinterpret_cast<uintptr_t>(a.ntpr) |
+        reinterpret_cast<uintptr_t>(a.send_head)) & 15u) != 0)
+    return none;
+  // whole channels per workgroup: as many as fit in one wavefront (tuning:
+  // notify_chan > 0 caps it)
+  int cpw = tc <= kWave ? kWave / tc : 1;
+  if (tuning().notify_chan > 0 && cpw > tuning().notify_chan) cpw = tuning().notify_chan;
+  const int threads = (cpw * tc + kWave - 1) / kWave * kWave;
+  const int64_t pieces = static_cast<int64_t>(a.T) * a.R / 16;
+  if ((pieces + threads - 1) / threads > kChanMaxPieces) return none;
+  return ChanGeom{threads, cpw};
+}
+
+template <bool HNT>
+static hipError_t launch_notify_chan(const NotifyArgs& a, const ChanGeom& g, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((a.nonempty + g.cpw - 1) / g.cpw), static_cast<unsigned>(a.S));
+  switch (a.R) {
+    case 8: hipLaunchKernelGGL((notify_chan_kernel<8, HNT>), grid, dim3(g.threads), 0, st, a, g.cpw); break;
+    case 16: hipLaunchKernelGGL((notify_chan_kernel<16, HNT>), grid, dim3(g.threads), 0, st, a, g.cpw); break;
+    case 32: hipLaunchKernelGGL((notify_chan_kernel<32, HNT>), grid, dim3(g.threads), 0, st, a, g.cpw); break;
+    default: hipLaunchKernelGGL((notify_chan_kernel<64, HNT>), grid, dim3(g.threads), 0, st, a, g.cpw); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
   if (a.S == 0) return hipSuccess;
+  const int64_t head_bytes = static_cast<int64_t>(a.S) * a.T * a.R * 4;
+  const bool hnt = head_bytes > kHeadStreamBytes && head_bytes < (1ll << 31);
+  const ChanGeom g = chan_geom(a);
+  if (g.threads > 0) return hnt ? launch_notify_chan<true>(a, g, st) : launch_notify_chan<false>(a, g, st);
   int threads = ((a.T + kWave - 1) / kWave) * kWave;
   threads = threads < kWave ? kWave : (threads > kNotifyMaxWaves * kWave ? kNotifyMaxWaves * kWave : threads);
   const int ne_max = (a.E + a.S - 1) / a.S;  // experts owned by workgroup 0 (the most)
@@ -535,8 +969,6 @@ hipError_t launch_notify(const NotifyArgs& a, hipStream_t st) {
   // notify 18.0 -> 15.3 us with it, while 8 groups took 7.3 us with ballots
   // against 11.1 us transposed)
   // streaming send_head stores (buffer offsets are 32 bits: arrays below 2 GiB)
-  const int64_t head_bytes = static_cast<int64_t>(a.S) * a.T * a.R * 4;
-  const bool hnt = head_bytes > kHeadStreamBytes && head_bytes < (1ll << 31);
   if (hnt) return launch_notify_cfg<true>(a, threads, lds, st);
   return launch_notify_cfg<false>(a, threads, lds, st);
 }

@@ -31,9 +31,9 @@ __global__ __launch_bounds__(256) void relay_meta_kernel(RelayMetaArgs a) {
   if (h < 0) return;
   const int64_t row = static_cast<int64_t>(a.rdma_off[g]) + h;
   if (row >= a.rdma_capacity) return;
-  const int4* src = reinterpret_cast<const int4*>(a.send_head + n * a.R + g * 8);
-  const int4 lo = src[0], hi = src[1];
-  int4* dst = reinterpret_cast<int4*>(a.send_nvl_head + row * 8);
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.send_head + n * a.R + g * 8);
+  const u32x4 lo = src[0], hi = src[1];
+  u32x4* dst = reinterpret_cast<u32x4*>(a.send_nvl_head + row * 8);
   __builtin_nontemporal_store(lo, dst);
   __builtin_nontemporal_store(hi, dst + 1);
   __builtin_nontemporal_store(static_cast<int32_t>(n), a.rdma_src_idx + row);

@@ -100,6 +100,10 @@ SMALL = [
     ("rec-1025", 2, 1025, 64, 64, 16, 8, 24, 1),     # one token more: the records go back inline
     ("rec-k64", 3, 130, 64, 256, 8, 64, 5, 1),       # top-64: one record row per store instruction
     ("rec-k20-r64", 2, 200, 64, 128, 64, 20, 7, 1),  # 3 rows per store, 64 ranks, four 64-token chunks
+    ("chan-odd", 3, 210, 64, 64, 8, 4, 10, 1),       # channel groups of 3 x 21 tokens: odd first token (half piece)
+    ("chan-2wave", 2, 512, 64, 64, 32, 6, 4, 1),     # 128-token channels: two wavefronts per workgroup
+    ("chan-many-src", 70, 32, 64, 512, 8, 6, 4, 1),  # > 64 sources, > 4 experts per workgroup
+    ("chan-r32", 4, 160, 64, 128, 32, 8, 24, 2),     # 32 ranks: 9 channels of 7 tokens per workgroup
 ]
 
 
