@@ -581,10 +581,12 @@ KERNEL_SRC = {"combine": ("combine.hip", "device.h"), "pack": ("pack.hip", "devi
 
 
 def _kernel_key(name):
-    for k in ("ll_combine_kernel", "combine_kernel", "pack_cast_kernel", "pack_kernel", "notify_kernel",
-              "layout_kernel", "ll_send_kernel", "ll_count_kernel", "relay_meta_kernel"):
+    for k, key in (("ll_combine_kernel", "ll_combine"), ("combine_kernel", "combine"), ("pack_cast_kernel", "pack_cast"),
+                   ("pack_kernel", "pack"), ("notify_chan_kernel", "notify"), ("notify_kernel", "notify"),
+                   ("layout_kernel", "layout"), ("ll_send_kernel", "ll_send"), ("ll_count_src_kernel", "ll_count"),
+                   ("ll_count_kernel", "ll_count"), ("relay_meta_kernel", "relay_meta")):
         if "miep::" + k in name:
-            return k.replace("_kernel", "")
+            return key
     return None
 
 
