@@ -214,7 +214,8 @@ const char* miep_version(void) { return "miep 0.1 gfx950"; }
 
 int64_t miep_ll_msg_bytes(int32_t hidden, int32_t use_fp8) {
   if (hidden <= 0) return -1;
-  return 16 + (use_fp8 ? static_cast<int64_t>(hidden) + 4ll * (hidden / miep::kFp8Group) : 2ll * hidden);
+  const int64_t used = 16 + (use_fp8 ? static_cast<int64_t>(hidden) + 4ll * (hidden / miep::kFp8Group) : 2ll * hidden);
+  return (used + 15) / 16 * 16;   // 16-byte message stride
 }
 
 miep_status miep_get_dispatch_layout(const miep_problem* p, const int64_t* topk_idx, int32_t* num_tokens_per_rank,
@@ -591,8 +592,8 @@ miep_status ll_dispatch_args(const miep_ll_problem* q, const uint16_t* x, const 
             E = q->num_experts, d = q->dest_rank;
   if (use_ue8m0 && !round_scale) return fail(MIEP_EINVAL, "use_ue8m0 requires round_scale");
   if (use_ue8m0 && !use_fp8) return fail(MIEP_EINVAL, "use_ue8m0 requires use_fp8");
-  if (use_fp8 && H % 512 != 0)
-    return fail(MIEP_EUNSUPPORTED, "FP8 low-latency messages need hidden % 512 == 0 (16-byte message stride)");
+  if (use_fp8 && H % miep::kFp8Group != 0)
+    return fail(MIEP_EINVAL, "FP8 low-latency messages need hidden % 128 == 0 (whole scale groups)");
   if ((T > 0 && (!x || !topk_idx)) || (with_msgs && (!msg_buf || !msg_count)) || !packed_recv_x ||
       !packed_recv_src_info || !packed_recv_layout_range || !packed_recv_count)
     return fail(MIEP_EINVAL, "a required pointer is NULL");

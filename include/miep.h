@@ -281,7 +281,9 @@ typedef struct miep_ll_problem {
 
 /* Bytes of one low-latency message ([Phil] message format): a 16-byte
  * header (int32 source token index + 3 reserved int32, zero here), then
- * either H E4M3 bytes and H/128 fp32 scales, or 2H bf16 bytes.  Host-only. */
+ * either H E4M3 bytes and H/128 fp32 scales, or 2H bf16 bytes, rounded up
+ * to a multiple of 16 bytes (FP8 with H % 512 != 0: up to 12 padding bytes,
+ * left unwritten).  Host-only; -1 for hidden <= 0. */
 int64_t miep_ll_msg_bytes(int32_t hidden, int32_t use_fp8);
 
 /* low_latency_dispatch -- [NvLL] low-latency dispatch (send loop, receive
@@ -306,9 +308,9 @@ int64_t miep_ll_msg_bytes(int32_t hidden, int32_t use_fp8);
  *                  send loop and receive wait), nonzero = masked.  If rank d
  *                  or source s is masked, no message travels from s to d:
  *                  the (l, s) blocks hold 0 rows.
- * Errors: EINVAL for bad sizes or flags or a null required pointer;
- * EUNSUPPORTED for R > 1024, M > 4096, K > 64, H % 8 != 0, FP8 with
- * H % 512 != 0, or misaligned x / msg_buf / packed_recv_x. */
+ * Errors: EINVAL for bad sizes or flags, FP8 with H % 128 != 0, or a null
+ * required pointer; EUNSUPPORTED for R > 1024, M > 4096, K > 64,
+ * H % 8 != 0, or misaligned x / msg_buf / packed_recv_x. */
 miep_status miep_ll_dispatch(const miep_ll_problem* q, const uint16_t* x, const int64_t* topk_idx, int32_t use_fp8,
                              int32_t round_scale, int32_t use_ue8m0, void* msg_buf, int32_t* msg_count,
                              void* packed_recv_x, float* packed_recv_x_scales, uint8_t* packed_recv_x_scales_ue8m0,

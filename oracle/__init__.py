@@ -50,8 +50,8 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)                        # missing or older than oracle.c
         _lib = ctypes.CDLL(_LIB)
         _declare(_lib)
     return _lib

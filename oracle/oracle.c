@@ -476,8 +476,12 @@ int oracle_combine(int S, int T, int H, int K, int R, const uint16_t* y, const f
  * mask array [R] (nonzero = masked), nothing travels to rank d if d is
  * masked, and nothing from a masked source s -- its (l, s) blocks hold 0
  * messages.  */
+/* The message stride is the header plus payload rounded up to 16 bytes
+ * (messages are written in 16-byte pieces); the padding bytes carry no
+ * value.  At H % 512 == 0 (FP8) and any H % 8 == 0 (bf16) there is none. */
 int64_t oracle_ll_msg_bytes(int H, int use_fp8) {
-    return 16 + (use_fp8 ? (int64_t)H + 4LL * (H / ORC_FP8_GROUP) : 2LL * H);
+    const int64_t used = 16 + (use_fp8 ? (int64_t)H + 4LL * (H / ORC_FP8_GROUP) : 2LL * H);
+    return (used + 15) / 16 * 16;
 }
 
 int oracle_ll_dispatch(int S, int T, int M, int H, int K, int E, int R, int d,

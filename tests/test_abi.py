@@ -49,6 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_host_helpers(lib):
     assert lib.miep_ll_msg_bytes(7168, 1) == 7408
     assert lib.miep_ll_msg_bytes(7168, 0) == 14352
+    assert lib.miep_ll_msg_bytes(128, 1) == 160 and lib.miep_ll_msg_bytes(640, 1) == 688   # 16-byte stride
     assert lib.miep_ll_msg_bytes(0, 1) == -1
     assert b"gfx950" in lib.miep_version()
 
@@ -192,7 +193,7 @@ def test_ll_validation(lib):
     assert lib.miep_ll_dispatch(ctypes.byref(q(num_topk=65)), *args) == _lib.MIEP_EUNSUPPORTED
     assert lib.miep_ll_dispatch(ctypes.byref(q(num_experts=250)), *args) == _lib.MIEP_EINVAL
     assert lib.miep_ll_dispatch(ctypes.byref(q(dest_rank=32)), *args) == _lib.MIEP_EINVAL
-    assert lib.miep_ll_dispatch(ctypes.byref(q(hidden=7040)), *args) == _lib.MIEP_EUNSUPPORTED
+    assert lib.miep_ll_dispatch(ctypes.byref(q(hidden=7000)), *args) == _lib.MIEP_EINVAL   # FP8 needs H % 128 == 0
     bad = list(args)
     bad[3], bad[4] = 0, 1                      # ue8m0 without round_scale
     assert lib.miep_ll_dispatch(ctypes.byref(q()), *bad) == _lib.MIEP_EINVAL

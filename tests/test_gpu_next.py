@@ -215,7 +215,7 @@ def test_ll_combine_small(case, weighted):
             miep.update_mask_buffer(mask, r, True)
         mref = np.zeros(R, np.int32)
         mref[list(masked)] = 1
-    use_fp8 = H % 512 == 0 and name != "ll-wide"
+    use_fp8 = H % 128 == 0 and name != "ll-wide"
     out = miep.low_latency_dispatch(x.to(DEV), idx.to(DEV), M, E, d, R, use_fp8, mask_buffer=mask)
     ref = oracle.ll_dispatch(wl.bf16_bits(x), idx.numpy(), S=R, M=M, E=E, R=R, dest_rank=d, use_fp8=use_fp8,
                              round_scale=False, use_ue8m0=False, mask=mref)

@@ -19,30 +19,41 @@ def _case(S, T, M, H, E, K, seed, dup=False, mask_p=0.0):
     return x, idx
 
 
-def _msg_bytes_formula(H, use_fp8):
+def _msg_used(H, use_fp8):
     # int4 header + (H FP8 bytes + H/128 fp32 scales) or 2H bf16 bytes
     return 16 + (H + (H // 128) * 4 if use_fp8 else 2 * H)
+
+
+def _msg_bytes_formula(H, use_fp8):
+    # the stride: rounded up to whole 16-byte pieces
+    return -(-_msg_used(H, use_fp8) // 16) * 16
 
 
 def test_msg_bytes(orc):
     assert orc.ll_msg_bytes(7168, True) == 7408 == 463 * 16
     assert orc.ll_msg_bytes(7168, False) == 14352
-    for H in (128, 256, 4096):
+    assert orc.ll_msg_bytes(128, True) == 160          # 148 used bytes, 12 of padding
+    assert orc.ll_msg_bytes(640, True) == 688          # 676 used
+    for H in (128, 256, 384, 512, 640, 4096):
         for f in (True, False):
             assert orc.ll_msg_bytes(H, f) == _msg_bytes_formula(H, f)
+            assert orc.ll_msg_bytes(H, f) % 16 == 0
+            assert 0 <= orc.ll_msg_bytes(H, f) - _msg_used(H, f) < 16
 
 
 @pytest.mark.parametrize("use_fp8,round_scale,use_ue8m0", [(False, False, False), (True, False, False),
                                                            (True, True, False), (True, True, True)])
 @pytest.mark.parametrize("dup,mask_p", [(False, 0.0), (True, 0.2)])
-def test_ll_matches_brute(orc, use_fp8, round_scale, use_ue8m0, dup, mask_p):
+@pytest.mark.parametrize("H", [256, 384])   # 384: FP8 messages with 4 bytes of padding
+def test_ll_matches_brute(orc, use_fp8, round_scale, use_ue8m0, dup, mask_p, H):
     S = R = 4
-    T, M, H, E, K, d = 6, 8, 256, 16, 3, 1
+    T, M, E, K, d = 6, 8, 16, 3, 1
     L = E // R
     x, idx = _case(S, T, M, H, E, K, 3, dup, mask_p)
     o = orc.ll_dispatch(x, idx, S=S, M=M, E=E, R=R, dest_rank=d, use_fp8=use_fp8, round_scale=round_scale,
                         use_ue8m0=use_ue8m0, cumulative_stats=np.full(L, 5, np.int32))
-    mb = _msg_bytes_formula(H, use_fp8)
+    mb = _msg_used(H, use_fp8)
+    assert o["msg_buf"].shape[-1] == _msg_bytes_formula(H, use_fp8)
     for l in range(L):
         begin = 0
         for s in range(S):
