@@ -30,6 +30,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB: load another build of oracle.c instead (the sanitizer test's), never rebuilt here
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
 
 X_BF16, X_FP8, X_BF16_CAST_FP8 = 0, 1, 2
 FP8_GROUP = 128
@@ -50,6 +52,10 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
+        if _LIB_OVERRIDE:
+            _lib = ctypes.CDLL(_LIB_OVERRIDE)
+            _declare(_lib)
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)                        # missing or older than oracle.c
         _lib = ctypes.CDLL(_LIB)
