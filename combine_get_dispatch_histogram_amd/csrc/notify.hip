@@ -11,16 +11,23 @@
 // exchange of counts; with the ranks as partitions of one GPU it is a local
 // scan.
 //
-// One workgroup per source partition s.  Its rank bases (rows of rank r
-// before source s) come from the layout's num_tokens_per_rank, so the
-// workgroups never wait on each other.  Within a wavefront of 64 tokens the
-// per-rank counts and prefixes come from one ballot per rank (rows of <= 8
-// ranks) or from a bit transpose of the tokens' rank masks through LDS
-// (wider rows); each wavefront adds the earlier wavefronts' counts from LDS
-// with independent reads; send_head rows leave as 16-byte stores.
-// (Splitting a source over several workgroups, each counting the earlier
-// tokens of its source itself, measured slower: 14.2 us with 64-token tiles
-// against 8.7 us for the normal workload.)
+// Two kernels, neither of which waits on another workgroup: rank bases
+// (rows of rank r before source s) come from the layout's
+// num_tokens_per_rank.
+//  - notify_chan_kernel (rows of 8, 16, 32 or 64 ranks, channels of at most
+//    256 tokens): one workgroup per run of whole channels of one source; the
+//    earlier channels' rows per rank come from a byte-wise sum of their
+//    membership rows (see the kernel's comment).
+//  - notify_kernel (other shapes, and the relay's group notify): one
+//    workgroup per source.  Within a wavefront of 64 tokens the per-rank
+//    counts and prefixes come from one ballot per rank (rows of <= 8 ranks)
+//    or from a bit transpose of the tokens' rank masks through LDS (wider
+//    rows); each wavefront adds the earlier wavefronts' counts from LDS with
+//    independent reads.
+// send_head rows leave as 16-byte stores in both.  (An earlier split of a
+// source over several workgroups that recounted its earlier tokens with
+// ballots measured slower: 14.2 us with 64-token tiles against 8.7 us for
+// the normal workload; the byte-wise sum is what made the split pay.)
 #include "device.h"
 #include "kernels.h"
 
