@@ -185,7 +185,10 @@ def mean(xs):
 
 
 # --------------------------------------------------------------------------- GPU legs
-def run_normal(torch, miep, wl, steps, warmup):
+def run_normal(torch, miep, wl, steps, warmup, only=None):
+    """The normal step.  only="warm": just the warm-up and timed step loop;
+    only="cold": just the cold-cache runs (for counter runs that must not mix
+    the two)."""
     w = wl.NORMAL
     dev = torch.device("cuda:0")
     inp = wl.normal_inputs(w, 0)
@@ -221,6 +224,10 @@ def run_normal(torch, miep, wl, steps, warmup):
             miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, None, rti, rtw, nrte)
             miep.combine_into(y, h, cx, rtw, cw)
 
+    if only == "cold":
+        return dict(cold=measure_cold(torch, dev, {
+            "dispatch": lambda: miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, None, rti, rtw, nrte),
+            "combine": lambda: miep.combine_into(y, h, cx, rtw, cw)}, steps))
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -230,6 +237,8 @@ def run_normal(torch, miep, wl, steps, warmup):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if only == "warm":
+        return dict(wall=wall)
     # (2) the same steps again with HIP events around every call
     tl, td, tc = Timer(torch, steps), Timer(torch, steps), Timer(torch, steps)
     torch.cuda.synchronize()
@@ -708,6 +717,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true", help="skip the separately measured stages")
+    ap.add_argument("--only-warm", action="store_true",
+                    help="normal workload: only the warm-up and timed step loop (for counter runs)")
+    ap.add_argument("--only-cold", action="store_true",
+                    help="normal workload: only the cold-cache dispatch / combine / pair runs (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -767,6 +780,14 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.only_warm or args.only_cold:
+        r = run_normal(torch, miep, wl, args.steps, args.warmup, "warm" if args.only_warm else "cold")
+        if args.only_warm:
+            print(json.dumps({"warm_ms_per_step": round(r["wall"] * 1e3 / args.steps, 4)}), flush=True)
+        else:
+            print(json.dumps({"cold_us_p50": {k: round(sorted(v)[len(v) // 2] * 1e3, 2)
+                                               for k, v in r["cold"].items()}}), flush=True)
+        return
     if args.workload_only:
         w = wl.SKEWED if args.workload_only == "skewed" else wl.LARGE
         print(json.dumps({args.workload_only: run_normal_variant(torch, miep, wl, w, args.steps,
