@@ -71,7 +71,33 @@ def _normal_cases(n=24, seed=2024):
     return out
 
 
-@pytest.mark.parametrize("case", _normal_cases(), ids=lambda c: "n%d-%s-R%d" % (c["i"], c["kind"], c["R"]))
+def _channel_group_cases(n=16, seed=77):
+    """Shapes of the channel-group notify (8/16/32/64 ranks, T * R a multiple of 16, channels of up to 256
+    tokens): channel groups that start on odd tokens, many sources, one-token channels, multi-wavefront
+    channels."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([8, 16, 32, 64]))
+        L = int(rng.integers(1, 4))
+        E = R * L
+        K = int(rng.integers(1, min(E, 9) + 1))
+        S = int(rng.choice([1, 3, 17, 70]))
+        T = int(rng.integers(1, 400))
+        if R == 8:
+            T += T % 2                            # T * R % 16 == 0
+        C = int(rng.choice([1, 2, 5, 7, 24, 41, T]))
+        kind = ["bf16", "cast", "fp8"][i % 3]
+        H = int(rng.choice([128, 256])) if kind != "bf16" else int(8 * rng.integers(1, 40))
+        out.append(dict(i=100 + i, R=R, E=E, K=K, S=S, T=T, C=C, H=H, kind=kind, seed=int(rng.integers(0, 2 ** 31)),
+                        mask_p=float(rng.choice([0.0, 0.15])), dup_p=float(rng.choice([0.0, 0.2])),
+                        oob_p=float(rng.choice([0.0, 0.05])), worst=bool(rng.random() < 0.3),
+                        bias=False, round_scale=bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("case", _normal_cases() + _channel_group_cases(),
+                         ids=lambda c: "n%d-%s-R%d" % (c["i"], c["kind"], c["R"]))
 def test_fuzz_normal(case):
     say("fuzz normal", case)
     c = case
@@ -109,6 +135,8 @@ def test_fuzz_normal(case):
     torch.cuda.synchronize()
     assert np.array_equal(npy(ntpr), lay["num_tokens_per_rank"])
     assert np.array_equal(npy(h.send_head), ref["send_head"])
+    assert np.array_equal(npy(h.rank_prefix_matrix), ref["rank_prefix_matrix"])
+    assert np.array_equal(npy(h.channel_prefix_matrix), ref["channel_prefix_matrix"])
     assert np.array_equal(npy(h.recv_channel_prefix_matrix), ref["recv_channel_prefix_matrix"])
     assert np.array_equal(npy(h.recv_rank_offset), ref["recv_rank_offset"])
     n = ref["num_recv"]
