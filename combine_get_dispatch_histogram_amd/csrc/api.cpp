@@ -427,7 +427,7 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
   ng.off = rh->recv_rdma_offset;
   ng.send_head = rh->send_rdma_head;
   ng.capacity = rh->rdma_capacity;
-  ng.status_or = 1;                  // keeps the first notify's verdict and adds the group rows' one
+  ng.status_or = 1;                  // keeps the first notify's status word, ORs in the group rows' overflow
   e = miep::launch_notify(ng, s);
   if (e != hipSuccess) return hip_status(e, "group notify launch");
   miep::RelayMetaArgs rm{};
