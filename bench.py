@@ -89,11 +89,13 @@ def bytes_relay_dispatch(N, H, K, R, S, C, E, rows, grows, kind="cast"):
     return notify + meta + hop1 + hop2
 
 
-def bytes_relay_combine(N, H, K, R, rows, grows, weights=True):
+def bytes_relay_combine(N, H, K, R, rows, grows, weights=True, partial_f32=False):
     """Two-level combine: every received row read once into its group row's
-    partial (written once), every partial read once into its token's row."""
+    partial (written once: 2H bytes, or 4H with fp32 partials), every partial
+    read once into its token's row."""
     G = R // 8
-    b = grows * 32 + rows * 2 * H + grows * 2 * H + N * G * 4 + grows * 2 * H + N * 2 * H
+    pb = 4 if partial_f32 else 2
+    b = grows * 32 + rows * 2 * H + grows * pb * H + N * G * 4 + grows * pb * H + N * 2 * H
     if weights:
         b += rows * 4 * K + 2 * grows * 4 * K + N * 4 * K
     return b
@@ -444,6 +446,11 @@ def run_relay(torch, miep, wl, iters):
     def rc():
         miep.relay_combine_into(y, h, rh, rdma_y, cx, rtw, rdma_w, cw)
 
+    rdma_y32 = torch.empty((grows, w.H), dtype=torch.float32, device=dev)
+
+    def rc32():                                   # fp32 group partials (rounded once)
+        miep.relay_combine_into(y, h, rh, rdma_y32, cx, rtw, rdma_w, cw)
+
     def dd():
         miep.dispatch_into(x, idx, wts, ntpr, ntpe, h, recv_x, recv_s, rti, rtw, nrte, cast_to_fp8=True)
 
@@ -451,17 +458,22 @@ def run_relay(torch, miep, wl, iters):
         miep.combine_into(y, h, cx, rtw, cw)
 
     t = {k: time_batched(torch, f, iters, batch=4) for k, f in
-         (("relay_dispatch", rd), ("relay_combine", rc), ("direct_dispatch", dd), ("direct_combine", dc))}
+         (("relay_dispatch", rd), ("relay_combine", rc), ("relay_combine_f32", rc32), ("direct_dispatch", dd),
+          ("direct_combine", dc))}
     bd = bytes_relay_dispatch(w.N, w.H, w.K, w.R, w.S, w.C, w.E, rows, grows)
     bc = bytes_relay_combine(w.N, w.H, w.K, w.R, rows, grows)
     return dict(rows=rows, group_rows=grows, groups_per_token=round(grows / w.N, 4),
                 relay_dispatch_us=round(t["relay_dispatch"] * 1e3, 1),
                 relay_combine_us=round(t["relay_combine"] * 1e3, 1),
+                relay_combine_f32_partials_us=round(t["relay_combine_f32"] * 1e3, 1),
                 direct_dispatch_us=round(t["direct_dispatch"] * 1e3, 1),
                 direct_combine_us=round(t["direct_combine"] * 1e3, 1),
                 relay_tokens_per_s=round(w.N / ((t["relay_dispatch"] + t["relay_combine"]) / 1e3), 1),
                 relay_dispatch_gbs=round(bd / (t["relay_dispatch"] / 1e3) / 1e9, 1),
-                relay_combine_gbs=round(bc / (t["relay_combine"] / 1e3) / 1e9, 1))
+                relay_combine_gbs=round(bc / (t["relay_combine"] / 1e3) / 1e9, 1),
+                relay_combine_f32_partials_gbs=round(
+                    bytes_relay_combine(w.N, w.H, w.K, w.R, rows, grows, partial_f32=True) /
+                    (t["relay_combine_f32"] / 1e3) / 1e9, 1))
 
 
 def cold_summary(cold, N, nbytes):

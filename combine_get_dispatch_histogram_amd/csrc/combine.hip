@@ -45,7 +45,12 @@ template <int VPL, int MAXR, int MW, int NT, int IO = kBf16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices) {
   constexpr bool kIn32 = IO == kFromF32;
   constexpr bool kOut32 = IO == kToF32;
-  constexpr int kInVec = kIn32 ? 2 : 1;          // 16-byte input vectors per 8 channels
+  // With an fp32 side the lane's 8 channels are two 4-channel quads 64
+  // lanes apart (quads 2*v0 + lane and 2*v0 + 64 + lane), so that every load
+  // and store instruction covers one contiguous run (512 B of bf16 or 1 KiB
+  // of fp32) instead of half of each 32-byte fp32 piece; the channels a
+  // wavefront covers, and each channel's order of additions, are the same.
+  constexpr bool kQuads = IO != kBf16;
   const int lane = lane_id();
   const int64_t gw = wave_index();
   const int64_t n = gw / nslices;
@@ -98,6 +103,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
   }
 
   const int nv = a.H / 8;  // groups of 8 channels
+  const int nq = a.H / 4;  // quads of 4 channels
   const uint8_t* y = reinterpret_cast<const uint8_t*>(a.y);
   const int64_t bf_row_bytes = 2 * static_cast<int64_t>(a.H);
   const int64_t in_row_bytes = (kIn32 ? 4 : 2) * static_cast<int64_t>(a.H);
@@ -131,11 +137,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
             const uint8_t* yrow = y + rows[q] * in_row_bytes;
 #pragma unroll
             for (int j = 0; j < VPL; ++j) {
-              const int v = v0 + j * kWave + lane;
-              if (v < nv) {
-#pragma unroll
-                for (int h = 0; h < kInVec; ++h)
-                  d[q][j][h] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(v) * (16 * kInVec) + 16 * h);
+              if constexpr (kQuads) {
+                const int qa = 2 * (v0 + j * kWave) + lane, qb = qa + kWave;   // this lane's two 4-channel quads
+                if constexpr (kIn32) {
+                  if (qa < nq) d[q][j][0] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(qa) * 16);
+                  if (qb < nq) d[q][j][1] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(qb) * 16);
+                } else {
+                  v2u ha{0u, 0u}, hb{0u, 0u};
+                  if (qa < nq) ha = ldb8<load_cpol(NT)>(yrow, static_cast<uint32_t>(qa) * 8);
+                  if (qb < nq) hb = ldb8<load_cpol(NT)>(yrow, static_cast<uint32_t>(qb) * 8);
+                  d[q][j][0] = v4u{ha.x, ha.y, hb.x, hb.y};
+                }
+              } else {
+                const int v = v0 + j * kWave + lane;
+                if (v < nv) d[q][j][0] = ldb16<load_cpol(NT)>(yrow, static_cast<uint32_t>(v) * 16);
               }
             }
           }
@@ -161,7 +176,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         const int v = v0 + j * kWave + lane;
-        if (v >= nv) continue;
+        const int qa = 2 * (v0 + j * kWave) + lane, qb = qa + kWave;
+        if (kQuads ? qa >= nq : v >= nv) continue;
         if (!have) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) acc[j][k] = 0.0f;
@@ -169,7 +185,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
         for (int b = 0; b < 2; ++b) {
           const uint16_t* bias = b == 0 ? a.bias0 : a.bias1;
           if (bias == nullptr) continue;
-          const v4u t = ld16(reinterpret_cast<const uint8_t*>(bias) + n * bf_row_bytes + static_cast<int64_t>(v) * 16);
+          const uint8_t* brow = reinterpret_cast<const uint8_t*>(bias) + n * bf_row_bytes;
+          v4u t;
+          if constexpr (kQuads) {
+            const uint2 ha = *reinterpret_cast<const uint2*>(brow + static_cast<int64_t>(qa) * 8);
+            const uint2 hb = qb < nq ? *reinterpret_cast<const uint2*>(brow + static_cast<int64_t>(qb) * 8) : uint2{0u, 0u};
+            t = v4u{ha.x, ha.y, hb.x, hb.y};
+          } else {
+            t = ld16(brow + static_cast<int64_t>(v) * 16);
+          }
           const float f[8] = {bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y),
                               bf16_lo(t.z), bf16_hi(t.z), bf16_lo(t.w), bf16_hi(t.w)};
 #pragma unroll
@@ -181,7 +205,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int v = v0 + j * kWave + lane;
-      if (v < nv) {
+      if constexpr (kQuads) {
+        const int qa = 2 * (v0 + j * kWave) + lane, qb = qa + kWave;
         if constexpr (kOut32) {
           const v4u o0 = have ? v4u{__float_as_uint(acc[j][0]), __float_as_uint(acc[j][1]), __float_as_uint(acc[j][2]),
                                     __float_as_uint(acc[j][3])}
@@ -189,9 +214,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int nslices
           const v4u o1 = have ? v4u{__float_as_uint(acc[j][4]), __float_as_uint(acc[j][5]), __float_as_uint(acc[j][6]),
                                     __float_as_uint(acc[j][7])}
                               : v4u{0u, 0u, 0u, 0u};
-          stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 32, o0);
-          stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(v) * 32 + 16, o1);
+          if (qa < nq) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(qa) * 16, o0);
+          if (qb < nq) stb16<store_cpol(NT)>(orow, static_cast<uint32_t>(qb) * 16, o1);
         } else {
+          const v2u o0 = have ? v2u{pack_bf16x2(acc[j][0], acc[j][1]), pack_bf16x2(acc[j][2], acc[j][3])} : v2u{0u, 0u};
+          const v2u o1 = have ? v2u{pack_bf16x2(acc[j][4], acc[j][5]), pack_bf16x2(acc[j][6], acc[j][7])} : v2u{0u, 0u};
+          if (qa < nq) stb8<store_cpol(NT)>(orow, static_cast<uint32_t>(qa) * 8, o0);
+          if (qb < nq) stb8<store_cpol(NT)>(orow, static_cast<uint32_t>(qb) * 8, o1);
+        }
+      } else if (v < nv) {
+        {
           v4u o;
           if (have) {
             o.x = pack_bf16x2(acc[j][0], acc[j][1]);
@@ -230,7 +262,14 @@ static hipError_t launch_combine_f32(const CombineArgs& a, hipStream_t st) {
   const int vpl = nv % kWave == 0 ? 4 : 8;
   const int span = vpl * kWave;
   const int nslices = (nv + span - 1) / span;
-  return vpl == 4 ? launch_combine_cfg<4, 2, 7, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 7, IO>(a, nslices, st);
+  const int nt = tuning().combine_nt >= 0 ? tuning().combine_nt & 7 : 7;
+  switch (nt) {
+    case 0: return vpl == 4 ? launch_combine_cfg<4, 2, 0, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 0, IO>(a, nslices, st);
+    case 1: return vpl == 4 ? launch_combine_cfg<4, 2, 1, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 1, IO>(a, nslices, st);
+    case 4: return vpl == 4 ? launch_combine_cfg<4, 2, 4, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 4, IO>(a, nslices, st);
+    case 5: return vpl == 4 ? launch_combine_cfg<4, 2, 5, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 5, IO>(a, nslices, st);
+    default: return vpl == 4 ? launch_combine_cfg<4, 2, 7, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 7, IO>(a, nslices, st);
+  }
 }
 
 // (vectors per lane, rows loaded per batch) pairs compiled in; register use

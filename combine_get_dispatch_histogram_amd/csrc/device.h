@@ -88,6 +88,20 @@ __device__ __forceinline__ void stb16(void* base, uint32_t off, const v4u& v) {
   __builtin_amdgcn_raw_buffer_store_b128(t, row_rsrc(base), off, 0, CPOL);
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int CPOL>
+__device__ __forceinline__ v2u ldb8(const void* base, uint32_t off) {
+  const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(row_rsrc(base), off, 0, CPOL);
+  return v2u{t.x, t.y};
+}
+
+template <int CPOL>
+__device__ __forceinline__ void stb8(void* base, uint32_t off, const v2u& v) {
+  const u32x2 t = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(t, row_rsrc(base), off, 0, CPOL);
+}
+
 // Wavefront index of the calling lane over the grid, computed from
 // wave-uniform values only (so the compiler keeps it in scalar registers).
 __device__ __forceinline__ int64_t wave_index() {

@@ -48,6 +48,17 @@ def test_layout_and_notify_bytes():
         (R + 1) * 4 + S * E * 4 + E * 4
 
 
+def test_relay_combine_bytes():
+    # 64 ranks in 8 groups: received rows read (2H) into group partials written
+    # and read once (2H bf16 or 4H fp32, plus a 32-byte head row each), the
+    # token rows written (2H) after reading one group-row index per group
+    Nn, Rr, rows, grows = 16384, 64, 125825, 86699
+    base = grows * 32 + rows * 2 * H + Nn * (Rr // 8) * 4 + Nn * 2 * H
+    w = rows * 4 * K + 2 * grows * 4 * K + Nn * 4 * K
+    assert bench.bytes_relay_combine(Nn, H, K, Rr, rows, grows) == base + 2 * grows * 2 * H + w
+    assert bench.bytes_relay_combine(Nn, H, K, Rr, rows, grows, partial_f32=True) == base + 2 * grows * 4 * H + w
+
+
 def test_ll_bytes():
     # FP8 message: 16-byte header + H codes + H/128 fp32 scales = 7408 bytes
     msgs, toks, Hh, L, Rr = 1024, 930, 7168, 8, 32
