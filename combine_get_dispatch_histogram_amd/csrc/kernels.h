@@ -108,6 +108,7 @@ struct PackArgs {
   const int32_t* rpm = nullptr;       // [S][R] inclusive rows per rank from sources 0..s
   const uint8_t* in_rank = nullptr;   // [S*T][R]
   int rec_waves = 0, rec_blocks = 0;  // set by launch_pack
+  int rec_parts = 1;                  // record wavefronts per (source, rank), each taking every rec_parts-th part
   int rec_last = 0;                   // record workgroups at the end of the grid instead of the front
 };
 hipError_t launch_pack(const PackArgs& a, hipStream_t st);

@@ -44,24 +44,34 @@ __device__ __forceinline__ int group_rank_base(const int32_t* group_off, int gro
 constexpr int kRecordMaxTokens = 1024;   // tokens per source for the record wavefronts
 constexpr int kRecordChunks = kRecordMaxTokens / kWave;
 constexpr int kRecordBatch = 8;          // store instructions per batch of gathered records
+constexpr int kRecordMaxParts = 16;      // record wavefronts per (source, rank) at most
 
-// Records of rank r's rows from source s (wavefront (s, r) = mw): the rows
+// Records of rank r's rows from source s (wavefronts (s, r, p), p <
+// rec_parts, mw = (s * R + r) * rec_parts + p): the rows
 // [off[r] + rpm[s-1][r], off[r] + rpm[s][r]) hold source s's tokens that go
 // to r, in token order.  Every membership byte of the column is loaded at
-// once (one load per lane per 64-token chunk, all in flight), ballots list
-// the members' tokens in this wavefront's LDS slot, and the top-k entries
-// and weights are gathered kRecordBatch store instructions at a time (all
-// loads of a batch issued before its stores): lane (j, k) writes entry k of
-// row j, so each store covers 64 / K whole rows.  The chain is one round
-// trip for the membership plus one per batch of 8 * (64 / K) rows.  The
+// once (one load per lane per 64-token chunk, all in flight) and ballots
+// list the members' tokens in this wavefront's LDS slot.  The members form
+// parts of kRecordBatch * (64 / K) rows; wavefront p takes parts p,
+// p + rec_parts, ... and gathers each part's top-k entries and weights with
+// every load in flight before its stores: lane (j, k) writes entry k of row
+// j, so each store covers 64 / K whole rows.  A wavefront's chain is one
+// round trip for the membership plus one per part it takes (the host picks
+// rec_parts from the rows a rank can expect, e.g. 8 wavefronts per
+// (source, rank) at 8 ranks: one (source, rank) pair holds ~340 rows, whose
+// six sequential batches had made the records outlast an FP8 payload).  The
 // records are written with the streaming (non-temporal) policy: their lines
 // are whole, and as ordinary dirty lines they cost the 64-rank FP8 dispatch
 // ~27 us (measured: 216.6 -> 189.6 us).
 __device__ __forceinline__ void pack_records(const PackArgs& a, int mw, int32_t* lst) {
   const int lane = lane_id();
   const int R = a.R, T = a.T, K = a.K;
-  const int s = mw / R;
-  const int r = mw - s * R;
+  const int P = a.rec_parts;
+  const int part = mw % P;
+  const int sr = mw / P;
+  const int s = sr / R;
+  const int r = sr - s * R;
+  const int part_rows = kRecordBatch * (kWave / (K > 0 ? K : 1));   // rows of one part (one batch)
   const int row0 = a.off[r] + (s > 0 ? a.rpm[(s - 1) * R + r] : 0);   // receive row of the first member
   const uint8_t* col = a.in_rank + static_cast<int64_t>(s) * T * R + r;
   const int nch = (T + kWave - 1) / kWave;
@@ -81,7 +91,8 @@ __device__ __forceinline__ void pack_records(const PackArgs& a, int mw, int32_t*
       const int t = c * kWave + lane;
       if (member) {
         lst[pos] = t;
-        if (row0 + pos < a.capacity) __builtin_nontemporal_store(t, a.recv_src_idx + row0 + pos);
+        if ((pos / part_rows) % P == part && row0 + pos < a.capacity)   // this wavefront's parts
+          __builtin_nontemporal_store(t, a.recv_src_idx + row0 + pos);
       }
       nm += __popcll(m);
     }
@@ -96,7 +107,7 @@ __device__ __forceinline__ void pack_records(const PackArgs& a, int mw, int32_t*
   const bool act = j_l < rows_per;
   const int64_t lo = static_cast<int64_t>(r) * a.L;
   const bool wts = a.recv_topk_weights != nullptr;
-  for (int j0 = 0; j0 < nm; j0 += kRecordBatch * rows_per) {
+  for (int j0 = part * part_rows; j0 < nm; j0 += P * part_rows) {   // this wavefront's parts, one batch each
     int64_t e[kRecordBatch];
     float wv[kRecordBatch];
 #pragma unroll
@@ -467,7 +478,16 @@ hipError_t launch_pack(const PackArgs& a_in, hipStream_t st) {
   const bool cast_tpb = a.kind == kPackCastFp8 && tu.cast_tpb > 0;
   if (a.meta && a.group_off == nullptr && a.src_tok == nullptr && a.count == nullptr && a.rpm != nullptr &&
       a.in_rank != nullptr && !cast_tpb && tu.pack_records != 0 && a.T <= kRecordMaxTokens) {
-    a.rec_waves = a.S * a.R;
+    // parts per (source, rank) from the rows a rank can expect: a source's T
+    // tokens reach at most min(K, R) ranks each, so a rank expects up to
+    // T * min(K, R) / R rows from it (every wavefront loops over its parts,
+    // so any routing is covered)
+    const int part_rows = kRecordBatch * (kWave / (a.K > 0 ? a.K : 1));
+    const int64_t expect = (static_cast<int64_t>(a.T) * (a.K < a.R ? a.K : a.R) + a.R - 1) / a.R;
+    int parts = static_cast<int>((expect + part_rows - 1) / part_rows);
+    parts = parts < 1 ? 1 : (parts > kRecordMaxParts ? kRecordMaxParts : parts);
+    a.rec_parts = parts;
+    a.rec_waves = a.S * a.R * parts;
     a.rec_blocks = (a.rec_waves + 3) / 4;
     a.rec_last = tu.pack_records == 2 ? 1 : 0;
   } else {
