@@ -201,7 +201,7 @@ const Tuning& tuning() {
                            env_int("MIEP_LLC_SLICES", 0),   env_int("MIEP_LLC_NT", -1),
                            env_int("MIEP_LL_NT", -1),       env_int("MIEP_PACK_RECORDS", -1),
                            env_int("MIEP_LL_TPB", 0),       env_int("MIEP_LL_COUNT_SRC", -1),
-                           env_int("MIEP_NOTIFY_CHAN", -1)};
+                           env_int("MIEP_NOTIFY_CHAN", -1), env_int("MIEP_BIAS_NT", -1)};
   return t;
 }
 }  // namespace miep

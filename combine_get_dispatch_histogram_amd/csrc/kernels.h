@@ -135,6 +135,7 @@ struct CombineArgs {
   // Row element types (the two-level combine's fp32 partials): y is fp32
   // [cap][H] when in_f32, out is fp32 [N][H] when out_f32 (no rounding).
   int in_f32 = 0, out_f32 = 0;
+  int bias_nt = 0;           // bias rows loaded non-temporally (set by launch_combine)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
 
@@ -198,7 +199,8 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // (MIEP_PACK_VPL, MIEP_PACK_SLICES, MIEP_COMBINE_VPL, MIEP_COMBINE_SLICES,
 // MIEP_COMBINE_MAXR, MIEP_PACK_NT, MIEP_COMBINE_NT, MIEP_LL_SPLIT,
 // MIEP_LL_VPL, MIEP_CAST_TPB, MIEP_LLC_VPL, MIEP_LLC_SLICES, MIEP_LLC_NT,
-// MIEP_LL_NT, MIEP_PACK_RECORDS, MIEP_LL_TPB, MIEP_LL_COUNT_SRC):
+// MIEP_LL_NT, MIEP_PACK_RECORDS, MIEP_LL_TPB, MIEP_LL_COUNT_SRC,
+// MIEP_NOTIFY_CHAN, MIEP_BIAS_NT):
 // used by geometry sweeps, never required.
 // combine_maxr: source rows whose loads are issued together.
 // pack_nt / combine_nt: cache policy of the row traffic, bit 0 =
@@ -222,10 +224,13 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // (l, s) block instead of one per source (-1, the default).  notify_chan: 0
 // runs the per-source notify everywhere, n > 0 caps the channels per
 // workgroup of the channel-group notify (-1, the default: as many whole
-// channels as fit in one wavefront, where supported).
+// channels as fit in one wavefront, where supported).  bias_nt: 1 loads the
+// combine's bias rows non-temporally, 0 with the default policy (-1, the
+// default: non-temporally when a bias is larger than half the 256 MiB
+// last-level cache, which it then could not hold anyway).
 struct Tuning {
   int pack_vpl, pack_slices, combine_vpl, combine_slices, combine_maxr, pack_nt, combine_nt, ll_split, ll_vpl,
-      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt, pack_records, ll_tpb, ll_count_src, notify_chan;
+      cast_tpb, llc_vpl, llc_slices, llc_nt, ll_nt, pack_records, ll_tpb, ll_count_src, notify_chan, bias_nt;
 };
 const Tuning& tuning();
 

@@ -109,6 +109,26 @@ def test_combine_bias_normal_single_tensor():
     assert np.array_equal(u16(cx2), rc2["combined_x"])
 
 
+def test_combine_bias_streamed():
+    """Two bias rows of 137.6 MB each (9600 tokens x hidden 7168), past the
+    128 MiB above which the combine loads a bias non-temporally: bit-exact
+    as with the default policy."""
+    w = wl.NormalWorkload("bias-stream", S=8, T=1200, H=7168, E=64, R=8, K=4, C=24)
+    assert w.N * 2 * w.H > 128 << 20
+    say("combine bias streamed", w.name)
+    inp = wl.normal_inputs(w, 5)
+    _, rtw, h, ref = _dispatch(w, inp["x"], inp["topk_idx"], inp["topk_weights"])
+    g = torch.Generator().manual_seed(23)
+    y = wl.activations(h.recv_capacity, w.H, g)
+    b0 = wl.activations(w.N, w.H, g)
+    b1 = wl.activations(w.N, w.H, g)
+    cx, cw = miep.combine(y.to(DEV), h, rtw, bias=(b0.to(DEV), b1.to(DEV)))
+    rc = oracle.combine(wl.bf16_bits(y), ref["recv_topk_weights"], ref["send_head"], ref["recv_rank_offset"], S=w.S,
+                        bias0=wl.bf16_bits(b0), bias1=wl.bf16_bits(b1))
+    assert np.array_equal(u16(cx), rc["combined_x"])
+    assert np.array_equal(npy(cw).view(np.uint32), rc["combined_topk_weights"].view(np.uint32))
+
+
 # --------------------------------------------------------------------------- rank mask
 def test_mask_helpers():
     say("mask helpers")
