@@ -100,6 +100,8 @@ SMALL = [
     ("rec-1025", 2, 1025, 64, 64, 16, 8, 24, 1),     # one token more: the records go back inline
     ("rec-k64", 3, 130, 64, 256, 8, 64, 5, 1),       # top-64: one record row per store instruction
     ("rec-k20-r64", 2, 200, 64, 128, 64, 20, 7, 1),  # 3 rows per store, 64 ranks, four 64-token chunks
+    ("rec-parts", 3, 1000, 64, 64, 8, 16, 24, 1),    # 16 record wavefronts per (source, rank), ~29 parts: two each
+    ("rec-parts-r16", 2, 700, 64, 128, 16, 12, 24, 1),  # 14 record wavefronts, parts of 40 rows, ragged last
     ("chan-odd", 3, 210, 64, 64, 8, 4, 10, 1),       # channel groups of 3 x 21 tokens: odd first token (half piece)
     ("chan-2wave", 2, 512, 64, 64, 32, 6, 4, 1),     # 128-token channels: two wavefronts per workgroup
     ("chan-many-src", 70, 32, 64, 512, 8, 6, 4, 1),  # > 64 sources, > 4 experts per workgroup
