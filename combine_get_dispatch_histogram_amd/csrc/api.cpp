@@ -31,11 +31,17 @@ miep_status hip_status(hipError_t e, const char* what) {
   return fail(MIEP_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Cache-policy code of the relay's packs and combines: non-temporal loads
-// and stores at device scope (measured on the 64-rank FP8 relay: dispatch
-// 464 -> 454 us, two-level combine 784 -> 750 us against the direct path's
-// codes).
+// Cache-policy codes of the relay's launches.  The forwarding pack and the
+// group-level combine: non-temporal loads and stores at device scope
+// (measured on the 64-rank FP8 relay: dispatch 464 -> 454 us, two-level
+// combine 784 -> 750 us against the direct path's codes).  Per launch, the
+// first hop keeps plain loads of x (its group rows still stream out) and the
+// token-level combine keeps device-scope write-back stores for its output,
+// the direct pack's and combine's codes (relay dispatch 430 -> 424 us,
+// two-level combine 739 -> 715 us).
 constexpr int kRelayCpol = 7;
+constexpr int kRelayHop1Cpol = 6;
+constexpr int kRelayTokenCpol = 5;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -449,7 +455,7 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
   a1.off = rh->recv_rdma_offset;
   a1.capacity = rh->rdma_capacity;
   a1.meta = 0;
-  a1.cpol = kRelayCpol;
+  a1.cpol = kRelayHop1Cpol;
   e = miep::launch_pack(a1, s);
   if (e != hipSuccess) return hip_status(e, "relay pack launch");
   // second hop: every group row to the group's receiving ranks, with metadata
@@ -496,7 +502,7 @@ miep_status miep_relay_cached_dispatch(const miep_problem* p, const void* x, int
   a1.off = rh->recv_rdma_offset;
   a1.capacity = rh->rdma_capacity;
   a1.meta = 0;
-  a1.cpol = kRelayCpol;
+  a1.cpol = kRelayHop1Cpol;
   hipError_t e = miep::launch_pack(a1, s);
   if (e != hipSuccess) return hip_status(e, "relay pack launch");
   const int fwd_kind = x_kind == MIEP_X_BF16 ? MIEP_X_BF16 : MIEP_X_FP8;
@@ -569,7 +575,7 @@ miep_status miep_relay_combine(const miep_problem* p, const uint16_t* y, const f
   c2.off = rh->recv_rdma_offset;
   c2.out = combined_x;
   c2.out_w = combined_topk_weights;
-  c2.cpol = kRelayCpol;
+  c2.cpol = kRelayTokenCpol;
   return hip_status(miep::launch_combine(c2, s), "relay combine (token level) launch");
 }
 

@@ -210,8 +210,9 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t 
 // back) pack 6 (plain loads of x, non-temporal device-scope stores) and
 // combine 5 (non-temporal loads of the expert outputs, device-scope
 // stores); setting both or neither of the non-temporal bits costs ~20% in
-// either kernel.  The relay's launches take 7 (its group rows are written
-// once and read once more right after).  ll_split: workgroups per
+// either kernel.  The relay's forwarding pack and group-level combine take 7
+// (its group rows are written once and read once more right after); its
+// first hop and token-level combine keep the direct path's 6 and 5.  ll_split: workgroups per
 // low-latency (expert, source) block.  cast_tpb: fused FP8 cast with one
 // token per workgroup (1), or 1 KiB slices (0 or -1, the default).
 // llc_vpl / llc_slices / llc_nt: low-latency combine vectors per lane,
