@@ -51,7 +51,7 @@ def _routing(rng, N, E, K, mask_p, dup_p, oob_p):
     return idx
 
 
-def _normal_cases(n=24, seed=2024):
+def _normal_cases(n=64, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -71,7 +71,7 @@ def _normal_cases(n=24, seed=2024):
     return out
 
 
-def _channel_group_cases(n=16, seed=77):
+def _channel_group_cases(n=40, seed=77):
     """Shapes of the channel-group notify (8/16/32/64 ranks, T * R a multiple of 16, channels of up to 256
     tokens): channel groups that start on odd tokens, many sources, one-token channels, multi-wavefront
     channels."""
@@ -158,7 +158,7 @@ def test_fuzz_normal(case):
     assert np.array_equal(npy(cw).view(np.uint32), rc["combined_topk_weights"].view(np.uint32))
 
 
-def _ll_cases(n=12, seed=7):
+def _ll_cases(n=30, seed=7):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -212,7 +212,7 @@ def test_fuzz_low_latency(case):
     assert np.array_equal(u16(cx), rc["combined_x"])
 
 
-def _relay_cases(n=8, seed=99):
+def _relay_cases(n=16, seed=99):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
