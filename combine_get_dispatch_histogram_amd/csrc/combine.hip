@@ -246,6 +246,7 @@ template <int VPL, int MAXR, int NT, int IO = kBf16>
 static hipError_t launch_combine_cfg(const CombineArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
   const int64_t blocks = (waves + 3) / 4;
+  if (blocks > max_blocks(256)) return hipErrorInvalidConfiguration;
   if (a.R <= 64)
     hipLaunchKernelGGL((combine_kernel<VPL, MAXR, 1, NT, IO>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                        a, nslices);

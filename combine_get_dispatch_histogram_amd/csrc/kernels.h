@@ -9,6 +9,10 @@
 namespace miep {
 
 constexpr int kWave = 64;          // CDNA wavefront width
+// A grid dimension counts its work-items in 32 bits: the largest number of
+// workgroups of `threads` threads one 1-D launch may ask for.  Launches past
+// it return hipErrorInvalidConfiguration instead of a truncated grid.
+constexpr int64_t max_blocks(int64_t threads) { return ((int64_t(1) << 32) - 1) / threads; }
 constexpr int kFp8Group = 128;     // channels per FP8 scale
 constexpr int kMaxRanks = 256;     // logical ranks supported by one call
 constexpr int kMaxExperts = 8192;  // experts (LDS histogram bound)

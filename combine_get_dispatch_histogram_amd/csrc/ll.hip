@@ -523,6 +523,7 @@ static hipError_t launch_ll_combine_cfg(const LLCombineArgs& a, int nslices, hip
   const int P = kWave / a.K;
   const int64_t groups = (static_cast<int64_t>(a.R) * a.T + P - 1) / P;
   const int64_t blocks = (groups * nslices + 3) / 4;
+  if (blocks > max_blocks(256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((ll_combine_kernel<VPL, MAXR, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                      nslices);
   return hipGetLastError();

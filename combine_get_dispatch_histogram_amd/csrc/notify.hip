@@ -902,6 +902,7 @@ __global__ void fill_zero_kernel(int32_t* p, int64_t n) {
 
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
+  if ((n + 255) / 256 > max_blocks(256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }

@@ -408,6 +408,7 @@ template <int VPL, int NT>
 static hipError_t launch_pack_cast_vpl(const PackArgs& a, hipStream_t st) {
   const int np = a.H / 16;   // pairs of 16-byte input vectors
   const int waves = (np + kWave * VPL - 1) / (kWave * VPL);
+  if (a.N > max_blocks(static_cast<int64_t>(waves) * kWave)) return hipErrorInvalidConfiguration;
   if (a.R <= 64)
     hipLaunchKernelGGL((pack_cast_kernel<VPL, 1, NT>), dim3(static_cast<unsigned>(a.N)), dim3(waves * kWave), 0, st,
                        a);
@@ -432,6 +433,7 @@ template <int KIND, int VPL, int NT>
 static hipError_t launch_pack_vpl(const PackArgs& a, int nslices, hipStream_t st) {
   const int64_t waves = a.N * nslices;
   const int64_t blocks = (waves + 3) / 4 + a.rec_blocks;
+  if (blocks > max_blocks(256)) return hipErrorInvalidConfiguration;
   if (a.R <= 64)
     hipLaunchKernelGGL((pack_kernel<KIND, VPL, 1, NT>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a,
                        nslices);
@@ -486,8 +488,9 @@ hipError_t launch_pack(const PackArgs& a_in, hipStream_t st) {
     const int64_t expect = (static_cast<int64_t>(a.T) * (a.K < a.R ? a.K : a.R) + a.R - 1) / a.R;
     int parts = static_cast<int>((expect + part_rows - 1) / part_rows);
     parts = parts < 1 ? 1 : (parts > kRecordMaxParts ? kRecordMaxParts : parts);
+    const int64_t rw = static_cast<int64_t>(a.S) * a.R * parts;
     a.rec_parts = parts;
-    a.rec_waves = a.S * a.R * parts;
+    a.rec_waves = rw <= (int64_t(1) << 30) ? static_cast<int>(rw) : 0;   // else the payload wavefronts write them
     a.rec_blocks = (a.rec_waves + 3) / 4;
     a.rec_last = tu.pack_records == 2 ? 1 : 0;
   } else {

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void relay_meta_kernel(RelayMetaArgs a) {
 hipError_t launch_relay_meta(const RelayMetaArgs& a, hipStream_t st) {
   const int64_t n = a.N * a.G;
   if (n == 0) return hipSuccess;
+  if ((n + 255) / 256 > max_blocks(256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(relay_meta_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
