@@ -70,6 +70,16 @@ miep_status check_problem(const miep_problem* p) {
   return ok();
 }
 
+// A dispatch's receive rows (and their prefixes in the handle) are int32: a
+// token reaches at most min(K, R) ranks, so N * min(K, R) bounds the total.
+miep_status check_rows(const miep_problem* p) {
+  const int64_t N = static_cast<int64_t>(p->num_src) * p->num_tokens;
+  const int64_t fan = p->num_topk < p->num_ranks ? p->num_topk : p->num_ranks;
+  if (N * fan > (1ll << 31) - 1)
+    return fail(MIEP_EUNSUPPORTED, "num_src * num_tokens * min(num_topk, num_ranks) > 2^31-1 (int32 receive rows)");
+  return ok();
+}
+
 static_assert(miep::kStatusCapacity == MIEP_ECAPACITY, "device status code must match the header");
 
 // use_ue8m0 needs power-of-two scales from the fused cast, and somewhere to put the bytes
@@ -262,6 +272,7 @@ miep_status miep_dispatch(const miep_problem* p, const void* x, int32_t x_kind, 
                           float* recv_topk_weights, int32_t* num_recv_tokens_per_expert, int32_t* status,
                           const miep_handle* h, void* stream) {
   miep_status st = check_problem(p);
+  if (st == MIEP_OK) st = check_rows(p);
   if (st != MIEP_OK) return st;
   if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
   if ((st = check_handle(p, h, true)) != MIEP_OK) return st;
@@ -383,6 +394,7 @@ miep_status miep_relay_dispatch(const miep_problem* p, const void* x, int32_t x_
                                 float* recv_topk_weights, int32_t* num_recv_tokens_per_expert, int32_t* status,
                                 const miep_handle* h, const miep_relay_handle* rh, void* stream) {
   miep_status st = check_problem(p);
+  if (st == MIEP_OK) st = check_rows(p);
   if (st != MIEP_OK) return st;
   if ((st = check_payload(p, x, x_kind, x_scales)) != MIEP_OK) return st;
   if ((st = check_handle(p, h, true)) != MIEP_OK) return st;

@@ -65,7 +65,8 @@ typedef struct miep_problem {
   int32_t num_src;          /* S: source partitions (the sending ranks), <= 2^20         */
   int32_t num_tokens;       /* T: tokens per source partition                             */
   int32_t hidden;           /* H: channels per token, <= 2^24                             */
-  int32_t num_topk;         /* K: experts per token                                       */
+  int32_t num_topk;         /* K: experts per token, <= 64; a dispatch needs
+                               N * min(K, R) <= 2^31-1 (int32 receive rows)                */
   int32_t num_experts;      /* E: experts; expert e lives on rank e / (E / R)              */
   int32_t num_ranks;        /* R: receiving ranks, 1..256; R > 8 needs R % 8 == 0          */
   int32_t num_channels;     /* C: channels splitting each source's tokens (ceil(T/C) each), <= 1024 */

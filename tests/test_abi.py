@@ -112,6 +112,12 @@ def test_dispatch_validation(lib):
     assert _dispatch(lib, p, h, kind=0, round_scale=1, use_ue8m0=1, ue=16) == _lib.MIEP_EINVAL
     assert _dispatch(lib, p, h, kind=2, recv_x_scales=16, round_scale=1, use_ue8m0=1) == _lib.MIEP_EINVAL
     assert "ue8m0" in lib.miep_last_error().decode()
+    # receive rows are int32: N * min(K, R) must stay below 2^31 (here 2^28 tokens reach up to 8 ranks each)
+    big = _problem(num_src=1 << 10, num_tokens=1 << 18, num_topk=8, num_ranks=8, num_experts=64)
+    assert _dispatch(lib, big, h) == _lib.MIEP_EUNSUPPORTED
+    assert "receive rows" in lib.miep_last_error().decode()
+    assert _dispatch(lib, _problem(num_src=1 << 10, num_tokens=1 << 18, num_topk=7, num_ranks=8, num_experts=64),
+                     h, x=8) == _lib.MIEP_EUNSUPPORTED and "aligned" in lib.miep_last_error().decode()
     # negative capacity
     hneg = _lib.HandleC(16, 16, 16, 16, 16, 16, 16, -1)
     rc = lib.miep_cached_dispatch(ctypes.byref(p), 16, 0, None, 0, 0, ctypes.byref(hneg), 16, None, None, None)
