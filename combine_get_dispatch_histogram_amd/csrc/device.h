@@ -37,12 +37,16 @@ __host__ __device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
 
 // Inclusive scan across the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(v, d, kWave);
-    if (l >= d) v += o;
-  }
+  // every lane active: DPP row shifts by 1, 2, 4 and 8 (lanes shifted in
+  // from outside the row read 0) scan each row of 16 lanes, then the row
+  // broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and
+  // 3) carry the lower rows' totals up; no LDS round trips
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);    // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);    // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);    // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);    // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
   return v;
 }
 
@@ -143,11 +147,17 @@ __device__ __forceinline__ uint8_t ue8m0_byte(float pow2_scale) {
   return static_cast<uint8_t>(__float_as_uint(pow2_scale) >> 23);
 }
 
-// Max over the 8 lanes that hold one 128-channel group (16 channels each).
+// Max over the 8 lanes that hold one 128-channel group (16 channels each),
+// every lane active: DPP quad permutes [1,0,3,2] and [2,3,0,1], then the
+// half-row mirror (lane i of each 8 reads lane 7 - i), no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float group8_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, 8));
-  v = fmaxf(v, __shfl_xor(v, 2, 8));
-  v = fmaxf(v, __shfl_xor(v, 4, 8));
+  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
   return v;
 }
 

@@ -183,9 +183,7 @@ __global__ __launch_bounds__(TPB) void ll_send_kernel(LLArgs a) {
   const int n = cnt < a.M ? cnt : a.M;
   int part = lane < s ? p_raw : 0;
   for (int q = lane + kWave; q < s; q += kWave) part += a.msg_count[l * a.R + q];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
-  const int begin = part;
+  const int begin = readlane(wave_inclusive_scan(part), kWave - 1);
   if (tid == 0 && blockIdx.y == 0) {             // once per (l, s), not per split workgroup
     a.layout_range[l * a.R + s] = (static_cast<int64_t>(begin) << 32) | static_cast<int64_t>(static_cast<uint32_t>(n));
     if (s == a.R - 1) {
