@@ -18,8 +18,8 @@
 // Row element types (IO): kBf16 reads bf16 rows and writes bf16 rows;
 // kToF32 writes the fp32 sums unrounded (the two-level combine's first
 // level with fp32 partials); kFromF32 reads fp32 rows (its second level).
-// A lane always owns 8 consecutive channels: one 16-byte vector of bf16 or
-// two of fp32.
+// A lane owns 8 channels: one 16-byte vector of bf16 rows, or with an fp32
+// side two 4-channel quads 64 lanes apart (see the kernel).
 #include "device.h"
 #include "kernels.h"
 

@@ -22,7 +22,7 @@
 // entries the row's rank owns and their weights) are not written by the
 // payload wavefronts, where each would leave as a scattered partial-line
 // piece per (token, destination): extra wavefronts at the front of the same
-// grid, one per (source, rank) pair, walk the source's tokens in order and
+// grid, a few per (source, rank) pair, walk the source's tokens in order and
 // write the rank's consecutive receive rows with coalesced stores, while
 // the payload wavefronts run.
 #include "device.h"
@@ -472,7 +472,7 @@ hipError_t launch_pack(const PackArgs& a_in, hipStream_t st) {
   if (a_in.N == 0) return hipSuccess;
   const Tuning& tu = tuning();
   PackArgs a = a_in;
-  // record wavefronts, one per (source, rank), for a fresh direct dispatch
+  // record wavefronts, rec_parts per (source, rank), for a fresh direct dispatch
   // whose sources hold at most kRecordMaxTokens tokens (a record wavefront
   // walks its source in 64-token chunks); forwarded group rows, longer
   // sources and the one-token-per-workgroup cast keep the records in their
