@@ -76,6 +76,42 @@ __device__ __forceinline__ int ll_slot_scan(const LLArgs& a, int l, int s, int32
   const int64_t* idx = a.topk_idx + static_cast<int64_t>(s) * a.T * a.K;
   // a masked destination is not sent to, a masked source is not received from
   const bool masked = a.mask != nullptr && (a.mask[a.d] != 0 || a.mask[s] != 0);
+  if (a.T <= TPB) {
+    // one chunk: every thread sums the wavefront totals itself (two
+    // barriers: the totals, then the slot list)
+    const int t = tid;
+    uint64_t kmask = 0;
+    if (t < a.T && !masked) {
+      const int64_t* row = idx + static_cast<int64_t>(t) * a.K;
+      for (int k0 = 0; k0 < a.K; k0 += 8) {
+        int64_t e8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e8[j] = k0 + j < a.K ? row[k0 + j] : -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kmask |= static_cast<uint64_t>(e8[j] == target) << (k0 + j);
+      }
+    }
+    const int cnt = __popcll(kmask);
+    const int inc = wave_inclusive_scan(cnt);
+    if (lane == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    int tot = 0, before = 0;
+#pragma unroll
+    for (int q = 0; q < TPB / kWave; ++q) {
+      const int v = wsum[q];
+      tot += v;
+      before += q < w ? v : 0;
+    }
+    if (slot_tok != nullptr) {
+      int j = before + inc - cnt;
+      for (uint64_t km = kmask; km != 0; km &= km - 1) {
+        if (j < a.M) slot_tok[j] = t;
+        ++j;
+      }
+    }
+    __syncthreads();
+    return tot;
+  }
   // the carry is first read after the first barrier of the loop, so its
   // reset needs no barrier of its own (the top-k loads go out at once)
   if (tid == 0) *carry_s = 0;
