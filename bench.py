@@ -778,12 +778,6 @@ def main():
     import combine_get_dispatch_histogram_amd as miep
     from combine_get_dispatch_histogram_amd import workloads as wl
 
-    if args.ll_only:
-        print(json.dumps({"ll": run_ll(torch, miep, wl, 20)}), flush=True)
-        return
-    if args.relay_only:
-        print(json.dumps({"large_fp8_relay": run_relay(torch, miep, wl, 5)}), flush=True)
-        return
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -792,6 +786,12 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.ll_only:
+        print(json.dumps({"ll": run_ll(torch, miep, wl, 20)}), flush=True)
+        return
+    if args.relay_only:
+        print(json.dumps({"large_fp8_relay": run_relay(torch, miep, wl, 5)}), flush=True)
+        return
     if args.only_warm or args.only_cold:
         r = run_normal(torch, miep, wl, args.steps, args.warmup, "warm" if args.only_warm else "cold")
         if args.only_warm:
