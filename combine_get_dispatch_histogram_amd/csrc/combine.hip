@@ -258,23 +258,34 @@ static hipError_t launch_combine_cfg(const CombineArgs& a, int nslices, hipStrea
   return hipGetLastError();
 }
 
-// The two-level combine with fp32 partials: one geometry, the relay's
-// cache-policy code (non-temporal loads and stores at device scope), and 4
-// channel groups per lane as the bf16 group level (8 for ragged rows).
+// The two-level combine with fp32 partials: the relay's cache-policy code
+// (non-temporal loads and stores at device scope).  Geometry per level,
+// measured on the 64-rank relay (two-level combine 1,217 -> 1,171 us
+// against 4 groups per lane with 2 rows in flight for both): the group
+// level (bf16 in, fp32 out) 2 channel groups per lane with 4 rows in
+// flight, the token level (fp32 in) 1 with 8 rows; ragged rows 8 with 2.
+template <int VPL, int MAXR, int IO>
+static hipError_t launch_combine_f32_cfg(const CombineArgs& a, int nslices, int nt, hipStream_t st) {
+  switch (nt) {
+    case 0: return launch_combine_cfg<VPL, MAXR, 0, IO>(a, nslices, st);
+    case 1: return launch_combine_cfg<VPL, MAXR, 1, IO>(a, nslices, st);
+    case 4: return launch_combine_cfg<VPL, MAXR, 4, IO>(a, nslices, st);
+    case 5: return launch_combine_cfg<VPL, MAXR, 5, IO>(a, nslices, st);
+    default: return launch_combine_cfg<VPL, MAXR, 7, IO>(a, nslices, st);
+  }
+}
+
 template <int IO>
 static hipError_t launch_combine_f32(const CombineArgs& a, hipStream_t st) {
   const int nv = a.H / 8;
-  const int vpl = nv % kWave == 0 ? 4 : 8;
+  const bool ragged = nv % kWave != 0;
+  const int vpl = ragged ? 8 : (IO == kToF32 ? 2 : 1);
   const int span = vpl * kWave;
   const int nslices = (nv + span - 1) / span;
   const int nt = tuning().combine_nt >= 0 ? tuning().combine_nt & 7 : 7;
-  switch (nt) {
-    case 0: return vpl == 4 ? launch_combine_cfg<4, 2, 0, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 0, IO>(a, nslices, st);
-    case 1: return vpl == 4 ? launch_combine_cfg<4, 2, 1, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 1, IO>(a, nslices, st);
-    case 4: return vpl == 4 ? launch_combine_cfg<4, 2, 4, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 4, IO>(a, nslices, st);
-    case 5: return vpl == 4 ? launch_combine_cfg<4, 2, 5, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 5, IO>(a, nslices, st);
-    default: return vpl == 4 ? launch_combine_cfg<4, 2, 7, IO>(a, nslices, st) : launch_combine_cfg<8, 2, 7, IO>(a, nslices, st);
-  }
+  if (ragged) return launch_combine_f32_cfg<8, 2, IO>(a, nslices, nt, st);
+  if constexpr (IO == kToF32) return launch_combine_f32_cfg<2, 4, IO>(a, nslices, nt, st);
+  else return launch_combine_f32_cfg<1, 8, IO>(a, nslices, nt, st);
 }
 
 // (vectors per lane, rows loaded per batch) pairs compiled in; register use
